@@ -1,0 +1,950 @@
+// Streaming engine of the layer-streamed trainer (MegaTrain summary page, 核心方法 and 方法步骤详情).
+//
+// Host memory owns every persistent tensor: fp32 masters, Adam moments, fp32 accumulated
+// gradients and a low-precision, layer-contiguous image whose sub-tensors are 4 KiB aligned so a
+// layer travels as one DMA burst (技术新颖性: layer-contiguous memory tiling). The GPU holds only
+// the template pool's working memory: two weight slots (the GPU-domain double buffer), a head
+// buffer, the checkpoint store (h every K layers), the activation store of one block, and two
+// gradient buffers.
+//
+// Three HIP streams (核心方法: compute, weight-transfer and gradient-transfer streams) are ordered
+// by events only (技术新颖性: weight-ready, backward-done and buffer-free events instead of host
+// barriers); nothing is captured into a graph, every StreamIn-Bind-Compute-Offload step is issued
+// explicitly:
+//   * h2d stream: wait buffer_free[slot] -> copy layer image into slot -> record weight_ready[slot]
+//   * compute   : wait weight_ready[slot] -> layer kernels -> record buffer_free[slot]
+//   * backward  : wait grad_free[g] -> layer backward into grad buffer g -> record backward_done[g]
+//   * d2h stream: wait backward_done[g] -> copy grad buffer to host -> record grad_free[g]
+//
+// Schedule of one forward_backward (phases 1-3 of the training step; block loop reading: block b
+// covers layers bK+1 .. min((b+1)K, L), checkpoints are h_0, h_K, h_2K, ... and h_L):
+//   FWD 1..L, HEAD (loss anchor), then for b = last .. 0: RECOMP layers of b in forward order,
+//   BWD layers of b in reverse order. A layer still resident in a slot is not streamed again.
+// Every micro-batch of the call is resident at once and processed by each resident layer
+// (layer-major order): GEMMs run over all T = batch*seq tokens, attention per sequence; the loss
+// weights each token by 1/(labelled tokens of its micro-batch), which makes the returned value the
+// sum of the micro-batch mean losses and the gradient the sum of the micro-batch gradients.
+#include "engine.h"
+
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <chrono>
+#include <sstream>
+
+#include "host_math.h"
+
+namespace hol {
+
+static thread_local std::string g_err;
+void set_error(const std::string& s) { g_err = s; }
+const char* last_error_cstr() { return g_err.c_str(); }
+
+#define HCHECK(expr)                                                                      \
+  do {                                                                                    \
+    hipError_t e__ = (expr);                                                              \
+    if (e__ != hipSuccess) {                                                              \
+      set_error(std::string(#expr) + ": " + hipGetErrorString(e__) + " (" __FILE__ ":" + \
+                std::to_string(__LINE__) + ")");                                          \
+      return HOL_EDEVICE;                                                                 \
+    }                                                                                     \
+  } while (0)
+
+#define KCHECK(expr)                                                                           \
+  do {                                                                                         \
+    int e__ = (expr);                                                                          \
+    if (e__ != 0) {                                                                            \
+      set_error(std::string(#expr) + ": " + hipGetErrorString((hipError_t)e__) + " (" __FILE__ \
+                ":" + std::to_string(__LINE__) + ")");                                         \
+      return HOL_EDEVICE;                                                                      \
+    }                                                                                          \
+  } while (0)
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+static double now_ms() {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+// ------------------------------------------------------------------------------------------
+// create / destroy
+// ------------------------------------------------------------------------------------------
+static hol_status validate_config(const hol_config& c) {
+  auto bad = [](const std::string& s) {
+    set_error("hol_create: " + s);
+    return HOL_EINVAL;
+  };
+  if (c.n_layers <= 0 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0)
+    return bad("non-positive shape");
+  if (c.n_q_heads % c.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (c.head_dim % 2 || c.head_dim > 128) return bad("head_dim must be even and <= 128");
+  if (c.hidden % 8 || c.hidden > 4096) return bad("hidden must be a multiple of 8 and <= 4096");
+  if (c.n_experts > 0 || c.lora_rank > 0) {
+    set_error("hol_create: MoE and LoRA layers are not implemented in this build");
+    return HOL_EUNSUPPORTED;
+  }
+  if (c.ffn <= 0 || c.ffn % 8) return bad("ffn must be a positive multiple of 8");
+  if (c.vocab < 0 || (c.vocab > 0 && c.vocab % 8)) return bad("vocab must be 0 or a multiple of 8");
+  if (c.ckpt_every_k <= 0) return bad("ckpt_every_k must be >= 1");
+  if (c.compute_dtype != HOL_F32 && c.compute_dtype != HOL_BF16) return bad("compute_dtype");
+  if (c.weight_decay != 0.f) return bad("weight_decay must be 0");
+  if (c.max_tokens <= 0 || c.max_seq <= 0 || c.max_seq > c.max_tokens) return bad("max_tokens / max_seq");
+  if (!(c.rms_eps > 0) || !(c.rope_base > 0)) return bad("rms_eps / rope_base");
+  return HOL_OK;
+}
+
+static void add_tensor(hol_model* m, const std::string& name, std::initializer_list<int64_t> shape, bool tr,
+                       int64_t flat, int block, int64_t img, bool f32) {
+  TensorDesc t;
+  t.name = name;
+  t.ndim = (int)shape.size();
+  int i = 0;
+  t.numel = 1;
+  for (int64_t s : shape) {
+    t.shape[i++] = s;
+    t.numel *= s;
+  }
+  t.trainable = tr;
+  t.flat = flat;
+  t.block = block;
+  t.img = img;
+  t.img_f32 = f32;
+  m->tensors.push_back(t);
+}
+
+static void* dev_alloc(hol_model* m, int64_t bytes, hol_status* st) {
+  void* p = nullptr;
+  if (bytes <= 0) bytes = 256;
+  if (hipMalloc(&p, (size_t)bytes) != hipSuccess) {
+    *st = HOL_ENOMEM_DEVICE;
+    set_error("hipMalloc of " + std::to_string(bytes) + " bytes failed");
+    return nullptr;
+  }
+  m->dev_allocs.push_back(p);
+  return p;
+}
+
+static void* pinned_alloc(hol_model* m, int64_t bytes, hol_status* st) {
+  void* p = nullptr;
+  if (bytes <= 0) bytes = 256;
+  if (hipHostMalloc(&p, (size_t)bytes, hipHostMallocDefault) != hipSuccess) {
+    *st = HOL_ENOMEM_HOST;
+    set_error("hipHostMalloc of " + std::to_string(bytes) + " bytes failed");
+    return nullptr;
+  }
+  m->pinned_allocs.push_back(p);
+  return p;
+}
+
+static float* host_alloc_f32(int64_t n) {
+  void* p = nullptr;
+  if (posix_memalign(&p, 4096, (size_t)std::max<int64_t>(n, 1) * 4) != 0) return nullptr;
+  return (float*)p;
+}
+
+// zero-fill with the host pool (first touch spreads pages over the pool's threads)
+static void parallel_zero(void* p, int64_t bytes) {
+  parallel_for(bytes, 1 << 22, [&](int64_t lo, int64_t hi) { memset((uint8_t*)p + lo, 0, (size_t)(hi - lo)); });
+}
+
+hol_status engine_create(const hol_config* cfg, hol_model** out) {
+  if (!cfg || !out) {
+    set_error("hol_create: null argument");
+    return HOL_EINVAL;
+  }
+  hol_status st = validate_config(*cfg);
+  if (st != HOL_OK) return st;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    set_error("hol_create: no HIP device available");
+    return HOL_EDEVICE;
+  }
+  if (cfg->device < 0 || cfg->device >= ndev) {
+    set_error("hol_create: bad device ordinal");
+    return HOL_EINVAL;
+  }
+  HCHECK(hipSetDevice(cfg->device));
+
+  hol_model* m = new hol_model();
+  m->cfg = *cfg;
+  const hol_config& c = m->cfg;
+  m->L = c.n_layers;
+  m->H = c.hidden;
+  m->nq = c.n_q_heads;
+  m->nkv = c.n_kv_heads;
+  m->d = c.head_dim;
+  m->F = c.ffn;
+  m->V = c.vocab;
+  m->nqd = m->nq * m->d;
+  m->QKV = (m->nq + 2 * m->nkv) * m->d;
+  m->dt = c.compute_dtype == HOL_BF16 ? DT_BF16 : DT_F32;
+  m->E = c.compute_dtype == HOL_BF16 ? 2 : 4;
+  m->Tmax = c.max_tokens;
+  m->Smax = c.max_seq;
+  m->K = c.ckpt_every_k;
+  m->nblocks = (m->L + m->K - 1) / m->K;
+  m->n_ckpt = m->nblocks + 1;
+  const int64_t H = m->H, L = m->L, F = m->F, V = m->V, QKV = m->QKV, nqd = m->nqd, E = m->E;
+
+  // ---- flat host layout: [embed] [layer 0 .. L-1] [final_norm, lm_head]
+  m->g_wqkv = 0;
+  m->g_wo = m->g_wqkv + QKV * H;
+  m->g_wgu = m->g_wo + H * nqd;
+  m->g_wd = m->g_wgu + 2 * F * H;
+  m->g_g1 = m->g_wd + H * F;
+  m->g_g2 = m->g_g1 + H;
+  m->layer_flat_n = m->g_g2 + H;
+  int64_t flat = 0;
+  if (V > 0) {
+    m->embed_flat0 = 0;
+    flat = V * H;
+  }
+  m->layer_flat0 = flat;
+  flat += L * m->layer_flat_n;
+  m->head_flat0 = flat;
+  m->head_flat_n = V > 0 ? H + V * H : 0;
+  flat += m->head_flat_n;
+  m->n_flat = flat;
+
+  // ---- image layout of one layer block (each sub-tensor 4 KiB aligned)
+  int64_t o = 0;
+  m->o_wqkv = o; o = align_up(o + QKV * H * E, 4096);
+  m->o_wo = o;   o = align_up(o + H * nqd * E, 4096);
+  m->o_wgu = o;  o = align_up(o + 2 * F * H * E, 4096);
+  m->o_wd = o;   o = align_up(o + H * F * E, 4096);
+  m->o_g1 = o;   o = align_up(o + H * 4, 4096);
+  m->o_g2 = o;   o = align_up(o + H * 4, 4096);
+  m->layer_img_bytes = o;
+  o = 0;
+  if (V > 0) {
+    m->o_gf = o;   o = align_up(o + H * 4, 4096);
+    m->o_wout = o; o = align_up(o + V * H * E, 4096);
+  }
+  m->head_img_bytes = o;
+  m->image_bytes = L * m->layer_img_bytes + m->head_img_bytes;
+
+  // ---- tensor directory (canonical order)
+  if (V > 0) add_tensor(m, "embed", {V, H}, true, 0, -2, -1, false);
+  for (int l = 0; l < L; ++l) {
+    const int64_t f0 = m->layer_flat0 + l * m->layer_flat_n;
+    const std::string p = "layers." + std::to_string(l) + ".";
+    add_tensor(m, p + "attn_norm", {H}, true, f0 + m->g_g1, l, m->o_g1, true);
+    add_tensor(m, p + "wq", {nqd, H}, true, f0 + m->g_wqkv, l, m->o_wqkv, false);
+    add_tensor(m, p + "wk", {(int64_t)m->nkv * m->d, H}, true, f0 + m->g_wqkv + nqd * H, l, m->o_wqkv + nqd * H * E, false);
+    add_tensor(m, p + "wv", {(int64_t)m->nkv * m->d, H}, true, f0 + m->g_wqkv + (nqd + (int64_t)m->nkv * m->d) * H, l,
+               m->o_wqkv + (nqd + (int64_t)m->nkv * m->d) * H * E, false);
+    add_tensor(m, p + "wo", {H, nqd}, true, f0 + m->g_wo, l, m->o_wo, false);
+    add_tensor(m, p + "mlp_norm", {H}, true, f0 + m->g_g2, l, m->o_g2, true);
+    add_tensor(m, p + "w_gate", {F, H}, true, f0 + m->g_wgu, l, m->o_wgu, false);
+    add_tensor(m, p + "w_up", {F, H}, true, f0 + m->g_wgu + F * H, l, m->o_wgu + F * H * E, false);
+    add_tensor(m, p + "w_down", {H, F}, true, f0 + m->g_wd, l, m->o_wd, false);
+  }
+  if (V > 0) {
+    add_tensor(m, "final_norm", {H}, true, m->head_flat0, -1, m->o_gf, true);
+    add_tensor(m, "lm_head", {V, H}, true, m->head_flat0 + H, -1, m->o_wout, false);
+  }
+
+  // ---- host allocations
+  m->master = host_alloc_f32(m->n_flat);
+  m->mom1 = host_alloc_f32(m->n_flat);
+  m->mom2 = host_alloc_f32(m->n_flat);
+  if (!m->master || !m->mom1 || !m->mom2) {
+    set_error("hol_create: host allocation of fp32 state failed");
+    engine_destroy(m);
+    return HOL_ENOMEM_HOST;
+  }
+  parallel_zero(m->master, m->n_flat * 4);
+  parallel_zero(m->mom1, m->n_flat * 4);
+  parallel_zero(m->mom2, m->n_flat * 4);
+  st = HOL_OK;
+  m->grad = (float*)pinned_alloc(m, m->n_flat * 4, &st);
+  m->image = (uint8_t*)pinned_alloc(m, m->image_bytes, &st);
+  const int64_t T = m->Tmax;
+  m->h_stage = (float*)pinned_alloc(m, T * H * 4, &st);
+  m->grad_stage = (float*)pinned_alloc(m, m->layer_flat_n * 4, &st);
+  m->head_stage = (float*)pinned_alloc(m, std::max<int64_t>(m->head_flat_n, 1) * 4, &st);
+  m->loss_stage = (float*)pinned_alloc(m, T * 4, &st);
+  m->lab_stage = (int32_t*)pinned_alloc(m, T * 4, &st);
+  m->w_stage = (float*)pinned_alloc(m, T * 4, &st);
+  if (st != HOL_OK) {
+    engine_destroy(m);
+    return st;
+  }
+  parallel_zero(m->grad, m->n_flat * 4);
+  parallel_zero(m->image, m->image_bytes);
+
+  // ---- device plan
+  auto D = [&](int64_t bytes) { return dev_alloc(m, align_up(bytes, 256), &st); };
+  m->slot[0] = (uint8_t*)D(m->layer_img_bytes);
+  m->slot[1] = (uint8_t*)D(m->layer_img_bytes);
+  if (V > 0) m->head_dev = (uint8_t*)D(m->head_img_bytes);
+  m->gdev[0] = (float*)D(m->layer_flat_n * 4);
+  m->gdev[1] = (float*)D(m->layer_flat_n * 4);
+  if (V > 0) m->head_gdev = (float*)D(m->head_flat_n * 4);
+  m->ckpt = (float*)D((int64_t)m->n_ckpt * T * H * 4);
+  // activation block: K layers
+  int64_t a = 0;
+  auto A = [&](int64_t bytes) {
+    const int64_t off = a;
+    a = align_up(a + bytes, 256);
+    return off;
+  };
+  m->ao_hin = A(T * H * 4);
+  m->ao_r1 = A(T * 4);
+  m->ao_n1 = A(T * H * E);
+  m->ao_qkv = A(T * QKV * E);
+  m->ao_o = A(T * nqd * E);
+  m->ao_lse = A(T * m->nq * 4);
+  m->ao_h1 = A(T * H * 4);
+  m->ao_r2 = A(T * 4);
+  m->ao_n2 = A(T * H * E);
+  m->ao_gu = A(T * 2 * F * E);
+  m->ao_a = A(T * F * E);
+  m->act_stride = a;
+  m->act_mem = (uint8_t*)D((int64_t)m->K * m->act_stride);
+  m->hbuf[0] = (float*)D(T * H * 4);
+  m->hbuf[1] = (float*)D(T * H * 4);
+  m->dh = (float*)D(T * H * 4);
+  m->dn = (float*)D(T * H * 4);
+  m->dhb = D(T * H * E);
+  m->dqkv = D(T * QKV * E);
+  m->dO = D(T * nqd * E);
+  m->da = D(T * F * E);
+  m->dgu = D(T * 2 * F * E);
+  m->delta = (float*)D(T * m->nq * 4);
+  m->partial = (float*)D((int64_t)rmsnorm_bwd_blocks((int)T) * H * 4);
+  m->labels_dev = (int32_t*)D(T * 4);
+  m->w_dev = (float*)D(T * 4);
+  m->rowloss_dev = (float*)D(T * 4);
+  if (V > 0) {
+    m->zbuf = D(T * H * E);
+    m->rz = (float*)D(T * 4);
+    // logits chunk: up to 4 GiB of fp32 logits, rows a multiple of 256
+    int64_t tc = std::max<int64_t>(256, ((int64_t)1 << 30) / V / 256 * 256);
+    tc = std::min<int64_t>(tc, align_up(T, 256));
+    m->Tc = (int)tc;
+    m->logits = (float*)D(tc * V * 4);
+    m->dlogits = D(tc * V * E);
+  }
+  const int half = m->d / 2;
+  m->cos_dev = (float*)D((int64_t)m->Smax * half * 4);
+  m->sin_dev = (float*)D((int64_t)m->Smax * half * 4);
+  if (st != HOL_OK) {
+    engine_destroy(m);
+    return st;
+  }
+  // RoPE tables: angle p * base^(-2j/d) in fp64, cos/sin rounded to fp32
+  {
+    std::vector<float> cs((size_t)m->Smax * half), sn((size_t)m->Smax * half);
+    for (int p = 0; p < m->Smax; ++p)
+      for (int j = 0; j < half; ++j) {
+        const double th = pow((double)c.rope_base, -2.0 * j / m->d);
+        const double ang = (double)p * th;
+        cs[(size_t)p * half + j] = (float)cos(ang);
+        sn[(size_t)p * half + j] = (float)sin(ang);
+      }
+    HCHECK(hipMemcpy(m->cos_dev, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+    HCHECK(hipMemcpy(m->sin_dev, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+  }
+  HCHECK(hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking));
+  HCHECK(hipStreamCreateWithFlags(&m->sh2d, hipStreamNonBlocking));
+  HCHECK(hipStreamCreateWithFlags(&m->sd2h, hipStreamNonBlocking));
+  for (int i = 0; i < 2; ++i) {
+    HCHECK(hipEventCreateWithFlags(&m->ev_ready[i], hipEventDisableTiming));
+    HCHECK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
+    HCHECK(hipEventCreateWithFlags(&m->ev_gdone[i], hipEventDisableTiming));
+    HCHECK(hipEventCreateWithFlags(&m->ev_gfree[i], hipEventDisableTiming));
+  }
+  HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
+  // timing events: two per compute op, weight stream and gradient copy (at most ~14 L + 8)
+  const int nt = 20 * m->L + 64;
+  m->tev.resize(nt);
+  for (int i = 0; i < nt; ++i) HCHECK(hipEventCreate(&m->tev[i]));
+  *out = m;
+  return HOL_OK;
+}
+
+void engine_destroy(hol_model* m) {
+  if (!m) return;
+  if (m->sc) hipStreamSynchronize(m->sc);
+  if (m->sh2d) hipStreamSynchronize(m->sh2d);
+  if (m->sd2h) hipStreamSynchronize(m->sd2h);
+  for (int i = 0; i < 2; ++i) {
+    if (m->ev_ready[i]) hipEventDestroy(m->ev_ready[i]);
+    if (m->ev_free[i]) hipEventDestroy(m->ev_free[i]);
+    if (m->ev_gdone[i]) hipEventDestroy(m->ev_gdone[i]);
+    if (m->ev_gfree[i]) hipEventDestroy(m->ev_gfree[i]);
+  }
+  if (m->ev_head) hipEventDestroy(m->ev_head);
+  for (auto e : m->tev)
+    if (e) hipEventDestroy(e);
+  if (m->sc) hipStreamDestroy(m->sc);
+  if (m->sh2d) hipStreamDestroy(m->sh2d);
+  if (m->sd2h) hipStreamDestroy(m->sd2h);
+  for (void* p : m->dev_allocs) hipFree(p);
+  for (void* p : m->pinned_allocs) hipHostFree(p);
+  free(m->master);
+  free(m->mom1);
+  free(m->mom2);
+  delete m;
+}
+
+// ------------------------------------------------------------------------------------------
+// image refresh (master -> low-precision copy)
+// ------------------------------------------------------------------------------------------
+static uint8_t* image_block(hol_model* m, int block) {
+  return block >= 0 ? m->image + (int64_t)block * m->layer_img_bytes : m->image + (int64_t)m->L * m->layer_img_bytes;
+}
+
+void refresh_image_tensor(hol_model* m, const TensorDesc& t) {
+  if (t.block == -2 || t.img < 0) return;
+  uint8_t* dst = image_block(m, t.block) + t.img;
+  const float* src = m->master + t.flat;
+  if (t.img_f32 || m->dt == DT_F32) {
+    parallel_for(t.numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy((float*)dst + lo, src + lo, (hi - lo) * 4); });
+  } else {
+    parallel_for(t.numel, 1 << 18,
+                 [&](int64_t lo, int64_t hi) { f32_to_bf16_range(src + lo, (uint16_t*)dst + lo, hi - lo); });
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// layer template: bind weights (slot pointers) and run kernels
+// ------------------------------------------------------------------------------------------
+struct W {
+  const void *wqkv, *wo, *wgu, *wd;
+  const float *g1, *g2;
+};
+static W bind(const hol_model* m, const uint8_t* slot) {
+  W w;
+  w.wqkv = slot + m->o_wqkv;
+  w.wo = slot + m->o_wo;
+  w.wgu = slot + m->o_wgu;
+  w.wd = slot + m->o_wd;
+  w.g1 = (const float*)(slot + m->o_g1);
+  w.g2 = (const float*)(slot + m->o_g2);
+  return w;
+}
+
+static Act act_at(const hol_model* m, int j) {
+  uint8_t* b = m->act_mem + (int64_t)j * m->act_stride;
+  Act a;
+  a.hin = (float*)(b + m->ao_hin);
+  a.r1 = (float*)(b + m->ao_r1);
+  a.n1 = b + m->ao_n1;
+  a.qkv = b + m->ao_qkv;
+  a.o = b + m->ao_o;
+  a.lse = (float*)(b + m->ao_lse);
+  a.h1 = (float*)(b + m->ao_h1);
+  a.r2 = (float*)(b + m->ao_r2);
+  a.n2 = b + m->ao_n2;
+  a.gu = b + m->ao_gu;
+  a.a = b + m->ao_a;
+  return a;
+}
+
+static Gemm gemm(int M, int N, int K, const void* A, int64_t lda, bool a_km, const void* B, int64_t ldb, bool b_kn,
+                 void* C, int64_t ldc, DType ab, DType c, int epi, const float* R = nullptr, int64_t ldr = 0) {
+  Gemm g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.a_km = a_km;
+  g.B = B; g.ldb = ldb; g.b_kn = b_kn;
+  g.C = C; g.ldc = ldc; g.ab = ab; g.c = c; g.epi = epi; g.R = R; g.ldr = ldr;
+  return g;
+}
+
+static hol_status layer_forward(hol_model* m, const W& w, const float* hin, float* hout, const Act& A, int T,
+                                int n_seq, int S) {
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
+  const DType dt = m->dt;
+  const int64_t E = m->E;
+  hipStream_t s = m->sc;
+  KCHECK(launch_rmsnorm_fwd(hin, w.g1, m->cfg.rms_eps, A.n1, dt, A.r1, T, H, s));
+  KCHECK(launch_gemm(gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE), s));
+  KCHECK(launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
+  KCHECK(launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
+  Attn at;
+  at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
+  at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
+  at.ldq = at.ldk = at.ldv = QKV;
+  at.o = A.o; at.ldo = nqd; at.lse = A.lse;
+  KCHECK(launch_attn_fwd(at, s));
+  KCHECK(launch_gemm(gemm(T, H, nqd, A.o, nqd, false, w.wo, nqd, false, A.h1, H, dt, DT_F32, EPI_RESID, hin, H), s));
+  KCHECK(launch_rmsnorm_fwd(A.h1, w.g2, m->cfg.rms_eps, A.n2, dt, A.r2, T, H, s));
+  KCHECK(launch_gemm(gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE), s));
+  KCHECK(launch_swiglu_fwd(A.gu, A.a, dt, T, F, s));
+  KCHECK(launch_gemm(gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H), s));
+  return HOL_OK;
+}
+
+// dh (fp32 [T,H]) holds d loss / d h_out on entry and d loss / d h_in on exit; G is the layer's
+// gradient block (fully overwritten).
+static hol_status layer_backward(hol_model* m, const W& w, const Act& A, const float* hin, float* G, int T, int n_seq,
+                                 int S) {
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
+  const DType dt = m->dt;
+  const int64_t E = m->E;
+  hipStream_t s = m->sc;
+  // MLP
+  KCHECK(launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+  KCHECK(launch_gemm(gemm(T, F, H, m->dhb, H, false, w.wd, F, true, m->da, F, dt, dt, EPI_STORE), s));
+  KCHECK(launch_gemm(gemm(H, F, T, m->dhb, H, true, A.a, F, true, G + m->g_wd, F, dt, DT_F32, EPI_STORE), s));
+  KCHECK(launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
+  KCHECK(launch_gemm(gemm(T, H, 2 * F, m->dgu, 2 * F, false, w.wgu, H, true, m->dn, H, dt, DT_F32, EPI_STORE), s));
+  KCHECK(launch_gemm(gemm(2 * F, H, T, m->dgu, 2 * F, true, A.n2, H, true, G + m->g_wgu, H, dt, DT_F32, EPI_STORE), s));
+  KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
+  KCHECK(launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, G + m->g_g2, m->partial, T, H, s));
+  // attention
+  KCHECK(launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+  KCHECK(launch_gemm(gemm(T, nqd, H, m->dhb, H, false, w.wo, nqd, true, m->dO, nqd, dt, dt, EPI_STORE), s));
+  KCHECK(launch_gemm(gemm(H, nqd, T, m->dhb, H, true, A.o, nqd, true, G + m->g_wo, nqd, dt, DT_F32, EPI_STORE), s));
+  Attn at;
+  at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
+  at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
+  at.ldq = at.ldk = at.ldv = QKV;
+  at.o = A.o; at.ldo = nqd; at.lse = A.lse;
+  at.dO = m->dO; at.lddo = nqd;
+  at.dq = m->dqkv; at.dk = (uint8_t*)m->dqkv + (int64_t)nqd * E; at.dv = (uint8_t*)m->dqkv + (int64_t)(nqd + m->nkv * d) * E;
+  at.lddq = at.lddk = at.lddv = QKV;
+  at.delta = m->delta;
+  KCHECK(launch_attn_bwd(at, s));
+  KCHECK(launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
+  KCHECK(launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
+  KCHECK(launch_gemm(gemm(T, H, QKV, m->dqkv, QKV, false, w.wqkv, H, true, m->dn, H, dt, DT_F32, EPI_STORE), s));
+  KCHECK(launch_gemm(gemm(QKV, H, T, m->dqkv, QKV, true, A.n1, H, true, G + m->g_wqkv, H, dt, DT_F32, EPI_STORE), s));
+  KCHECK(launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, G + m->g_g1, m->partial, T, H, s));
+  return HOL_OK;
+}
+
+// Loss anchor (phase 2): loss rows, head gradient into head_gdev, d loss / d h_L into m->dh.
+static hol_status head_forward_backward(hol_model* m, const float* hL, int T, hol_loss loss) {
+  hipStream_t s = m->sc;
+  const int H = m->H;
+  if (loss == HOL_LOSS_SUM_SQUARES) {
+    KCHECK(launch_sumsq(hL, m->rowloss_dev, m->dh, T, H, s));
+    return HOL_OK;
+  }
+  const int V = m->V;
+  const DType dt = m->dt;
+  const int64_t E = m->E;
+  const float* gf = (const float*)(m->head_dev + m->o_gf);
+  const void* wout = m->head_dev + m->o_wout;
+  KCHECK(launch_rmsnorm_fwd(hL, gf, m->cfg.rms_eps, m->zbuf, dt, m->rz, T, H, s));
+  float* gW = m->head_gdev + H;
+  for (int r0 = 0; r0 < T; r0 += m->Tc) {
+    const int tc = std::min(m->Tc, T - r0);
+    const void* zc = (const uint8_t*)m->zbuf + (int64_t)r0 * H * E;
+    KCHECK(launch_gemm(gemm(tc, V, H, zc, H, false, wout, H, false, m->logits, V, dt, DT_F32, EPI_STORE), s));
+    KCHECK(launch_ce_fwd_bwd(m->logits, V, m->labels_dev + r0, m->w_dev + r0, m->rowloss_dev + r0, m->dlogits, dt, V,
+                             tc, V, s));
+    KCHECK(launch_gemm(gemm(tc, H, V, m->dlogits, V, false, wout, H, true, m->dn + (int64_t)r0 * H, H, dt, DT_F32,
+                            EPI_STORE), s));
+    KCHECK(launch_gemm(gemm(V, H, tc, m->dlogits, V, true, zc, H, true, gW, H, dt, DT_F32,
+                            r0 == 0 ? EPI_STORE : EPI_ACCUM), s));
+  }
+  KCHECK(launch_fill_f32(m->head_gdev, 0.f, H, s));
+  KCHECK(launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, m->head_gdev, m->partial, T, H, s));
+  return HOL_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// forward_backward
+// ------------------------------------------------------------------------------------------
+struct AccumJob {
+  float* dst;
+  const float* src;
+  int64_t n;
+};
+static void host_accumulate(void* p) {
+  AccumJob* j = (AccumJob*)p;
+  parallel_for(j->n, 1 << 16, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) j->dst[i] += j->src[i];
+  });
+}
+
+hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out) {
+  const double t_start = now_ms();
+  // ---- validation (nothing touched before this passes)
+  auto bad = [](const std::string& s) {
+    set_error("hol_forward_backward: " + s);
+    return HOL_EINVAL;
+  };
+  if (!b || !out) return bad("null argument");
+  if (m->poisoned) {
+    set_error("hol_forward_backward: model poisoned by an earlier device error; call hol_zero_grad");
+    return HOL_ESTATE;
+  }
+  const int B = b->batch, S = b->seq, M = b->n_micro;
+  if (B <= 0 || S <= 0 || M <= 0) return bad("batch, seq and n_micro must be positive");
+  if (B % M) return bad("batch must be a multiple of n_micro");
+  const int64_t T64 = (int64_t)B * S;
+  if (T64 > m->Tmax) return bad("batch*seq exceeds max_tokens");
+  if (S > m->Smax) return bad("seq exceeds max_seq");
+  const int T = (int)T64, H = m->H;
+  if (loss == HOL_LOSS_NEXT_TOKEN_CE) {
+    if (m->V <= 0) return bad("cross entropy needs vocab > 0");
+    if (!b->tokens) return bad("tokens required");
+    for (int64_t i = 0; i < T64; ++i)
+      if (b->tokens[i] < 0 || b->tokens[i] >= m->V) return bad("token id out of range");
+    if (b->labels)
+      for (int64_t i = 0; i < T64; ++i)
+        if (b->labels[i] < -1 || b->labels[i] >= m->V) return bad("label out of range");
+  } else if (loss == HOL_LOSS_SUM_SQUARES) {
+    if (m->V > 0) {
+      if (!b->tokens) return bad("tokens required");
+      for (int64_t i = 0; i < T64; ++i)
+        if (b->tokens[i] < 0 || b->tokens[i] >= m->V) return bad("token id out of range");
+    } else if (!b->hidden_in) {
+      return bad("hidden_in required when vocab == 0");
+    }
+  } else {
+    return bad("unknown loss");
+  }
+  m->stats = Stats();
+  m->stats.tokens = T;
+  const int L = m->L, K = m->K;
+  const int64_t E = m->E;
+  // ---- labels and per-token weights (1/labelled count of the token's micro-batch)
+  if (loss == HOL_LOSS_NEXT_TOKEN_CE) {
+    const int per = B / M;
+    for (int mb = 0; mb < M; ++mb) {
+      int64_t cnt = 0;
+      const int64_t t0 = (int64_t)mb * per * S, t1 = t0 + (int64_t)per * S;
+      for (int64_t t = t0; t < t1; ++t) {
+        int32_t y;
+        if (b->labels) y = b->labels[t];
+        else y = ((t % S) == S - 1) ? -1 : b->tokens[t + 1];
+        m->lab_stage[t] = y;
+        if (y >= 0) ++cnt;
+      }
+      const float w = cnt ? (float)(1.0 / (double)cnt) : 0.f;
+      for (int64_t t = t0; t < t1; ++t) m->w_stage[t] = m->lab_stage[t] >= 0 ? w : 0.f;
+    }
+  }
+  // ---- h_0: embedding rows gathered on the host from the fp32 masters, or the given hidden states
+  const double te = now_ms();
+  if (m->V > 0) {
+    const float* emb = m->master + m->embed_flat0;
+    parallel_for(T64, 256, [&](int64_t lo, int64_t hi) {
+      for (int64_t t = lo; t < hi; ++t) memcpy(m->h_stage + t * H, emb + (int64_t)b->tokens[t] * H, (size_t)H * 4);
+    });
+  } else {
+    parallel_for(T64 * H, 1 << 20,
+                 [&](int64_t lo, int64_t hi) { memcpy(m->h_stage + lo, b->hidden_in + lo, (size_t)(hi - lo) * 4); });
+  }
+  m->stats.host_embed_ms = now_ms() - te;
+
+  hol_status st = HOL_OK;
+  auto fail = [&](hol_status s) {
+    m->poisoned = true;
+    hipDeviceSynchronize();
+    return s;
+  };
+#define STEP(expr)                    \
+  do {                                \
+    hol_status s__ = (expr);          \
+    if (s__ != HOL_OK) return fail(s__); \
+  } while (0)
+#define HSTEP(expr)                                                                        \
+  do {                                                                                     \
+    hipError_t e__ = (expr);                                                               \
+    if (e__ != hipSuccess) {                                                               \
+      set_error(std::string(#expr) + ": " + hipGetErrorString(e__) + " (" __FILE__ ":" + \
+                std::to_string(__LINE__) + ")");                                           \
+      return fail(HOL_EDEVICE);                                                            \
+    }                                                                                      \
+  } while (0)
+
+  HSTEP(hipSetDevice(m->cfg.device));
+  hipStream_t sc = m->sc, sh = m->sh2d, sd = m->sd2h;
+  // initial event states: every buffer free
+  for (int i = 0; i < 2; ++i) {
+    HSTEP(hipEventRecord(m->ev_free[i], sc));
+    HSTEP(hipEventRecord(m->ev_gfree[i], sd));
+  }
+  m->slot_layer[0] = m->slot_layer[1] = -1;
+  m->tev_used = 0;
+  auto tev = [&]() -> hipEvent_t { return m->tev[std::min<int>(m->tev_used++, (int)m->tev.size() - 1)]; };
+  struct Span { hipEvent_t a, b; int cls; };
+  std::vector<Span> spans;  // cls: 0 h2d, 1 d2h, 2 fwd, 3 recomp, 4 bwd, 5 head
+
+  if (loss == HOL_LOSS_NEXT_TOKEN_CE) {
+    HSTEP(hipMemcpyAsync(m->labels_dev, m->lab_stage, T64 * 4, hipMemcpyHostToDevice, sc));
+    HSTEP(hipMemcpyAsync(m->w_dev, m->w_stage, T64 * 4, hipMemcpyHostToDevice, sc));
+  }
+  HSTEP(hipMemcpyAsync(m->ckpt, m->h_stage, T64 * H * 4, hipMemcpyHostToDevice, sc));
+  m->stats.h2d_bytes += (double)T64 * H * 4;
+
+  // ---- op list
+  std::vector<Op> ops;
+  for (int l = 0; l < L; ++l) ops.push_back({OP_FWD, l, l / K, l % K});
+  ops.push_back({OP_HEAD, -1, -1, 0});
+  for (int bl = m->nblocks - 1; bl >= 0; --bl) {
+    const int l0 = bl * K, l1 = std::min(L, (bl + 1) * K);
+    for (int l = l0; l < l1; ++l) ops.push_back({OP_RECOMP, l, bl, l - l0});
+    for (int l = l1 - 1; l >= l0; --l) ops.push_back({OP_BWD, l, bl, l - l0});
+  }
+  auto ckpt_of = [&](int idx) { return m->ckpt + (int64_t)idx * T64 * H; };  // idx: block, or nblocks for h_L
+  const bool direct = m->grads_zero;
+
+  // ---- weight streaming helpers
+  int last_slot = 1;  // so the first load goes to slot 0
+  std::vector<int> op_slot(ops.size(), -1);
+  auto ensure_loaded = [&](size_t j) -> hol_status {
+    const Op& op = ops[j];
+    if (op.kind == OP_HEAD) return HOL_OK;
+    for (int s = 0; s < 2; ++s)
+      if (m->slot_layer[s] == op.layer) {
+        op_slot[j] = s;
+        return HOL_OK;
+      }
+    const int s = last_slot ^ 1;
+    HCHECK(hipStreamWaitEvent(sh, m->ev_free[s], 0));
+    hipEvent_t a = tev(), e = tev();
+    HCHECK(hipEventRecord(a, sh));
+    HCHECK(hipMemcpyAsync(m->slot[s], image_block(m, op.layer), m->layer_img_bytes, hipMemcpyHostToDevice, sh));
+    HCHECK(hipEventRecord(e, sh));
+    spans.push_back({a, e, 0});
+    HCHECK(hipEventRecord(m->ev_ready[s], sh));
+    m->slot_layer[s] = op.layer;
+    op_slot[j] = s;
+    m->stats.h2d_bytes += (double)m->layer_img_bytes;
+    m->stats.n_weight_streams++;
+    return HOL_OK;
+  };
+  auto next_layer_op = [&](size_t j) -> size_t {
+    size_t k = j + 1;
+    while (k < ops.size() && ops[k].kind == OP_HEAD) ++k;
+    return k;
+  };
+  bool head_loaded = false;
+  auto load_head = [&]() -> hol_status {
+    if (head_loaded || m->V <= 0 || loss != HOL_LOSS_NEXT_TOKEN_CE) return HOL_OK;
+    hipEvent_t a = tev(), e = tev();
+    HCHECK(hipEventRecord(a, sh));
+    HCHECK(hipMemcpyAsync(m->head_dev, image_block(m, -1), m->head_img_bytes, hipMemcpyHostToDevice, sh));
+    HCHECK(hipEventRecord(e, sh));
+    spans.push_back({a, e, 0});
+    HCHECK(hipEventRecord(m->ev_head, sh));
+    m->stats.h2d_bytes += (double)m->head_img_bytes;
+    head_loaded = true;
+    return HOL_OK;
+  };
+
+  STEP(ensure_loaded(0));
+  int gi = 0;  // grad buffer ping-pong
+  for (size_t j = 0; j < ops.size(); ++j) {
+    const Op& op = ops[j];
+    // bind
+    if (op.kind != OP_HEAD) {
+      if (op_slot[j] < 0) STEP(ensure_loaded(j));
+      last_slot = op_slot[j];
+    }
+    // prefetch the next layer's weights into the other slot (overlaps this op's compute)
+    auto prefetch = [&]() -> hol_status {
+      const size_t k = next_layer_op(j);
+      if (k < ops.size()) {
+        hol_status r = ensure_loaded(k);
+        if (r != HOL_OK) return r;
+      }
+      // the head follows the last forward layer's prefetch on the transfer stream
+      if (op.kind == OP_FWD && op.layer >= L - 2) return load_head();
+      return HOL_OK;
+    };
+    hipEvent_t ta = tev(), tb = tev();
+    if (op.kind == OP_HEAD) {
+      STEP(load_head());
+      if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE) HSTEP(hipStreamWaitEvent(sc, m->ev_head, 0));
+      HSTEP(hipEventRecord(ta, sc));
+      STEP(head_forward_backward(m, ckpt_of(m->nblocks), T, loss));
+      HSTEP(hipEventRecord(tb, sc));
+      spans.push_back({ta, tb, 5});
+      if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE) {
+        // head gradient to the host (gradient-transfer stream)
+        HSTEP(hipEventRecord(m->ev_gdone[0], sc));
+        HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[0], 0));
+        float* dst = direct ? m->grad + m->head_flat0 : m->head_stage;
+        hipEvent_t a = tev(), e = tev();
+        HSTEP(hipEventRecord(a, sd));
+        HSTEP(hipMemcpyAsync(dst, m->head_gdev, m->head_flat_n * 4, hipMemcpyDeviceToHost, sd));
+        HSTEP(hipEventRecord(e, sd));
+        spans.push_back({a, e, 1});
+        m->stats.d2h_bytes += (double)m->head_flat_n * 4;
+        if (!direct) {
+          static thread_local AccumJob job;
+          job = {m->grad + m->head_flat0, m->head_stage, m->head_flat_n};
+          HSTEP(hipLaunchHostFunc(sd, host_accumulate, &job));
+        }
+      }
+      STEP(prefetch());
+      continue;
+    }
+    const int s = op_slot[j];
+    const W w = bind(m, m->slot[s]);
+    HSTEP(hipStreamWaitEvent(sc, m->ev_ready[s], 0));
+    const int n_seq = B;
+    if (op.kind == OP_FWD) {
+      // h_in: checkpoint of the block for the block's first layer, else the previous output
+      const int l = op.layer;
+      const float* hin = (l == 0) ? ckpt_of(0) : ((l % K == 0) ? ckpt_of(l / K) : m->hbuf[(l - 1) & 1]);
+      float* hout;
+      if (l + 1 == L) hout = ckpt_of(m->nblocks);
+      else if ((l + 1) % K == 0) hout = ckpt_of((l + 1) / K);
+      else hout = m->hbuf[l & 1];
+      HSTEP(hipEventRecord(ta, sc));
+      STEP(layer_forward(m, w, hin, hout, act_at(m, 0), T, n_seq, S));
+      HSTEP(hipEventRecord(tb, sc));
+      spans.push_back({ta, tb, 2});
+    } else if (op.kind == OP_RECOMP) {
+      const int l1 = std::min(L, (op.block + 1) * K);
+      const Act A = act_at(m, op.pos);
+      const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
+      float* hout = (op.layer + 1 < l1) ? act_at(m, op.pos + 1).hin : m->hbuf[0];
+      HSTEP(hipEventRecord(ta, sc));
+      STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S));
+      HSTEP(hipEventRecord(tb, sc));
+      spans.push_back({ta, tb, 3});
+    } else {  // OP_BWD
+      const Act A = act_at(m, op.pos);
+      const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
+      HSTEP(hipStreamWaitEvent(sc, m->ev_gfree[gi], 0));
+      HSTEP(hipEventRecord(ta, sc));
+      STEP(layer_backward(m, w, A, hin, m->gdev[gi], T, n_seq, S));
+      HSTEP(hipEventRecord(tb, sc));
+      spans.push_back({ta, tb, 4});
+      HSTEP(hipEventRecord(m->ev_gdone[gi], sc));
+      // gradient offload on the gradient-transfer stream
+      HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
+      float* lg = m->grad + m->layer_flat0 + (int64_t)op.layer * m->layer_flat_n;
+      hipEvent_t a = tev(), e = tev();
+      HSTEP(hipEventRecord(a, sd));
+      HSTEP(hipMemcpyAsync(direct ? lg : m->grad_stage, m->gdev[gi], m->layer_flat_n * 4, hipMemcpyDeviceToHost, sd));
+      HSTEP(hipEventRecord(e, sd));
+      spans.push_back({a, e, 1});
+      if (!direct) {
+        static thread_local std::vector<AccumJob> jobs;
+        jobs.resize(L);
+        jobs[op.layer] = {lg, m->grad_stage, m->layer_flat_n};
+        HSTEP(hipLaunchHostFunc(sd, host_accumulate, &jobs[op.layer]));
+      }
+      HSTEP(hipEventRecord(m->ev_gfree[gi], sd));
+      m->stats.d2h_bytes += (double)m->layer_flat_n * 4;
+      gi ^= 1;
+    }
+    HSTEP(hipEventRecord(m->ev_free[s], sc));
+    STEP(prefetch());
+  }
+  // ---- first-layer gradient (embedding rows) and loss rows back to the host
+  if (m->V > 0) {
+    HSTEP(hipMemcpyAsync(m->h_stage, m->dh, T64 * H * 4, hipMemcpyDeviceToHost, sc));
+    m->stats.d2h_bytes += (double)T64 * H * 4;
+  }
+  HSTEP(hipMemcpyAsync(m->loss_stage, m->rowloss_dev, T64 * 4, hipMemcpyDeviceToHost, sc));
+  HSTEP(hipStreamSynchronize(sc));
+  HSTEP(hipStreamSynchronize(sh));
+  HSTEP(hipStreamSynchronize(sd));
+  HSTEP(hipGetLastError());
+  // embedding gradient: rows added in token order (columns split over threads: deterministic)
+  if (m->V > 0) {
+    float* gE = m->grad + m->embed_flat0;
+    parallel_for(H, 64, [&](int64_t lo, int64_t hi) {
+      for (int64_t t = 0; t < T64; ++t) {
+        float* dst = gE + (int64_t)b->tokens[t] * H;
+        const float* src = m->h_stage + t * H;
+        for (int64_t c = lo; c < hi; ++c) dst[c] += src[c];
+      }
+    });
+  }
+  double total = 0.0;
+  for (int64_t t = 0; t < T64; ++t) total += (double)m->loss_stage[t];
+  *out = total;
+  m->grads_zero = false;
+  // ---- stats
+  for (auto& sp : spans) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, sp.a, sp.b) != hipSuccess) continue;
+    switch (sp.cls) {
+      case 0: m->stats.h2d_busy_ms += ms; break;
+      case 1: m->stats.d2h_busy_ms += ms; break;
+      case 2: m->stats.fwd_ms += ms; m->stats.compute_busy_ms += ms; break;
+      case 3: m->stats.recomp_ms += ms; m->stats.compute_busy_ms += ms; break;
+      case 4: m->stats.bwd_ms += ms; m->stats.compute_busy_ms += ms; break;
+      case 5: m->stats.head_ms += ms; m->stats.compute_busy_ms += ms; break;
+    }
+  }
+  m->stats.fb_ms = now_ms() - t_start;
+  (void)E;
+  (void)st;
+#undef STEP
+#undef HSTEP
+  return HOL_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// step: host Adam, refresh of the low-precision image, zero_grad
+// ------------------------------------------------------------------------------------------
+hol_status engine_step(hol_model* m) {
+  if (m->poisoned) {
+    set_error("hol_step: model poisoned by an earlier device error; call hol_zero_grad");
+    return HOL_ESTATE;
+  }
+  const double t0 = now_ms();
+  const hol_config& c = m->cfg;
+  const AdamConsts k = adam_consts(m->step_t + 1, c.lr, c.beta1, c.beta2, c.adam_eps);
+  for (const TensorDesc& t : m->tensors) {
+    if (!t.trainable) continue;
+    float* th = m->master + t.flat;
+    const float* g = m->grad + t.flat;
+    float* m1 = m->mom1 + t.flat;
+    float* m2 = m->mom2 + t.flat;
+    const bool to_bf16 = !(t.img_f32 || m->dt == DT_F32) && t.img >= 0 && t.block != -2;
+    uint8_t* dst = (t.block == -2 || t.img < 0) ? nullptr : image_block(m, t.block) + t.img;
+    parallel_for(t.numel, 1 << 16, [&](int64_t lo, int64_t hi) {
+      // chunked so the refreshed values are still in cache when converted
+      for (int64_t a = lo; a < hi; a += 4096) {
+        const int64_t n = std::min<int64_t>(4096, hi - a);
+        adam_range(th + a, g + a, m1 + a, m2 + a, n, k);
+        if (dst) {
+          if (to_bf16) f32_to_bf16_range(th + a, (uint16_t*)dst + a, n);
+          else memcpy((float*)dst + a, th + a, (size_t)n * 4);
+        }
+      }
+    });
+  }
+  m->step_t += 1;
+  parallel_zero(m->grad, m->n_flat * 4);
+  m->grads_zero = true;
+  m->stats.step_ms = now_ms() - t0;
+  return HOL_OK;
+}
+
+hol_status engine_zero_grad(hol_model* m) {
+  if (m->sc) hipStreamSynchronize(m->sc);
+  if (m->sh2d) hipStreamSynchronize(m->sh2d);
+  if (m->sd2h) hipStreamSynchronize(m->sd2h);
+  parallel_zero(m->grad, m->n_flat * 4);
+  m->grads_zero = true;
+  m->poisoned = false;
+  return HOL_OK;
+}
+
+std::string stats_json(const hol_model* m) {
+  const Stats& s = m->stats;
+  std::ostringstream o;
+  o.precision(6);
+  o << std::fixed;
+  o << "{\"tokens\":" << s.tokens << ",\"fb_ms\":" << s.fb_ms << ",\"step_ms\":" << s.step_ms
+    << ",\"h2d_bytes\":" << s.h2d_bytes << ",\"d2h_bytes\":" << s.d2h_bytes << ",\"h2d_busy_ms\":" << s.h2d_busy_ms
+    << ",\"d2h_busy_ms\":" << s.d2h_busy_ms << ",\"compute_busy_ms\":" << s.compute_busy_ms
+    << ",\"fwd_ms\":" << s.fwd_ms << ",\"recomp_ms\":" << s.recomp_ms << ",\"bwd_ms\":" << s.bwd_ms
+    << ",\"head_ms\":" << s.head_ms << ",\"host_embed_ms\":" << s.host_embed_ms
+    << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
+    << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads() << "}";
+  return o.str();
+}
+
+}  // namespace hol

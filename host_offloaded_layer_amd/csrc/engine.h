@@ -1,0 +1,141 @@
+// The streamed trainer behind the C ABI: host state, HBM plan, streams/events and the
+// phase 1-3 schedule of MegaTrain's streaming training step.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/hol.h"
+#include "kernels.h"
+
+namespace hol {
+
+struct TensorDesc {
+  std::string name;
+  int ndim = 0;
+  int64_t shape[4] = {0, 0, 0, 0};
+  int64_t numel = 0;
+  bool trainable = true;
+  int64_t flat = 0;      // offset (floats) in the flat host arrays (master / grad / m / v)
+  int block = 0;         // image block: layer index, or -1 for the head block, -2 none (embed)
+  int64_t img = -1;      // byte offset inside that image block
+  bool img_f32 = false;  // kept fp32 in the image (norm gains)
+};
+
+// Saved intermediates of one layer (row-major, T tokens).
+struct Act {
+  float* hin = nullptr;  // layer input (fp32 [T,H]); for the first layer of a block: a checkpoint
+  float* r1 = nullptr;   // rstd of the attention norm [T]
+  void* n1 = nullptr;    // normed input [T,H]
+  void* qkv = nullptr;   // [T, QKV] (q, k after RoPE)
+  void* o = nullptr;     // attention output [T, nq*d]
+  float* lse = nullptr;  // [n_seq, nq, S]
+  float* h1 = nullptr;   // residual after attention (fp32 [T,H])
+  float* r2 = nullptr;   // rstd of the MLP norm [T]
+  void* n2 = nullptr;    // [T,H]
+  void* gu = nullptr;    // [T, 2F] (gate | up)
+  void* a = nullptr;     // silu(gate)*up [T, F]
+};
+
+enum OpKind { OP_FWD = 0, OP_RECOMP = 1, OP_BWD = 2, OP_HEAD = 3 };
+struct Op {
+  OpKind kind;
+  int layer;  // 0-based
+  int block;  // checkpoint block of the layer
+  int pos;    // position inside the block
+};
+
+struct Stats {
+  double fb_ms = 0, step_ms = 0, h2d_bytes = 0, d2h_bytes = 0, h2d_busy_ms = 0, d2h_busy_ms = 0,
+         compute_busy_ms = 0, fwd_ms = 0, recomp_ms = 0, bwd_ms = 0, head_ms = 0, host_embed_ms = 0;
+  int n_weight_streams = 0;
+  int tokens = 0;
+};
+
+}  // namespace hol
+
+struct hol_model {
+  hol_config cfg{};
+  // derived shape
+  int L = 0, H = 0, nq = 0, nkv = 0, d = 0, F = 0, V = 0, QKV = 0, nqd = 0;
+  int E = 4;  // bytes per compute element
+  hol::DType dt = hol::DT_F32;
+  int Tmax = 0, Smax = 0, K = 1, nblocks = 0, n_ckpt = 0;
+  std::vector<hol::TensorDesc> tensors;
+
+  // host state (flat arrays; per layer contiguous in device grad-block order)
+  int64_t n_flat = 0, layer_flat0 = 0, layer_flat_n = 0, head_flat0 = 0, head_flat_n = 0, embed_flat0 = -1;
+  float* master = nullptr;   // fp32 masters
+  float* grad = nullptr;     // fp32 accumulated gradients (pinned)
+  float* mom1 = nullptr;
+  float* mom2 = nullptr;
+  uint8_t* image = nullptr;  // low-precision copy, layer-contiguous, 4 KiB aligned (pinned)
+  int64_t layer_img_bytes = 0, head_img_bytes = 0, image_bytes = 0;
+  int64_t o_wqkv = 0, o_wo = 0, o_wgu = 0, o_wd = 0, o_g1 = 0, o_g2 = 0;  // layer image offsets
+  int64_t o_gf = 0, o_wout = 0;                                           // head image offsets
+  int64_t g_wqkv = 0, g_wo = 0, g_wgu = 0, g_wd = 0, g_g1 = 0, g_g2 = 0;  // layer grad offsets (floats)
+
+  // pinned host staging
+  float* h_stage = nullptr;      // [Tmax, H] embedding rows up / first-layer gradient down
+  float* grad_stage = nullptr;   // layer grad block (accumulate mode)
+  float* head_stage = nullptr;   // head grad (accumulate mode)
+  float* loss_stage = nullptr;   // [Tmax]
+  int32_t* lab_stage = nullptr;  // [Tmax]
+  float* w_stage = nullptr;      // [Tmax]
+
+  // device
+  hipStream_t sc = nullptr, sh2d = nullptr, sd2h = nullptr;
+  uint8_t* slot[2] = {nullptr, nullptr};
+  int slot_layer[2] = {-1, -1};
+  hipEvent_t ev_ready[2] = {}, ev_free[2] = {}, ev_gdone[2] = {}, ev_gfree[2] = {}, ev_head = nullptr;
+  uint8_t* head_dev = nullptr;
+  float* gdev[2] = {nullptr, nullptr};
+  float* head_gdev = nullptr;
+  float* ckpt = nullptr;
+  uint8_t* act_mem = nullptr;
+  int64_t act_stride = 0;
+  int64_t ao_hin = 0, ao_r1 = 0, ao_n1 = 0, ao_qkv = 0, ao_o = 0, ao_lse = 0, ao_h1 = 0, ao_r2 = 0, ao_n2 = 0,
+          ao_gu = 0, ao_a = 0;
+  float* hbuf[2] = {nullptr, nullptr};
+  float* dh = nullptr;
+  float* dn = nullptr;
+  void* dhb = nullptr;
+  void* dqkv = nullptr;
+  void* dO = nullptr;
+  void* da = nullptr;
+  void* dgu = nullptr;
+  float* delta = nullptr;
+  float* partial = nullptr;
+  void* zbuf = nullptr;
+  float* rz = nullptr;
+  float* logits = nullptr;
+  void* dlogits = nullptr;
+  int Tc = 0;
+  int32_t* labels_dev = nullptr;
+  float* w_dev = nullptr;
+  float* rowloss_dev = nullptr;
+  float* cos_dev = nullptr;
+  float* sin_dev = nullptr;
+  std::vector<void*> dev_allocs;
+  std::vector<void*> pinned_allocs;
+  std::vector<hipEvent_t> tev;  // timing events
+  int tev_used = 0;
+
+  int64_t step_t = 0;
+  bool poisoned = false;
+  bool grads_zero = true;
+  hol::Stats stats;
+};
+
+namespace hol {
+hol_status engine_create(const hol_config* cfg, hol_model** out);
+void engine_destroy(hol_model* m);
+hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out);
+hol_status engine_step(hol_model* m);
+hol_status engine_zero_grad(hol_model* m);
+void refresh_image_tensor(hol_model* m, const TensorDesc& t);
+std::string stats_json(const hol_model* m);
+void set_error(const std::string& s);
+}  // namespace hol

@@ -1,0 +1,321 @@
+// Row-wise and elementwise kernels of the decoder-layer template: RMSNorm forward/backward, RoPE,
+// SwiGLU, casts, the next-token cross entropy of the loss anchor and the sum-of-squares loss.
+// All are HBM-bound: one wavefront per row, 16-byte vector accesses, wavefront reductions, and
+// deterministic two-stage reductions (no atomics) for the RMSNorm gain gradient.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hol {
+
+// ------------------------------------------------------------------------------------------
+// RMSNorm
+// ------------------------------------------------------------------------------------------
+template <typename TO>
+__device__ __forceinline__ void store4(TO* p, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) { *(float4*)p = v; }
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
+  bf16x4 b = {(bf16)v.x, (bf16)v.y, (bf16)v.z, (bf16)v.w};
+  *(bf16x4*)p = b;
+}
+
+// one wavefront per row; H % 4 == 0
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const float* __restrict__ x, const float* __restrict__ g,
+                                                     float eps, TO* __restrict__ y, float* __restrict__ rstd,
+                                                     int T, int H) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= T) return;
+  const float* xr = x + (int64_t)row * H;
+  float ss = 0.f;
+  for (int j = lane * 4; j < H; j += 256) {
+    float4 v = *(const float4*)(xr + j);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (lane == 0) rstd[row] = r;
+  TO* yr = y + (int64_t)row * H;
+  for (int j = lane * 4; j < H; j += 256) {
+    float4 v = *(const float4*)(xr + j);
+    float4 gg = *(const float4*)(g + j);
+    store4<TO>(yr + j, make_float4(v.x * r * gg.x, v.y * r * gg.y, v.z * r * gg.z, v.w * r * gg.w));
+  }
+}
+
+int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, DType yt, float* rstd,
+                       int T, int H, hipStream_t s) {
+  if (T <= 0) return 0;
+  if (H % 4) return (int)hipErrorInvalidValue;
+  dim3 grid((T + 3) / 4);
+  if (yt == DT_BF16) hipLaunchKernelGGL(rmsnorm_fwd_k<bf16>, grid, dim3(256), 0, s, x, gamma, eps, (bf16*)y, rstd, T, H);
+  else hipLaunchKernelGGL(rmsnorm_fwd_k<float>, grid, dim3(256), 0, s, x, gamma, eps, (float*)y, rstd, T, H);
+  return (int)hipGetLastError();
+}
+
+constexpr int RMS_BWD_BLOCKS = 256;
+int rmsnorm_bwd_blocks(int T) { return T < RMS_BWD_BLOCKS * 4 ? (T + 3) / 4 : RMS_BWD_BLOCKS; }
+
+// Each block handles rows blockIdx.x*4 + wave, stepping by gridDim.x*4; NV = float4s per lane.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ g, const float* __restrict__ rstd,
+                                                     float* __restrict__ dx, int accumulate,
+                                                     float* __restrict__ partial, int T, int H) {
+  __shared__ float red[4][NV * 256];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float4 dg[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) dg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int row = blockIdx.x * 4 + w; row < T; row += gridDim.x * 4) {
+    const float r = rstd[row];
+    const float* xr = x + (int64_t)row * H;
+    const float* dyr = dy + (int64_t)row * H;
+    float4 xv[NV], dv[NV];
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = lane * 4 + i * 256;
+      if (j < H) {
+        xv[i] = *(const float4*)(xr + j);
+        dv[i] = *(const float4*)(dyr + j);
+        const float4 gg = *(const float4*)(g + j);
+        // xhat = x r ; dxhat = dy g ; accumulate dg += dy xhat and dot += dxhat xhat
+        dg[i].x += dv[i].x * xv[i].x * r; dg[i].y += dv[i].y * xv[i].y * r;
+        dg[i].z += dv[i].z * xv[i].z * r; dg[i].w += dv[i].w * xv[i].w * r;
+        dv[i].x *= gg.x; dv[i].y *= gg.y; dv[i].z *= gg.z; dv[i].w *= gg.w;
+        dot += (dv[i].x * xv[i].x + dv[i].y * xv[i].y + dv[i].z * xv[i].z + dv[i].w * xv[i].w) * r;
+      }
+    }
+    dot = wave_sum(dot) / (float)H;
+    float* dxr = dx + (int64_t)row * H;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = lane * 4 + i * 256;
+      if (j < H) {
+        float4 o;
+        o.x = r * (dv[i].x - xv[i].x * r * dot); o.y = r * (dv[i].y - xv[i].y * r * dot);
+        o.z = r * (dv[i].z - xv[i].z * r * dot); o.w = r * (dv[i].w - xv[i].w * r * dot);
+        if (accumulate) {
+          const float4 p = *(const float4*)(dxr + j);
+          o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
+        }
+        *(float4*)(dxr + j) = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) *(float4*)&red[w][lane * 4 + i * 256] = dg[i];
+  __syncthreads();
+  for (int j = threadIdx.x; j < H; j += 256)
+    partial[(int64_t)blockIdx.x * H + j] = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
+}
+
+__global__ void reduce_cols_add_k(const float* __restrict__ partial, int nb, int H, float* __restrict__ out) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= H) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b) s += partial[(int64_t)b * H + j];
+  out[j] += s;
+}
+
+int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd, float* dx_out,
+                       bool accumulate, float* dgamma_acc, float* partial, int T, int H, hipStream_t s) {
+  if (T <= 0) return 0;
+  if (H % 4 || H > 4096) return (int)hipErrorInvalidValue;
+  const int nb = rmsnorm_bwd_blocks(T);
+  const int nv = (H + 255) / 256;
+#define RB(NVV)                                                                                   \
+  hipLaunchKernelGGL(rmsnorm_bwd_k<NVV>, dim3(nb), dim3(256), 0, s, dy, x, gamma, rstd, dx_out, \
+                     (int)accumulate, partial, T, H)
+  if (nv <= 1) RB(1);
+  else if (nv <= 2) RB(2);
+  else if (nv <= 4) RB(4);
+  else if (nv <= 8) RB(8);
+  else RB(16);
+#undef RB
+  if (dgamma_acc) hipLaunchKernelGGL(reduce_cols_add_k, dim3((H + 255) / 256), dim3(256), 0, s, partial, nb, H, dgamma_acc);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// RoPE (rotate-half). One thread per rotated pair.
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void rope_k(T* __restrict__ x, int64_t ld, int Tn, int heads, int d, int S,
+                       const float* __restrict__ cs, const float* __restrict__ sn, float sgn) {
+  const int half = d >> 1;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)Tn * heads * half;
+  if (i >= total) return;
+  const int j = (int)(i % half);
+  const int64_t th = i / half;
+  const int h = (int)(th % heads);
+  const int64_t t = th / heads;
+  const int p = (int)(t % S);
+  T* row = x + t * ld + (int64_t)h * d;
+  const float c = cs[(int64_t)p * half + j], s_ = sgn * sn[(int64_t)p * half + j];
+  const float a = to_f(row[j]), b = to_f(row[j + half]);
+  row[j] = from_f<T>(a * c - b * s_);
+  row[j + half] = from_f<T>(b * c + a * s_);
+}
+
+int launch_rope(void* x, DType xt, int64_t ld, int T, int heads, int d, int S, const float* cos_t,
+                const float* sin_t, bool inverse, hipStream_t s) {
+  const int64_t total = (int64_t)T * heads * (d / 2);
+  if (total <= 0) return 0;
+  const float sgn = inverse ? -1.f : 1.f;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (xt == DT_BF16) hipLaunchKernelGGL(rope_k<bf16>, grid, dim3(256), 0, s, (bf16*)x, ld, T, heads, d, S, cos_t, sin_t, sgn);
+  else hipLaunchKernelGGL(rope_k<float>, grid, dim3(256), 0, s, (float*)x, ld, T, heads, d, S, cos_t, sin_t, sgn);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// SwiGLU
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+
+template <typename T>
+__global__ void swiglu_fwd_k(const T* __restrict__ gu, T* __restrict__ a, int Tn, int F) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)Tn * F) return;
+  const int64_t t = i / F;
+  const int f = (int)(i % F);
+  const float g = to_f(gu[t * 2 * F + f]), u = to_f(gu[t * 2 * F + F + f]);
+  a[i] = from_f<T>(g * sigm(g) * u);
+}
+
+template <typename T>
+__global__ void swiglu_bwd_k(const T* __restrict__ da, const T* __restrict__ gu, T* __restrict__ dgu, int Tn, int F) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)Tn * F) return;
+  const int64_t t = i / F;
+  const int f = (int)(i % F);
+  const float g = to_f(gu[t * 2 * F + f]), u = to_f(gu[t * 2 * F + F + f]);
+  const float d = to_f(da[i]);
+  const float sg = sigm(g);
+  dgu[t * 2 * F + f] = from_f<T>(d * u * sg * (1.f + g * (1.f - sg)));
+  dgu[t * 2 * F + F + f] = from_f<T>(d * g * sg);
+}
+
+int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_t s) {
+  const int64_t n = (int64_t)T * F;
+  if (n <= 0) return 0;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (t == DT_BF16) hipLaunchKernelGGL(swiglu_fwd_k<bf16>, grid, dim3(256), 0, s, (const bf16*)gu, (bf16*)a, T, F);
+  else hipLaunchKernelGGL(swiglu_fwd_k<float>, grid, dim3(256), 0, s, (const float*)gu, (float*)a, T, F);
+  return (int)hipGetLastError();
+}
+
+int launch_swiglu_bwd(const void* da, const void* gu, void* dgu, DType t, int T, int F, hipStream_t s) {
+  const int64_t n = (int64_t)T * F;
+  if (n <= 0) return 0;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (t == DT_BF16) hipLaunchKernelGGL(swiglu_bwd_k<bf16>, grid, dim3(256), 0, s, (const bf16*)da, (const bf16*)gu, (bf16*)dgu, T, F);
+  else hipLaunchKernelGGL(swiglu_bwd_k<float>, grid, dim3(256), 0, s, (const float*)da, (const float*)gu, (float*)dgu, T, F);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// casts and fills
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void cast_k(const float* __restrict__ x, T* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = from_f<T>(x[i]);
+}
+__global__ void fill_k(float* x, float v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+__global__ void scale_k(const float* x, float a, float* y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = a * x[i];
+}
+
+int launch_cast_f32(const float* x, void* y, DType yt, int64_t n, hipStream_t s) {
+  if (n <= 0) return 0;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (yt == DT_BF16) hipLaunchKernelGGL(cast_k<bf16>, grid, dim3(256), 0, s, x, (bf16*)y, n);
+  else hipLaunchKernelGGL(cast_k<float>, grid, dim3(256), 0, s, x, (float*)y, n);
+  return (int)hipGetLastError();
+}
+int launch_fill_f32(float* x, float v, int64_t n, hipStream_t s) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(fill_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, v, n);
+  return (int)hipGetLastError();
+}
+int launch_scale_f32(const float* x, float a, float* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(scale_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, a, y, n);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// cross entropy over rows of fp32 logits (loss anchor). One 256-thread block per row:
+// online (max, sum-exp) in one pass, then the weighted softmax-minus-onehot gradient.
+// ------------------------------------------------------------------------------------------
+template <typename TD>
+__global__ __launch_bounds__(256) void ce_k(const float* __restrict__ z, int64_t ld, const int32_t* __restrict__ lab,
+                                            const float* __restrict__ wt, float* __restrict__ row_loss,
+                                            TD* __restrict__ dz, int64_t ldd, int V) {
+  __shared__ float red[16];
+  const int row = blockIdx.x;
+  const float* zr = z + (int64_t)row * ld;
+  float m = -INFINITY, s = 0.f;
+  for (int j = threadIdx.x; j < V; j += 256) {
+    const float v = zr[j];
+    if (v > m) { s = s * __expf(m - v) + 1.f; m = v; }
+    else s += __expf(v - m);
+  }
+  // combine (m, s) across the block
+  const float M = block_max(m, red);
+  s = (m == -INFINITY) ? 0.f : s * __expf(m - M);
+  const float S = block_sum(s, red);
+  const float lse = M + __logf(S);
+  const int y = lab[row];
+  const float w = wt[row];
+  if (threadIdx.x == 0) row_loss[row] = (y >= 0) ? w * (lse - zr[y]) : 0.f;
+  TD* dr = dz + (int64_t)row * ldd;
+  for (int j = threadIdx.x; j < V; j += 256) {
+    float p = __expf(zr[j] - lse);
+    if (j == y) p -= 1.f;
+    dr[j] = from_f<TD>(y >= 0 ? w * p : 0.f);
+  }
+}
+
+int launch_ce_fwd_bwd(const float* logits, int64_t ld, const int32_t* labels, const float* w, float* row_loss,
+                      void* dlogits, DType dt, int64_t ldd, int Tc, int V, hipStream_t s) {
+  if (Tc <= 0) return 0;
+  if (dt == DT_BF16) hipLaunchKernelGGL(ce_k<bf16>, dim3(Tc), dim3(256), 0, s, logits, ld, labels, w, row_loss, (bf16*)dlogits, ldd, V);
+  else hipLaunchKernelGGL(ce_k<float>, dim3(Tc), dim3(256), 0, s, logits, ld, labels, w, row_loss, (float*)dlogits, ldd, V);
+  return (int)hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void sumsq_k(const float* __restrict__ h, float* __restrict__ row_loss,
+                                               float* __restrict__ dh, int T, int H) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= T) return;
+  const float* hr = h + (int64_t)row * H;
+  float* dr = dh + (int64_t)row * H;
+  float ss = 0.f;
+  for (int j = lane; j < H; j += 64) {
+    const float v = hr[j];
+    ss += v * v;
+    dr[j] = 2.f * v;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) row_loss[row] = ss;
+}
+
+int launch_sumsq(const float* h, float* row_loss, float* dh, int T, int H, hipStream_t s) {
+  if (T <= 0) return 0;
+  hipLaunchKernelGGL(sumsq_k, dim3((T + 3) / 4), dim3(256), 0, s, h, row_loss, dh, T, H);
+  return (int)hipGetLastError();
+}
+
+}  // namespace hol

@@ -1,0 +1,90 @@
+// Host-callable launchers of the HIP kernels that make up the weight-free decoder-layer template
+// (MegaTrain summary page, 核心方法: a stateless template pool of Attention and MLP kernels bound
+// to whatever weights were streamed in). Every pointer is a device pointer; every launcher is
+// asynchronous on `stream` and returns 0 or a hipError_t code.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace hol {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// GEMM epilogues
+enum Epi : int {
+  EPI_STORE = 0,   // C = alpha * A.B
+  EPI_ACCUM = 1,   // C += alpha * A.B          (C fp32)
+  EPI_RESID = 2,   // C = R + alpha * A.B       (C, R fp32; R may alias C)
+};
+
+// C[M,N] (op) sum_k A(m,k) B(k,n)
+//   A(m,k) = a_km ? A[k*lda + m] : A[m*lda + k]
+//   B(k,n) = b_kn ? B[k*ldb + n] : B[n*ldb + k]
+// Forward y = x W^T: a_km = 0, b_kn = 0. dX = dY W: a_km = 0, b_kn = 1. dW += dY^T X: a_km = 1, b_kn = 1.
+// `batch` > 1 repeats the product with element strides sA, sB, sC (and sR).
+struct Gemm {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr; int64_t lda = 0; bool a_km = false;
+  const void* B = nullptr; int64_t ldb = 0; bool b_kn = false;
+  void* C = nullptr; int64_t ldc = 0;
+  const float* R = nullptr; int64_t ldr = 0;
+  DType ab = DT_F32, c = DT_F32;
+  int epi = EPI_STORE;
+  float alpha = 1.f;
+  int batch = 1; int64_t sA = 0, sB = 0, sC = 0, sR = 0;
+};
+int launch_gemm(const Gemm& g, hipStream_t s);
+
+// RMSNorm forward: y = x * rstd * gamma, rstd = 1/sqrt(mean(x^2)+eps). x fp32 [T,H].
+int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, DType yt,
+                       float* rstd, int T, int H, hipStream_t s);
+// RMSNorm backward. dx_out = (accumulate ? dx_out : 0) + dx; dgamma_acc += sum_t dy*x*rstd.
+// `partial` is scratch of nb*H floats, nb = rmsnorm_bwd_blocks(T).
+int rmsnorm_bwd_blocks(int T);
+int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd,
+                       float* dx_out, bool accumulate, float* dgamma_acc, float* partial,
+                       int T, int H, hipStream_t s);
+
+// RoPE (rotate-half) on `heads` heads of width d at row stride ld (elements); position = t % S.
+// inverse = rotation by the negative angle (the backward).
+int launch_rope(void* x, DType xt, int64_t ld, int T, int heads, int d, int S, const float* cos_t,
+                const float* sin_t, bool inverse, hipStream_t s);
+
+// SwiGLU: gu holds [g | u] row-wise ([T, 2F], g first); a = silu(g) * u.
+int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_t s);
+// dgu = [dg | du] from da.
+int launch_swiglu_bwd(const void* da, const void* gu, void* dgu, DType t, int T, int F, hipStream_t s);
+
+// Elementwise helpers
+int launch_cast_f32(const float* x, void* y, DType yt, int64_t n, hipStream_t s);
+int launch_fill_f32(float* x, float v, int64_t n, hipStream_t s);
+int launch_scale_f32(const float* x, float a, float* y, int64_t n, hipStream_t s);
+
+// Causal GQA attention for `n_seq` sequences of length S. q/k/v/o are rows of a token-major
+// activation ([T, *] with row strides ldq, ldk, ldv, ldo). lse fp32 [n_seq, nq, S].
+struct Attn {
+  int n_seq = 0, S = 0, nq = 0, nkv = 0, d = 0;
+  DType t = DT_F32;
+  const void* q = nullptr; const void* k = nullptr; const void* v = nullptr;
+  int64_t ldq = 0, ldk = 0, ldv = 0;
+  void* o = nullptr; int64_t ldo = 0;
+  float* lse = nullptr;
+  // backward
+  const void* dO = nullptr; int64_t lddo = 0;
+  void* dq = nullptr; void* dk = nullptr; void* dv = nullptr;
+  int64_t lddq = 0, lddk = 0, lddv = 0;
+  float* delta = nullptr;    // scratch fp32 [n_seq, nq, S]
+};
+int launch_attn_fwd(const Attn& a, hipStream_t s);
+int launch_attn_bwd(const Attn& a, hipStream_t s);
+
+// Next-token cross entropy over one chunk of rows. logits fp32 [Tc, V]; labels int32 (-1 =
+// ignore); w fp32 per-row weight (1/count of the row's micro-batch, 0 if ignored).
+// row_loss[t] = w[t] * (lse - z[label]); dlogits = w[t] * (softmax - onehot) in type dt.
+int launch_ce_fwd_bwd(const float* logits, int64_t ld, const int32_t* labels, const float* w,
+                      float* row_loss, void* dlogits, DType dt, int64_t ldd, int Tc, int V,
+                      hipStream_t s);
+// Sum of squares: row_loss[t] = sum_j h^2, dh = 2h.
+int launch_sumsq(const float* h, float* row_loss, float* dh, int T, int H, hipStream_t s);
+
+}  // namespace hol

@@ -1,0 +1,158 @@
+/* hol.h - layer-streamed training with host-resident model state on one AMD MI355X (gfx950).
+ *
+ * The GPU holds no persistent model state (RoundPipe popular article §二, the computation-dispatch
+ * paradigm; MegaTrain summary page, 研究动机 and 核心方法: host memory owns parameters, optimiser
+ * state and accumulated gradients, device memory holds only a template pool). One call of
+ * hol_forward_backward streams every decoder layer's weights host->HBM into one of two slots,
+ * binds them to a weight-free layer template, runs the forward pass keeping a checkpoint every K
+ * layers, then runs the loss anchor and a block-wise backward (recompute each block from its
+ * checkpoint, then backward layer by layer), streaming each layer's gradient back to the host
+ * (MegaTrain summary page, 方法步骤详情 phases 1-3). hol_step runs Adam on the host (phase 4).
+ *
+ * The two training calls follow the RoundPipe user guide (核心概念): forward_backward(input,
+ * label, loss_fn) returns the SUM of the micro-batch losses and accumulates gradients
+ * (输入分割与 microbatch 执行), and step() runs the optimiser then zero_grad().
+ *
+ * Conventions
+ *  - Every pointer argument is a HOST pointer owned by the caller, read or written only during
+ *    the call (the library copies what it keeps). Device memory is private to the library.
+ *  - Calls are synchronous. A model is not re-entrant; distinct models are independent.
+ *  - All functions return hol_status. On error, hol_last_error() returns a message
+ *    (thread-local, valid until the next call on the same thread).
+ *  - HOL_EINVAL is returned before any work is done and leaves the model untouched.
+ *  - A device failure inside forward_backward or step returns HOL_EDEVICE and poisons the model:
+ *    further forward_backward / step return HOL_ESTATE until hol_zero_grad() is called.
+ *  - Allocation failures (HOL_ENOMEM_HOST / HOL_ENOMEM_DEVICE) come from hol_create only: all
+ *    host and device memory is planned and allocated there.
+ */
+#ifndef HOL_H
+#define HOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HOL_OK = 0,
+  HOL_EINVAL = -1,        /* bad argument, shape or state; nothing was done */
+  HOL_ENOMEM_HOST = -2,   /* host (pageable or pinned) allocation failed in hol_create */
+  HOL_ENOMEM_DEVICE = -3, /* HBM allocation failed in hol_create */
+  HOL_EDEVICE = -4,       /* HIP runtime or kernel failure; the model is poisoned */
+  HOL_ESTATE = -5,        /* model poisoned by an earlier device error */
+  HOL_EUNSUPPORTED = -6   /* configuration this build does not implement */
+} hol_status;
+
+typedef enum { HOL_F32 = 0, HOL_BF16 = 1 } hol_dtype;   /* compute dtype; masters/Adam are fp32 */
+typedef enum { HOL_LOSS_NEXT_TOKEN_CE = 0, HOL_LOSS_SUM_SQUARES = 1 } hol_loss;
+
+typedef struct hol_model hol_model; /* opaque, library-owned */
+
+/* Model and run configuration. Layer math (not fixed by the pages; the plain reading):
+ * pre-norm decoder layer = RMSNorm -> q,k,v projections -> RoPE (rotate-half, theta_j =
+ * rope_base^(-2j/head_dim)) -> causal grouped-query attention (q head h uses kv head
+ * h / (n_q_heads / n_kv_heads)) -> output projection + residual -> RMSNorm -> SwiGLU MLP
+ * (silu(x W_gate^T) * (x W_up^T)) W_down^T + residual. Weights are [out, in] (y = x W^T). */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn;
+  int32_t vocab;              /* > 0: token input with untied embedding and LM head;
+                                 0: hidden-state input, no embedding, no head */
+  int32_t n_experts, top_k, expert_ffn; /* n_experts == 0: dense SwiGLU (MoE: HOL_EUNSUPPORTED) */
+  int32_t lora_rank;          /* 0: full fine-tune (LoRA: HOL_EUNSUPPORTED in this build) */
+  float lora_scale;
+  float rope_base, rms_eps;   /* e.g. 10000, 1e-5 */
+  int32_t ckpt_every_k;       /* keep h_0, h_K, h_2K, ... in HBM (MegaTrain: checkpoint every K) */
+  hol_dtype compute_dtype;    /* HOL_F32 or HOL_BF16 (bf16 operands, fp32 accumulation) */
+  float lr, beta1, beta2, adam_eps, weight_decay; /* weight_decay must be 0 */
+  int32_t device;             /* HIP device ordinal */
+  int32_t max_tokens;         /* largest batch*seq passed to forward_backward (sizes the HBM plan) */
+  int32_t max_seq;            /* longest sequence (sizes the RoPE table) */
+} hol_config;
+
+/* One forward_backward input. tokens: int32 [batch*seq] (vocab > 0); labels: int32
+ * [batch*seq] or NULL for next-token labels (last position of every sequence ignored); a label
+ * of -1 is ignored. hidden_in: fp32 [batch*seq*hidden] when vocab == 0. The batch is split into
+ * n_micro contiguous groups of batch/n_micro sequences (RoundPipe user guide, 输入分割与
+ * microbatch 执行); batch % n_micro != 0 is HOL_EINVAL. */
+typedef struct {
+  const int32_t* tokens;
+  const int32_t* labels;
+  const float* hidden_in;
+  int32_t batch, seq, n_micro;
+} hol_batch;
+
+/* Creates a model: plans and allocates all host state (fp32 masters, Adam m/v, pinned fp32
+ * gradients, pinned layer-contiguous low-precision image with 4 KiB-aligned sub-tensors) and all
+ * device memory (two weight slots, head buffer, checkpoint store, block activation store,
+ * gradient buffers). Weights start at zero; load them with hol_set_tensor. */
+hol_status hol_create(const hol_config* cfg, hol_model** out);
+void hol_destroy(hol_model* m);
+
+/* Tensor directory: index i in [0, n). name is NUL-terminated (truncated to cap). shape[0..ndim-1].
+ * trainable == 0 for frozen tensors. */
+hol_status hol_num_tensors(const hol_model* m, int32_t* n);
+hol_status hol_tensor_info(const hol_model* m, int32_t i, char* name, size_t cap, int64_t shape[4],
+                           int32_t* ndim, int32_t* trainable);
+/* fp32 master <- src (numel floats, row-major) and refresh of the low-precision image. */
+hol_status hol_set_tensor(hol_model* m, int32_t i, const float* src, int64_t numel);
+hol_status hol_get_tensor(const hol_model* m, int32_t i, float* dst, int64_t numel);
+/* Accumulated gradient of a trainable tensor (zeros after hol_step / hol_zero_grad). */
+hol_status hol_get_grad(const hol_model* m, int32_t i, float* dst, int64_t numel);
+/* Adam moments and the step counter (number of hol_step calls so far); set restores them. */
+hol_status hol_get_adam_state(const hol_model* m, int32_t i, float* mom1, float* mom2, int64_t numel,
+                              int64_t* step);
+hol_status hol_set_adam_state(hol_model* m, int32_t i, const float* mom1, const float* mom2,
+                              int64_t numel, int64_t step);
+
+/* Zeroes accumulated gradients and clears the poisoned state. */
+hol_status hol_zero_grad(hol_model* m);
+
+/* One streamed forward + backward over all micro-batches (MegaTrain summary page, 方法步骤详情
+ * phases 1-3). *loss_sum_out = sum over micro-batches of the micro-batch loss: the mean
+ * next-token cross entropy over the micro-batch's labelled positions, or the plain sum of squares
+ * of the last hidden state. Gradients are ADDED to the host accumulators. Returns after every
+ * gradient is in host memory. */
+hol_status hol_forward_backward(hol_model* m, const hol_batch* batch, hol_loss loss,
+                                double* loss_sum_out);
+
+/* Host Adam over every trainable tensor, step counter += 1, refresh of the low-precision image,
+ * then zero_grad (MegaTrain summary page, 方法步骤详情 phase 4; RoundPipe user guide, 核心概念). */
+hol_status hol_step(hol_model* m);
+
+/* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated,
+ * truncated to cap). Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms,
+ * compute_busy_ms, n_weight_streams, per-kernel-class compute ms. */
+hol_status hol_last_stats(const hol_model* m, char* json, size_t cap);
+
+/* Stage partition (host only). RoundPipe popular article §六 and paper summary (方法步骤详情,
+ * step 2): contiguous stages with a bound t_max on every stage's time and a memory cap; forward
+ * and backward partitioned separately (backward filled from the last layer). Objective (reading):
+ * minimise J = (n_micro*(S_f+S_b) + n_gpus*(n_gpus-1)) * t_max over candidate t_max values (every
+ * contiguous sum of t_f and of t_b), ties to the smaller t_max; for each candidate the greedy
+ * pass packs the longest stages allowed. Inputs int64 [L]; outputs: f_bounds[0..*n_f) = first
+ * layer of each forward stage (ascending), b_bounds[0..*n_b) = highest layer of each backward
+ * stage (descending from L-1); both arrays need L entries. *J_out may be NULL. Returns HOL_EINVAL
+ * when some layer exceeds mem_cap or on bad sizes. Exact (integer) result. */
+hol_status hol_partition(const int64_t* t_f, const int64_t* t_b, const int64_t* m_f,
+                         const int64_t* m_b, int32_t L, int64_t mem_cap, int32_t n_gpus,
+                         int32_t n_micro, int32_t* f_bounds, int32_t* n_f, int32_t* b_bounds,
+                         int32_t* n_b, int64_t* t_max, int64_t* J_out);
+
+/* The host optimiser step on one fp32 tensor (what hol_step runs per tensor), exposed for
+ * testing: theta, grad, mom1, mom2 are host arrays of n floats; step_t >= 1. The arithmetic order
+ * is fixed (bias corrections 1 - beta^t in fp64 rounded to fp32 once; no fused multiply-add):
+ * m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2; theta -= (lr m/bc1) / (sqrt(v/bc2) + eps). */
+hol_status hol_host_adam(float* theta, const float* grad, float* mom1, float* mom2, int64_t n,
+                         int64_t step_t, float lr, float beta1, float beta2, float eps);
+/* fp32 -> bf16 round-to-nearest-even (the low-precision refresh), host only. */
+hol_status hol_host_bf16_round(const float* src, uint16_t* dst, int64_t n);
+
+const char* hol_last_error(void);
+const char* hol_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HOL_H */

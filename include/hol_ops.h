@@ -1,0 +1,83 @@
+/* hol_ops.h - the kernels of the weight-free decoder-layer template, one entry point each.
+ *
+ * MegaTrain summary page, 核心方法: the GPU keeps a pool of stateless layer templates, each
+ * wrapping the kernels of the Attention and MLP blocks and holding no weight pointers; streamed
+ * weights are bound to it per layer. These entry points expose those kernels individually (the
+ * same launchers hol_forward_backward uses) so each can be checked in isolation.
+ *
+ * Every data pointer is a DEVICE pointer owned by the caller. `stream` is a hipStream_t (NULL for
+ * the default stream). Calls are asynchronous on that stream and return HOL_OK when the launch
+ * was accepted, HOL_EINVAL for unsupported shapes/alignments, HOL_EDEVICE for launch failures.
+ * Layouts are row-major; dtype 0 = fp32, 1 = bf16 (hol_dtype).
+ */
+#ifndef HOL_OPS_H
+#define HOL_OPS_H
+
+#include <stdint.h>
+
+#include "hol.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[M,N] op= alpha * sum_k A(m,k) B(k,n), fp32 accumulation.
+ *   A(m,k) = a_km ? A[k*lda+m] : A[m*lda+k];   B(k,n) = b_kn ? B[k*ldb+n] : B[n*ldb+k]
+ * epi 0: C = alpha*AB (C fp32 or bf16); 1: C += alpha*AB (C fp32); 2: C = R + alpha*AB (C, R fp32).
+ * bf16 operands need K, lda, ldb multiples of 8 and 16-byte aligned A, B. */
+hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_km,
+                       const void* B, int64_t ldb, int32_t b_kn, void* C, int64_t ldc,
+                       const float* R, int64_t ldr, hol_dtype ab, hol_dtype c, int32_t epi,
+                       float alpha, void* stream);
+
+/* RMSNorm: y = x * rstd * gamma, rstd = 1/sqrt(mean(x^2) + eps); x fp32 [T,H], y [T,H] of
+ * dtype yt, rstd fp32 [T]. H % 4 == 0. */
+hol_status hol_op_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, hol_dtype yt,
+                              float* rstd, int32_t T, int32_t H, void* stream);
+/* Backward: dx (fp32 [T,H]) = dx_in_place_if(accumulate) + d RMSNorm; dgamma (fp32 [H]) +=.
+ * workspace: fp32 buffer of hol_op_rmsnorm_bwd_workspace(T, H) floats. */
+int64_t hol_op_rmsnorm_bwd_workspace(int32_t T, int32_t H);
+hol_status hol_op_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd,
+                              float* dx, int32_t accumulate, float* dgamma, float* workspace,
+                              int32_t T, int32_t H, void* stream);
+
+/* RoPE in place on `heads` heads of width d (row stride ld elements), position = t % S, with
+ * fp32 tables cos/sin [S, d/2]. inverse != 0 rotates by the negative angle (the backward). */
+hol_status hol_op_rope(void* x, hol_dtype t, int64_t ld, int32_t T, int32_t heads, int32_t d,
+                       int32_t S, const float* cos_t, const float* sin_t, int32_t inverse,
+                       void* stream);
+
+/* SwiGLU: gu = [g | u] ([T, 2F]); a = silu(g) u ([T, F]). Backward: dgu = [dg | du]. */
+hol_status hol_op_swiglu_fwd(const void* gu, void* a, hol_dtype t, int32_t T, int32_t F, void* stream);
+hol_status hol_op_swiglu_bwd(const void* da, const void* gu, void* dgu, hol_dtype t, int32_t T,
+                             int32_t F, void* stream);
+
+/* Causal GQA attention over n_seq sequences of length S (token-major rows, T = n_seq*S).
+ * q [T, nq*d] at row stride ldq, k/v [T, nkv*d] at ldk/ldv, o [T, nq*d] at ldo, lse fp32
+ * [n_seq, nq, S]. Scale 1/sqrt(d). */
+hol_status hol_op_attention_fwd(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d,
+                                hol_dtype t, const void* q, int64_t ldq, const void* k, int64_t ldk,
+                                const void* v, int64_t ldv, void* o, int64_t ldo, float* lse,
+                                void* stream);
+/* Backward: dq/dk/dv written (not accumulated). delta: fp32 scratch [n_seq, nq, S]. */
+hol_status hol_op_attention_bwd(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d,
+                                hol_dtype t, const void* q, int64_t ldq, const void* k, int64_t ldk,
+                                const void* v, int64_t ldv, const void* o, int64_t ldo,
+                                const float* lse, const void* dO, int64_t lddo, void* dq,
+                                int64_t lddq, void* dk, int64_t lddk, void* dv, int64_t lddv,
+                                float* delta, void* stream);
+
+/* Cross entropy rows (loss anchor): logits fp32 [Tc, V] (row stride ld); labels int32 [Tc]
+ * (-1 ignored); w fp32 [Tc] per-row weight. row_loss[t] = w[t] (logsumexp - z[label]);
+ * dlogits [Tc, V] (dtype dt, row stride ldd) = w[t] (softmax - onehot). */
+hol_status hol_op_cross_entropy(const float* logits, int64_t ld, const int32_t* labels, const float* w,
+                                float* row_loss, void* dlogits, hol_dtype dt, int64_t ldd, int32_t Tc,
+                                int32_t V, void* stream);
+
+/* Blocks until all work on `stream` is done; HOL_EDEVICE with the HIP error text on failure. */
+hol_status hol_op_sync(void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HOL_OPS_H */

@@ -16,7 +16,9 @@ per step, so that any implementation following the same order agrees bit for bit
     vhat  = v / bc2                 bc2 = f32(1 - b2^t)
     theta = theta - (lr * mhat) / (sqrt(vhat) + eps)
 
-where b1, b2, (1 - b1), (1 - b2), lr and eps are float32 constants ((1 - b) formed in fp64).
+where b1, b2, lr and eps are the configured values rounded to float32 (a configuration holds
+them as float32), and (1 - b1), (1 - b2), bc1, bc2 are formed in fp64 from those float32 values
+and rounded to float32 once.
 """
 from __future__ import annotations
 
@@ -26,8 +28,9 @@ F32 = np.float32
 
 
 def adam_constants(t: int, lr: float, b1: float, b2: float, eps: float):
-    return dict(b1=F32(b1), b2=F32(b2), omb1=F32(1.0 - b1), omb2=F32(1.0 - b2),
-                bc1=F32(1.0 - b1 ** t), bc2=F32(1.0 - b2 ** t), lr=F32(lr), eps=F32(eps))
+    b1d, b2d = float(F32(b1)), float(F32(b2))
+    return dict(b1=F32(b1), b2=F32(b2), omb1=F32(1.0 - b1d), omb2=F32(1.0 - b2d),
+                bc1=F32(1.0 - b1d ** t), bc2=F32(1.0 - b2d ** t), lr=F32(lr), eps=F32(eps))
 
 
 def adam_update(theta: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, t: int,
