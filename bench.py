@@ -1,0 +1,236 @@
+"""Benchmark: layer-streamed training throughput on one MI355X.
+
+One step = hol_forward_backward over one batch (every row of the hot path: weight streaming,
+template kernels, checkpoint/recompute, gradient offload) + hol_step (host Adam and bf16
+refresh). Default workload: LLaMA-3.1-8B-shaped decoder, 4 micro-batches of one 4096-token
+sequence, K = 4, bf16 compute with fp32 host masters; seeded synthetic weights N(0, 0.02) and
+uniform random tokens.
+
+Prints ONE JSON line. Extra fields: fb-only throughput, host step time, H2D/D2H rates against the
+measured pinned-copy peak, per-kernel-class rates, the end-to-end per-layer roofline, and the
+oracle's CPU baseline on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "train tokens/sec on 1 MI355X (8B-shape, seq 4K); MFMA util; H2D GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def link_peak_gbs(torch, nbytes=1 << 30, reps=4):
+    """Pinned hipMemcpyAsync H2D and D2H peak (GB/s) through torch's copy engine path."""
+    h = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d = reps * nbytes / (time.perf_counter() - t) / 1e9
+    t = time.perf_counter()
+    for _ in range(reps):
+        h.copy_(d, non_blocking=True)
+    torch.cuda.synchronize()
+    d2h = reps * nbytes / (time.perf_counter() - t) / 1e9
+    del h, d
+    return h2d, d2h
+
+
+def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int):
+    """Algorithmic FLOPs and streamed bytes of one forward_backward (recompute included)."""
+    s = w.shape
+    H, d, nq, nkv, F, V = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads, s.ffn, s.vocab
+    T, S, M = w.tokens, w.seq, w.batch
+    p_layer = H * (nq * d) * 2 + H * (nkv * d) * 2 + 3 * H * F
+    attn_fwd = 2.0 * d * nq * S * (S + 1) * M
+    f_layer = 4 * (2.0 * p_layer * T) + 4.5 * attn_fwd   # fwd + recompute + bwd (dX, dW)
+    f_head = 3 * 2.0 * H * V * T
+    return dict(p_layer=p_layer, f_layer=f_layer, f_head=f_head,
+                flops=s.n_layers * f_layer + f_head,
+                h2d=n_streams * layer_bytes + head_bytes + 4.0 * T * H)
+
+
+def cpu_baseline(w: W.Workload):
+    """The oracle (NumPy fp32) on a bounded sample of the same workload: one decoder layer's
+    forward, recompute and backward on one 4096-token sequence, the loss anchor on 512 tokens, and
+    Adam on 2^24 parameters; scaled to one step of the full workload."""
+    from oracle import adam as OA
+    from oracle import decoder as D
+    s = D.Shape.of(w.shape)
+    one = w.with_shape(n_layers=1).with_(batch=1)
+    P = W.make_params(one)
+    tok = W.make_tokens(one)
+    S = w.seq
+    cos, sin = D.rope_tables(S, s.head_dim, s.rope_base, np.float32)
+    h = P["embed"][tok.reshape(-1)]
+    G = D.zero_grads(P, s)
+    t0 = time.perf_counter()
+    out, _ = D.layer_forward(P, 0, h, s, 1, cos, sin)
+    _, c = D.layer_forward(P, 0, h, s, 1, cos, sin)
+    D.layer_backward(P, 0, c, np.ones_like(out) * 1e-3, s, 1, cos, sin, G)
+    t_layer = time.perf_counter() - t0
+    del c
+    n_head = 512
+    z = h[:n_head]
+    t0 = time.perf_counter()
+    zz, rz = D.rmsnorm(z, P["final_norm"], s.rms_eps)
+    logits = zz @ P["lm_head"].T
+    lab = tok.reshape(-1)[1:n_head + 1]
+    _, dl = D.cross_entropy(logits, lab)
+    dz = dl @ P["lm_head"]
+    G["lm_head"] += dl.T @ zz
+    D.rmsnorm_bwd(dz, z, P["final_norm"], rz)
+    t_head = time.perf_counter() - t0
+    n_adam = 1 << 24
+    th = P["lm_head"].reshape(-1)[:n_adam].copy()
+    g = G["lm_head"].reshape(-1)[:n_adam].copy()
+    mm = np.zeros_like(th)
+    vv = np.zeros_like(th)
+    t0 = time.perf_counter()
+    OA.adam_update(th, g, mm, vv, 1)
+    t_adam = time.perf_counter() - t0
+    total_params = W.n_params(w.shape)
+    t_step = (w.batch * s.n_layers * t_layer + w.tokens / n_head * t_head
+              + total_params / n_adam * t_adam)
+    try:
+        import threadpoolctl
+        cores = max(x.get("num_threads", 1) for x in threadpoolctl.threadpool_info())
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": w.tokens / t_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"NumPy fp32 oracle: 1 layer fwd+recompute+bwd on 1x{S} tokens ({t_layer:.2f} s), "
+                       f"loss anchor on {n_head} tokens ({t_head:.2f} s), Adam on 2^24 params "
+                       f"({t_adam:.2f} s); scaled to {w.batch}x{s.n_layers} layer passes, "
+                       f"{w.tokens} head tokens, {total_params} params: {t_step:.1f} s/step")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "qwen3_1p7b", "llama8b_16k", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU dispatch is not implemented)"}))
+        sys.exit(2)
+    import torch
+    import host_offloaded_layer_amd as hol
+    w = W.WORKLOADS[args.workload]
+    s = w.shape
+    log(f"[bench] workload {w.name}: L={s.n_layers} H={s.hidden} tokens={w.tokens} K={w.ckpt_every_k}")
+    t0 = time.perf_counter()
+    params = W.make_params(w)
+    tokens = W.make_tokens(w)
+    log(f"[bench] params generated in {time.perf_counter() - t0:.1f} s")
+    cfg = hol.make_config(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab,
+                          ckpt_every_k=w.ckpt_every_k,
+                          compute_dtype=hol.BF16 if w.compute == "bf16" else hol.F32,
+                          max_tokens=w.tokens, max_seq=w.seq, lr=w.lr)
+    t0 = time.perf_counter()
+    m = hol.Model(cfg)
+    m.set_params(params)
+    del params
+    log(f"[bench] model created and loaded in {time.perf_counter() - t0:.1f} s")
+    h2d_peak, d2h_peak = link_peak_gbs(torch)
+    log(f"[bench] pinned copy peak: H2D {h2d_peak:.1f} GB/s, D2H {d2h_peak:.1f} GB/s")
+
+    def one_step():
+        loss = m.forward_backward(w.n_micro, tokens=tokens)
+        fb = m.stats()
+        m.step()
+        st = m.stats()
+        return loss, fb, st["step_ms"]
+
+    for i in range(args.warmup):
+        loss, fb, step_ms = one_step()
+        log(f"[bench] warmup {i}: loss {loss:.4f} fb {fb['fb_ms']:.0f} ms step {step_ms:.0f} ms")
+    m.set_kernel_timing(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    recs = []
+    for i in range(args.steps):
+        loss, fb, step_ms = one_step()
+        recs.append((loss, fb, step_ms))
+        log(f"[bench] step {i}: loss {loss:.4f} fb {fb['fb_ms']:.0f} ms step {step_ms:.0f} ms "
+            f"h2d busy {fb['h2d_busy_ms']:.0f} ms compute busy {fb['compute_busy_ms']:.0f} ms")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    m.set_kernel_timing(False)
+    ms_step = 1e3 * elapsed / args.steps
+    value = w.tokens * args.steps / elapsed
+    fb_ms = float(np.mean([r[1]["fb_ms"] for r in recs]))
+    step_ms = float(np.mean([r[2] for r in recs]))
+    fb0 = recs[-1][1]
+    kern = {}
+    for c in fb0["kernels"]:
+        ms = sum(r[1]["kernels"][c]["ms"] for r in recs)
+        fl = sum(r[1]["kernels"][c]["flops"] for r in recs)
+        by = sum(r[1]["kernels"][c]["bytes"] for r in recs)
+        n = sum(r[1]["kernels"][c]["launches"] for r in recs)
+        if n:
+            kern[c] = {"launches_per_step": n // args.steps, "ms_per_step": ms / args.steps,
+                       "tflops": fl / ms / 1e9 if ms else 0.0, "gbs": by / ms / 1e6 if ms else 0.0}
+    g = kern.get("gemm", {"ms_per_step": 0, "tflops": 0, "launches_per_step": 0})
+    alg = algorithmic(w, fb0["n_weight_streams"], fb0["layer_image_bytes"], fb0["head_image_bytes"])
+    # per-layer roofline: every layer pass bounded by max(MFMA time, streamed bytes / link peak)
+    link = h2d_peak * 1e9
+    per_stream_layer = fb0["n_weight_streams"] / s.n_layers
+    t_layer = max(alg["f_layer"] / (BF16_PEAK_TFLOPS * 1e12), per_stream_layer * fb0["layer_image_bytes"] / link)
+    t_head = max(alg["f_head"] / (BF16_PEAK_TFLOPS * 1e12), fb0["head_image_bytes"] / link)
+    t_roof = s.n_layers * t_layer + t_head
+    h2d_gbs_busy = fb0["h2d_bytes"] / (fb0["h2d_busy_ms"] * 1e6) if fb0["h2d_busy_ms"] else 0.0
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.compute == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x {s.head_dim}, "
+                               f"ffn {s.ffn}, vocab {s.vocab}; {w.n_micro} micro-batches x {w.batch // w.n_micro} x {w.seq} tokens; K={w.ckpt_every_k}",
+                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU, layer streaming)"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_mfma (all decoder and head GEMMs)",
+                     "achieved": round(g["tflops"], 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "fb_tokens_per_s": round(w.tokens / (fb_ms / 1e3), 1), "fb_ms": round(fb_ms, 1), "step_ms": round(step_ms, 1),
+        "loss": recs[-1][0],
+        "e2e_roofline": {"tokens_per_s": round(w.tokens / t_roof, 1), "frac_fb": round(t_roof / (fb_ms / 1e3), 4),
+                         "model": "sum over layers of max(layer FLOPs / bf16 peak, streamed layer bytes / measured H2D peak) + head"},
+        "link": {"h2d_peak_gbs": round(h2d_peak, 1), "d2h_peak_gbs": round(d2h_peak, 1),
+                 "h2d_gbs_busy": round(h2d_gbs_busy, 1), "h2d_gbs_wall": round(fb0["h2d_bytes"] / (fb0["fb_ms"] * 1e6), 1),
+                 "h2d_bytes": fb0["h2d_bytes"], "d2h_bytes": fb0["d2h_bytes"], "weight_streams": fb0["n_weight_streams"]},
+        "model_tflops": round(alg["flops"] / (fb_ms / 1e3) / 1e12, 1),
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in kern.items()},
+    }
+    m.close()
+    del m
+    if not args.no_cpu_baseline and w.name != "tiny":
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(w)
+        log(f"[bench] cpu baseline in {time.perf_counter() - t0:.1f} s")
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,7 +51,7 @@ class Batch(C.Structure):
 
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m host_offloaded_layer_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python host_offloaded_layer_amd/build.py`")
     lib = C.CDLL(LIB_PATH)
     P, I32, I64, F, D = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_double
     sigs = {
@@ -64,6 +64,8 @@ def _load() -> C.CDLL:
         "hol_get_adam_state": [P, I32, P, P, I64, C.POINTER(I64)],
         "hol_set_adam_state": [P, I32, P, P, I64, I64],
         "hol_zero_grad": [P],
+        "hol_set_ckpt_every_k": [P, I32],
+        "hol_set_kernel_timing": [P, I32],
         "hol_forward_backward": [P, C.POINTER(Batch), I32, C.POINTER(D)],
         "hol_step": [P],
         "hol_last_stats": [P, C.c_char_p, C.c_size_t],
@@ -101,7 +103,8 @@ lib = _load()
 # every symbol include/hol.h and include/hol_ops.h declare
 EXPORTED = ["hol_create", "hol_destroy", "hol_num_tensors", "hol_tensor_info", "hol_set_tensor",
             "hol_get_tensor", "hol_get_grad", "hol_get_adam_state", "hol_set_adam_state",
-            "hol_zero_grad", "hol_forward_backward", "hol_step", "hol_last_stats", "hol_partition",
+            "hol_zero_grad", "hol_set_ckpt_every_k", "hol_set_kernel_timing",
+            "hol_forward_backward", "hol_step", "hol_last_stats", "hol_partition",
             "hol_host_adam", "hol_host_bf16_round", "hol_last_error", "hol_version",
             "hol_op_gemm", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
             "hol_op_rope", "hol_op_swiglu_fwd", "hol_op_swiglu_bwd", "hol_op_attention_fwd",
@@ -190,6 +193,12 @@ class Model:
 
     def zero_grad(self) -> None:
         check(lib.hol_zero_grad(self._h))
+
+    def set_ckpt_every_k(self, k: int) -> None:
+        check(lib.hol_set_ckpt_every_k(self._h, k))
+
+    def set_kernel_timing(self, on: bool) -> None:
+        check(lib.hol_set_kernel_timing(self._h, int(on)))
 
     def forward_backward(self, n_micro: int, tokens: Optional[np.ndarray] = None,
                          labels: Optional[np.ndarray] = None, hidden: Optional[np.ndarray] = None,

@@ -1,6 +1,7 @@
 """Builds ``libhol.so`` in-tree: HIP kernels with hipcc for gfx950, host code with g++.
 
-Usage: ``python -m host_offloaded_layer_amd.build`` (or ``build()``). Always recompiles.
+Usage: ``python host_offloaded_layer_amd/build.py`` (run as a script, so the package, which
+loads the library, is not imported first) or ``__graft_entry__.build()``. Always recompiles.
 """
 from __future__ import annotations
 
@@ -16,7 +17,7 @@ OUT = os.path.join(HERE, "libhol.so")
 OBJ = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SRCS = ["k_gemm.hip", "k_elem.hip", "k_attn.hip"]
+HIP_SRCS = ["k_gemm.hip", "k_elem.hip", "k_attn.hip", "k_attn_mfma.hip"]
 CPP_SRCS = ["host_math.cpp", "engine.cpp", "api.cpp"]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

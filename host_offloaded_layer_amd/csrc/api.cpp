@@ -132,6 +132,18 @@ hol_status hol_set_adam_state(hol_model* m, int32_t i, const float* mom1, const 
   return HOL_OK;
 }
 
+hol_status hol_set_ckpt_every_k(hol_model* m, int32_t k) {
+  if (!m) return einval("hol_set_ckpt_every_k", "null model");
+  return engine_set_k(m, k);
+}
+
+hol_status hol_set_kernel_timing(hol_model* m, int32_t on) {
+  GUARD_BEGIN
+  if (!m) return einval("hol_set_kernel_timing", "null model");
+  return engine_set_kernel_timing(m, on != 0);
+  GUARD_END
+}
+
 hol_status hol_zero_grad(hol_model* m) {
   GUARD_BEGIN
   if (!m) return einval("hol_zero_grad", "null model");

@@ -87,8 +87,11 @@ static hol_status validate_config(const hol_config& c) {
     set_error("hol_create: MoE and LoRA layers are not implemented in this build");
     return HOL_EUNSUPPORTED;
   }
-  if (c.ffn <= 0 || c.ffn % 8) return bad("ffn must be a positive multiple of 8");
-  if (c.vocab < 0 || (c.vocab > 0 && c.vocab % 8)) return bad("vocab must be 0 or a multiple of 8");
+  if (c.ffn <= 0) return bad("ffn must be positive");
+  if (c.vocab < 0) return bad("vocab must be >= 0");
+  // bf16 operands go through the MFMA GEMM, whose rows are moved in 16-byte pieces
+  if (c.compute_dtype == HOL_BF16 && (c.ffn % 8 || c.vocab % 8 || c.head_dim % 8))
+    return bad("bf16 compute needs ffn, vocab and head_dim multiples of 8");
   if (c.ckpt_every_k <= 0) return bad("ckpt_every_k must be >= 1");
   if (c.compute_dtype != HOL_F32 && c.compute_dtype != HOL_BF16) return bad("compute_dtype");
   if (c.weight_decay != 0.f) return bad("weight_decay must be 0");
@@ -186,8 +189,9 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->Tmax = c.max_tokens;
   m->Smax = c.max_seq;
   m->K = c.ckpt_every_k;
+  m->Kmax = m->K;
   m->nblocks = (m->L + m->K - 1) / m->K;
-  m->n_ckpt = m->nblocks + 1;
+  m->n_ckpt = m->L + 1;  // enough for any k <= Kmax, down to k = 1
   const int64_t H = m->H, L = m->L, F = m->F, V = m->V, QKV = m->QKV, nqd = m->nqd, E = m->E;
 
   // ---- flat host layout: [embed] [layer 0 .. L-1] [final_norm, lm_head]
@@ -305,7 +309,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->ao_gu = A(T * 2 * F * E);
   m->ao_a = A(T * F * E);
   m->act_stride = a;
-  m->act_mem = (uint8_t*)D((int64_t)m->K * m->act_stride);
+  m->act_mem = (uint8_t*)D((int64_t)m->Kmax * m->act_stride);
   m->hbuf[0] = (float*)D(T * H * 4);
   m->hbuf[1] = (float*)D(T * H * 4);
   m->dh = (float*)D(T * H * 4);
@@ -382,6 +386,8 @@ void engine_destroy(hol_model* m) {
   if (m->ev_head) hipEventDestroy(m->ev_head);
   for (auto e : m->tev)
     if (e) hipEventDestroy(e);
+  for (auto e : m->kev)
+    if (e) hipEventDestroy(e);
   if (m->sc) hipStreamDestroy(m->sc);
   if (m->sh2d) hipStreamDestroy(m->sh2d);
   if (m->sd2h) hipStreamDestroy(m->sd2h);
@@ -447,6 +453,30 @@ static Act act_at(const hol_model* m, int j) {
   return a;
 }
 
+// Runs `launch` on the compute stream; with kernel timing on, brackets it with events and
+// records its class and algorithmic work.
+template <typename F>
+static int timed(hol_model* m, int cls, double flops, double bytes, F&& launch) {
+  if (!m->ktiming || (size_t)m->krec.size() * 2 + 2 > m->kev.size()) return launch();
+  const int e = (int)m->krec.size() * 2;
+  hipError_t r = hipEventRecord(m->kev[e], m->sc);
+  if (r != hipSuccess) return (int)r;
+  const int rc = launch();
+  if (rc) return rc;
+  r = hipEventRecord(m->kev[e + 1], m->sc);
+  if (r != hipSuccess) return (int)r;
+  m->krec.push_back({cls, e, flops, bytes});
+  return 0;
+}
+
+static int run_gemm(hol_model* m, const Gemm& g) {
+  const double E = (g.ab == DT_BF16) ? 2 : 4, Ec = (g.c == DT_BF16) ? 2 : 4;
+  const double bytes = E * ((double)g.M * g.K + (double)g.N * g.K) + Ec * (double)g.M * g.N * (g.epi == EPI_STORE ? 1 : 2);
+  return timed(m, KC_GEMM, 2.0 * g.M * g.N * g.K * g.batch, bytes, [&] { return launch_gemm(g, m->sc); });
+}
+
+#define KT(cls, flops, bytes, expr) KCHECK(timed(m, cls, (double)(flops), (double)(bytes), [&] { return (expr); }))
+
 static Gemm gemm(int M, int N, int K, const void* A, int64_t lda, bool a_km, const void* B, int64_t ldb, bool b_kn,
                  void* C, int64_t ldc, DType ab, DType c, int epi, const float* R = nullptr, int64_t ldr = 0) {
   Gemm g;
@@ -463,21 +493,21 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   const DType dt = m->dt;
   const int64_t E = m->E;
   hipStream_t s = m->sc;
-  KCHECK(launch_rmsnorm_fwd(hin, w.g1, m->cfg.rms_eps, A.n1, dt, A.r1, T, H, s));
-  KCHECK(launch_gemm(gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE), s));
-  KCHECK(launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
-  KCHECK(launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
+  KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hin, w.g1, m->cfg.rms_eps, A.n1, dt, A.r1, T, H, s));
+  KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE)));
+  KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
+  KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
   at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
   at.ldq = at.ldk = at.ldv = QKV;
   at.o = A.o; at.ldo = nqd; at.lse = A.lse;
-  KCHECK(launch_attn_fwd(at, s));
-  KCHECK(launch_gemm(gemm(T, H, nqd, A.o, nqd, false, w.wo, nqd, false, A.h1, H, dt, DT_F32, EPI_RESID, hin, H), s));
-  KCHECK(launch_rmsnorm_fwd(A.h1, w.g2, m->cfg.rms_eps, A.n2, dt, A.r2, T, H, s));
-  KCHECK(launch_gemm(gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE), s));
-  KCHECK(launch_swiglu_fwd(A.gu, A.a, dt, T, F, s));
-  KCHECK(launch_gemm(gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H), s));
+  KT(KC_ATTN_FWD, 2.0 * d * m->nq * (double)S * (S + 1) * n_seq, (double)T * (QKV + nqd) * E, launch_attn_fwd(at, s));
+  KCHECK(run_gemm(m, gemm(T, H, nqd, A.o, nqd, false, w.wo, nqd, false, A.h1, H, dt, DT_F32, EPI_RESID, hin, H)));
+  KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(A.h1, w.g2, m->cfg.rms_eps, A.n2, dt, A.r2, T, H, s));
+  KCHECK(run_gemm(m, gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE)));
+  KT(KC_SWIGLU, 0, 3.0 * T * F * E, launch_swiglu_fwd(A.gu, A.a, dt, T, F, s));
+  KCHECK(run_gemm(m, gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H)));
   return HOL_OK;
 }
 
@@ -490,18 +520,18 @@ static hol_status layer_backward(hol_model* m, const W& w, const Act& A, const f
   const int64_t E = m->E;
   hipStream_t s = m->sc;
   // MLP
-  KCHECK(launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
-  KCHECK(launch_gemm(gemm(T, F, H, m->dhb, H, false, w.wd, F, true, m->da, F, dt, dt, EPI_STORE), s));
-  KCHECK(launch_gemm(gemm(H, F, T, m->dhb, H, true, A.a, F, true, G + m->g_wd, F, dt, DT_F32, EPI_STORE), s));
-  KCHECK(launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
-  KCHECK(launch_gemm(gemm(T, H, 2 * F, m->dgu, 2 * F, false, w.wgu, H, true, m->dn, H, dt, DT_F32, EPI_STORE), s));
-  KCHECK(launch_gemm(gemm(2 * F, H, T, m->dgu, 2 * F, true, A.n2, H, true, G + m->g_wgu, H, dt, DT_F32, EPI_STORE), s));
+  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+  KCHECK(run_gemm(m, gemm(T, F, H, m->dhb, H, false, w.wd, F, true, m->da, F, dt, dt, EPI_STORE)));
+  KCHECK(run_gemm(m, gemm(H, F, T, m->dhb, H, true, A.a, F, true, G + m->g_wd, F, dt, DT_F32, EPI_STORE)));
+  KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
+  KCHECK(run_gemm(m, gemm(T, H, 2 * F, m->dgu, 2 * F, false, w.wgu, H, true, m->dn, H, dt, DT_F32, EPI_STORE)));
+  KCHECK(run_gemm(m, gemm(2 * F, H, T, m->dgu, 2 * F, true, A.n2, H, true, G + m->g_wgu, H, dt, DT_F32, EPI_STORE)));
   KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
-  KCHECK(launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, G + m->g_g2, m->partial, T, H, s));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, G + m->g_g2, m->partial, T, H, s));
   // attention
-  KCHECK(launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
-  KCHECK(launch_gemm(gemm(T, nqd, H, m->dhb, H, false, w.wo, nqd, true, m->dO, nqd, dt, dt, EPI_STORE), s));
-  KCHECK(launch_gemm(gemm(H, nqd, T, m->dhb, H, true, A.o, nqd, true, G + m->g_wo, nqd, dt, DT_F32, EPI_STORE), s));
+  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+  KCHECK(run_gemm(m, gemm(T, nqd, H, m->dhb, H, false, w.wo, nqd, true, m->dO, nqd, dt, dt, EPI_STORE)));
+  KCHECK(run_gemm(m, gemm(H, nqd, T, m->dhb, H, true, A.o, nqd, true, G + m->g_wo, nqd, dt, DT_F32, EPI_STORE)));
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
   at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
@@ -511,12 +541,12 @@ static hol_status layer_backward(hol_model* m, const W& w, const Act& A, const f
   at.dq = m->dqkv; at.dk = (uint8_t*)m->dqkv + (int64_t)nqd * E; at.dv = (uint8_t*)m->dqkv + (int64_t)(nqd + m->nkv * d) * E;
   at.lddq = at.lddk = at.lddv = QKV;
   at.delta = m->delta;
-  KCHECK(launch_attn_bwd(at, s));
-  KCHECK(launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
-  KCHECK(launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
-  KCHECK(launch_gemm(gemm(T, H, QKV, m->dqkv, QKV, false, w.wqkv, H, true, m->dn, H, dt, DT_F32, EPI_STORE), s));
-  KCHECK(launch_gemm(gemm(QKV, H, T, m->dqkv, QKV, true, A.n1, H, true, G + m->g_wqkv, H, dt, DT_F32, EPI_STORE), s));
-  KCHECK(launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, G + m->g_g1, m->partial, T, H, s));
+  KT(KC_ATTN_BWD, 5.0 * d * m->nq * (double)S * (S + 1) * n_seq, (double)T * (2 * QKV + 3 * nqd) * E, launch_attn_bwd(at, s));
+  KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
+  KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
+  KCHECK(run_gemm(m, gemm(T, H, QKV, m->dqkv, QKV, false, w.wqkv, H, true, m->dn, H, dt, DT_F32, EPI_STORE)));
+  KCHECK(run_gemm(m, gemm(QKV, H, T, m->dqkv, QKV, true, A.n1, H, true, G + m->g_wqkv, H, dt, DT_F32, EPI_STORE)));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, G + m->g_g1, m->partial, T, H, s));
   return HOL_OK;
 }
 
@@ -525,7 +555,7 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
   hipStream_t s = m->sc;
   const int H = m->H;
   if (loss == HOL_LOSS_SUM_SQUARES) {
-    KCHECK(launch_sumsq(hL, m->rowloss_dev, m->dh, T, H, s));
+    KT(KC_OTHER, 0, 8.0 * T * H, launch_sumsq(hL, m->rowloss_dev, m->dh, T, H, s));
     return HOL_OK;
   }
   const int V = m->V;
@@ -533,21 +563,21 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
   const int64_t E = m->E;
   const float* gf = (const float*)(m->head_dev + m->o_gf);
   const void* wout = m->head_dev + m->o_wout;
-  KCHECK(launch_rmsnorm_fwd(hL, gf, m->cfg.rms_eps, m->zbuf, dt, m->rz, T, H, s));
+  KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hL, gf, m->cfg.rms_eps, m->zbuf, dt, m->rz, T, H, s));
   float* gW = m->head_gdev + H;
   for (int r0 = 0; r0 < T; r0 += m->Tc) {
     const int tc = std::min(m->Tc, T - r0);
     const void* zc = (const uint8_t*)m->zbuf + (int64_t)r0 * H * E;
-    KCHECK(launch_gemm(gemm(tc, V, H, zc, H, false, wout, H, false, m->logits, V, dt, DT_F32, EPI_STORE), s));
-    KCHECK(launch_ce_fwd_bwd(m->logits, V, m->labels_dev + r0, m->w_dev + r0, m->rowloss_dev + r0, m->dlogits, dt, V,
-                             tc, V, s));
-    KCHECK(launch_gemm(gemm(tc, H, V, m->dlogits, V, false, wout, H, true, m->dn + (int64_t)r0 * H, H, dt, DT_F32,
-                            EPI_STORE), s));
-    KCHECK(launch_gemm(gemm(V, H, tc, m->dlogits, V, true, zc, H, true, gW, H, dt, DT_F32,
-                            r0 == 0 ? EPI_STORE : EPI_ACCUM), s));
+    KCHECK(run_gemm(m, gemm(tc, V, H, zc, H, false, wout, H, false, m->logits, V, dt, DT_F32, EPI_STORE)));
+    KT(KC_CE, 0, (double)tc * V * (4 + E), launch_ce_fwd_bwd(m->logits, V, m->labels_dev + r0, m->w_dev + r0,
+                                                             m->rowloss_dev + r0, m->dlogits, dt, V, tc, V, s));
+    KCHECK(run_gemm(m, gemm(tc, H, V, m->dlogits, V, false, wout, H, true, m->dn + (int64_t)r0 * H, H, dt, DT_F32,
+                            EPI_STORE)));
+    KCHECK(run_gemm(m, gemm(V, H, tc, m->dlogits, V, true, zc, H, true, gW, H, dt, DT_F32,
+                            r0 == 0 ? EPI_STORE : EPI_ACCUM)));
   }
   KCHECK(launch_fill_f32(m->head_gdev, 0.f, H, s));
-  KCHECK(launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, m->head_gdev, m->partial, T, H, s));
+  KT(KC_RMSNORM, 0, 12.0 * T * H, launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, m->head_gdev, m->partial, T, H, s));
   return HOL_OK;
 }
 
@@ -668,6 +698,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   }
   m->slot_layer[0] = m->slot_layer[1] = -1;
   m->tev_used = 0;
+  m->krec.clear();
   auto tev = [&]() -> hipEvent_t { return m->tev[std::min<int>(m->tev_used++, (int)m->tev.size() - 1)]; };
   struct Span { hipEvent_t a, b; int cls; };
   std::vector<Span> spans;  // cls: 0 h2d, 1 d2h, 2 fwd, 3 recomp, 4 bwd, 5 head
@@ -876,6 +907,16 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       case 5: m->stats.head_ms += ms; m->stats.compute_busy_ms += ms; break;
     }
   }
+  for (const auto& r : m->krec) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, m->kev[r.ev], m->kev[r.ev + 1]) != hipSuccess) continue;
+    KStat& k = m->stats.k[r.cls];
+    k.launches++;
+    k.ms += ms;
+    k.flops += r.flops;
+    k.bytes += r.bytes;
+  }
+  m->krec.clear();
   m->stats.fb_ms = now_ms() - t_start;
   (void)E;
   (void)st;
@@ -922,6 +963,25 @@ hol_status engine_step(hol_model* m) {
   return HOL_OK;
 }
 
+hol_status engine_set_k(hol_model* m, int k) {
+  if (k < 1 || k > m->Kmax) {
+    set_error("hol_set_ckpt_every_k: k must be in [1, ckpt_every_k given at create]");
+    return HOL_EINVAL;
+  }
+  m->K = k;
+  m->nblocks = (m->L + k - 1) / k;
+  return HOL_OK;
+}
+
+hol_status engine_set_kernel_timing(hol_model* m, bool on) {
+  if (on && m->kev.empty()) {
+    m->kev.resize(16384);
+    for (auto& e : m->kev) HCHECK(hipEventCreate(&e));
+  }
+  m->ktiming = on;
+  return HOL_OK;
+}
+
 hol_status engine_zero_grad(hol_model* m) {
   if (m->sc) hipStreamSynchronize(m->sc);
   if (m->sh2d) hipStreamSynchronize(m->sh2d);
@@ -943,7 +1003,15 @@ std::string stats_json(const hol_model* m) {
     << ",\"fwd_ms\":" << s.fwd_ms << ",\"recomp_ms\":" << s.recomp_ms << ",\"bwd_ms\":" << s.bwd_ms
     << ",\"head_ms\":" << s.head_ms << ",\"host_embed_ms\":" << s.host_embed_ms
     << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
-    << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads() << "}";
+    << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads();
+  static const char* names[KC_N] = {"gemm", "attn_fwd", "attn_bwd", "rmsnorm", "rope", "swiglu", "ce", "other"};
+  o << ",\"kernels\":{";
+  for (int c = 0; c < KC_N; ++c) {
+    if (c) o << ",";
+    o << "\"" << names[c] << "\":{\"launches\":" << s.k[c].launches << ",\"ms\":" << s.k[c].ms
+      << ",\"flops\":" << s.k[c].flops << ",\"bytes\":" << s.k[c].bytes << "}";
+  }
+  o << "}}";
   return o.str();
 }
 

@@ -47,11 +47,18 @@ struct Op {
   int pos;    // position inside the block
 };
 
+enum KClass { KC_GEMM = 0, KC_ATTN_FWD, KC_ATTN_BWD, KC_RMSNORM, KC_ROPE, KC_SWIGLU, KC_CE, KC_OTHER, KC_N };
+struct KStat {
+  int launches = 0;
+  double ms = 0, flops = 0, bytes = 0;
+};
+
 struct Stats {
   double fb_ms = 0, step_ms = 0, h2d_bytes = 0, d2h_bytes = 0, h2d_busy_ms = 0, d2h_busy_ms = 0,
          compute_busy_ms = 0, fwd_ms = 0, recomp_ms = 0, bwd_ms = 0, head_ms = 0, host_embed_ms = 0;
   int n_weight_streams = 0;
   int tokens = 0;
+  KStat k[KC_N];
 };
 
 }  // namespace hol
@@ -62,7 +69,7 @@ struct hol_model {
   int L = 0, H = 0, nq = 0, nkv = 0, d = 0, F = 0, V = 0, QKV = 0, nqd = 0;
   int E = 4;  // bytes per compute element
   hol::DType dt = hol::DT_F32;
-  int Tmax = 0, Smax = 0, K = 1, nblocks = 0, n_ckpt = 0;
+  int Tmax = 0, Smax = 0, K = 1, Kmax = 1, nblocks = 0, n_ckpt = 0;
   std::vector<hol::TensorDesc> tensors;
 
   // host state (flat arrays; per layer contiguous in device grad-block order)
@@ -122,6 +129,10 @@ struct hol_model {
   std::vector<void*> pinned_allocs;
   std::vector<hipEvent_t> tev;  // timing events
   int tev_used = 0;
+  bool ktiming = false;                 // per-kernel-launch events
+  std::vector<hipEvent_t> kev;          // pool for per-kernel events
+  struct KRec { int cls; int ev; double flops, bytes; };
+  std::vector<KRec> krec;
 
   int64_t step_t = 0;
   bool poisoned = false;
@@ -135,6 +146,8 @@ void engine_destroy(hol_model* m);
 hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out);
 hol_status engine_step(hol_model* m);
 hol_status engine_zero_grad(hol_model* m);
+hol_status engine_set_k(hol_model* m, int k);
+hol_status engine_set_kernel_timing(hol_model* m, bool on);
 void refresh_image_tensor(hol_model* m, const TensorDesc& t);
 std::string stats_json(const hol_model* m);
 void set_error(const std::string& s);

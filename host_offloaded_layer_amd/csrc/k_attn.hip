@@ -5,7 +5,8 @@
 // blocks; nothing is accumulated with atomics, so a recompute reproduces results bit for bit.
 //
 // This file holds the plain LDS-tiled version (fp32 arithmetic on fp32 or bf16 storage): tiles
-// of 64 queries x 64 keys, 4 threads per row. It serves the fp32 path and any head width.
+// of 64 queries x 64 keys, 4 threads per row. It serves the fp32 path and head widths the matrix-
+// core kernels (k_attn_mfma.hip: bf16, head width 64 or 128) do not take.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -278,6 +279,11 @@ __global__ __launch_bounds__(256) void attn_dq_tiled(Attn a) {
   }
 }
 
+bool attn_mfma_supported(const Attn& a);
+bool attn_mfma_bwd_supported(const Attn& a);
+int launch_attn_fwd_mfma(const Attn& a, hipStream_t s);
+int launch_attn_bwd_mfma(const Attn& a, hipStream_t s);
+
 static size_t tiled_smem(int d) { return (size_t)(4 * AT_B * (d + 1) + AT_B * 65) * sizeof(float); }
 
 template <typename K>
@@ -288,6 +294,7 @@ static void allow_smem(K kern, size_t bytes) {
 int launch_attn_fwd(const Attn& a, hipStream_t s) {
   if (a.n_seq <= 0 || a.S <= 0) return 0;
   if (a.d > 128 || a.nkv <= 0 || a.nq % a.nkv) return (int)hipErrorInvalidValue;
+  if (attn_mfma_supported(a)) return launch_attn_fwd_mfma(a, s);
   const size_t sm = tiled_smem(a.d) - AT_B * (a.d + 1) * sizeof(float);
   dim3 grid((a.S + AT_B - 1) / AT_B, a.nq, a.n_seq);
   if (a.t == DT_BF16) {
@@ -303,6 +310,7 @@ int launch_attn_fwd(const Attn& a, hipStream_t s) {
 int launch_attn_bwd(const Attn& a, hipStream_t s) {
   if (a.n_seq <= 0 || a.S <= 0) return 0;
   if (a.d > 128 || a.nkv <= 0 || a.nq % a.nkv) return (int)hipErrorInvalidValue;
+  if (attn_mfma_bwd_supported(a)) return launch_attn_bwd_mfma(a, s);
   const size_t sm = tiled_smem(a.d);
   const int64_t rows = (int64_t)a.n_seq * a.S * a.nq;
   const int nt = (a.S + AT_B - 1) / AT_B;

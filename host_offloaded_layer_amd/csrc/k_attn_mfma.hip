@@ -1,0 +1,476 @@
+// Causal grouped-query attention on CDNA4 matrix cores (bf16 operands, fp32 accumulation and
+// softmax), head width 64 or 128: the Attention block of the weight-free layer template
+// (MegaTrain summary page, 核心方法). Forward keeps the log-sum-exp per query; backward recomputes
+// P from it. Deterministic: the dK/dV kernel owns a key tile and loops over the queries and every q
+// head of its kv group; the dQ kernel owns a query tile and loops over the keys; no atomics.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 lane layout (lane l, h = l / 32):
+//   A[i][k]: i = l % 32, k = 8h .. 8h+7           B[k][j]: j = l % 32, k = 8h .. 8h+7
+//   D[i][j]: j = l % 32, i = 8 (r / 4) + 4h + r % 4 for accumulator element r = 0..15
+// A score product computed so that the contraction index of the NEXT product lies along i gives
+// every lane exactly the B fragment of that next product for k-step ks (16 rows):
+//   rows 16 ks + 4h + {0,1,2,3}  and  16 ks + 8 + 4h + {0,1,2,3}  = accumulator elements
+//   4 (2 ks') + {0..3} and 4 (2 ks' + 1) + {0..3} of 32-row block ks / 2 (ks' = ks % 2).
+// The matching A fragment is read from a transposed LDS tile with two 8-byte reads at those rows.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hol {
+
+namespace fa {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero(f32x16& x) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = 0.f;
+}
+
+// B fragment of k-step ks' (0 or 1) inside a 32-row accumulator block
+__device__ __forceinline__ bf16x8 acc_frag(const f32x16& acc, int ksp) {
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[i] = (bf16)acc[8 * ksp + i];
+    b[4 + i] = (bf16)acc[8 * ksp + 4 + i];
+  }
+  return b;
+}
+
+// A fragment from a transposed LDS tile Xt[row][col] (pitch P): row = r, cols 16 ks + 4h + 0..3 and +8
+__device__ __forceinline__ bf16x8 tfrag(const bf16* Xt, int P, int row, int ks, int h) {
+  const bf16* p = Xt + row * P + 16 * ks + 4 * h;
+  const u32x2 lo = *(const u32x2*)p;
+  const u32x2 hi = *(const u32x2*)(p + 8);
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int w = c >> 1;
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) out[c][p] = __builtin_amdgcn_perm(in[2 * p + 1][w], in[2 * p][w], sel);
+  }
+}
+
+// rows [row0, row0 + R) of a token-major matrix (row stride ld, D columns starting at col0) into
+// LDS row-major with pitch P; rows >= nvalid are clamped to the last valid row.
+template <int R, int D>
+__device__ __forceinline__ void load_rows(bf16* dst, int P, const bf16* src, int64_t ld, int64_t row0, int nvalid) {
+  constexpr int CH = R * D / 8;
+  for (int c = threadIdx.x; c < CH; c += 256) {
+    const int r = c / (D / 8), k = (c % (D / 8)) * 8;
+    const int rr = r < nvalid ? r : nvalid - 1;
+    *(u32x4*)(dst + r * P + k) = *(const u32x4*)(src + (row0 + rr) * ld + k);
+  }
+}
+
+// the same rows transposed: dst[d][r] with pitch P (P a multiple of 4 elements)
+template <int R, int D>
+__device__ __forceinline__ void load_rows_t(bf16* dst, int P, const bf16* src, int64_t ld, int64_t row0, int nvalid) {
+  constexpr int NB = (R / 8) * (D / 8);
+  for (int b = threadIdx.x; b < NB; b += 256) {
+    const int rb = b % (R / 8), db = b / (R / 8);
+    u32x4 in[8], out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = rb * 8 + i;
+      const int rr = r < nvalid ? r : nvalid - 1;
+      in[i] = *(const u32x4*)(src + (row0 + rr) * ld + db * 8);
+    }
+    transpose8x8(in, out);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      bf16* q = dst + (db * 8 + c) * P + rb * 8;
+      *(u32x2*)q = u32x2{out[c][0], out[c][1]};
+      *(u32x2*)(q + 4) = u32x2{out[c][2], out[c][3]};
+    }
+  }
+}
+
+// 4 consecutive fp32 values -> 4 bf16 (8-byte store)
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *(bf16x4*)p = v;
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+// ------------------------------------------------------------------------------------------
+// forward: block = 4 waves x 32 queries; key tiles of 64
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_mfma(Attn a) {
+  constexpr int BQ = 128, BK = 64, KP = D + 8, VP = BK + 12;
+  __shared__ bf16 Ks[BK * KP];
+  __shared__ bf16 Vt[D * VP];
+  const int S = a.S;
+  const int nqt = (S + BQ - 1) / BQ;
+  const int qt = nqt - 1 - (int)blockIdx.x;  // longest (latest) query tiles first
+  const int h = blockIdx.y, seq = blockIdx.z;
+  const int kvh = h / (a.nq / a.nkv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int q0 = qt * BQ;
+  const int qi = q0 + 32 * w + lq;  // this lane's query (column of every accumulator)
+  const int64_t base = (int64_t)seq * S;
+  const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
+  const bf16* K = (const bf16*)a.k + (int64_t)kvh * D;
+  const bf16* V = (const bf16*)a.v + (int64_t)kvh * D;
+
+  bf16x8 qf[D / 16];
+  {
+    const bf16* qp = Q + (base + min(qi, S - 1)) * a.ldq;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * hh);
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) zero(o[i]);
+  const float sl2 = LOG2E / sqrtf((float)D);
+  float m = -INFINITY, l = 0.f;
+  const int qmax = min(q0 + BQ, S) - 1;
+  const int nkt = qmax / BK + 1;
+  const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK;
+    const int nk = min(BK, S - k0);
+    __syncthreads();
+    load_rows<BK, D>(Ks, KP, K, a.ldk, base + k0, nk);
+    load_rows_t<BK, D>(Vt, VP, V, a.ldv, base + k0, nk);
+    __syncthreads();
+    if (k0 > wave_qmax) continue;  // every key of this tile is in this wave's future
+    f32x16 s[2];
+    zero(s[0]);
+    zero(s[1]);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *(const bf16x8*)(Ks + (kb * 32 + lq) * KP + 16 * kk + 8 * hh);
+        s[kb] = mfma(kf, qf[kk], s[kb]);
+      }
+    }
+    // s[kb][r] = score(key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi)
+    const bool diag = (k0 + BK - 1 > q0 + 32 * w) || (k0 + BK > S);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = s[kb][r] * sl2;
+        if (diag) {
+          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (kj > qi || kj >= S) v = -INFINITY;
+        }
+        s[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float corr = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = (s[kb][r] == -INFINITY) ? 0.f : exp2f(s[kb][r] - mn);
+        s[kb][r] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    l = l * corr + ls;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= corr;
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const bf16x8 pb = acc_frag(s[ks >> 1], ks & 1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] = mfma(tfrag(Vt, VP, db * 32 + lq, ks, hh), pb, o[db]);
+    }
+  }
+  if (qi < S) {
+    const float inv = 1.f / l;
+    bf16* op = (bf16*)a.o + (base + qi) * a.ldo + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(op + db * 32 + 8 * g + 4 * hh, o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+               o[db][4 * g + 3] * inv);
+    if (hh == 0) a.lse[((int64_t)seq * a.nq + h) * S + qi] = (m + __log2f(l)) * LN2;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// backward, dK/dV: block = 4 waves x 32 keys (128 keys) of one kv head; loops over the q heads
+// of the group and over query tiles of 64 from the diagonal to the end.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
+  constexpr int BKV = 128, BQ = 64, KP = D + 8, TP = BQ + 12;
+  __shared__ bf16 Qs[BQ * KP];
+  __shared__ bf16 Gs[BQ * KP];  // dO
+  __shared__ bf16 Qt[D * TP];
+  __shared__ bf16 Gt[D * TP];
+  __shared__ float lse2[BQ], dlt[BQ];
+  const int S = a.S;
+  const int nkt = (S + BKV - 1) / BKV;
+  const int kt = nkt - 1 - (int)blockIdx.x;  // early keys see the most queries: schedule them first
+  const int kvh = blockIdx.y, seq = blockIdx.z;
+  const int group = a.nq / a.nkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int k0 = kt * BKV;
+  const int kj = k0 + 32 * w + lq;  // this lane's key (column of the S / dP accumulators)
+  const int64_t base = (int64_t)seq * S;
+  const float sl2 = LOG2E / sqrtf((float)D);
+  const float scale = 1.f / sqrtf((float)D);
+
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const int64_t row = base + min(kj, S - 1);
+    const bf16* kp = (const bf16*)a.k + row * a.ldk + (int64_t)kvh * D;
+    const bf16* vp = (const bf16*)a.v + row * a.ldv + (int64_t)kvh * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = *(const bf16x8*)(kp + 16 * kk + 8 * hh);
+      vf[kk] = *(const bf16x8*)(vp + 16 * kk + 8 * hh);
+    }
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    zero(dv[i]);
+    zero(dk[i]);
+  }
+  const int wave_kmin = k0 + 32 * w;
+  const int nqt = (S + BQ - 1) / BQ;
+  for (int hq = 0; hq < group; ++hq) {
+    const int h = kvh * group + hq;
+    const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
+    const bf16* G = (const bf16*)a.dO + (int64_t)h * D;
+    const float* L = a.lse + ((int64_t)seq * a.nq + h) * S;
+    const float* Dl = a.delta + ((int64_t)seq * a.nq + h) * S;
+    for (int qt = k0 / BQ; qt < nqt; ++qt) {
+      const int q0 = qt * BQ;
+      const int nq = min(BQ, S - q0);
+      __syncthreads();
+      load_rows<BQ, D>(Qs, KP, Q, a.ldq, base + q0, nq);
+      load_rows<BQ, D>(Gs, KP, G, a.lddo, base + q0, nq);
+      load_rows_t<BQ, D>(Qt, TP, Q, a.ldq, base + q0, nq);
+      load_rows_t<BQ, D>(Gt, TP, G, a.lddo, base + q0, nq);
+      if (threadIdx.x < BQ) {
+        const int qq = q0 + threadIdx.x;
+        lse2[threadIdx.x] = qq < S ? L[qq] * LOG2E : 0.f;
+        dlt[threadIdx.x] = qq < S ? Dl[qq] : 0.f;
+      }
+      __syncthreads();
+      if (q0 + BQ - 1 < wave_kmin) continue;  // all queries before this wave's keys
+      // S[q][key], dP[q][key] for 2 blocks of 32 queries
+      f32x16 s[2], dp[2];
+      zero(s[0]); zero(s[1]); zero(dp[0]); zero(dp[1]);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = mfma(*(const bf16x8*)(Qs + (qb * 32 + lq) * KP + 16 * kk + 8 * hh), kf[kk], s[qb]);
+          dp[qb] = mfma(*(const bf16x8*)(Gs + (qb * 32 + lq) * KP + 16 * kk + 8 * hh), vf[kk], dp[qb]);
+        }
+      // element r of block qb: query q0 + 32 qb + 8 (r/4) + 4 hh + r%4, key kj
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int qq = q0 + qloc;
+          const bool ok = qq < S && kj <= qq && kj < S;
+          const float p = ok ? exp2f(s[qb][r] * sl2 - lse2[qloc]) : 0.f;
+          s[qb][r] = p;
+          dp[qb][r] = p * (dp[qb][r] - dlt[qloc]);
+        }
+      // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+      for (int ks = 0; ks < BQ / 16; ++ks) {
+        const bf16x8 pb = acc_frag(s[ks >> 1], ks & 1);
+        const bf16x8 sb = acc_frag(dp[ks >> 1], ks & 1);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = mfma(tfrag(Gt, TP, db * 32 + lq, ks, hh), pb, dv[db]);
+          dk[db] = mfma(tfrag(Qt, TP, db * 32 + lq, ks, hh), sb, dk[db]);
+        }
+      }
+    }
+  }
+  if (kj < S) {
+    bf16* dkp = (bf16*)a.dk + (base + kj) * a.lddk + (int64_t)kvh * D;
+    bf16* dvp = (bf16*)a.dv + (base + kj) * a.lddv + (int64_t)kvh * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = db * 32 + 8 * g + 4 * hh;
+        store4(dkp + dd, dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+               dk[db][4 * g + 3] * scale);
+        store4(dvp + dd, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// backward, dQ: block = 4 waves x 32 queries of one q head; key tiles of 64 up to the diagonal
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_dq_mfma(Attn a) {
+  constexpr int BQ = 128, BK = 64, KP = D + 8, TP = BK + 12;
+  __shared__ bf16 Ks[BK * KP];
+  __shared__ bf16 Vs[BK * KP];
+  __shared__ bf16 Kt[D * TP];
+  const int S = a.S;
+  const int nqt = (S + BQ - 1) / BQ;
+  const int qt = nqt - 1 - (int)blockIdx.x;
+  const int h = blockIdx.y, seq = blockIdx.z;
+  const int kvh = h / (a.nq / a.nkv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int q0 = qt * BQ;
+  const int qi = q0 + 32 * w + lq;
+  const int64_t base = (int64_t)seq * S;
+  const float sl2 = LOG2E / sqrtf((float)D);
+  const float scale = 1.f / sqrtf((float)D);
+  const bf16* K = (const bf16*)a.k + (int64_t)kvh * D;
+  const bf16* V = (const bf16*)a.v + (int64_t)kvh * D;
+
+  bf16x8 qf[D / 16], gf[D / 16];
+  {
+    const int64_t row = base + min(qi, S - 1);
+    const bf16* qp = (const bf16*)a.q + row * a.ldq + (int64_t)h * D;
+    const bf16* gp = (const bf16*)a.dO + row * a.lddo + (int64_t)h * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * hh);
+      gf[kk] = *(const bf16x8*)(gp + 16 * kk + 8 * hh);
+    }
+  }
+  const bool qv = qi < S;
+  const float lse_q = qv ? a.lse[((int64_t)seq * a.nq + h) * S + qi] * LOG2E : 0.f;
+  const float dl_q = qv ? a.delta[((int64_t)seq * a.nq + h) * S + qi] : 0.f;
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) zero(dq[i]);
+  const int qmax = min(q0 + BQ, S) - 1;
+  const int nkt = qmax / BK + 1;
+  const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK;
+    const int nk = min(BK, S - k0);
+    __syncthreads();
+    load_rows<BK, D>(Ks, KP, K, a.ldk, base + k0, nk);
+    load_rows<BK, D>(Vs, KP, V, a.ldv, base + k0, nk);
+    load_rows_t<BK, D>(Kt, TP, K, a.ldk, base + k0, nk);
+    __syncthreads();
+    if (k0 > wave_qmax) continue;
+    f32x16 s[2], dp[2];
+    zero(s[0]); zero(s[1]); zero(dp[0]); zero(dp[1]);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma(*(const bf16x8*)(Ks + (kb * 32 + lq) * KP + 16 * kk + 8 * hh), qf[kk], s[kb]);
+        dp[kb] = mfma(*(const bf16x8*)(Vs + (kb * 32 + lq) * KP + 16 * kk + 8 * hh), gf[kk], dp[kb]);
+      }
+    // element r of block kb: key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool ok = qv && kk <= qi && kk < S;
+        const float p = ok ? exp2f(s[kb][r] * sl2 - lse_q) : 0.f;
+        dp[kb][r] = p * (dp[kb][r] - dl_q);
+      }
+    // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const bf16x8 sb = acc_frag(dp[ks >> 1], ks & 1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) dq[db] = mfma(tfrag(Kt, TP, db * 32 + lq, ks, hh), sb, dq[db]);
+    }
+  }
+  if (qv) {
+    bf16* dqp = (bf16*)a.dq + (base + qi) * a.lddq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(dqp + db * 32 + 8 * g + 4 * hh, dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale,
+               dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+  }
+}
+
+// delta[seq, h, i] = sum_d dO * O  (one wavefront per (token, head))
+__global__ __launch_bounds__(256) void attn_delta_bf16(Attn a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t total = (int64_t)a.n_seq * a.S * a.nq;
+  if (row >= total) return;
+  const int h = (int)(row % a.nq);
+  const int64_t t = row / a.nq;
+  const bf16* o = (const bf16*)a.o + t * a.ldo + (int64_t)h * a.d;
+  const bf16* g = (const bf16*)a.dO + t * a.lddo + (int64_t)h * a.d;
+  float s = 0.f;
+  for (int j = lane * 2; j < a.d; j += 128) s += (float)o[j] * (float)g[j] + (float)o[j + 1] * (float)g[j + 1];
+  s = wave_sum(s);
+  const int seq = (int)(t / a.S), i = (int)(t % a.S);
+  if (lane == 0) a.delta[((int64_t)seq * a.nq + h) * a.S + i] = s;
+}
+
+bool attn_mfma_supported(const Attn& a) {
+  const bool aligned = ((a.ldq | a.ldk | a.ldv | a.ldo) % 8 == 0) &&
+                       ((((uintptr_t)a.q) | ((uintptr_t)a.k) | ((uintptr_t)a.v) | ((uintptr_t)a.o)) % 16 == 0);
+  return a.t == DT_BF16 && (a.d == 64 || a.d == 128) && aligned;
+}
+
+bool attn_mfma_bwd_supported(const Attn& a) {
+  const bool aligned = ((a.lddo | a.lddq | a.lddk | a.lddv) % 8 == 0) &&
+                       ((((uintptr_t)a.dO) | ((uintptr_t)a.dq) | ((uintptr_t)a.dk) | ((uintptr_t)a.dv)) % 16 == 0);
+  return attn_mfma_supported(a) && aligned;
+}
+
+int launch_attn_fwd_mfma(const Attn& a, hipStream_t s) {
+  dim3 grid((a.S + 127) / 128, a.nq, a.n_seq);
+  if (a.d == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_attn_bwd_mfma(const Attn& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.n_seq * a.S * a.nq;
+  hipLaunchKernelGGL(attn_delta_bf16, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  dim3 gk((a.S + 127) / 128, a.nkv, a.n_seq), gq((a.S + 127) / 128, a.nq, a.n_seq);
+  if (a.d == 128) {
+    hipLaunchKernelGGL(attn_dkdv_mfma<128>, gk, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_dq_mfma<128>, gq, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(attn_dkdv_mfma<64>, gk, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_dq_mfma<64>, gq, dim3(256), 0, s, a);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace hol

@@ -106,6 +106,11 @@ hol_status hol_get_adam_state(const hol_model* m, int32_t i, float* mom1, float*
 hol_status hol_set_adam_state(hol_model* m, int32_t i, const float* mom1, const float* mom2,
                               int64_t numel, int64_t step);
 
+/* Checkpoint interval for later forward_backward calls: 1 <= k <= cfg.ckpt_every_k (the
+ * activation store is planned for cfg.ckpt_every_k layers, the checkpoint store for k = 1).
+ * Results do not depend on k (the recompute repeats the forward bit for bit). */
+hol_status hol_set_ckpt_every_k(hol_model* m, int32_t k);
+
 /* Zeroes accumulated gradients and clears the poisoned state. */
 hol_status hol_zero_grad(hol_model* m);
 
@@ -120,6 +125,11 @@ hol_status hol_forward_backward(hol_model* m, const hol_batch* batch, hol_loss l
 /* Host Adam over every trainable tensor, step counter += 1, refresh of the low-precision image,
  * then zero_grad (MegaTrain summary page, 方法步骤详情 phase 4; RoundPipe user guide, 核心概念). */
 hol_status hol_step(hol_model* m);
+
+/* on != 0: every kernel launch of later forward_backward calls is bracketed by HIP events on the
+ * compute stream and hol_last_stats reports, per kernel class (gemm, attn_fwd, attn_bwd, rmsnorm,
+ * rope, swiglu, ce, other), the launch count, summed duration, algorithmic FLOPs and bytes. */
+hol_status hol_set_kernel_timing(hol_model* m, int32_t on);
 
 /* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated,
  * truncated to cap). Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms,

@@ -1,0 +1,251 @@
+"""Kernel parity on the GPU: every layer-template kernel, called through the C ABI
+(include/hol_ops.h), against the oracle's function on identical seeded inputs.
+
+Inputs of bf16 kernels are rounded to bf16 first and the oracle runs in fp64 on those rounded
+values, so the only differences left are the kernel's fp32 accumulation order and its output
+rounding. Shapes span several tiles plus a ragged tail."""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import host_offloaded_layer_amd as hol  # noqa: E402
+from oracle import decoder as D  # noqa: E402
+
+DEV = "cuda"
+
+
+def dev(a, dtype=torch.float32):
+    return torch.as_tensor(np.ascontiguousarray(a)).to(DEV).to(dtype).contiguous()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bf(a):
+    """Round to bf16 and back (fp64 copy of the rounded values)."""
+    return torch.as_tensor(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def sync():
+    hol.check(hol.lib.hol_op_sync(None))
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+# ------------------------------------------------------------------ GEMM
+def gemm_case(M, N, K, a_km, b_kn, dt, epi, seed=0, out_bf16=False):
+    r = np.random.default_rng(seed)
+    A = r.standard_normal((K, M) if a_km else (M, K)).astype(np.float32)
+    B = r.standard_normal((K, N) if b_kn else (N, K)).astype(np.float32)
+    Rm = r.standard_normal((M, N)).astype(np.float32)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    if dt == hol.BF16:
+        A64, B64 = bf(A), bf(B)
+    else:
+        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    Am = A64.T if a_km else A64
+    Bm = B64 if b_kn else B64.T
+    ref = Am @ Bm
+    # leading dimensions padded to a multiple of 8 (16-byte rows for the bf16 kernel)
+    lda = -(-A.shape[1] // 8) * 8
+    ldb = -(-B.shape[1] // 8) * 8
+    Ap = np.zeros((A.shape[0], lda), np.float32); Ap[:, :A.shape[1]] = A
+    Bp = np.zeros((B.shape[0], ldb), np.float32); Bp[:, :B.shape[1]] = B
+    a, b = dev(Ap, tdt), dev(Bp, tdt)
+    cdt = torch.bfloat16 if out_bf16 else torch.float32
+    c = dev(Rm, cdt) if epi == 1 else torch.zeros((M, N), dtype=cdt, device=DEV)
+    rr = dev(Rm) if epi == 2 else None
+    hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), lda, int(a_km), b.data_ptr(), ldb,
+                                  int(b_kn), c.data_ptr(), N, rr.data_ptr() if rr is not None else None, N,
+                                  dt, hol.BF16 if out_bf16 else hol.F32, epi, 1.0, None))
+    sync()
+    if epi in (1, 2):
+        ref = ref + Rm
+    return host(c), ref
+
+
+@pytest.mark.parametrize("a_km,b_kn", [(0, 0), (0, 1), (1, 1), (1, 0)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (512, 384, 256), (37, 129, 8)])
+def test_gemm_bf16_mfma_layouts(M, N, K, a_km, b_kn):
+    got, ref = gemm_case(M, N, K, a_km, b_kn, hol.BF16, 0)
+    # fp32 accumulation of exact bf16 products: error well below 1e-5 of the typical magnitude
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + math.sqrt(K))) < 1e-5
+
+
+@pytest.mark.parametrize("epi", [1, 2])
+def test_gemm_bf16_epilogues(epi):
+    got, ref = gemm_case(260, 140, 64, 1, 1, hol.BF16, epi, seed=3)
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < 1e-5
+
+
+def test_gemm_bf16_output_rounding():
+    got, ref = gemm_case(256, 128, 128, 0, 0, hol.BF16, 0, seed=4, out_bf16=True)
+    np.testing.assert_allclose(got, ref, rtol=2 ** -8, atol=1e-3)
+
+
+@pytest.mark.parametrize("a_km,b_kn", [(0, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("epi", [0, 1, 2])
+def test_gemm_f32_tiled(a_km, b_kn, epi):
+    got, ref = gemm_case(130, 70, 50, a_km, b_kn, hol.F32, epi, seed=5)
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < 1e-6
+
+
+def test_gemm_rejects_misaligned_bf16():
+    a = torch.zeros(64, 12, dtype=torch.bfloat16, device=DEV)
+    c = torch.zeros(64, 64, device=DEV)
+    st = hol.lib.hol_op_gemm(64, 64, 12, a.data_ptr(), 12, 0, a.data_ptr(), 12, 0, c.data_ptr(), 64, None, 0,
+                             hol.BF16, hol.F32, 0, 1.0, None)
+    assert st == hol.HOL_EINVAL
+
+
+# ------------------------------------------------------------------ RMSNorm
+@pytest.mark.parametrize("H,T,yt", [(64, 37, hol.F32), (4096, 300, hol.BF16), (2048, 1100, hol.F32)])
+def test_rmsnorm_fwd_bwd(H, T, yt):
+    r = np.random.default_rng(H + T)
+    x = r.standard_normal((T, H)).astype(np.float32) * 3
+    g = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    dy = r.standard_normal((T, H)).astype(np.float32)
+    dx0 = r.standard_normal((T, H)).astype(np.float32)
+    xd, gd, dyd = dev(x), dev(g), dev(dy)
+    y = torch.empty((T, H), dtype=torch.bfloat16 if yt == hol.BF16 else torch.float32, device=DEV)
+    rs = torch.empty(T, device=DEV)
+    hol.check(hol.lib.hol_op_rmsnorm_fwd(xd.data_ptr(), gd.data_ptr(), 1e-5, y.data_ptr(), yt, rs.data_ptr(), T, H, None))
+    dx = dev(dx0)
+    dgam = torch.full((H,), 0.5, device=DEV)
+    ws = torch.empty(hol.lib.hol_op_rmsnorm_bwd_workspace(T, H), device=DEV)
+    hol.check(hol.lib.hol_op_rmsnorm_bwd(dyd.data_ptr(), xd.data_ptr(), gd.data_ptr(), rs.data_ptr(), dx.data_ptr(), 1,
+                                         dgam.data_ptr(), ws.data_ptr(), T, H, None))
+    sync()
+    ry, rr = D.rmsnorm(x.astype(np.float64), g.astype(np.float64), 1e-5)
+    rdx, rdg = D.rmsnorm_bwd(dy.astype(np.float64), x.astype(np.float64), g.astype(np.float64), rr)
+    np.testing.assert_allclose(host(rs), rr, rtol=1e-6)
+    tol = 2 ** -8 if yt == hol.BF16 else 1e-6
+    np.testing.assert_allclose(host(y), ry, rtol=tol, atol=tol)
+    np.testing.assert_allclose(host(dx), rdx + dx0, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(host(dgam), rdg + 0.5, rtol=1e-5, atol=1e-4)
+
+
+# ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("dt", [hol.F32, hol.BF16])
+def test_rope_fwd_and_inverse(dt):
+    S, nseq, heads, d, ld = 70, 2, 3, 128, 3 * 128 + 64
+    r = np.random.default_rng(9)
+    x = r.standard_normal((nseq * S, ld)).astype(np.float32)
+    cos, sin = D.rope_tables(S, d, 10000.0, np.float32)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    xd = dev(x, tdt)
+    xin = host(xd)
+    cd, sd = dev(cos), dev(sin)   # keep references: the kernel runs after the call returns
+    hol.check(hol.lib.hol_op_rope(xd.data_ptr(), dt, ld, nseq * S, heads, d, S, cd.data_ptr(),
+                                  sd.data_ptr(), 0, None))
+    sync()
+    out = host(xd)
+    for b in range(nseq):
+        blk = xin[b * S:(b + 1) * S, :heads * d].reshape(S, heads, d)
+        ref = D.rope(blk, cos.astype(np.float64), sin.astype(np.float64)).reshape(S, heads * d)
+        tol = 2 ** -7 if dt == hol.BF16 else 1e-6
+        np.testing.assert_allclose(out[b * S:(b + 1) * S, :heads * d], ref, rtol=tol, atol=tol)
+    np.testing.assert_array_equal(out[:, heads * d:], xin[:, heads * d:])  # untouched columns
+    if dt == hol.F32:
+        hol.check(hol.lib.hol_op_rope(xd.data_ptr(), dt, ld, nseq * S, heads, d, S, cd.data_ptr(), sd.data_ptr(), 1, None))
+        sync()
+        np.testing.assert_allclose(host(xd), xin, atol=1e-5)
+
+
+# ------------------------------------------------------------------ SwiGLU
+@pytest.mark.parametrize("dt", [hol.F32, hol.BF16])
+def test_swiglu_fwd_bwd(dt):
+    T, F = 77, 344
+    r = np.random.default_rng(2)
+    gu = r.standard_normal((T, 2 * F)).astype(np.float32) * 2
+    da = r.standard_normal((T, F)).astype(np.float32)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    gud, dad = dev(gu, tdt), dev(da, tdt)
+    a = torch.empty((T, F), dtype=tdt, device=DEV)
+    dgu = torch.empty((T, 2 * F), dtype=tdt, device=DEV)
+    hol.check(hol.lib.hol_op_swiglu_fwd(gud.data_ptr(), a.data_ptr(), dt, T, F, None))
+    hol.check(hol.lib.hol_op_swiglu_bwd(dad.data_ptr(), gud.data_ptr(), dgu.data_ptr(), dt, T, F, None))
+    sync()
+    g64, u64, da64 = host(gud)[:, :F], host(gud)[:, F:], host(dad)
+    tol = 2 ** -7 if dt == hol.BF16 else 2e-6
+    np.testing.assert_allclose(host(a), D.swiglu(g64, u64), rtol=tol, atol=tol)
+    dg, du = D.swiglu_bwd(da64, g64, u64)
+    np.testing.assert_allclose(host(dgu), np.concatenate([dg, du], 1), rtol=tol, atol=tol)
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("dt,S,nseq,nq,nkv,d", [
+    (hol.F32, 32, 2, 4, 4, 16),
+    (hol.F32, 100, 2, 4, 2, 64),
+    (hol.BF16, 200, 1, 8, 2, 128),
+    (hol.BF16, 130, 2, 4, 1, 128),
+])
+def test_attention_fwd_bwd(dt, S, nseq, nq, nkv, d):
+    r = np.random.default_rng(S + nq)
+    T = nseq * S
+    q = r.standard_normal((T, nq * d)).astype(np.float32)
+    k = r.standard_normal((T, nkv * d)).astype(np.float32)
+    v = r.standard_normal((T, nkv * d)).astype(np.float32)
+    do = r.standard_normal((T, nq * d)).astype(np.float32)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    qd, kd, vd, dod = dev(q, tdt), dev(k, tdt), dev(v, tdt), dev(do, tdt)
+    o = torch.empty((T, nq * d), dtype=tdt, device=DEV)
+    lse = torch.empty((nseq, nq, S), device=DEV)
+    hol.check(hol.lib.hol_op_attention_fwd(nseq, S, nq, nkv, d, dt, qd.data_ptr(), nq * d, kd.data_ptr(), nkv * d,
+                                           vd.data_ptr(), nkv * d, o.data_ptr(), nq * d, lse.data_ptr(), None))
+    dq = torch.empty_like(qd); dk = torch.empty_like(kd); dv = torch.empty_like(vd)
+    delta = torch.empty((nseq, nq, S), device=DEV)
+    hol.check(hol.lib.hol_op_attention_bwd(nseq, S, nq, nkv, d, dt, qd.data_ptr(), nq * d, kd.data_ptr(), nkv * d,
+                                           vd.data_ptr(), nkv * d, o.data_ptr(), nq * d, lse.data_ptr(),
+                                           dod.data_ptr(), nq * d, dq.data_ptr(), nq * d, dk.data_ptr(), nkv * d,
+                                           dv.data_ptr(), nkv * d, delta.data_ptr(), None))
+    sync()
+    q64, k64, v64, do64 = host(qd), host(kd), host(vd), host(dod)
+    o_h = host(o)
+    for b in range(nseq):
+        sl = slice(b * S, (b + 1) * S)
+        ro, rl = D.attention(q64[sl].reshape(S, nq, d), k64[sl].reshape(S, nkv, d), v64[sl].reshape(S, nkv, d))
+        # the backward is checked against the oracle given the kernel's own (rounded) output
+        rdq, rdk, rdv = D.attention_bwd(do64[sl].reshape(S, nq, d), q64[sl].reshape(S, nq, d),
+                                        k64[sl].reshape(S, nkv, d), v64[sl].reshape(S, nkv, d),
+                                        o_h[sl].reshape(S, nq, d), rl)
+        if dt == hol.BF16:
+            assert rel(o_h[sl], ro.reshape(S, -1)) < 6e-3
+            assert rel(host(dq)[sl], rdq.reshape(S, -1)) < 1e-2
+            assert rel(host(dk)[sl], rdk.reshape(S, -1)) < 1e-2
+            assert rel(host(dv)[sl], rdv.reshape(S, -1)) < 1e-2
+        else:
+            np.testing.assert_allclose(o_h[sl], ro.reshape(S, -1), rtol=1e-5, atol=1e-5)
+            np.testing.assert_allclose(host(dq)[sl], rdq.reshape(S, -1), rtol=1e-4, atol=1e-4)
+            np.testing.assert_allclose(host(dk)[sl], rdk.reshape(S, -1), rtol=1e-4, atol=1e-4)
+            np.testing.assert_allclose(host(dv)[sl], rdv.reshape(S, -1), rtol=1e-4, atol=1e-4)
+        np.testing.assert_allclose(host(lse)[b], rl, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------------ cross entropy
+@pytest.mark.parametrize("dt,V", [(hol.F32, 256), (hol.BF16, 5000)])
+def test_cross_entropy_rows(dt, V):
+    Tc = 40
+    r = np.random.default_rng(V)
+    z = (r.standard_normal((Tc, V)) * 2).astype(np.float32)
+    lab = r.integers(0, V, Tc).astype(np.int32)
+    lab[[3, 17]] = -1
+    w = np.where(lab >= 0, 1.0 / np.sum(lab >= 0), 0.0).astype(np.float32)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    zd, ld, wd = dev(z), torch.as_tensor(lab).to(DEV), dev(w)
+    rl = torch.empty(Tc, device=DEV)
+    dz = torch.empty((Tc, V), dtype=tdt, device=DEV)
+    hol.check(hol.lib.hol_op_cross_entropy(zd.data_ptr(), V, ld.data_ptr(), wd.data_ptr(), rl.data_ptr(),
+                                           dz.data_ptr(), dt, V, Tc, V, None))
+    sync()
+    loss, dref = D.cross_entropy(z.astype(np.float64), lab)
+    assert abs(host(rl).sum() - loss) < 1e-5 * loss
+    tol = 2 ** -8 if dt == hol.BF16 else 1e-6
+    np.testing.assert_allclose(host(dz), dref, rtol=tol, atol=tol * np.abs(dref).max())
