@@ -334,6 +334,13 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     m->logits = (float*)D(tc * V * 4);
     m->dlogits = D(tc * V * E);
   }
+  if (m->dt == DT_BF16) {
+    m->wT = D(m->layer_img_bytes);
+    const int64_t Tc64 = V > 0 ? m->Tc : 0;
+    m->yT = D(std::max<int64_t>(T * std::max<int64_t>(2 * F, std::max<int64_t>(QKV, H)), Tc64 * V) * 2);
+    m->xT = D(std::max<int64_t>(T * std::max<int64_t>(F, std::max<int64_t>(nqd, H)), Tc64 * H) * 2);
+    if (V > 0) m->woutT = D(V * H * 2);
+  }
   const int half = m->d / 2;
   m->cos_dev = (float*)D((int64_t)m->Smax * half * 4);
   m->sin_dev = (float*)D((int64_t)m->Smax * half * 4);
@@ -476,6 +483,11 @@ static int run_gemm(hol_model* m, const Gemm& g) {
 }
 
 #define KT(cls, flops, bytes, expr) KCHECK(timed(m, cls, (double)(flops), (double)(bytes), [&] { return (expr); }))
+#define STEP_OK(expr)               \
+  do {                              \
+    hol_status st__ = (expr);       \
+    if (st__ != HOL_OK) return st__; \
+  } while (0)
 
 static Gemm gemm(int M, int N, int K, const void* A, int64_t lda, bool a_km, const void* B, int64_t ldb, bool b_kn,
                  void* C, int64_t ldc, DType ab, DType c, int epi, const float* R = nullptr, int64_t ldr = 0) {
@@ -511,10 +523,92 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   return HOL_OK;
 }
 
+// out[c][r] = in[r][c] (bf16)
+static int tr(hol_model* m, const void* in, int64_t ldi, void* out, int64_t ldo, int R, int C) {
+  return timed(m, KC_TRANSPOSE, 0, 4.0 * R * C, [&] { return launch_transpose_bf16(in, ldi, out, ldo, R, C, m->sc); });
+}
+
+// C[M,N] = A[M,K] B[N,K]^T with both operands K-contiguous (the fast NT kernel)
+static Gemm nt(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+               DType c, int epi = EPI_STORE) {
+  Gemm g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc; g.ab = DT_BF16; g.c = c; g.epi = epi;
+  return g;
+}
+
+// Transposes the resident layer's weights into m->wT (same sub-tensor offsets as the slot):
+// Wqkv^T [H, QKV], Wo^T [nqd, H], Wgu^T [H, 2F], Wd^T [F, H].
+static hol_status transpose_layer_weights(hol_model* m, const W& w) {
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F;
+  uint8_t* t = (uint8_t*)m->wT;
+  KCHECK(tr(m, w.wqkv, H, t + m->o_wqkv, QKV, QKV, H));
+  KCHECK(tr(m, w.wo, nqd, t + m->o_wo, H, H, nqd));
+  KCHECK(tr(m, w.wgu, H, t + m->o_wgu, 2 * F, 2 * F, H));
+  KCHECK(tr(m, w.wd, F, t + m->o_wd, H, H, F));
+  return HOL_OK;
+}
+
+// bf16 backward: identical dataflow to layer_backward, every product as NT.
+static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, const float* hin, float* G, int T,
+                                      int n_seq, int S) {
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
+  const DType dt = DT_BF16;
+  const int64_t E = 2;
+  hipStream_t s = m->sc;
+  const uint8_t* wt = (const uint8_t*)m->wT;
+  const void* WqkvT = wt + m->o_wqkv;  // [H, QKV]
+  const void* WoT = wt + m->o_wo;      // [nqd, H]
+  const void* WguT = wt + m->o_wgu;    // [H, 2F]
+  const void* WdT = wt + m->o_wd;      // [F, H]
+  STEP_OK(transpose_layer_weights(m, w));
+  // MLP: da = dh Wd, dWd = dh^T a
+  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+  KCHECK(run_gemm(m, nt(T, F, H, m->dhb, H, WdT, H, m->da, F, dt)));
+  KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
+  KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
+  KCHECK(run_gemm(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
+  KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
+  // dn2 = dgu Wgu, dWgu = dgu^T n2
+  KCHECK(run_gemm(m, nt(T, H, 2 * F, m->dgu, 2 * F, WguT, 2 * F, m->dn, H, DT_F32)));
+  KCHECK(tr(m, m->dgu, 2 * F, m->yT, T, T, 2 * F));
+  KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
+  KCHECK(run_gemm(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
+  KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, G + m->g_g2, m->partial, T, H, s));
+  // attention output projection: dO = dh1 Wo, dWo = dh1^T o
+  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+  KCHECK(run_gemm(m, nt(T, nqd, H, m->dhb, H, WoT, H, m->dO, nqd, dt)));
+  KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));
+  KCHECK(tr(m, A.o, nqd, m->xT, T, T, nqd));
+  KCHECK(run_gemm(m, nt(H, nqd, T, m->yT, T, m->xT, T, G + m->g_wo, nqd, DT_F32)));
+  Attn at;
+  at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
+  at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
+  at.ldq = at.ldk = at.ldv = QKV;
+  at.o = A.o; at.ldo = nqd; at.lse = A.lse;
+  at.dO = m->dO; at.lddo = nqd;
+  at.dq = m->dqkv; at.dk = (uint8_t*)m->dqkv + (int64_t)nqd * E; at.dv = (uint8_t*)m->dqkv + (int64_t)(nqd + m->nkv * d) * E;
+  at.lddq = at.lddk = at.lddv = QKV;
+  at.delta = m->delta;
+  KT(KC_ATTN_BWD, 5.0 * d * m->nq * (double)S * (S + 1) * n_seq, (double)T * (2 * QKV + 3 * nqd) * E, launch_attn_bwd(at, s));
+  KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
+  KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
+  // q/k/v projections: dn1 = dqkv Wqkv, dWqkv = dqkv^T n1
+  KCHECK(run_gemm(m, nt(T, H, QKV, m->dqkv, QKV, WqkvT, QKV, m->dn, H, DT_F32)));
+  KCHECK(tr(m, m->dqkv, QKV, m->yT, T, T, QKV));
+  KCHECK(tr(m, A.n1, H, m->xT, T, T, H));
+  KCHECK(run_gemm(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, G + m->g_g1, m->partial, T, H, s));
+  return HOL_OK;
+}
+
 // dh (fp32 [T,H]) holds d loss / d h_out on entry and d loss / d h_in on exit; G is the layer's
 // gradient block (fully overwritten).
 static hol_status layer_backward(hol_model* m, const W& w, const Act& A, const float* hin, float* G, int T, int n_seq,
                                  int S) {
+  if (m->dt == DT_BF16) return layer_backward_bf16(m, w, A, hin, G, T, n_seq, S);
   const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
   const DType dt = m->dt;
   const int64_t E = m->E;
@@ -565,10 +659,20 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
   const void* wout = m->head_dev + m->o_wout;
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hL, gf, m->cfg.rms_eps, m->zbuf, dt, m->rz, T, H, s));
   float* gW = m->head_gdev + H;
+  if (dt == DT_BF16) KCHECK(tr(m, wout, H, m->woutT, V, V, H));  // W_out^T [H, V]
   for (int r0 = 0; r0 < T; r0 += m->Tc) {
     const int tc = std::min(m->Tc, T - r0);
     const void* zc = (const uint8_t*)m->zbuf + (int64_t)r0 * H * E;
     KCHECK(run_gemm(m, gemm(tc, V, H, zc, H, false, wout, H, false, m->logits, V, dt, DT_F32, EPI_STORE)));
+    if (dt == DT_BF16) {
+      KT(KC_CE, 0, (double)tc * V * (4 + E), launch_ce_fwd_bwd(m->logits, V, m->labels_dev + r0, m->w_dev + r0,
+                                                               m->rowloss_dev + r0, m->dlogits, dt, V, tc, V, s));
+      KCHECK(run_gemm(m, nt(tc, H, V, m->dlogits, V, m->woutT, V, m->dn + (int64_t)r0 * H, H, DT_F32)));
+      KCHECK(tr(m, m->dlogits, V, m->yT, tc, tc, V));   // dlogits^T [V, tc]
+      KCHECK(tr(m, zc, H, m->xT, tc, tc, H));           // z^T [H, tc]
+      KCHECK(run_gemm(m, nt(V, H, tc, m->yT, tc, m->xT, tc, gW, H, DT_F32, r0 == 0 ? EPI_STORE : EPI_ACCUM)));
+      continue;
+    }
     KT(KC_CE, 0, (double)tc * V * (4 + E), launch_ce_fwd_bwd(m->logits, V, m->labels_dev + r0, m->w_dev + r0,
                                                              m->rowloss_dev + r0, m->dlogits, dt, V, tc, V, s));
     KCHECK(run_gemm(m, gemm(tc, H, V, m->dlogits, V, false, wout, H, true, m->dn + (int64_t)r0 * H, H, dt, DT_F32,
@@ -614,6 +718,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   const int64_t T64 = (int64_t)B * S;
   if (T64 > m->Tmax) return bad("batch*seq exceeds max_tokens");
   if (S > m->Smax) return bad("seq exceeds max_seq");
+  if (m->dt == DT_BF16 && T64 % 8) return bad("bf16 compute needs batch*seq to be a multiple of 8");
   const int T = (int)T64, H = m->H;
   if (loss == HOL_LOSS_NEXT_TOKEN_CE) {
     if (m->V <= 0) return bad("cross entropy needs vocab > 0");
@@ -1004,7 +1109,7 @@ std::string stats_json(const hol_model* m) {
     << ",\"head_ms\":" << s.head_ms << ",\"host_embed_ms\":" << s.host_embed_ms
     << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
     << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads();
-  static const char* names[KC_N] = {"gemm", "attn_fwd", "attn_bwd", "rmsnorm", "rope", "swiglu", "ce", "other"};
+  static const char* names[KC_N] = {"gemm", "attn_fwd", "attn_bwd", "rmsnorm", "rope", "swiglu", "ce", "transpose", "other"};
   o << ",\"kernels\":{";
   for (int c = 0; c < KC_N; ++c) {
     if (c) o << ",";

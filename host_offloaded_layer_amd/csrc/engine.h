@@ -47,7 +47,7 @@ struct Op {
   int pos;    // position inside the block
 };
 
-enum KClass { KC_GEMM = 0, KC_ATTN_FWD, KC_ATTN_BWD, KC_RMSNORM, KC_ROPE, KC_SWIGLU, KC_CE, KC_OTHER, KC_N };
+enum KClass { KC_GEMM = 0, KC_ATTN_FWD, KC_ATTN_BWD, KC_RMSNORM, KC_ROPE, KC_SWIGLU, KC_CE, KC_TRANSPOSE, KC_OTHER, KC_N };
 struct KStat {
   int launches = 0;
   double ms = 0, flops = 0, bytes = 0;
@@ -125,6 +125,12 @@ struct hol_model {
   float* rowloss_dev = nullptr;
   float* cos_dev = nullptr;
   float* sin_dev = nullptr;
+  // bf16 path: every backward product runs as C = A B^T with both operands K-contiguous, so the
+  // layer's weights, the upstream gradients and the saved activations are transposed first
+  void* wT = nullptr;     // transposed weights of the resident layer (layer image size)
+  void* yT = nullptr;     // transposed upstream gradient (largest: [2F, T] or the head's [V, Tc])
+  void* xT = nullptr;     // transposed activation (largest: [F, T])
+  void* woutT = nullptr;  // transposed LM head [H, V]
   std::vector<void*> dev_allocs;
   std::vector<void*> pinned_allocs;
   std::vector<hipEvent_t> tev;  // timing events

@@ -220,6 +220,79 @@ int launch_swiglu_bwd(const void* da, const void* gu, void* dgu, DType t, int T,
 }
 
 // ------------------------------------------------------------------------------------------
+// bf16 transpose out[c][r] = in[r][c] through a 128 x 128 LDS tile: coalesced 16-byte loads of
+// input rows, 8 x 8 register transposes of LDS blocks, coalesced 16-byte stores of output rows.
+// LDS chunk c of tile row r is stored at chunk c ^ ((r / 8) % 16).
+// ------------------------------------------------------------------------------------------
+typedef uint32_t tu32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void tr8x8(const tu32x4 in[8], tu32x4 out[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int w = c >> 1;
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) out[c][p] = __builtin_amdgcn_perm(in[2 * p + 1][w], in[2 * p][w], sel);
+  }
+}
+
+__global__ __launch_bounds__(256) void transpose_bf16_k(const uint16_t* __restrict__ in, int64_t ldi,
+                                                        uint16_t* __restrict__ out, int64_t ldo, int R, int C) {
+  __shared__ tu32x4 tile[128 * 16];
+  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const int t = threadIdx.x;
+  // phase 1: rows r0 + t/16 + 16 k, chunk t % 16
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = t / 16 + 16 * k, ch = t % 16;
+    const int gr = r0 + r, gc = c0 + ch * 8;
+    tu32x4 v = {0u, 0u, 0u, 0u};
+    if (gr < R) {
+      if (gc + 8 <= C) {
+        v = *(const tu32x4*)(in + (int64_t)gr * ldi + gc);
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = gc + j < C ? in[(int64_t)gr * ldi + gc + j] : (uint16_t)0;
+        v = tu32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                   e[6] | ((uint32_t)e[7] << 16)};
+      }
+    }
+    tile[r * 16 + (ch ^ ((r >> 3) & 15))] = v;
+  }
+  __syncthreads();
+  // phase 2: thread owns the 8x8 block (row block rb = t % 16, column chunk cb = t / 16)
+  const int rb = t % 16, cb = t / 16;
+  tu32x4 in8[8], o8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rb * 8 + i;
+    in8[i] = tile[r * 16 + (cb ^ ((r >> 3) & 15))];
+  }
+  tr8x8(in8, o8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int oc = c0 + cb * 8 + j;   // output row
+    const int orr = r0 + rb * 8;      // output column
+    if (oc >= C) continue;
+    if (orr + 8 <= R) {
+      *(tu32x4*)(out + (int64_t)oc * ldo + orr) = o8[j];
+    } else {
+      const uint16_t* e = (const uint16_t*)&o8[j];
+      for (int q = 0; q < 8 && orr + q < R; ++q) out[(int64_t)oc * ldo + orr + q] = e[q];
+    }
+  }
+}
+
+int launch_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, int R, int C, hipStream_t s) {
+  if (R <= 0 || C <= 0) return 0;
+  if (ldi % 8 || ldo % 8 || ((uintptr_t)in | (uintptr_t)out) % 16) return (int)hipErrorInvalidValue;
+  dim3 grid((C + 127) / 128, (R + 127) / 128);
+  hipLaunchKernelGGL(transpose_bf16_k, grid, dim3(256), 0, s, (const uint16_t*)in, ldi, (uint16_t*)out, ldo, R, C);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // casts and fills
 // ------------------------------------------------------------------------------------------
 template <typename T>

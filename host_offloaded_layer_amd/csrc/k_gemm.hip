@@ -6,7 +6,7 @@
 // Two kernels:
 //  * gemm_mfma  - bf16 operands, fp32 accumulation on CDNA4 matrix cores
 //                 (v_mfma_f32_32x32x16_bf16). 256x128x64 block tile, 4 waves of 128x64,
-//                 LDS double buffer with padded K-contiguous rows. Operands stored MN-contiguous
+//                 LDS double buffer with XOR-swizzled K-contiguous rows. Operands stored MN-contiguous
 //                 (the backward layouts) are transposed 8x8 in registers on their way into LDS,
 //                 so every MFMA fragment is one 16-byte LDS read.
 //  * gemm_tiled - plain LDS-tiled FMA kernel for fp32 operands (the fp32 path).
@@ -88,8 +88,14 @@ __global__ __launch_bounds__(256) void gemm_tiled(Gemm g) {
 // bf16 MFMA GEMM
 // ------------------------------------------------------------------------------------------
 constexpr int MF_BM = 256, MF_BN = 128, MF_BK = 64;
-constexpr int MF_P = MF_BK + 8;                 // LDS row pitch (bf16): 144 B, conflict-free b128 reads
+constexpr int MF_P = MF_BK;                      // LDS row pitch (bf16): 128 B = 8 chunks of 16 B
 constexpr int MF_STAGE = (MF_BM + MF_BN) * MF_P; // bf16 elements per LDS stage
+
+// LDS swizzle: logical 16-byte chunk c of tile row r lives at physical chunk c ^ sw(r). Eight
+// consecutive rows (an MFMA fragment read) and rows eight apart (a transposed 8x8 store) both map
+// one chunk onto eight different bank groups.
+__device__ __forceinline__ int sw(int r) { return (r & 7) ^ ((r >> 3) & 7); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * MF_P + ((c ^ sw(r)) << 3); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -160,7 +166,7 @@ struct TileLoader {
     if constexpr (!KM) {
       const int c = t & 7;
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) *(u32x4*)(lds + ((t >> 3) + 32 * i) * MF_P + c * 8) = r[i];
+      for (int i = 0; i < NREG; ++i) *(u32x4*)(lds + lds_off((t >> 3) + 32 * i, c)) = r[i];
     } else {
       constexpr int NB = (ROWS / 8) * (MF_BK / 8);
 #pragma unroll
@@ -169,7 +175,7 @@ struct TileLoader {
         if (b < NB) {
           const int mb = b % (ROWS / 8), kb = b / (ROWS / 8);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) *(u32x4*)(lds + (mb * 8 + j) * MF_P + kb * 8) = r[bi * 8 + j];
+          for (int j = 0; j < 8; ++j) *(u32x4*)(lds + lds_off(mb * 8 + j, kb)) = r[bi * 8 + j];
         }
       }
     }
@@ -228,11 +234,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma(Gemm g) {
 #pragma unroll
     for (int kk = 0; kk < MF_BK / 16; ++kk) {
       bf16x8 a[4], b[2];
-      const int kc = kk * 16 + (lane >> 5) * 8;
+      const int kc = kk * 2 + (lane >> 5);  // logical chunk
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(As + (wm * 128 + i * 32 + (lane & 31)) * MF_P + kc);
+      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(As + lds_off(wm * 128 + i * 32 + (lane & 31), kc));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)(Bs + (wn * 64 + j * 32 + (lane & 31)) * MF_P + kc);
+      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)(Bs + lds_off(wn * 64 + j * 32 + (lane & 31), kc));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -269,6 +275,173 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma(Gemm g) {
     }
 }
 
+
+// ------------------------------------------------------------------------------------------
+// bf16 MFMA GEMM, both operands K-contiguous (the forward products y = x W^T, and any product
+// whose operands were laid out K-contiguous): 256x256 block tile, 4 waves of 128x128 (fp32
+// accumulators in AGPRs), BK = 32, a 4-stage LDS ring filled by global_load_lds_dwordx4 (each
+// lane's 16 bytes land at LDS base + 16 * lane, no register staging), loads issued 4 tiles ahead.
+// Tile rows are 64 bytes (4 chunks of 16 B); two consecutive tile rows share one 128-byte LDS row
+// (chunks 0-3: even row, 4-7: odd row) and the 8 chunks of LDS row R are XOR-swizzled with
+// (R & 7) ^ ((R >> 3) & 7), so any 8 consecutive lanes of a fragment read hit 8 distinct 16-byte
+// bank groups. Requires K % 32 == 0.
+// ------------------------------------------------------------------------------------------
+constexpr int N2_BM = 256, N2_BN = 256, N2_BK = 32, N2_ST = 4;
+constexpr int N2_TILE = (N2_BM + N2_BN) * N2_BK;  // bf16 elements per stage
+
+__device__ __forceinline__ int n2_sw(int R) { return (R & 7) ^ ((R >> 3) & 7); }
+// element offset of logical chunk c (0..3) of tile row r
+__device__ __forceinline__ int n2_off(int r, int c) { return (r >> 1) * 64 + ((((r & 1) << 2) | c) ^ n2_sw(r >> 1)) * 8; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
+
+// Issue this wave's share of one stage: LDS rows [8 q, 8 q + 8) (tile rows [16 q, 16 q + 16)) of
+// the A tile, q = wave, wave+4, wave+8, wave+12, and the same of the B tile. Lane i fills LDS row
+// 8 q + i / 8 at physical chunk i % 8, so it fetches the logical (row, chunk) stored there.
+__device__ __forceinline__ void n2_issue(bf16* stage, const bf16* __restrict__ A, int64_t lda, int m0, int M,
+                                         const bf16* __restrict__ B, int64_t ldb, int n0, int N, int k0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int R = (w + 4 * i) * 8 + (lane >> 3);  // LDS row
+    const int lc = (lane & 7) ^ n2_sw(R);         // logical 8-chunk index: (odd row?) * 4 + chunk
+    const int r = 2 * R + (lc >> 2);              // tile row
+    const int c = lc & 3;
+    int gr = m0 + r;
+    gr = gr < M ? gr : M - 1;
+    const bf16* src = A + (int64_t)gr * lda + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + (w + 4 * i) * 16 * N2_BK), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int R = (w + 4 * i) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ n2_sw(R);
+    const int r = 2 * R + (lc >> 2);
+    const int c = lc & 3;
+    int gr = n0 + r;
+    gr = gr < N ? gr : N - 1;
+    const bf16* src = B + (int64_t)gr * ldb + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + N2_BM * N2_BK + (w + 4 * i) * 16 * N2_BK),
+                                     16, 0, 0);
+  }
+}
+
+template <int EPI, typename TO>
+__global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
+  __shared__ __attribute__((aligned(1024))) bf16 lds[N2_ST * N2_TILE];
+  const int M = g.M, N = g.N, K = g.K;
+  const int z = blockIdx.y;
+  const bf16* __restrict__ A = (const bf16*)g.A + z * g.sA;
+  const bf16* __restrict__ B = (const bf16*)g.B + z * g.sB;
+  const int tiles_m = (M + N2_BM - 1) / N2_BM, tiles_n = (N + N2_BN - 1) / N2_BN;
+  const int ntiles = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+  const int GM = 4;
+  const int group = GM * tiles_n;
+  const int first_m = (pid / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % group) % gsz;
+  const int tn = (pid % group) / gsz;
+  const int m0 = tm * N2_BM, n0 = tn * N2_BN;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / N2_BK;
+  // prologue fills the whole ring: stages 0 .. N2_ST-1; iteration kt refills the slot of stage kt
+  // with stage kt + N2_ST once stage kt is in registers
+#pragma unroll
+  for (int s = 0; s < N2_ST; ++s)
+    if (s < nk) n2_issue(lds + s * N2_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, s * N2_BK);
+
+  // Fragments: F0 = k-step 0 of the current stage, F1 = k-step 1. Each k-step's 16 MFMAs run
+  // while the next k-step's 8 fragments are being read from LDS.
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
+    const bf16* As = st;
+    const bf16* Bs = st + N2_BM * N2_BK;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(As + n2_off(wm * 128 + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(Bs + n2_off(wn * 128 + j * 32 + (lane & 31), c));
+  };
+  auto mma = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  // Stage t is ready for everyone once this wave's loads of it are done (at most `later` later
+  // stages of 8 loads each may still be in flight) and every wave has passed the barrier; the
+  // barrier also certifies that nobody still reads the slot the next issue overwrites.
+  // (__syncthreads would drain every prefetched stage: it waits for all outstanding loads.)
+  // When stage t is awaited, stages up to t + 2 have been issued (t + 3 for t = 0, right after
+  // the prologue).
+  auto stage_ready = [&](int t) {
+    const int later = min(t == 0 ? N2_ST - 1 : N2_ST - 2, nk - 1 - t);
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(24)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  stage_ready(0);
+  frags(lds, 0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const bf16* st = lds + (kt % N2_ST) * N2_TILE;
+    frags(st, 1, a1, b1);
+    mma(a0, b0);
+    if (kt + 1 < nk) {
+      stage_ready(kt + 1);  // stage kt is fully in registers now: its slot can be refilled
+      if (kt + N2_ST < nk)
+        n2_issue(lds + (kt % N2_ST) * N2_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, (kt + N2_ST) * N2_BK);
+      frags(lds + ((kt + 1) % N2_ST) * N2_TILE, 0, a0, b0);
+    }
+    mma(a1, b1);
+  }
+
+  TO* C = (TO*)g.C + z * g.sC;
+  const float* R = g.R ? g.R + z * g.sR : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= M) continue;
+        float v = g.alpha * acc[i][j][r];
+        TO* c = C + (int64_t)row * g.ldc + col;
+        if constexpr (EPI == EPI_ACCUM) v += to_f(*c);
+        if constexpr (EPI == EPI_RESID) v += R[(int64_t)row * g.ldr + col];
+        *c = from_f<TO>(v);
+      }
+    }
+}
+
+template <int EPI, typename TO>
+static int launch_nt2_t(const Gemm& g, hipStream_t s) {
+  const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
+  hipLaunchKernelGGL((gemm_nt2<EPI, TO>), dim3(tiles, g.batch), dim3(256), 0, s, g);
+  return (int)hipGetLastError();
+}
+
+static int launch_nt2(const Gemm& g, hipStream_t s) {
+  if (g.epi == EPI_STORE) return g.c == DT_BF16 ? launch_nt2_t<EPI_STORE, bf16>(g, s) : launch_nt2_t<EPI_STORE, float>(g, s);
+  if (g.epi == EPI_ACCUM) return launch_nt2_t<EPI_ACCUM, float>(g, s);
+  return launch_nt2_t<EPI_RESID, float>(g, s);
+}
+
 template <bool AK, bool BK_, int EPI, typename TO>
 static int launch_mfma_t(const Gemm& g, hipStream_t s) {
   const int tiles = ((g.M + MF_BM - 1) / MF_BM) * ((g.N + MF_BN - 1) / MF_BN);
@@ -298,6 +471,7 @@ int launch_gemm(const Gemm& g, hipStream_t s) {
                          (((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0) &&
                          (g.batch == 1 || (g.sA % 8 == 0 && g.sB % 8 == 0));
     if (!aligned) return (int)hipErrorInvalidValue;
+    if (!g.a_km && !g.b_kn && g.K % N2_BK == 0) return launch_nt2(g, s);
     if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
     if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);
     if (g.a_km && g.b_kn) return launch_mfma_l<true, true>(g, s);

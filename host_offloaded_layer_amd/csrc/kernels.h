@@ -55,6 +55,10 @@ int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_
 // dgu = [dg | du] from da.
 int launch_swiglu_bwd(const void* da, const void* gu, void* dgu, DType t, int T, int F, hipStream_t s);
 
+// out[c][r] = in[r][c] for an R x C bf16 matrix (row strides ldi, ldo; multiples of 8, 16-byte
+// aligned pointers).
+int launch_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, int R, int C, hipStream_t s);
+
 // Elementwise helpers
 int launch_cast_f32(const float* x, void* y, DType yt, int64_t n, hipStream_t s);
 int launch_fill_f32(float* x, float v, int64_t n, hipStream_t s);
