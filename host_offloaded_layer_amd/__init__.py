@@ -67,6 +67,7 @@ def _load() -> C.CDLL:
         "hol_set_ckpt_every_k": [P, I32],
         "hol_set_kernel_timing": [P, I32],
         "hol_forward_backward": [P, C.POINTER(Batch), I32, C.POINTER(D)],
+        "hol_forward_backward_step": [P, C.POINTER(Batch), I32, C.POINTER(D)],
         "hol_step": [P],
         "hol_last_stats": [P, C.c_char_p, C.c_size_t],
         "hol_partition": [P, P, P, P, I32, I64, I32, I32, P, C.POINTER(I32), P, C.POINTER(I32),
@@ -104,7 +105,7 @@ lib = _load()
 EXPORTED = ["hol_create", "hol_destroy", "hol_num_tensors", "hol_tensor_info", "hol_set_tensor",
             "hol_get_tensor", "hol_get_grad", "hol_get_adam_state", "hol_set_adam_state",
             "hol_zero_grad", "hol_set_ckpt_every_k", "hol_set_kernel_timing",
-            "hol_forward_backward", "hol_step", "hol_last_stats", "hol_partition",
+            "hol_forward_backward", "hol_forward_backward_step", "hol_step", "hol_last_stats", "hol_partition",
             "hol_host_adam", "hol_host_bf16_round", "hol_last_error", "hol_version",
             "hol_op_gemm", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
             "hol_op_rope", "hol_op_swiglu_fwd", "hol_op_swiglu_bwd", "hol_op_attention_fwd",
@@ -202,7 +203,7 @@ class Model:
 
     def forward_backward(self, n_micro: int, tokens: Optional[np.ndarray] = None,
                          labels: Optional[np.ndarray] = None, hidden: Optional[np.ndarray] = None,
-                         loss: int = LOSS_CE) -> float:
+                         loss: int = LOSS_CE, and_step: bool = False) -> float:
         b = Batch()
         keep = []
         if tokens is not None:
@@ -221,7 +222,8 @@ class Model:
             b.batch, b.seq = hd.shape[0], hd.shape[1]
         b.n_micro = n_micro
         out = C.c_double()
-        check(lib.hol_forward_backward(self._h, C.byref(b), loss, C.byref(out)))
+        fn = lib.hol_forward_backward_step if and_step else lib.hol_forward_backward
+        check(fn(self._h, C.byref(b), loss, C.byref(out)))
         return out.value
 
     def step(self) -> None:

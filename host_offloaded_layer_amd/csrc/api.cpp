@@ -158,6 +158,13 @@ hol_status hol_forward_backward(hol_model* m, const hol_batch* batch, hol_loss l
   GUARD_END
 }
 
+hol_status hol_forward_backward_step(hol_model* m, const hol_batch* batch, hol_loss loss, double* loss_sum_out) {
+  GUARD_BEGIN
+  if (!m) return einval("hol_forward_backward_step", "null model");
+  return engine_forward_backward(m, batch, loss, loss_sum_out, true);
+  GUARD_END
+}
+
 hol_status hol_step(hol_model* m) {
   GUARD_BEGIN
   if (!m) return einval("hol_step", "null model");

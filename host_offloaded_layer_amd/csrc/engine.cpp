@@ -371,6 +371,14 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     HCHECK(hipEventCreateWithFlags(&m->ev_gfree[i], hipEventDisableTiming));
   }
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
+  m->unit_tensors.assign(m->L + 2, {});
+  for (int i = 0; i < (int)m->tensors.size(); ++i) {
+    const TensorDesc& t = m->tensors[i];
+    const int u = t.block == -2 ? 0 : (t.block == -1 ? m->L + 1 : 1 + t.block);
+    m->unit_tensors[u].push_back(i);
+  }
+  m->ev_unit.resize(m->L + 2);
+  for (auto& e : m->ev_unit) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   // timing events: two per compute op, weight stream and gradient copy (at most ~14 L + 8)
   const int nt = 20 * m->L + 64;
   m->tev.resize(nt);
@@ -394,6 +402,8 @@ void engine_destroy(hol_model* m) {
   for (auto e : m->tev)
     if (e) hipEventDestroy(e);
   for (auto e : m->kev)
+    if (e) hipEventDestroy(e);
+  for (auto e : m->ev_unit)
     if (e) hipEventDestroy(e);
   if (m->sc) hipStreamDestroy(m->sc);
   if (m->sh2d) hipStreamDestroy(m->sh2d);
@@ -700,7 +710,69 @@ static void host_accumulate(void* p) {
   });
 }
 
-hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out) {
+static void adam_unit(hol_model* m, int u, const AdamConsts& k);
+
+// Host worker of the fused forward_backward + step: runs the optimiser on each unit as soon as
+// that unit's gradient copy (enqueued by the main thread, in backward order) has completed.
+struct FusedWorker {
+  hol_model* m;
+  std::thread th;
+  bool running = false;
+  bool failed = false;
+  double busy_ms = 0;
+  void start(const AdamConsts& kc) {
+    {
+      std::lock_guard<std::mutex> g(m->fmu);
+      m->unit_queue.clear();
+      m->fused_abort = false;
+    }
+    running = true;
+    th = std::thread([this, kc] {
+      (void)hipSetDevice(m->cfg.device);
+      size_t next = 0;
+      for (;;) {
+        int u;
+        {
+          std::unique_lock<std::mutex> lk(m->fmu);
+          m->fcv.wait(lk, [&] { return m->fused_abort || next < m->unit_queue.size(); });
+          if (m->fused_abort) return;
+          u = m->unit_queue[next++];
+        }
+        if (u < 0) return;  // every unit handed over
+        if (hipEventSynchronize(m->ev_unit[u]) != hipSuccess) {
+          failed = true;
+          return;
+        }
+        const double t0 = now_ms();
+        adam_unit(m, u, kc);
+        busy_ms += now_ms() - t0;
+      }
+    });
+  }
+  void push(int u) {
+    {
+      std::lock_guard<std::mutex> g(m->fmu);
+      m->unit_queue.push_back(u);
+    }
+    m->fcv.notify_one();
+  }
+  // waits for every handed-over unit (finish) or stops after the current one (abort)
+  void stop(bool abort) {
+    if (!running) return;
+    if (abort) {
+      std::lock_guard<std::mutex> g(m->fmu);
+      m->fused_abort = true;
+    } else {
+      push(-1);
+    }
+    m->fcv.notify_one();
+    th.join();
+    running = false;
+  }
+  ~FusedWorker() { stop(true); }
+};
+
+hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out, bool fuse_step) {
   const double t_start = now_ms();
   // ---- validation (nothing touched before this passes)
   auto bad = [](const std::string& s) {
@@ -779,6 +851,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     hipDeviceSynchronize();
     return s;
   };
+  // (the FusedWorker destructor stops the worker on every early return)
 #define STEP(expr)                    \
   do {                                \
     hol_status s__ = (expr);          \
@@ -826,6 +899,12 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   }
   auto ckpt_of = [&](int idx) { return m->ckpt + (int64_t)idx * T64 * H; };  // idx: block, or nblocks for h_L
   const bool direct = m->grads_zero;
+  // fused optimiser: only when this call's gradients are the whole gradient (nothing accumulated)
+  const bool fused = fuse_step && direct;
+  const hol_config& cf = m->cfg;
+  const AdamConsts kc = adam_consts(m->step_t + 1, cf.lr, cf.beta1, cf.beta2, cf.adam_eps);
+  FusedWorker worker{m};
+  if (fused) worker.start(kc);
 
   // ---- weight streaming helpers
   int last_slot = 1;  // so the first load goes to slot 0
@@ -915,6 +994,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
           job = {m->grad + m->head_flat0, m->head_stage, m->head_flat_n};
           HSTEP(hipLaunchHostFunc(sd, host_accumulate, &job));
         }
+        if (fused) {
+          HSTEP(hipEventRecord(m->ev_unit[m->L + 1], sd));
+          worker.push(m->L + 1);
+        }
       }
       STEP(prefetch());
       continue;
@@ -968,6 +1051,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
         HSTEP(hipLaunchHostFunc(sd, host_accumulate, &jobs[op.layer]));
       }
       HSTEP(hipEventRecord(m->ev_gfree[gi], sd));
+      if (fused) {
+        HSTEP(hipEventRecord(m->ev_unit[1 + op.layer], sd));
+        worker.push(1 + op.layer);
+      }
       m->stats.d2h_bytes += (double)m->layer_flat_n * 4;
       gi ^= 1;
     }
@@ -999,6 +1086,22 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   for (int64_t t = 0; t < T64; ++t) total += (double)m->loss_stage[t];
   *out = total;
   m->grads_zero = false;
+  if (fused) {
+    const double t_gpu_done = now_ms();
+    worker.stop(false);
+    if (worker.failed) {
+      set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
+      return fail(HOL_EDEVICE);
+    }
+    adam_unit(m, 0, kc);  // the embedding gradient is complete only after the host scatter-add
+    m->step_t += 1;
+    m->grads_zero = true;
+    m->stats.step_ms = now_ms() - t_gpu_done;  // optimiser time not hidden under the GPU work
+    m->fused_overlap_ms = worker.busy_ms;
+  } else if (fuse_step) {
+    m->stats.fb_ms = now_ms() - t_start;
+    return engine_step(m);
+  }
   // ---- stats
   for (auto& sp : spans) {
     float ms = 0.f;
@@ -1033,18 +1136,14 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 // ------------------------------------------------------------------------------------------
 // step: host Adam, refresh of the low-precision image, zero_grad
 // ------------------------------------------------------------------------------------------
-hol_status engine_step(hol_model* m) {
-  if (m->poisoned) {
-    set_error("hol_step: model poisoned by an earlier device error; call hol_zero_grad");
-    return HOL_ESTATE;
-  }
-  const double t0 = now_ms();
-  const hol_config& c = m->cfg;
-  const AdamConsts k = adam_consts(m->step_t + 1, c.lr, c.beta1, c.beta2, c.adam_eps);
-  for (const TensorDesc& t : m->tensors) {
+// Adam on every trainable tensor of optimiser unit u, refresh of its low-precision image, and
+// zeroing of its gradients.
+static void adam_unit(hol_model* m, int u, const AdamConsts& k) {
+  for (int ti : m->unit_tensors[u]) {
+    const TensorDesc& t = m->tensors[ti];
     if (!t.trainable) continue;
     float* th = m->master + t.flat;
-    const float* g = m->grad + t.flat;
+    float* g = m->grad + t.flat;
     float* m1 = m->mom1 + t.flat;
     float* m2 = m->mom2 + t.flat;
     const bool to_bf16 = !(t.img_f32 || m->dt == DT_F32) && t.img >= 0 && t.block != -2;
@@ -1058,11 +1157,23 @@ hol_status engine_step(hol_model* m) {
           if (to_bf16) f32_to_bf16_range(th + a, (uint16_t*)dst + a, n);
           else memcpy((float*)dst + a, th + a, (size_t)n * 4);
         }
+        memset(g + a, 0, (size_t)n * 4);
       }
     });
   }
+}
+
+hol_status engine_step(hol_model* m) {
+  if (m->poisoned) {
+    set_error("hol_step: model poisoned by an earlier device error; call hol_zero_grad");
+    return HOL_ESTATE;
+  }
+  const double t0 = now_ms();
+  const hol_config& c = m->cfg;
+  const AdamConsts k = adam_consts(m->step_t + 1, c.lr, c.beta1, c.beta2, c.adam_eps);
+  for (int u = 0; u < (int)m->unit_tensors.size(); ++u) adam_unit(m, u, k);
   m->step_t += 1;
-  parallel_zero(m->grad, m->n_flat * 4);
+  // every trainable gradient was zeroed by its unit; frozen tensors never hold gradients
   m->grads_zero = true;
   m->stats.step_ms = now_ms() - t0;
   return HOL_OK;

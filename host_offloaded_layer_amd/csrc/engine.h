@@ -4,7 +4,10 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <condition_variable>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/hol.h"
@@ -144,12 +147,23 @@ struct hol_model {
   bool poisoned = false;
   bool grads_zero = true;
   hol::Stats stats;
+
+  // optimiser units: 0 = embedding, 1 + l = layer l, L + 1 = final norm and LM head
+  std::vector<std::vector<int>> unit_tensors;
+  // fused forward_backward + step: per-unit gradient-arrival events and the host worker
+  std::vector<hipEvent_t> ev_unit;     // recorded on the d2h stream after a unit's gradient copy
+  std::mutex fmu;
+  std::condition_variable fcv;
+  std::vector<int> unit_queue;         // units whose gradient copy has been enqueued, in order
+  bool fused_abort = false;
+  double fused_overlap_ms = 0, fused_tail_ms = 0;
 };
 
 namespace hol {
 hol_status engine_create(const hol_config* cfg, hol_model** out);
 void engine_destroy(hol_model* m);
-hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out);
+hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out,
+                                  bool fuse_step = false);
 hol_status engine_step(hol_model* m);
 hol_status engine_zero_grad(hol_model* m);
 hol_status engine_set_k(hol_model* m, int k);

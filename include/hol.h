@@ -131,6 +131,14 @@ hol_status hol_step(hol_model* m);
  * rope, swiglu, ce, other), the launch count, summed duration, algorithmic FLOPs and bytes. */
 hol_status hol_set_kernel_timing(hol_model* m, int32_t on);
 
+/* forward_backward followed by step, with the same result bit for bit: when no gradient is
+ * accumulated from earlier calls, each layer's host optimiser update (and the refresh of its
+ * low-precision copy) starts as soon as that layer's gradient is in host memory, so the optimiser
+ * runs under the remaining backward pass; otherwise the two calls run one after the other. A device
+ * error inside the call may leave the step applied to some tensors only (the model is poisoned). */
+hol_status hol_forward_backward_step(hol_model* m, const hol_batch* batch, hol_loss loss,
+                                     double* loss_sum_out);
+
 /* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated,
  * truncated to cap). Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms,
  * compute_busy_ms, n_weight_streams, per-kernel-class compute ms. */

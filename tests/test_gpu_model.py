@@ -137,3 +137,32 @@ def test_bf16_real_layer_shapes_matches_oracle(name):
     must finish in seconds); every kernel runs in the tile configuration of the full workload."""
     w = W.WORKLOADS[name].with_(batch=2, seq=256, n_micro=2).with_shape(n_layers=2)
     _bf16_parity(w, k=1)
+
+
+def _state(m):
+    return {n: (m.get_tensor(n), *m.get_adam_state(n)[:2]) for n in m.index}
+
+
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
+def test_fused_forward_backward_step_is_bitwise_fb_then_step(wname):
+    w = TINY if wname == "tiny" else BF16_SMALL
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+    with lib_model(w, params) as a, lib_model(w, params) as b:
+        for it in range(2):
+            la = lib_fb(a, w, batch)
+            a.step()
+            lb = b.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+            assert la == lb, (it, la, lb)
+        sa, sb = _state(a), _state(b)
+        for n in sa:
+            for x, y in zip(sa[n], sb[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+        # with gradients already accumulated the fused call is the plain sequence
+        lib_fb(a, w, batch); lib_fb(a, w, batch); a.step()
+        lib_fb(b, w, batch); b.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        sa, sb = _state(a), _state(b)
+        for n in sa:
+            for x, y in zip(sa[n], sb[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+            assert not np.any(b.get_grad(n))
