@@ -340,6 +340,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     m->yT = D(std::max<int64_t>(T * std::max<int64_t>(2 * F, std::max<int64_t>(QKV, H)), Tc64 * V) * 2);
     m->xT = D(std::max<int64_t>(T * std::max<int64_t>(F, std::max<int64_t>(nqd, H)), Tc64 * H) * 2);
     if (V > 0) m->woutT = D(V * H * 2);
+    m->qkvf = (float*)D(T * QKV * 4);
   }
   const int half = m->d / 2;
   m->cos_dev = (float*)D((int64_t)m->Smax * half * 4);
@@ -516,9 +517,16 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   const int64_t E = m->E;
   hipStream_t s = m->sc;
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hin, w.g1, m->cfg.rms_eps, A.n1, dt, A.r1, T, H, s));
-  KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE)));
-  KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
-  KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
+  if (dt == DT_BF16) {
+    // fp32 projection output, then RoPE and one rounding to bf16
+    KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, m->qkvf, QKV, dt, DT_F32, EPI_STORE)));
+    KT(KC_ROPE, 0, (double)T * QKV * (4 + E), launch_rope_qkv(m->qkvf, QKV, A.qkv, QKV, T, m->nq, m->nkv, d, S,
+                                                              m->cos_dev, m->sin_dev, s));
+  } else {
+    KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE)));
+    KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
+    KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
+  }
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
   at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;

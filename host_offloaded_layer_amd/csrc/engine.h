@@ -134,6 +134,7 @@ struct hol_model {
   void* yT = nullptr;     // transposed upstream gradient (largest: [2F, T] or the head's [V, Tc])
   void* xT = nullptr;     // transposed activation (largest: [F, T])
   void* woutT = nullptr;  // transposed LM head [H, V]
+  float* qkvf = nullptr;  // fp32 q/k/v projection output before RoPE and the single bf16 rounding
   std::vector<void*> dev_allocs;
   std::vector<void*> pinned_allocs;
   std::vector<hipEvent_t> tev;  // timing events

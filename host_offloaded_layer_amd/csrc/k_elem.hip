@@ -173,6 +173,42 @@ int launch_rope(void* x, DType xt, int64_t ld, int T, int heads, int d, int S, c
   return (int)hipGetLastError();
 }
 
+// RoPE fused with the cast of the projection output: in = fp32 [T, QKV] rows (q heads, k heads,
+// v heads), out = bf16 rows with q and k rotated; one rounding per element. One thread per pair.
+__global__ void rope_qkv_k(const float* __restrict__ in, int64_t ldi, bf16* __restrict__ out, int64_t ldo, int Tn,
+                           int nq, int nkv, int d, int S, const float* __restrict__ cs, const float* __restrict__ sn) {
+  const int half = d >> 1;
+  const int heads = nq + 2 * nkv;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)Tn * heads * half;
+  if (i >= total) return;
+  const int j = (int)(i % half);
+  const int64_t th = i / half;
+  const int h = (int)(th % heads);
+  const int64_t t = th / heads;
+  const float* r = in + t * ldi + (int64_t)h * d;
+  bf16* o = out + t * ldo + (int64_t)h * d;
+  const float a = r[j], b = r[j + half];
+  if (h < nq + nkv) {
+    const int p = (int)(t % S);
+    const float c = cs[(int64_t)p * half + j], s_ = sn[(int64_t)p * half + j];
+    o[j] = (bf16)(a * c - b * s_);
+    o[j + half] = (bf16)(b * c + a * s_);
+  } else {
+    o[j] = (bf16)a;
+    o[j + half] = (bf16)b;
+  }
+}
+
+int launch_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int T, int nq, int nkv, int d, int S,
+                    const float* cos_t, const float* sin_t, hipStream_t s) {
+  const int64_t total = (int64_t)T * (nq + 2 * nkv) * (d / 2);
+  if (total <= 0) return 0;
+  hipLaunchKernelGGL(rope_qkv_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in, ldi, (bf16*)out, ldo, T,
+                     nq, nkv, d, S, cos_t, sin_t);
+  return (int)hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------------
 // SwiGLU
 // ------------------------------------------------------------------------------------------

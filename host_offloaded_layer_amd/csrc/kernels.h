@@ -50,6 +50,11 @@ int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, cons
 int launch_rope(void* x, DType xt, int64_t ld, int T, int heads, int d, int S, const float* cos_t,
                 const float* sin_t, bool inverse, hipStream_t s);
 
+// RoPE of q and k fused with the fp32 -> bf16 cast of the whole q/k/v projection output (in fp32
+// [T, (nq + 2 nkv) d], out bf16 with the same layout): one rounding per element.
+int launch_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int T, int nq, int nkv, int d, int S,
+                    const float* cos_t, const float* sin_t, hipStream_t s);
+
 // SwiGLU: gu holds [g | u] row-wise ([T, 2F], g first); a = silu(g) * u.
 int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_t s);
 // dgu = [dg | du] from da.
