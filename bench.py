@@ -69,6 +69,20 @@ def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int
                 h2d=n_streams * layer_bytes + head_bytes + 4.0 * T * H)
 
 
+def profiled_traffic(workload: str):
+    """HBM bytes per gemm_nt2 launch from the committed rocprofv3 counter summary, or None when
+    there is none for this workload or the GEMM source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_nt2_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and " " not in l.strip())
+    src = os.path.join(ROOT, "host_offloaded_layer_amd", "csrc", "k_gemm.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv.get("k_gemm_sha256"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w: W.Workload):
     """The oracle (NumPy fp32) on a bounded sample of the same workload: one decoder layer's
     forward, recompute and backward on one 4096-token sequence, the loss anchor on 512 tokens, and
@@ -130,6 +144,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "qwen3_1p7b", "llama8b_16k", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -153,6 +170,13 @@ def main():
     m.set_params(params)
     del params
     log(f"[bench] model created and loaded in {time.perf_counter() - t0:.1f} s")
+    if args.traffic_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     h2d_peak, d2h_peak = link_peak_gbs(torch)
     log(f"[bench] pinned copy peak: H2D {h2d_peak:.1f} GB/s, D2H {d2h_peak:.1f} GB/s")
 
@@ -211,7 +235,9 @@ def main():
                    "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU, layer streaming)"},
         "roofline": {"bound": "mfma", "kernel": "gemm_mfma (all decoder and head GEMMs)",
                      "achieved": round(g["tflops"], 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(g["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": profiled_traffic(w.name),
+                     "launches_per_step": g["launches_per_step"],
+                     "avg_launch_us": round(1e3 * g["ms_per_step"] / max(g["launches_per_step"], 1), 1)},
         "fb_tokens_per_s": round(w.tokens / (fb_ms / 1e3), 1), "fb_ms": round(fb_ms, 1),
         "step_tail_ms": round(step_ms, 1),
         "loss": recs[-1][0],
