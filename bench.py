@@ -62,10 +62,14 @@ def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int
     T, S, M = w.tokens, w.seq, w.batch
     p_layer = H * (nq * d) * 2 + H * (nkv * d) * 2 + 3 * H * F
     attn_fwd = 2.0 * d * nq * S * (S + 1) * M
-    f_layer = 4 * (2.0 * p_layer * T) + 4.5 * attn_fwd   # fwd + recompute + bwd (dX, dW)
+    L, K = s.n_layers, w.ckpt_every_k
+    n_recomp = L - (L - ((L + K - 1) // K - 1) * K)          # every block but the last is recomputed
+    f_fwd = 2.0 * p_layer * T + attn_fwd
+    f_bwd = 2 * (2.0 * p_layer * T) + 2.5 * attn_fwd          # dX and dW; attention backward
+    f_layers = L * (f_fwd + f_bwd) + n_recomp * f_fwd
     f_head = 3 * 2.0 * H * V * T
-    return dict(p_layer=p_layer, f_layer=f_layer, f_head=f_head,
-                flops=s.n_layers * f_layer + f_head,
+    return dict(p_layer=p_layer, f_layer=f_layers / L, f_head=f_head, n_recomp=n_recomp,
+                flops=f_layers + f_head,
                 h2d=n_streams * layer_bytes + head_bytes + 4.0 * T * H)
 
 
@@ -199,6 +203,13 @@ def main():
         recs.append((loss, fb, step_ms))
         log(f"[bench] step {i}: loss {loss:.4f} fb {fb['fb_ms']:.0f} ms step {step_ms:.0f} ms "
             f"h2d busy {fb['h2d_busy_ms']:.0f} ms compute busy {fb['compute_busy_ms']:.0f} ms")
+        u = fb.get("units") or []
+        if u:
+            lag = [e - a for _, a, e in u]
+            log(f"[bench]   host: gpu done at {fb['gpu_done_ms']:.0f} ms, scatter done {fb['scatter_done_ms']:.0f} ms, "
+                f"optimiser busy {fb['worker_busy_ms']:.0f} ms over {len(u)} units (first start {u[0][1]:.0f}, "
+                f"last end {u[-1][2]:.0f}, max unit {max(lag):.0f} ms); starts "
+                + " ".join(f"{int(x)}:{a:.0f}" for x, a, _ in u[::4]))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     m.set_kernel_timing(False)

@@ -23,7 +23,7 @@ CPP_SRCS = ["host_math.cpp", "engine.cpp", "api.cpp"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-result"]
-CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-ffp-contract=off", "-fno-fast-math",
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-ffp-contract=off", "-fno-fast-math", "-fno-math-errno",
              "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-Wall", "-Wno-unused-variable",
              "-Wno-unused-but-set-variable", "-Wno-unused-result", "-pthread"]
 

@@ -176,8 +176,9 @@ hol_status hol_last_stats(const hol_model* m, char* json, size_t cap) {
   GUARD_BEGIN
   if (!m || !json || !cap) return einval("hol_last_stats", "null argument");
   const std::string s = stats_json(m);
-  strncpy(json, s.c_str(), cap - 1);
-  json[cap - 1] = 0;
+  if (s.size() + 1 > cap)
+    return einval("hol_last_stats", ("buffer too small: needs " + std::to_string(s.size() + 1) + " bytes").c_str());
+  memcpy(json, s.c_str(), s.size() + 1);
   return HOL_OK;
   GUARD_END
 }
@@ -279,6 +280,12 @@ hol_status hol_op_swiglu_bwd(const void* da, const void* gu, void* dgu, hol_dtyp
                              void* stream) {
   return launched(launch_swiglu_bwd(da, gu, dgu, t == HOL_BF16 ? DT_BF16 : DT_F32, T, F, (hipStream_t)stream),
                   "hol_op_swiglu_bwd");
+}
+
+hol_status hol_op_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, int32_t R, int32_t C,
+                                 void* stream) {
+  if (R < 0 || C < 0) return einval("hol_op_transpose_bf16", "negative size");
+  return launched(launch_transpose_bf16(in, ldi, out, ldo, R, C, (hipStream_t)stream), "hol_op_transpose_bf16");
 }
 
 static Attn attn_args(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d, hol_dtype t, const void* q,

@@ -19,7 +19,8 @@
 // Schedule of one forward_backward (phases 1-3 of the training step; block loop reading: block b
 // covers layers bK+1 .. min((b+1)K, L), checkpoints are h_0, h_K, h_2K, ... and h_L):
 //   FWD 1..L, HEAD (loss anchor), then for b = last .. 0: RECOMP layers of b in forward order,
-//   BWD layers of b in reverse order. A layer still resident in a slot is not streamed again.
+//   BWD layers of b in reverse order. A layer still resident in a slot is not streamed again, and
+//   the last block is not recomputed: its forward writes the activation store directly.
 // Every micro-batch of the call is resident at once and processed by each resident layer
 // (layer-major order): GEMMs run over all T = batch*seq tokens, attention per sequence; the loss
 // weights each token by 1/(labelled tokens of its micro-batch), which makes the returned value the
@@ -728,7 +729,9 @@ struct FusedWorker {
   bool running = false;
   bool failed = false;
   double busy_ms = 0;
-  void start(const AdamConsts& kc) {
+  double t_call = 0;
+  void start(const AdamConsts& kc, double t_start) {
+    t_call = t_start;
     {
       std::lock_guard<std::mutex> g(m->fmu);
       m->unit_queue.clear();
@@ -753,7 +756,9 @@ struct FusedWorker {
         }
         const double t0 = now_ms();
         adam_unit(m, u, kc);
-        busy_ms += now_ms() - t0;
+        const double t1 = now_ms();
+        busy_ms += t1 - t0;
+        m->stats.units.push_back({(double)u, t0 - t_call, t1 - t_call});
       }
     });
   }
@@ -902,7 +907,9 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   ops.push_back({OP_HEAD, -1, -1, 0});
   for (int bl = m->nblocks - 1; bl >= 0; --bl) {
     const int l0 = bl * K, l1 = std::min(L, (bl + 1) * K);
-    for (int l = l0; l < l1; ++l) ops.push_back({OP_RECOMP, l, bl, l - l0});
+    // the last block's forward already stored its activations: no recompute for it
+    if (bl < m->nblocks - 1)
+      for (int l = l0; l < l1; ++l) ops.push_back({OP_RECOMP, l, bl, l - l0});
     for (int l = l1 - 1; l >= l0; --l) ops.push_back({OP_BWD, l, bl, l - l0});
   }
   auto ckpt_of = [&](int idx) { return m->ckpt + (int64_t)idx * T64 * H; };  // idx: block, or nblocks for h_L
@@ -912,7 +919,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   const hol_config& cf = m->cfg;
   const AdamConsts kc = adam_consts(m->step_t + 1, cf.lr, cf.beta1, cf.beta2, cf.adam_eps);
   FusedWorker worker{m};
-  if (fused) worker.start(kc);
+  if (fused) worker.start(kc, t_start);
 
   // ---- weight streaming helpers
   int last_slot = 1;  // so the first load goes to slot 0
@@ -1017,13 +1024,22 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     if (op.kind == OP_FWD) {
       // h_in: checkpoint of the block for the block's first layer, else the previous output
       const int l = op.layer;
+      const int lb0 = (m->nblocks - 1) * K;  // first layer of the last block
       const float* hin = (l == 0) ? ckpt_of(0) : ((l % K == 0) ? ckpt_of(l / K) : m->hbuf[(l - 1) & 1]);
       float* hout;
       if (l + 1 == L) hout = ckpt_of(m->nblocks);
       else if ((l + 1) % K == 0) hout = ckpt_of((l + 1) / K);
       else hout = m->hbuf[l & 1];
+      // The last block keeps its forward activations in the store, where the backward reads them
+      // (the recompute of that block would reproduce them bit for bit).
+      Act A = act_at(m, 0);
+      if (l >= lb0) {
+        A = act_at(m, l - lb0);
+        if (l > lb0) hin = A.hin;
+        if (l + 1 < L) hout = act_at(m, l - lb0 + 1).hin;
+      }
       HSTEP(hipEventRecord(ta, sc));
-      STEP(layer_forward(m, w, hin, hout, act_at(m, 0), T, n_seq, S));
+      STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S));
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 2});
     } else if (op.kind == OP_RECOMP) {
@@ -1078,6 +1094,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   HSTEP(hipStreamSynchronize(sc));
   HSTEP(hipStreamSynchronize(sh));
   HSTEP(hipStreamSynchronize(sd));
+  m->stats.gpu_done_ms = now_ms() - t_start;
   HSTEP(hipGetLastError());
   // embedding gradient: rows added in token order (columns split over threads: deterministic)
   if (m->V > 0) {
@@ -1094,9 +1111,11 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   for (int64_t t = 0; t < T64; ++t) total += (double)m->loss_stage[t];
   *out = total;
   m->grads_zero = false;
+  m->stats.scatter_done_ms = now_ms() - t_start;
   if (fused) {
     const double t_gpu_done = now_ms();
     worker.stop(false);
+    m->stats.worker_busy_ms = worker.busy_ms;
     if (worker.failed) {
       set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
       return fail(HOL_EDEVICE);
@@ -1227,7 +1246,12 @@ std::string stats_json(const hol_model* m) {
     << ",\"fwd_ms\":" << s.fwd_ms << ",\"recomp_ms\":" << s.recomp_ms << ",\"bwd_ms\":" << s.bwd_ms
     << ",\"head_ms\":" << s.head_ms << ",\"host_embed_ms\":" << s.host_embed_ms
     << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
-    << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads();
+    << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads()
+    << ",\"gpu_done_ms\":" << s.gpu_done_ms << ",\"scatter_done_ms\":" << s.scatter_done_ms
+    << ",\"worker_busy_ms\":" << s.worker_busy_ms << ",\"units\":[";
+  for (size_t i = 0; i < s.units.size(); ++i)
+    o << (i ? "," : "") << "[" << (int)s.units[i][0] << "," << s.units[i][1] << "," << s.units[i][2] << "]";
+  o << "]";
   static const char* names[KC_N] = {"gemm", "attn_fwd", "attn_bwd", "rmsnorm", "rope", "swiglu", "ce", "transpose", "other"};
   o << ",\"kernels\":{";
   for (int c = 0; c < KC_N; ++c) {

@@ -8,6 +8,7 @@
 #include <mutex>
 #include <string>
 #include <thread>
+#include <array>
 #include <vector>
 
 #include "../../include/hol.h"
@@ -59,6 +60,10 @@ struct KStat {
 struct Stats {
   double fb_ms = 0, step_ms = 0, h2d_bytes = 0, d2h_bytes = 0, h2d_busy_ms = 0, d2h_busy_ms = 0,
          compute_busy_ms = 0, fwd_ms = 0, recomp_ms = 0, bwd_ms = 0, head_ms = 0, host_embed_ms = 0;
+  // host timeline of a fused call (ms from the call's start): GPU work drained, embedding
+  // scatter-add done; per optimiser unit: gradient arrived on the host, Adam done
+  double gpu_done_ms = 0, scatter_done_ms = 0, worker_busy_ms = 0;
+  std::vector<std::array<double, 3>> units;  // {unit, arrived, done}
   int n_weight_streams = 0;
   int tokens = 0;
   KStat k[KC_N];

@@ -46,10 +46,14 @@ class Pool {
   }
   int size() const { return nthreads_; }
 
+  // Dynamic schedule: about 8 chunks per thread (none below min_chunk) handed out through an
+  // atomic counter, so a thread that loses its core for a while (other busy threads in the
+  // process) only takes fewer chunks instead of holding every other thread up.
   void run(int64_t n, int64_t min_chunk, const std::function<void(int64_t, int64_t)>& fn) {
     if (n <= 0) return;
-    int64_t parts = std::min<int64_t>(nthreads_, std::max<int64_t>(1, n / std::max<int64_t>(1, min_chunk)));
-    if (parts <= 1) {
+    const int64_t chunk = std::max<int64_t>(std::max<int64_t>(1, min_chunk), n / ((int64_t)nthreads_ * 8));
+    const int64_t nchunks = (n + chunk - 1) / chunk;
+    if (nchunks <= 1 || nthreads_ <= 1) {
       fn(0, n);
       return;
     }
@@ -58,21 +62,28 @@ class Pool {
       std::lock_guard<std::mutex> g(mu_);
       fn_ = &fn;
       n_ = n;
-      parts_ = (int)parts;
-      pending_ = (int)parts - 1;
+      chunk_ = chunk;
+      nchunks_ = nchunks;
+      next_.store(0, std::memory_order_relaxed);
+      helpers_ = (int)std::min<int64_t>(nthreads_ - 1, nchunks - 1);
+      pending_ = helpers_;
       ++gen_;
     }
     cv_.notify_all();
-    chunk(0);
+    work();
     std::unique_lock<std::mutex> lk(mu_);
     done_cv_.wait(lk, [this] { return pending_ == 0; });
     fn_ = nullptr;
   }
 
  private:
-  void chunk(int i) {
-    const int64_t lo = n_ * i / parts_, hi = n_ * (i + 1) / parts_;
-    if (hi > lo) (*fn_)(lo, hi);
+  void work() {
+    for (;;) {
+      const int64_t c = next_.fetch_add(1, std::memory_order_relaxed);
+      if (c >= nchunks_) return;
+      const int64_t lo = c * chunk_, hi = std::min(n_, lo + chunk_);
+      (*fn_)(lo, hi);
+    }
   }
   void loop(int id) {
     uint64_t seen = 0;
@@ -81,9 +92,9 @@ class Pool {
       cv_.wait(lk, [&] { return gen_ != seen; });
       seen = gen_;
       if (stop_) return;
-      if (id >= parts_ || fn_ == nullptr) continue;
+      if (id > helpers_ || fn_ == nullptr) continue;
       lk.unlock();
-      chunk(id);
+      work();
       lk.lock();
       if (--pending_ == 0) done_cv_.notify_one();
     }
@@ -93,8 +104,9 @@ class Pool {
   std::mutex mu_, run_mu_;
   std::condition_variable cv_, done_cv_;
   const std::function<void(int64_t, int64_t)>* fn_ = nullptr;
-  int64_t n_ = 0;
-  int parts_ = 0, pending_ = 0;
+  int64_t n_ = 0, chunk_ = 1, nchunks_ = 0;
+  std::atomic<int64_t> next_{0};
+  int helpers_ = 0, pending_ = 0;
   uint64_t gen_ = 0;
   bool stop_ = false;
 };

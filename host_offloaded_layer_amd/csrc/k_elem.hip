@@ -20,8 +20,9 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
   *(bf16x4*)p = b;
 }
 
-// one wavefront per row; H % 4 == 0
-template <typename TO>
+// One wavefront per row; H % 4 == 0. For H <= 256 NV the row stays in registers between the
+// sum of squares and the scaling, so x is read from HBM once; wider rows take two passes.
+template <typename TO, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const float* __restrict__ x, const float* __restrict__ g,
                                                      float eps, TO* __restrict__ y, float* __restrict__ rstd,
                                                      int T, int H) {
@@ -29,20 +30,56 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const float* __restrict__ x
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
   const float* xr = x + (int64_t)row * H;
-  float ss = 0.f;
-  for (int j = lane * 4; j < H; j += 256) {
-    float4 v = *(const float4*)(xr + j);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  if (lane == 0) rstd[row] = r;
   TO* yr = y + (int64_t)row * H;
-  for (int j = lane * 4; j < H; j += 256) {
-    float4 v = *(const float4*)(xr + j);
-    float4 gg = *(const float4*)(g + j);
-    store4<TO>(yr + j, make_float4(v.x * r * gg.x, v.y * r * gg.y, v.z * r * gg.z, v.w * r * gg.w));
+  float ss = 0.f;
+  if constexpr (NV > 0) {
+    float4 xv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = lane * 4 + i * 256;
+      xv[i] = j < H ? *(const float4*)(xr + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    if (lane == 0) rstd[row] = r;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = lane * 4 + i * 256;
+      if (j < H) {
+        const float4 gg = *(const float4*)(g + j);
+        store4<TO>(yr + j, make_float4(xv[i].x * r * gg.x, xv[i].y * r * gg.y, xv[i].z * r * gg.z, xv[i].w * r * gg.w));
+      }
+    }
+  } else {
+    for (int j = lane * 4; j < H; j += 256) {
+      float4 v = *(const float4*)(xr + j);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    if (lane == 0) rstd[row] = r;
+    for (int j = lane * 4; j < H; j += 256) {
+      float4 v = *(const float4*)(xr + j);
+      float4 gg = *(const float4*)(g + j);
+      store4<TO>(yr + j, make_float4(v.x * r * gg.x, v.y * r * gg.y, v.z * r * gg.z, v.w * r * gg.w));
+    }
   }
+}
+
+template <typename TO>
+static void rmsnorm_fwd_dispatch(dim3 grid, hipStream_t s, const float* x, const float* gamma, float eps, TO* y,
+                                 float* rstd, int T, int H) {
+  const int nv = (H + 255) / 256;
+#define RMSF(NV) hipLaunchKernelGGL((rmsnorm_fwd_k<TO, NV>), grid, dim3(256), 0, s, x, gamma, eps, y, rstd, T, H)
+  if (nv <= 1) RMSF(1);
+  else if (nv <= 2) RMSF(2);
+  else if (nv <= 4) RMSF(4);
+  else if (nv <= 8) RMSF(8);
+  else if (nv <= 16) RMSF(16);
+  else RMSF(0);
+#undef RMSF
 }
 
 int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, DType yt, float* rstd,
@@ -50,8 +87,8 @@ int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, D
   if (T <= 0) return 0;
   if (H % 4) return (int)hipErrorInvalidValue;
   dim3 grid((T + 3) / 4);
-  if (yt == DT_BF16) hipLaunchKernelGGL(rmsnorm_fwd_k<bf16>, grid, dim3(256), 0, s, x, gamma, eps, (bf16*)y, rstd, T, H);
-  else hipLaunchKernelGGL(rmsnorm_fwd_k<float>, grid, dim3(256), 0, s, x, gamma, eps, (float*)y, rstd, T, H);
+  if (yt == DT_BF16) rmsnorm_fwd_dispatch<bf16>(grid, s, x, gamma, eps, (bf16*)y, rstd, T, H);
+  else rmsnorm_fwd_dispatch<float>(grid, s, x, gamma, eps, (float*)y, rstd, T, H);
   return (int)hipGetLastError();
 }
 
@@ -272,29 +309,44 @@ __device__ __forceinline__ void tr8x8(const tu32x4 in[8], tu32x4 out[8]) {
   }
 }
 
+__device__ __forceinline__ tu32x4 load8_bf16_tail(const uint16_t* row, int gc, int C) {
+  uint16_t e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = gc + j < C ? row[gc + j] : (uint16_t)0;
+  return tu32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                e[6] | ((uint32_t)e[7] << 16)};
+}
+
+// Interior tiles take a branch-free path whose eight 16-byte loads are all in flight before the
+// first LDS write; edge tiles take a guarded path.
 __global__ __launch_bounds__(256) void transpose_bf16_k(const uint16_t* __restrict__ in, int64_t ldi,
                                                         uint16_t* __restrict__ out, int64_t ldo, int R, int C) {
   __shared__ tu32x4 tile[128 * 16];
   const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
   const int t = threadIdx.x;
+  const bool full = r0 + 128 <= R && c0 + 128 <= C;
   // phase 1: rows r0 + t/16 + 16 k, chunk t % 16
+  const int ch = t % 16;
+  tu32x4 v[8];
+  if (full) {
+    const uint16_t* src = in + (int64_t)(r0 + t / 16) * ldi + c0 + ch * 8;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = t / 16 + 16 * k, ch = t % 16;
-    const int gr = r0 + r, gc = c0 + ch * 8;
-    tu32x4 v = {0u, 0u, 0u, 0u};
-    if (gr < R) {
-      if (gc + 8 <= C) {
-        v = *(const tu32x4*)(in + (int64_t)gr * ldi + gc);
-      } else {
-        uint16_t e[8];
+    for (int k = 0; k < 8; ++k) v[k] = *(const tu32x4*)(src + (int64_t)(16 * k) * ldi);
+  } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = gc + j < C ? in[(int64_t)gr * ldi + gc + j] : (uint16_t)0;
-        v = tu32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
-                   e[6] | ((uint32_t)e[7] << 16)};
+    for (int k = 0; k < 8; ++k) {
+      const int gr = r0 + t / 16 + 16 * k, gc = c0 + ch * 8;
+      v[k] = tu32x4{0u, 0u, 0u, 0u};
+      if (gr < R) {
+        const uint16_t* row = in + (int64_t)gr * ldi;
+        v[k] = gc + 8 <= C ? *(const tu32x4*)(row + gc) : load8_bf16_tail(row, gc, C);
       }
     }
-    tile[r * 16 + (ch ^ ((r >> 3) & 15))] = v;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = t / 16 + 16 * k;
+    tile[r * 16 + (ch ^ ((r >> 3) & 15))] = v[k];
   }
   __syncthreads();
   // phase 2: thread owns the 8x8 block (row block rb = t % 16, column chunk cb = t / 16)
@@ -306,10 +358,16 @@ __global__ __launch_bounds__(256) void transpose_bf16_k(const uint16_t* __restri
     in8[i] = tile[r * 16 + (cb ^ ((r >> 3) & 15))];
   }
   tr8x8(in8, o8);
+  const int orr = r0 + rb * 8;      // output column
+  if (full) {
+    uint16_t* dst = out + (int64_t)(c0 + cb * 8) * ldo + orr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(tu32x4*)(dst + (int64_t)j * ldo) = o8[j];
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int oc = c0 + cb * 8 + j;   // output row
-    const int orr = r0 + rb * 8;      // output column
     if (oc >= C) continue;
     if (orr + 8 <= R) {
       *(tu32x4*)(out + (int64_t)oc * ldo + orr) = o8[j];

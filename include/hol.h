@@ -139,9 +139,12 @@ hol_status hol_set_kernel_timing(hol_model* m, int32_t on);
 hol_status hol_forward_backward_step(hol_model* m, const hol_batch* batch, hol_loss loss,
                                      double* loss_sum_out);
 
-/* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated,
- * truncated to cap). Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms,
- * compute_busy_ms, n_weight_streams, per-kernel-class compute ms. */
+/* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated).
+ * Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms, compute_busy_ms,
+ * n_weight_streams, per-kernel-class compute ms, and for hol_forward_backward_step the host
+ * timeline (gpu_done_ms, scatter_done_ms, worker_busy_ms, units = [unit, start, end] of each
+ * optimiser unit in ms from the call's start). HOL_EINVAL, with nothing written, when the
+ * object does not fit in cap bytes. */
 hol_status hol_last_stats(const hol_model* m, char* json, size_t cap);
 
 /* Stage partition (host only). RoundPipe popular article §六 and paper summary (方法步骤详情,

@@ -35,6 +35,7 @@ hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t l
 hol_status hol_op_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, hol_dtype yt,
                               float* rstd, int32_t T, int32_t H, void* stream);
 /* Backward: dx (fp32 [T,H]) = dx_in_place_if(accumulate) + d RMSNorm; dgamma (fp32 [H]) +=.
+ * H must be a multiple of 4 and at most 4096, else HOL_EINVAL.
  * workspace: fp32 buffer of hol_op_rmsnorm_bwd_workspace(T, H) floats. */
 int64_t hol_op_rmsnorm_bwd_workspace(int32_t T, int32_t H);
 hol_status hol_op_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd,
@@ -51,6 +52,12 @@ hol_status hol_op_rope(void* x, hol_dtype t, int64_t ld, int32_t T, int32_t head
 hol_status hol_op_swiglu_fwd(const void* gu, void* a, hol_dtype t, int32_t T, int32_t F, void* stream);
 hol_status hol_op_swiglu_bwd(const void* da, const void* gu, void* dgu, hol_dtype t, int32_t T,
                              int32_t F, void* stream);
+
+/* bf16 transpose out[c][r] = in[r][c] of an R x C matrix at row strides ldi, ldo (elements,
+ * multiples of 8; 16-byte aligned pointers, else HOL_EINVAL). The backward uses it to present
+ * every product to the GEMM as A row-major by K and B row-major by K. */
+hol_status hol_op_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, int32_t R,
+                                 int32_t C, void* stream);
 
 /* Causal GQA attention over n_seq sequences of length S (token-major rows, T = n_seq*S).
  * q [T, nq*d] at row stride ldq, k/v [T, nkv*d] at ldk/ldv, o [T, nq*d] at ldo, lse fp32

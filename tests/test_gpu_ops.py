@@ -105,8 +105,30 @@ def test_gemm_rejects_misaligned_bf16():
     assert st == hol.HOL_EINVAL
 
 
+# ------------------------------------------------------------------ transpose (pure data movement: bit-exact)
+@pytest.mark.parametrize("R,C,ldi,ldo", [(256, 384, 384, 256), (300, 136, 136, 304), (1000, 2056, 2064, 1008),
+                                         (8, 8, 8, 8), (129, 127, 128, 136)])
+def test_transpose_bf16_bitexact(R, C, ldi, ldo):
+    g = torch.Generator().manual_seed(R * 7 + C)
+    x = torch.randn(R, ldi, generator=g).to(torch.bfloat16).to(DEV)
+    out = torch.full((C, ldo), 7.0, dtype=torch.bfloat16, device=DEV)
+    hol.check(hol.lib.hol_op_transpose_bf16(x.data_ptr(), ldi, out.data_ptr(), ldo, R, C, None))
+    sync()
+    xv = x.cpu().view(torch.int16).numpy()
+    ov = out.cpu().view(torch.int16).numpy()
+    assert np.array_equal(ov[:, :R], xv[:, :C].T)
+    pad = torch.tensor(7.0, dtype=torch.bfloat16).view(torch.int16).item()
+    assert np.all(ov[:, R:] == pad)      # nothing written past the R columns of each output row
+
+
+def test_transpose_rejects_misaligned():
+    x = torch.zeros(16, 12, dtype=torch.bfloat16, device=DEV)
+    assert hol.lib.hol_op_transpose_bf16(x.data_ptr(), 12, x.data_ptr(), 16, 16, 12, None) == hol.HOL_EINVAL
+
+
 # ------------------------------------------------------------------ RMSNorm
-@pytest.mark.parametrize("H,T,yt", [(64, 37, hol.F32), (4096, 300, hol.BF16), (2048, 1100, hol.F32)])
+@pytest.mark.parametrize("H,T,yt", [(64, 37, hol.F32), (4096, 300, hol.BF16), (2048, 1100, hol.F32),
+                                    (5000, 70, hol.BF16)])
 def test_rmsnorm_fwd_bwd(H, T, yt):
     r = np.random.default_rng(H + T)
     x = r.standard_normal((T, H)).astype(np.float32) * 3
@@ -120,13 +142,20 @@ def test_rmsnorm_fwd_bwd(H, T, yt):
     dx = dev(dx0)
     dgam = torch.full((H,), 0.5, device=DEV)
     ws = torch.empty(hol.lib.hol_op_rmsnorm_bwd_workspace(T, H), device=DEV)
+    ry, rr = D.rmsnorm(x.astype(np.float64), g.astype(np.float64), 1e-5)
+    tol = 2 ** -8 if yt == hol.BF16 else 1e-6
+    if H > 4096:   # forward only (two-pass path); the backward kernel is for rows up to 4096 wide
+        assert hol.lib.hol_op_rmsnorm_bwd(dyd.data_ptr(), xd.data_ptr(), gd.data_ptr(), rs.data_ptr(), dx.data_ptr(),
+                                          1, dgam.data_ptr(), ws.data_ptr(), T, H, None) == hol.HOL_EINVAL
+        sync()
+        np.testing.assert_allclose(host(rs), rr, rtol=1e-6)
+        np.testing.assert_allclose(host(y), ry, rtol=tol, atol=tol)
+        return
     hol.check(hol.lib.hol_op_rmsnorm_bwd(dyd.data_ptr(), xd.data_ptr(), gd.data_ptr(), rs.data_ptr(), dx.data_ptr(), 1,
                                          dgam.data_ptr(), ws.data_ptr(), T, H, None))
     sync()
-    ry, rr = D.rmsnorm(x.astype(np.float64), g.astype(np.float64), 1e-5)
     rdx, rdg = D.rmsnorm_bwd(dy.astype(np.float64), x.astype(np.float64), g.astype(np.float64), rr)
     np.testing.assert_allclose(host(rs), rr, rtol=1e-6)
-    tol = 2 ** -8 if yt == hol.BF16 else 1e-6
     np.testing.assert_allclose(host(y), ry, rtol=tol, atol=tol)
     np.testing.assert_allclose(host(dx), rdx + dx0, rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(host(dgam), rdg + 0.5, rtol=1e-5, atol=1e-4)
