@@ -61,6 +61,7 @@ def _load() -> C.CDLL:
         "hol_set_tensor": [P, I32, P, I64],
         "hol_get_tensor": [P, I32, P, I64],
         "hol_get_grad": [P, I32, P, I64],
+        "hol_get_routing": [P, I32, P, I64],
         "hol_get_adam_state": [P, I32, P, P, I64, C.POINTER(I64)],
         "hol_set_adam_state": [P, I32, P, P, I64, I64],
         "hol_zero_grad": [P],
@@ -104,7 +105,7 @@ lib = _load()
 
 # every symbol include/hol.h and include/hol_ops.h declare
 EXPORTED = ["hol_create", "hol_destroy", "hol_num_tensors", "hol_tensor_info", "hol_set_tensor",
-            "hol_get_tensor", "hol_get_grad", "hol_get_adam_state", "hol_set_adam_state",
+            "hol_get_tensor", "hol_get_grad", "hol_get_routing", "hol_get_adam_state", "hol_set_adam_state",
             "hol_zero_grad", "hol_set_ckpt_every_k", "hol_set_kernel_timing",
             "hol_forward_backward", "hol_forward_backward_step", "hol_step", "hol_last_stats", "hol_partition",
             "hol_host_adam", "hol_host_bf16_round", "hol_last_error", "hol_version",
@@ -143,6 +144,7 @@ class Model:
             check(lib.hol_tensor_info(h, i, name, 256, shape, C.byref(nd), C.byref(tr)))
             self.tensors.append((name.value.decode(), tuple(shape[k] for k in range(nd.value)), bool(tr.value)))
         self.index = {t[0]: i for i, t in enumerate(self.tensors)}
+        self.trainable = {t[0]: t[2] for t in self.tensors}
 
     def close(self):
         if getattr(self, "_h", None):
@@ -171,6 +173,12 @@ class Model:
         i = self.index[name]
         out = np.empty(self.tensors[i][1], np.float32)
         check(lib.hol_get_tensor(self._h, i, _ptr(out), out.size))
+        return out
+
+    def get_routing(self, layer: int, n_tokens: int, top_k: int) -> np.ndarray:
+        """Expert ids [n_tokens, top_k] chosen in `layer` by the last forward_backward."""
+        out = np.empty((n_tokens, top_k), np.int32)
+        check(lib.hol_get_routing(self._h, layer, _ptr(out), out.size))
         return out
 
     def get_grad(self, name: str) -> np.ndarray:

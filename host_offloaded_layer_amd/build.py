@@ -17,7 +17,7 @@ OUT = os.path.join(HERE, "libhol.so")
 OBJ = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SRCS = ["k_gemm.hip", "k_elem.hip", "k_attn.hip", "k_attn_mfma.hip"]
+HIP_SRCS = ["k_gemm.hip", "k_elem.hip", "k_attn.hip", "k_attn_mfma.hip", "k_moe.hip"]
 CPP_SRCS = ["host_math.cpp", "engine.cpp", "api.cpp"]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -81,6 +81,10 @@ hol_status hol_set_tensor(hol_model* m, int32_t i, const float* src, int64_t num
   const TensorDesc* t = tensor_at(m, i);
   if (!t || !src) return einval("hol_set_tensor", "bad model, index or pointer");
   if (numel != t->numel) return einval("hol_set_tensor", "numel mismatch");
+  if (t->flat < 0) {  // frozen tensor without an fp32 copy: straight into the image
+    write_image_tensor(m, *t, src);
+    return HOL_OK;
+  }
   float* dst = m->master + t->flat;
   parallel_for(numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy(dst + lo, src + lo, (size_t)(hi - lo) * 4); });
   refresh_image_tensor(m, *t);
@@ -93,6 +97,10 @@ hol_status hol_get_tensor(const hol_model* m, int32_t i, float* dst, int64_t num
   const TensorDesc* t = tensor_at(m, i);
   if (!t || !dst) return einval("hol_get_tensor", "bad model, index or pointer");
   if (numel != t->numel) return einval("hol_get_tensor", "numel mismatch");
+  if (t->flat < 0) {
+    read_image_tensor(m, *t, dst);
+    return HOL_OK;
+  }
   const float* src = m->master + t->flat;
   parallel_for(numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy(dst + lo, src + lo, (size_t)(hi - lo) * 4); });
   return HOL_OK;
@@ -115,6 +123,7 @@ hol_status hol_get_adam_state(const hol_model* m, int32_t i, float* mom1, float*
   const TensorDesc* t = tensor_at(m, i);
   if (!t) return einval("hol_get_adam_state", "bad model or index");
   if (numel != t->numel) return einval("hol_get_adam_state", "numel mismatch");
+  if (!t->trainable) return einval("hol_get_adam_state", "tensor is frozen");
   if (mom1) memcpy(mom1, m->mom1 + t->flat, (size_t)numel * 4);
   if (mom2) memcpy(mom2, m->mom2 + t->flat, (size_t)numel * 4);
   if (step) *step = m->step_t;
@@ -126,10 +135,18 @@ hol_status hol_set_adam_state(hol_model* m, int32_t i, const float* mom1, const 
   const TensorDesc* t = tensor_at(m, i);
   if (!t) return einval("hol_set_adam_state", "bad model or index");
   if (numel != t->numel || step < 0) return einval("hol_set_adam_state", "numel or step invalid");
+  if (!t->trainable) return einval("hol_set_adam_state", "tensor is frozen");
   if (mom1) memcpy(m->mom1 + t->flat, mom1, (size_t)numel * 4);
   if (mom2) memcpy(m->mom2 + t->flat, mom2, (size_t)numel * 4);
   m->step_t = step;
   return HOL_OK;
+}
+
+hol_status hol_get_routing(const hol_model* m, int32_t layer, int32_t* ids, int64_t n) {
+  GUARD_BEGIN
+  if (!m || !ids) return einval("hol_get_routing", "null argument");
+  return engine_get_routing(m, layer, ids, n);
+  GUARD_END
 }
 
 hol_status hol_set_ckpt_every_k(hol_model* m, int32_t k) {

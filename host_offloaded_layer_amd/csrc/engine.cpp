@@ -84,15 +84,20 @@ static hol_status validate_config(const hol_config& c) {
   if (c.n_q_heads % c.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
   if (c.head_dim % 2 || c.head_dim > 128) return bad("head_dim must be even and <= 128");
   if (c.hidden % 8 || c.hidden > 4096) return bad("hidden must be a multiple of 8 and <= 4096");
-  if (c.n_experts > 0 || c.lora_rank > 0) {
-    set_error("hol_create: MoE and LoRA layers are not implemented in this build");
-    return HOL_EUNSUPPORTED;
+  if (c.n_experts < 0 || c.lora_rank < 0) return bad("n_experts / lora_rank must be >= 0");
+  if (c.n_experts > 0) {
+    if (c.n_experts > 512) return bad("n_experts must be <= 512");
+    if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 16) return bad("top_k must be in [1, min(n_experts, 16)]");
+    if (c.expert_ffn <= 0) return bad("expert_ffn must be positive");
+  } else if (c.ffn <= 0) {
+    return bad("ffn must be positive");
   }
-  if (c.ffn <= 0) return bad("ffn must be positive");
+  if (c.lora_rank > 64) return bad("lora_rank must be <= 64");
   if (c.vocab < 0) return bad("vocab must be >= 0");
   // bf16 operands go through the MFMA GEMM, whose rows are moved in 16-byte pieces
-  if (c.compute_dtype == HOL_BF16 && (c.ffn % 8 || c.vocab % 8 || c.head_dim % 8))
-    return bad("bf16 compute needs ffn, vocab and head_dim multiples of 8");
+  if (c.compute_dtype == HOL_BF16 && (c.vocab % 8 || c.head_dim % 8 ||
+                                      (c.n_experts > 0 ? c.expert_ffn % 8 : c.ffn % 8)))
+    return bad("bf16 compute needs ffn (expert_ffn), vocab and head_dim multiples of 8");
   if (c.ckpt_every_k <= 0) return bad("ckpt_every_k must be >= 1");
   if (c.compute_dtype != HOL_F32 && c.compute_dtype != HOL_BF16) return bad("compute_dtype");
   if (c.weight_decay != 0.f) return bad("weight_decay must be 0");
@@ -181,7 +186,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->nq = c.n_q_heads;
   m->nkv = c.n_kv_heads;
   m->d = c.head_dim;
-  m->F = c.ffn;
+  m->F = c.n_experts > 0 ? 0 : c.ffn;  // a mixture-of-experts layer has no dense MLP
   m->V = c.vocab;
   m->nqd = m->nq * m->d;
   m->QKV = (m->nq + 2 * m->nkv) * m->d;
@@ -195,34 +200,38 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->n_ckpt = m->L + 1;  // enough for any k <= Kmax, down to k = 1
   const int64_t H = m->H, L = m->L, F = m->F, V = m->V, QKV = m->QKV, nqd = m->nqd, E = m->E;
 
-  // ---- flat host layout: [embed] [layer 0 .. L-1] [final_norm, lm_head]
-  m->g_wqkv = 0;
-  m->g_wo = m->g_wqkv + QKV * H;
-  m->g_wgu = m->g_wo + H * nqd;
-  m->g_wd = m->g_wgu + 2 * F * H;
-  m->g_g1 = m->g_wd + H * F;
-  m->g_g2 = m->g_g1 + H;
-  m->layer_flat_n = m->g_g2 + H;
-  int64_t flat = 0;
-  if (V > 0) {
-    m->embed_flat0 = 0;
-    flat = V * H;
-  }
-  m->layer_flat0 = flat;
-  flat += L * m->layer_flat_n;
-  m->head_flat0 = flat;
-  m->head_flat_n = V > 0 ? H + V * H : 0;
-  flat += m->head_flat_n;
-  m->n_flat = flat;
+  m->NE = c.n_experts;
+  m->topk = c.n_experts > 0 ? c.top_k : 0;
+  m->Fe = c.n_experts > 0 ? c.expert_ffn : 0;
+  m->R = c.lora_rank;
+  m->base_trainable = m->R == 0;
+  m->embed_trainable = V > 0 && m->base_trainable;
+  m->head_trainable = V > 0 && m->base_trainable;
+  const int64_t F_ = m->F, NE = m->NE, Fe = m->Fe, R = m->R, kvd = (int64_t)m->nkv * m->d;
 
   // ---- image layout of one layer block (each sub-tensor 4 KiB aligned)
   int64_t o = 0;
   m->o_wqkv = o; o = align_up(o + QKV * H * E, 4096);
   m->o_wo = o;   o = align_up(o + H * nqd * E, 4096);
-  m->o_wgu = o;  o = align_up(o + 2 * F * H * E, 4096);
-  m->o_wd = o;   o = align_up(o + H * F * E, 4096);
+  m->wT_bytes = o;
+  if (NE > 0) {
+    m->o_router = o; o = align_up(o + NE * H * E, 4096);
+    m->o_egate = o;  o = align_up(o + NE * Fe * H * E, 4096);
+    m->o_eup = o;    o = align_up(o + NE * Fe * H * E, 4096);
+    m->o_edown = o;  o = align_up(o + NE * H * Fe * E, 4096);
+  } else {
+    m->o_wgu = o;  o = align_up(o + 2 * F_ * H * E, 4096);
+    m->o_wd = o;   o = align_up(o + H * F_ * E, 4096);
+    m->wT_bytes = o;
+  }
   m->o_g1 = o;   o = align_up(o + H * 4, 4096);
   m->o_g2 = o;   o = align_up(o + H * 4, 4096);
+  // LoRA factors (fp32): q, k, v on the attention-norm output, o on the attention output
+  const int64_t l_in[4] = {H, H, H, nqd}, l_out[4] = {nqd, kvd, kvd, H};
+  for (int j = 0; j < 4 && R > 0; ++j) {
+    m->o_lA[j] = o; o = align_up(o + R * l_in[j] * 4, 4096);
+    m->o_lB[j] = o; o = align_up(o + l_out[j] * R * 4, 4096);
+  }
   m->layer_img_bytes = o;
   o = 0;
   if (V > 0) {
@@ -232,25 +241,76 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->head_img_bytes = o;
   m->image_bytes = L * m->layer_img_bytes + m->head_img_bytes;
 
+  // ---- layer gradient block (= the flat host order of the layer's trainable tensors)
+  int64_t g = 0;
+  if (m->base_trainable) {
+    m->g_wqkv = g; g += QKV * H;
+    m->g_wo = g;   g += H * nqd;
+    if (NE > 0) {
+      m->g_router = g; g += NE * H;
+      m->g_egate = g;  g += NE * Fe * H;
+      m->g_eup = g;    g += NE * Fe * H;
+      m->g_edown = g;  g += NE * H * Fe;
+    } else {
+      m->g_wgu = g; g += 2 * F_ * H;
+      m->g_wd = g;  g += H * F_;
+    }
+    m->g_g1 = g; g += H;
+    m->g_g2 = g; g += H;
+  }
+  for (int j = 0; j < 4 && R > 0; ++j) {
+    m->g_lA[j] = g; g += R * l_in[j];
+    m->g_lB[j] = g; g += l_out[j] * R;
+  }
+  m->layer_flat_n = g;
+
+  // ---- flat host layout: [embed] [layer 0 .. L-1] [final_norm, lm_head (when trainable)]
+  int64_t flat = 0;
+  if (V > 0) {  // the embedding lives only on the host: it always has an fp32 copy
+    m->embed_flat0 = 0;
+    flat = V * H;
+  }
+  m->layer_flat0 = flat;
+  flat += L * m->layer_flat_n;
+  m->head_flat0 = flat;
+  m->head_flat_n = m->head_trainable ? H + V * H : 0;
+  flat += m->head_flat_n;
+  m->n_flat = flat;
+
   // ---- tensor directory (canonical order)
-  if (V > 0) add_tensor(m, "embed", {V, H}, true, 0, -2, -1, false);
+  const bool bt = m->base_trainable;
+  auto gofs = [&](int64_t f0, int64_t go) -> int64_t { return go < 0 ? -1 : f0 + go; };
+  if (V > 0) add_tensor(m, "embed", {V, H}, m->embed_trainable, 0, -2, -1, false);
   for (int l = 0; l < L; ++l) {
     const int64_t f0 = m->layer_flat0 + l * m->layer_flat_n;
     const std::string p = "layers." + std::to_string(l) + ".";
-    add_tensor(m, p + "attn_norm", {H}, true, f0 + m->g_g1, l, m->o_g1, true);
-    add_tensor(m, p + "wq", {nqd, H}, true, f0 + m->g_wqkv, l, m->o_wqkv, false);
-    add_tensor(m, p + "wk", {(int64_t)m->nkv * m->d, H}, true, f0 + m->g_wqkv + nqd * H, l, m->o_wqkv + nqd * H * E, false);
-    add_tensor(m, p + "wv", {(int64_t)m->nkv * m->d, H}, true, f0 + m->g_wqkv + (nqd + (int64_t)m->nkv * m->d) * H, l,
-               m->o_wqkv + (nqd + (int64_t)m->nkv * m->d) * H * E, false);
-    add_tensor(m, p + "wo", {H, nqd}, true, f0 + m->g_wo, l, m->o_wo, false);
-    add_tensor(m, p + "mlp_norm", {H}, true, f0 + m->g_g2, l, m->o_g2, true);
-    add_tensor(m, p + "w_gate", {F, H}, true, f0 + m->g_wgu, l, m->o_wgu, false);
-    add_tensor(m, p + "w_up", {F, H}, true, f0 + m->g_wgu + F * H, l, m->o_wgu + F * H * E, false);
-    add_tensor(m, p + "w_down", {H, F}, true, f0 + m->g_wd, l, m->o_wd, false);
+    add_tensor(m, p + "attn_norm", {H}, bt, gofs(f0, m->g_g1), l, m->o_g1, true);
+    add_tensor(m, p + "wq", {nqd, H}, bt, gofs(f0, m->g_wqkv), l, m->o_wqkv, false);
+    add_tensor(m, p + "wk", {kvd, H}, bt, bt ? f0 + m->g_wqkv + nqd * H : -1, l, m->o_wqkv + nqd * H * E, false);
+    add_tensor(m, p + "wv", {kvd, H}, bt, bt ? f0 + m->g_wqkv + (nqd + kvd) * H : -1, l,
+               m->o_wqkv + (nqd + kvd) * H * E, false);
+    add_tensor(m, p + "wo", {H, nqd}, bt, gofs(f0, m->g_wo), l, m->o_wo, false);
+    add_tensor(m, p + "mlp_norm", {H}, bt, gofs(f0, m->g_g2), l, m->o_g2, true);
+    if (NE > 0) {
+      add_tensor(m, p + "router", {NE, H}, bt, gofs(f0, m->g_router), l, m->o_router, false);
+      add_tensor(m, p + "experts.w_gate", {NE, Fe, H}, bt, gofs(f0, m->g_egate), l, m->o_egate, false);
+      add_tensor(m, p + "experts.w_up", {NE, Fe, H}, bt, gofs(f0, m->g_eup), l, m->o_eup, false);
+      add_tensor(m, p + "experts.w_down", {NE, H, Fe}, bt, gofs(f0, m->g_edown), l, m->o_edown, false);
+    } else {
+      add_tensor(m, p + "w_gate", {F_, H}, bt, gofs(f0, m->g_wgu), l, m->o_wgu, false);
+      add_tensor(m, p + "w_up", {F_, H}, bt, bt ? f0 + m->g_wgu + F_ * H : -1, l, m->o_wgu + F_ * H * E, false);
+      add_tensor(m, p + "w_down", {H, F_}, bt, gofs(f0, m->g_wd), l, m->o_wd, false);
+    }
+    static const char* lname[4] = {"q", "k", "v", "o"};
+    for (int j = 0; j < 4 && R > 0; ++j) {
+      add_tensor(m, p + "lora." + lname[j] + ".A", {R, l_in[j]}, true, f0 + m->g_lA[j], l, m->o_lA[j], true);
+      add_tensor(m, p + "lora." + lname[j] + ".B", {l_out[j], R}, true, f0 + m->g_lB[j], l, m->o_lB[j], true);
+    }
   }
   if (V > 0) {
-    add_tensor(m, "final_norm", {H}, true, m->head_flat0, -1, m->o_gf, true);
-    add_tensor(m, "lm_head", {V, H}, true, m->head_flat0 + H, -1, m->o_wout, false);
+    const bool ht = m->head_trainable;
+    add_tensor(m, "final_norm", {H}, ht, ht ? m->head_flat0 : -1, -1, m->o_gf, true);
+    add_tensor(m, "lm_head", {V, H}, ht, ht ? m->head_flat0 + H : -1, -1, m->o_wout, false);
   }
 
   // ---- host allocations
@@ -275,6 +335,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->loss_stage = (float*)pinned_alloc(m, T * 4, &st);
   m->lab_stage = (int32_t*)pinned_alloc(m, T * 4, &st);
   m->w_stage = (float*)pinned_alloc(m, T * 4, &st);
+  if (m->NE > 0) m->counts_stage = (int32_t*)pinned_alloc(m, (int64_t)m->NE * 4, &st);
   if (st != HOL_OK) {
     engine_destroy(m);
     return st;
@@ -309,7 +370,18 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->ao_n2 = A(T * H * E);
   m->ao_gu = A(T * 2 * F * E);
   m->ao_a = A(T * F * E);
+  const int64_t Tk = T * m->topk;
+  if (NE > 0) {
+    m->ao_probs = A(T * NE * 4);
+    m->ao_ids = A(Tk * 4);
+    m->ao_w = A(Tk * 4);
+    m->ao_slot = A(Tk * 4);
+    m->ao_perm = A(Tk * 4);
+    m->ao_gup = A(Tk * 2 * Fe * E);
+    m->ao_yp = A(Tk * H * 4);
+  }
   m->act_stride = a;
+  m->act_counts.assign(m->Kmax, std::vector<int32_t>(std::max<int64_t>(NE, 1), 0));
   m->act_mem = (uint8_t*)D((int64_t)m->Kmax * m->act_stride);
   m->hbuf[0] = (float*)D(T * H * 4);
   m->hbuf[1] = (float*)D(T * H * 4);
@@ -335,13 +407,32 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     m->logits = (float*)D(tc * V * 4);
     m->dlogits = D(tc * V * E);
   }
+  if (NE > 0) {
+    m->mlogits = (float*)D(T * NE * 4);
+    m->mcounts = (int32_t*)D((NE + 1) * 4);
+    m->moffsets = (int32_t*)D((NE + 1) * 4);
+    m->mcursor = (int32_t*)D((NE + 1) * 4);
+    m->xp = D(Tk * H * E);
+    m->ap = D(Tk * Fe * E);
+    m->dyp = D(Tk * H * E);
+    m->dap = D(Tk * Fe * E);
+    m->dgup = D(Tk * 2 * Fe * E);
+    m->dxp = (float*)D(Tk * H * 4);
+    m->dwr = (float*)D(Tk * 4);
+    m->dlogr = D(T * NE * E);
+    m->route_rec = (int32_t*)D(L * Tk * 4);
+  }
+  if (m->R > 0) {
+    m->lu = (float*)D(T * m->R * 4);
+    m->lg = (float*)D(T * m->R * 4);
+  }
   if (m->dt == DT_BF16) {
-    m->wT = D(m->layer_img_bytes);
+    m->wT = D(m->wT_bytes);
     const int64_t Tc64 = V > 0 ? m->Tc : 0;
     m->yT = D(std::max<int64_t>(T * std::max<int64_t>(2 * F, std::max<int64_t>(QKV, H)), Tc64 * V) * 2);
     m->xT = D(std::max<int64_t>(T * std::max<int64_t>(F, std::max<int64_t>(nqd, H)), Tc64 * H) * 2);
     if (V > 0) m->woutT = D(V * H * 2);
-    m->qkvf = (float*)D(T * QKV * 4);
+    m->qkvf = (float*)D(T * std::max<int64_t>(QKV, H) * 4);  // also the fp32 dO under LoRA
   }
   const int half = m->d / 2;
   m->cos_dev = (float*)D((int64_t)m->Smax * half * 4);
@@ -377,7 +468,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   for (int i = 0; i < (int)m->tensors.size(); ++i) {
     const TensorDesc& t = m->tensors[i];
     const int u = t.block == -2 ? 0 : (t.block == -1 ? m->L + 1 : 1 + t.block);
-    m->unit_tensors[u].push_back(i);
+    if (t.trainable) m->unit_tensors[u].push_back(i);
   }
   m->ev_unit.resize(m->L + 2);
   for (auto& e : m->ev_unit) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
@@ -426,9 +517,30 @@ static uint8_t* image_block(hol_model* m, int block) {
 }
 
 void refresh_image_tensor(hol_model* m, const TensorDesc& t) {
+  if (t.flat >= 0) write_image_tensor(m, t, m->master + t.flat);
+}
+
+// Tensor values as the image holds them (fp32, or bf16 widened); for frozen tensors this is the
+// only copy.
+void read_image_tensor(const hol_model* m, const TensorDesc& t, float* dst) {
+  const uint8_t* src = (t.block == -1 ? m->image + (int64_t)m->L * m->layer_img_bytes
+                                      : m->image + (int64_t)t.block * m->layer_img_bytes) + t.img;
+  if (t.img_f32 || m->dt == DT_F32) {
+    parallel_for(t.numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy(dst + lo, (const float*)src + lo, (hi - lo) * 4); });
+  } else {
+    parallel_for(t.numel, 1 << 18, [&](int64_t lo, int64_t hi) {
+      const uint16_t* b = (const uint16_t*)src;
+      for (int64_t i = lo; i < hi; ++i) {
+        const uint32_t u = (uint32_t)b[i] << 16;
+        memcpy(dst + i, &u, 4);
+      }
+    });
+  }
+}
+
+void write_image_tensor(hol_model* m, const TensorDesc& t, const float* src) {
   if (t.block == -2 || t.img < 0) return;
   uint8_t* dst = image_block(m, t.block) + t.img;
-  const float* src = m->master + t.flat;
   if (t.img_f32 || m->dt == DT_F32) {
     parallel_for(t.numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy((float*)dst + lo, src + lo, (hi - lo) * 4); });
   } else {
@@ -443,15 +555,25 @@ void refresh_image_tensor(hol_model* m, const TensorDesc& t) {
 struct W {
   const void *wqkv, *wo, *wgu, *wd;
   const float *g1, *g2;
+  const void *router, *egate, *eup, *edown;  // mixture of experts
+  const float *lA[4], *lB[4];                 // LoRA factors of q, k, v, o
 };
 static W bind(const hol_model* m, const uint8_t* slot) {
-  W w;
+  W w{};
   w.wqkv = slot + m->o_wqkv;
   w.wo = slot + m->o_wo;
   w.wgu = slot + m->o_wgu;
   w.wd = slot + m->o_wd;
   w.g1 = (const float*)(slot + m->o_g1);
   w.g2 = (const float*)(slot + m->o_g2);
+  w.router = slot + m->o_router;
+  w.egate = slot + m->o_egate;
+  w.eup = slot + m->o_eup;
+  w.edown = slot + m->o_edown;
+  for (int j = 0; j < 4; ++j) {
+    w.lA[j] = (const float*)(slot + m->o_lA[j]);
+    w.lB[j] = (const float*)(slot + m->o_lB[j]);
+  }
   return w;
 }
 
@@ -469,6 +591,13 @@ static Act act_at(const hol_model* m, int j) {
   a.n2 = b + m->ao_n2;
   a.gu = b + m->ao_gu;
   a.a = b + m->ao_a;
+  a.probs = (float*)(b + m->ao_probs);
+  a.ids = (int32_t*)(b + m->ao_ids);
+  a.w = (float*)(b + m->ao_w);
+  a.slot_pos = (int32_t*)(b + m->ao_slot);
+  a.perm_slot = (int32_t*)(b + m->ao_perm);
+  a.gup = b + m->ao_gup;
+  a.yp = (float*)(b + m->ao_yp);
   return a;
 }
 
@@ -511,20 +640,178 @@ static Gemm gemm(int M, int N, int K, const void* A, int64_t lda, bool a_km, con
   return g;
 }
 
+// Operands of different types (fp32 adapter factors against activations of the compute type).
+static Gemm mixed(int M, int N, int K, const void* A, int64_t lda, bool a_km, DType at, const void* B, int64_t ldb,
+                  bool b_kn, DType bt, void* C, int64_t ldc, int epi, float alpha) {
+  Gemm g = gemm(M, N, K, A, lda, a_km, B, ldb, b_kn, C, ldc, at, DT_F32, epi);
+  g.bt = bt;
+  g.alpha = alpha;
+  return g;
+}
+
+// LoRA branch of one projection (reading: y += s (x A^T) B^T, A [r, in], B [out, r], fp32):
+// y is fp32 [T, out] at row stride ldy, x the projection's input in the compute type.
+static hol_status lora_fwd(hol_model* m, const void* x, int64_t ldx, int in, int out, const float* A, const float* B,
+                           float* y, int64_t ldy, int T) {
+  const int r = m->R;
+  KCHECK(run_gemm(m, mixed(T, r, in, x, ldx, false, m->dt, A, in, false, DT_F32, m->lu, r, EPI_STORE, 1.f)));
+  KCHECK(run_gemm(m, mixed(T, out, r, m->lu, r, false, DT_F32, B, r, false, DT_F32, y, ldy, EPI_ACCUM,
+                           m->cfg.lora_scale)));
+  return HOL_OK;
+}
+
+// Its backward: u = x A^T, g = dy B; gB = s dy^T u, gA = s g^T x (stored), dx (fp32) += s g A.
+static hol_status lora_bwd(hol_model* m, const void* dy, int64_t lddy, const void* x, int64_t ldx, int in, int out,
+                           const float* A, const float* B, float* gA, float* gB, float* dx, int64_t lddx, int T) {
+  const int r = m->R;
+  const float sc = m->cfg.lora_scale;
+  const DType dt = m->dt;
+  KCHECK(run_gemm(m, mixed(T, r, in, x, ldx, false, dt, A, in, false, DT_F32, m->lu, r, EPI_STORE, 1.f)));
+  KCHECK(run_gemm(m, mixed(out, r, T, dy, lddy, true, dt, m->lu, r, true, DT_F32, gB, r, EPI_STORE, sc)));
+  KCHECK(run_gemm(m, mixed(T, r, out, dy, lddy, false, dt, B, r, true, DT_F32, m->lg, r, EPI_STORE, 1.f)));
+  KCHECK(run_gemm(m, mixed(r, in, T, m->lg, r, true, DT_F32, x, ldx, true, dt, gA, in, EPI_STORE, sc)));
+  KCHECK(run_gemm(m, mixed(T, in, r, m->lg, r, false, DT_F32, A, in, true, DT_F32, dx, lddx, EPI_ACCUM, sc)));
+  return HOL_OK;
+}
+
+// Mixture-of-experts MLP: hout = h1 + sum_i w_i SwiGLU_{e_i}(n2). Routing, the permutation and the
+// expert outputs go to the activation store; the expert row counts to act_counts[pos] (the host
+// reads them to launch one pair of GEMMs per expert).
+static hol_status moe_forward(hol_model* m, const W& w, const Act& A, int T, float* hout, int pos) {
+  const int H = m->H, NE = m->NE, k = m->topk, Fe = m->Fe;
+  const DType dt = m->dt;
+  const int64_t E = m->E, Tk = (int64_t)T * k;
+  hipStream_t s = m->sc;
+  KCHECK(run_gemm(m, gemm(T, NE, H, A.n2, H, false, w.router, H, false, m->mlogits, NE, dt, DT_F32, EPI_STORE)));
+  KT(KC_OTHER, 0, (double)T * NE * 8, launch_moe_route(m->mlogits, T, NE, k, A.probs, A.ids, A.w, m->mcounts, s));
+  KT(KC_OTHER, 0, (double)Tk * 16, launch_moe_permute(A.ids, T, NE, k, m->mcounts, m->moffsets, m->mcursor,
+                                                      A.perm_slot, A.slot_pos, s));
+  HCHECK(hipMemcpyAsync(m->counts_stage, m->mcounts, (size_t)NE * 4, hipMemcpyDeviceToHost, s));
+  HCHECK(hipStreamSynchronize(s));
+  std::vector<int32_t>& cnt = m->act_counts[pos];
+  memcpy(cnt.data(), m->counts_stage, (size_t)NE * 4);
+  KT(KC_OTHER, 0, 2.0 * Tk * H * E, launch_moe_gather(A.n2, dt, A.perm_slot, k, Tk, H, m->xp, s));
+  int64_t off = 0;
+  for (int e = 0; e < NE; ++e) {
+    const int me = cnt[e];
+    if (me > 0) {
+      const uint8_t* X = (const uint8_t*)m->xp + off * H * E;
+      uint8_t* GU = (uint8_t*)A.gup + off * 2 * Fe * E;
+      const int64_t wo = (int64_t)e * Fe * H * E;
+      KCHECK(run_gemm(m, gemm(me, Fe, H, X, H, false, (const uint8_t*)w.egate + wo, H, false, GU, 2 * Fe, dt, dt, EPI_STORE)));
+      KCHECK(run_gemm(m, gemm(me, Fe, H, X, H, false, (const uint8_t*)w.eup + wo, H, false, GU + Fe * E, 2 * Fe, dt, dt,
+                              EPI_STORE)));
+    }
+    off += me;
+  }
+  KT(KC_SWIGLU, 0, 3.0 * Tk * Fe * E, launch_swiglu_fwd(A.gup, m->ap, dt, (int)Tk, Fe, s));
+  off = 0;
+  for (int e = 0; e < NE; ++e) {
+    const int me = cnt[e];
+    if (me > 0)
+      KCHECK(run_gemm(m, gemm(me, H, Fe, (const uint8_t*)m->ap + off * Fe * E, Fe, false,
+                              (const uint8_t*)w.edown + (int64_t)e * H * Fe * E, Fe, false, A.yp + off * H, H, dt, DT_F32,
+                              EPI_STORE)));
+    off += me;
+  }
+  KT(KC_OTHER, 0, (double)T * H * 8 + (double)Tk * H * 4, launch_moe_combine(A.h1, A.yp, A.w, A.slot_pos, T, k, H, hout, s));
+  return HOL_OK;
+}
+
+// Backward of moe_forward: m->dh holds d loss / d hout; writes dn = d loss / d n2 (fp32, stored)
+// and, when the MoE weights train, their gradients into the layer block G.
+static hol_status moe_backward(hol_model* m, const W& w, const Act& A, int T, float* G, int pos) {
+  const int H = m->H, NE = m->NE, k = m->topk, Fe = m->Fe;
+  const DType dt = m->dt;
+  const int64_t E = m->E, Tk = (int64_t)T * k;
+  hipStream_t s = m->sc;
+  const std::vector<int32_t>& cnt = m->act_counts[pos];
+  const bool tr_w = m->base_trainable;
+  KT(KC_OTHER, 0, (double)Tk * H * (4 + 4 + E), launch_moe_combine_bwd(m->dh, A.yp, A.w, A.slot_pos, T, k, H, m->dwr, m->dyp, dt, s));
+  if (tr_w) KT(KC_SWIGLU, 0, 3.0 * Tk * Fe * E, launch_swiglu_fwd(A.gup, m->ap, dt, (int)Tk, Fe, s));
+  int64_t off = 0;
+  for (int e = 0; e < NE; ++e) {
+    const int me = cnt[e];
+    const uint8_t* dY = (const uint8_t*)m->dyp + off * H * E;
+    const uint8_t* Wd = (const uint8_t*)w.edown + (int64_t)e * H * Fe * E;
+    if (me > 0) KCHECK(run_gemm(m, gemm(me, Fe, H, dY, H, false, Wd, Fe, true, (uint8_t*)m->dap + off * Fe * E, Fe, dt, dt, EPI_STORE)));
+    if (tr_w) {
+      float* gWd = G + m->g_edown + (int64_t)e * H * Fe;
+      if (me > 0) {
+        Gemm g = gemm(H, Fe, me, dY, H, true, (const uint8_t*)m->ap + off * Fe * E, Fe, true, gWd, Fe, dt, DT_F32, EPI_STORE);
+        g.any_align = true;
+        KCHECK(run_gemm(m, g));
+      } else {
+        KCHECK(launch_fill_f32(gWd, 0.f, (int64_t)H * Fe, s));
+      }
+    }
+    off += me;
+  }
+  KT(KC_SWIGLU, 0, 5.0 * Tk * Fe * E, launch_swiglu_bwd(m->dap, A.gup, m->dgup, dt, (int)Tk, Fe, s));
+  if (tr_w) KT(KC_OTHER, 0, 2.0 * Tk * H * E, launch_moe_gather(A.n2, dt, A.perm_slot, k, Tk, H, m->xp, s));
+  off = 0;
+  for (int e = 0; e < NE; ++e) {
+    const int me = cnt[e];
+    const uint8_t* dGU = (const uint8_t*)m->dgup + off * 2 * Fe * E;
+    const int64_t wo = (int64_t)e * Fe * H * E;
+    if (me > 0) {
+      KCHECK(run_gemm(m, gemm(me, H, Fe, dGU, 2 * Fe, false, (const uint8_t*)w.egate + wo, H, true, m->dxp + off * H, H, dt,
+                              DT_F32, EPI_STORE)));
+      KCHECK(run_gemm(m, gemm(me, H, Fe, dGU + Fe * E, 2 * Fe, false, (const uint8_t*)w.eup + wo, H, true, m->dxp + off * H,
+                              H, dt, DT_F32, EPI_ACCUM)));
+    }
+    if (tr_w) {
+      float* gG = G + m->g_egate + (int64_t)e * Fe * H;
+      float* gU = G + m->g_eup + (int64_t)e * Fe * H;
+      if (me > 0) {
+        const uint8_t* X = (const uint8_t*)m->xp + off * H * E;
+        Gemm g1 = gemm(Fe, H, me, dGU, 2 * Fe, true, X, H, true, gG, H, dt, DT_F32, EPI_STORE);
+        Gemm g2 = gemm(Fe, H, me, dGU + Fe * E, 2 * Fe, true, X, H, true, gU, H, dt, DT_F32, EPI_STORE);
+        g1.any_align = g2.any_align = true;
+        KCHECK(run_gemm(m, g1));
+        KCHECK(run_gemm(m, g2));
+      } else {
+        KCHECK(launch_fill_f32(gG, 0.f, (int64_t)Fe * H, s));
+        KCHECK(launch_fill_f32(gU, 0.f, (int64_t)Fe * H, s));
+      }
+    }
+    off += me;
+  }
+  KT(KC_OTHER, 0, (double)Tk * H * 4 + (double)T * H * 4, launch_moe_unpermute(m->dxp, A.slot_pos, T, k, H, m->dn, s));
+  // router: dn += dlogits W_r, dW_r = dlogits^T n2
+  KT(KC_OTHER, 0, (double)T * NE * 8, launch_moe_router_bwd(A.probs, A.ids, A.w, m->dwr, T, NE, k, m->dlogr, dt, s));
+  {
+    Gemm g = gemm(T, H, NE, m->dlogr, NE, false, w.router, H, true, m->dn, H, dt, DT_F32, EPI_ACCUM);
+    g.any_align = true;
+    KCHECK(run_gemm(m, g));
+  }
+  if (tr_w) {
+    Gemm g = gemm(NE, H, T, m->dlogr, NE, true, A.n2, H, true, G + m->g_router, H, dt, DT_F32, EPI_STORE);
+    g.any_align = true;
+    KCHECK(run_gemm(m, g));
+  }
+  return HOL_OK;
+}
+
 static hol_status layer_forward(hol_model* m, const W& w, const float* hin, float* hout, const Act& A, int T,
-                                int n_seq, int S) {
-  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
+                                int n_seq, int S, int pos) {
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d, kvd = m->nkv * m->d;
   const DType dt = m->dt;
   const int64_t E = m->E;
   hipStream_t s = m->sc;
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hin, w.g1, m->cfg.rms_eps, A.n1, dt, A.r1, T, H, s));
+  // fp32 q | k | v projection output (the bf16 path rounds once, after RoPE)
+  float* qkv32 = dt == DT_BF16 ? m->qkvf : (float*)A.qkv;
+  KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, qkv32, QKV, dt, DT_F32, EPI_STORE)));
+  if (m->R > 0) {
+    const int c0[3] = {0, nqd, nqd + kvd}, outd[3] = {nqd, kvd, kvd};
+    for (int j = 0; j < 3; ++j)
+      STEP_OK(lora_fwd(m, A.n1, H, H, outd[j], w.lA[j], w.lB[j], qkv32 + c0[j], QKV, T));
+  }
   if (dt == DT_BF16) {
-    // fp32 projection output, then RoPE and one rounding to bf16
-    KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, m->qkvf, QKV, dt, DT_F32, EPI_STORE)));
     KT(KC_ROPE, 0, (double)T * QKV * (4 + E), launch_rope_qkv(m->qkvf, QKV, A.qkv, QKV, T, m->nq, m->nkv, d, S,
                                                               m->cos_dev, m->sin_dev, s));
   } else {
-    KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE)));
     KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
     KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
   }
@@ -535,7 +822,9 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   at.o = A.o; at.ldo = nqd; at.lse = A.lse;
   KT(KC_ATTN_FWD, 2.0 * d * m->nq * (double)S * (S + 1) * n_seq, (double)T * (QKV + nqd) * E, launch_attn_fwd(at, s));
   KCHECK(run_gemm(m, gemm(T, H, nqd, A.o, nqd, false, w.wo, nqd, false, A.h1, H, dt, DT_F32, EPI_RESID, hin, H)));
+  if (m->R > 0) STEP_OK(lora_fwd(m, A.o, nqd, nqd, H, w.lA[3], w.lB[3], A.h1, H, T));
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(A.h1, w.g2, m->cfg.rms_eps, A.n2, dt, A.r2, T, H, s));
+  if (m->NE > 0) return moe_forward(m, w, A, T, hout, pos);
   KCHECK(run_gemm(m, gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE)));
   KT(KC_SWIGLU, 0, 3.0 * T * F * E, launch_swiglu_fwd(A.gu, A.a, dt, T, F, s));
   KCHECK(run_gemm(m, gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H)));
@@ -558,23 +847,26 @@ static Gemm nt(int M, int N, int K, const void* A, int64_t lda, const void* B, i
 }
 
 // Transposes the resident layer's weights into m->wT (same sub-tensor offsets as the slot):
-// Wqkv^T [H, QKV], Wo^T [nqd, H], Wgu^T [H, 2F], Wd^T [F, H].
+// Wqkv^T [H, QKV], Wo^T [nqd, H], and for a dense MLP Wgu^T [H, 2F], Wd^T [F, H].
 static hol_status transpose_layer_weights(hol_model* m, const W& w) {
   const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F;
   uint8_t* t = (uint8_t*)m->wT;
   KCHECK(tr(m, w.wqkv, H, t + m->o_wqkv, QKV, QKV, H));
   KCHECK(tr(m, w.wo, nqd, t + m->o_wo, H, H, nqd));
+  if (m->NE > 0) return HOL_OK;
   KCHECK(tr(m, w.wgu, H, t + m->o_wgu, 2 * F, 2 * F, H));
   KCHECK(tr(m, w.wd, F, t + m->o_wd, H, H, F));
   return HOL_OK;
 }
 
-// bf16 backward: identical dataflow to layer_backward, every product as NT.
+// bf16 backward: identical dataflow to layer_backward, every dense product as NT. Frozen base
+// weights (LoRA) get no gradient products; the adapters' products run in fp32.
 static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, const float* hin, float* G, int T,
-                                      int n_seq, int S) {
-  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
+                                      int n_seq, int S, int pos) {
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d, kvd = m->nkv * m->d;
   const DType dt = DT_BF16;
   const int64_t E = 2;
+  const bool tw = m->base_trainable;
   hipStream_t s = m->sc;
   const uint8_t* wt = (const uint8_t*)m->wT;
   const void* WqkvT = wt + m->o_wqkv;  // [H, QKV]
@@ -582,26 +874,44 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   const void* WguT = wt + m->o_wgu;    // [H, 2F]
   const void* WdT = wt + m->o_wd;      // [F, H]
   STEP_OK(transpose_layer_weights(m, w));
-  // MLP: da = dh Wd, dWd = dh^T a
+  if (m->NE > 0) {
+    STEP_OK(moe_backward(m, w, A, T, G, pos));
+  } else {
+    // MLP: da = dh Wd, dWd = dh^T a
+    KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+    KCHECK(run_gemm(m, nt(T, F, H, m->dhb, H, WdT, H, m->da, F, dt)));
+    if (tw) {
+      KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
+      KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
+      KCHECK(run_gemm(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
+    }
+    KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
+    // dn2 = dgu Wgu, dWgu = dgu^T n2
+    KCHECK(run_gemm(m, nt(T, H, 2 * F, m->dgu, 2 * F, WguT, 2 * F, m->dn, H, DT_F32)));
+    if (tw) {
+      KCHECK(tr(m, m->dgu, 2 * F, m->yT, T, T, 2 * F));
+      KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
+      KCHECK(run_gemm(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
+    }
+  }
+  if (tw) KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, tw ? G + m->g_g2 : nullptr,
+                                                      m->partial, T, H, s));
+  // attention output projection: dO = dh1 Wo (+ LoRA), dWo = dh1^T o
   KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
-  KCHECK(run_gemm(m, nt(T, F, H, m->dhb, H, WdT, H, m->da, F, dt)));
-  KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
-  KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
-  KCHECK(run_gemm(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
-  KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
-  // dn2 = dgu Wgu, dWgu = dgu^T n2
-  KCHECK(run_gemm(m, nt(T, H, 2 * F, m->dgu, 2 * F, WguT, 2 * F, m->dn, H, DT_F32)));
-  KCHECK(tr(m, m->dgu, 2 * F, m->yT, T, T, 2 * F));
-  KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
-  KCHECK(run_gemm(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
-  KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
-  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, G + m->g_g2, m->partial, T, H, s));
-  // attention output projection: dO = dh1 Wo, dWo = dh1^T o
-  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
-  KCHECK(run_gemm(m, nt(T, nqd, H, m->dhb, H, WoT, H, m->dO, nqd, dt)));
-  KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));
-  KCHECK(tr(m, A.o, nqd, m->xT, T, T, nqd));
-  KCHECK(run_gemm(m, nt(H, nqd, T, m->yT, T, m->xT, T, G + m->g_wo, nqd, DT_F32)));
+  if (m->R > 0) {
+    float* dO32 = m->qkvf;  // fp32 [T, nqd]
+    KCHECK(run_gemm(m, nt(T, nqd, H, m->dhb, H, WoT, H, dO32, nqd, DT_F32)));
+    STEP_OK(lora_bwd(m, m->dhb, H, A.o, nqd, nqd, H, w.lA[3], w.lB[3], G + m->g_lA[3], G + m->g_lB[3], dO32, nqd, T));
+    KT(KC_OTHER, 0, (double)T * nqd * (4 + E), launch_cast_f32(dO32, m->dO, dt, (int64_t)T * nqd, s));
+  } else {
+    KCHECK(run_gemm(m, nt(T, nqd, H, m->dhb, H, WoT, H, m->dO, nqd, dt)));
+  }
+  if (tw) {
+    KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));
+    KCHECK(tr(m, A.o, nqd, m->xT, T, T, nqd));
+    KCHECK(run_gemm(m, nt(H, nqd, T, m->yT, T, m->xT, T, G + m->g_wo, nqd, DT_F32)));
+  }
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
   at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
@@ -614,37 +924,55 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   KT(KC_ATTN_BWD, 5.0 * d * m->nq * (double)S * (S + 1) * n_seq, (double)T * (2 * QKV + 3 * nqd) * E, launch_attn_bwd(at, s));
   KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
   KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
-  // q/k/v projections: dn1 = dqkv Wqkv, dWqkv = dqkv^T n1
+  // q/k/v projections: dn1 = dqkv Wqkv (+ LoRA), dWqkv = dqkv^T n1
   KCHECK(run_gemm(m, nt(T, H, QKV, m->dqkv, QKV, WqkvT, QKV, m->dn, H, DT_F32)));
-  KCHECK(tr(m, m->dqkv, QKV, m->yT, T, T, QKV));
-  KCHECK(tr(m, A.n1, H, m->xT, T, T, H));
-  KCHECK(run_gemm(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
-  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, G + m->g_g1, m->partial, T, H, s));
+  if (m->R > 0) {
+    const int c0[3] = {0, nqd, nqd + kvd}, outd[3] = {nqd, kvd, kvd};
+    for (int j = 0; j < 3; ++j)
+      STEP_OK(lora_bwd(m, (const uint8_t*)m->dqkv + (int64_t)c0[j] * E, QKV, A.n1, H, H, outd[j], w.lA[j], w.lB[j],
+                       G + m->g_lA[j], G + m->g_lB[j], m->dn, H, T));
+  }
+  if (tw) {
+    KCHECK(tr(m, m->dqkv, QKV, m->yT, T, T, QKV));
+    KCHECK(tr(m, A.n1, H, m->xT, T, T, H));
+    KCHECK(run_gemm(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
+  }
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, tw ? G + m->g_g1 : nullptr,
+                                                      m->partial, T, H, s));
   return HOL_OK;
 }
 
 // dh (fp32 [T,H]) holds d loss / d h_out on entry and d loss / d h_in on exit; G is the layer's
 // gradient block (fully overwritten).
 static hol_status layer_backward(hol_model* m, const W& w, const Act& A, const float* hin, float* G, int T, int n_seq,
-                                 int S) {
-  if (m->dt == DT_BF16) return layer_backward_bf16(m, w, A, hin, G, T, n_seq, S);
-  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d;
+                                 int S, int pos) {
+  if (m->dt == DT_BF16) return layer_backward_bf16(m, w, A, hin, G, T, n_seq, S, pos);
+  const int H = m->H, QKV = m->QKV, nqd = m->nqd, F = m->F, d = m->d, kvd = m->nkv * m->d;
   const DType dt = m->dt;
   const int64_t E = m->E;
+  const bool tw = m->base_trainable;
   hipStream_t s = m->sc;
   // MLP
-  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
-  KCHECK(run_gemm(m, gemm(T, F, H, m->dhb, H, false, w.wd, F, true, m->da, F, dt, dt, EPI_STORE)));
-  KCHECK(run_gemm(m, gemm(H, F, T, m->dhb, H, true, A.a, F, true, G + m->g_wd, F, dt, DT_F32, EPI_STORE)));
-  KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
-  KCHECK(run_gemm(m, gemm(T, H, 2 * F, m->dgu, 2 * F, false, w.wgu, H, true, m->dn, H, dt, DT_F32, EPI_STORE)));
-  KCHECK(run_gemm(m, gemm(2 * F, H, T, m->dgu, 2 * F, true, A.n2, H, true, G + m->g_wgu, H, dt, DT_F32, EPI_STORE)));
-  KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
-  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, G + m->g_g2, m->partial, T, H, s));
+  if (m->NE > 0) {
+    STEP_OK(moe_backward(m, w, A, T, G, pos));
+  } else {
+    KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+    KCHECK(run_gemm(m, gemm(T, F, H, m->dhb, H, false, w.wd, F, true, m->da, F, dt, dt, EPI_STORE)));
+    if (tw) KCHECK(run_gemm(m, gemm(H, F, T, m->dhb, H, true, A.a, F, true, G + m->g_wd, F, dt, DT_F32, EPI_STORE)));
+    KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
+    KCHECK(run_gemm(m, gemm(T, H, 2 * F, m->dgu, 2 * F, false, w.wgu, H, true, m->dn, H, dt, DT_F32, EPI_STORE)));
+    if (tw) KCHECK(run_gemm(m, gemm(2 * F, H, T, m->dgu, 2 * F, true, A.n2, H, true, G + m->g_wgu, H, dt, DT_F32, EPI_STORE)));
+  }
+  if (tw) KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, tw ? G + m->g_g2 : nullptr,
+                                                      m->partial, T, H, s));
   // attention
   KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
   KCHECK(run_gemm(m, gemm(T, nqd, H, m->dhb, H, false, w.wo, nqd, true, m->dO, nqd, dt, dt, EPI_STORE)));
-  KCHECK(run_gemm(m, gemm(H, nqd, T, m->dhb, H, true, A.o, nqd, true, G + m->g_wo, nqd, dt, DT_F32, EPI_STORE)));
+  if (m->R > 0)
+    STEP_OK(lora_bwd(m, m->dhb, H, A.o, nqd, nqd, H, w.lA[3], w.lB[3], G + m->g_lA[3], G + m->g_lB[3], (float*)m->dO,
+                     nqd, T));
+  if (tw) KCHECK(run_gemm(m, gemm(H, nqd, T, m->dhb, H, true, A.o, nqd, true, G + m->g_wo, nqd, dt, DT_F32, EPI_STORE)));
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
   at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
@@ -658,8 +986,15 @@ static hol_status layer_backward(hol_model* m, const W& w, const Act& A, const f
   KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
   KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
   KCHECK(run_gemm(m, gemm(T, H, QKV, m->dqkv, QKV, false, w.wqkv, H, true, m->dn, H, dt, DT_F32, EPI_STORE)));
-  KCHECK(run_gemm(m, gemm(QKV, H, T, m->dqkv, QKV, true, A.n1, H, true, G + m->g_wqkv, H, dt, DT_F32, EPI_STORE)));
-  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, G + m->g_g1, m->partial, T, H, s));
+  if (m->R > 0) {
+    const int c0[3] = {0, nqd, nqd + kvd}, outd[3] = {nqd, kvd, kvd};
+    for (int j = 0; j < 3; ++j)
+      STEP_OK(lora_bwd(m, (const uint8_t*)m->dqkv + (int64_t)c0[j] * E, QKV, A.n1, H, H, outd[j], w.lA[j], w.lB[j],
+                       G + m->g_lA[j], G + m->g_lB[j], m->dn, H, T));
+  }
+  if (tw) KCHECK(run_gemm(m, gemm(QKV, H, T, m->dqkv, QKV, true, A.n1, H, true, G + m->g_wqkv, H, dt, DT_F32, EPI_STORE)));
+  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, tw ? G + m->g_g1 : nullptr,
+                                                      m->partial, T, H, s));
   return HOL_OK;
 }
 
@@ -677,7 +1012,8 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
   const float* gf = (const float*)(m->head_dev + m->o_gf);
   const void* wout = m->head_dev + m->o_wout;
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hL, gf, m->cfg.rms_eps, m->zbuf, dt, m->rz, T, H, s));
-  float* gW = m->head_gdev + H;
+  const bool ht = m->head_trainable;  // frozen under LoRA: no W_out / final-norm gradient
+  float* gW = ht ? m->head_gdev + H : nullptr;
   if (dt == DT_BF16) KCHECK(tr(m, wout, H, m->woutT, V, V, H));  // W_out^T [H, V]
   for (int r0 = 0; r0 < T; r0 += m->Tc) {
     const int tc = std::min(m->Tc, T - r0);
@@ -687,6 +1023,7 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
       KT(KC_CE, 0, (double)tc * V * (4 + E), launch_ce_fwd_bwd(m->logits, V, m->labels_dev + r0, m->w_dev + r0,
                                                                m->rowloss_dev + r0, m->dlogits, dt, V, tc, V, s));
       KCHECK(run_gemm(m, nt(tc, H, V, m->dlogits, V, m->woutT, V, m->dn + (int64_t)r0 * H, H, DT_F32)));
+      if (!ht) continue;
       KCHECK(tr(m, m->dlogits, V, m->yT, tc, tc, V));   // dlogits^T [V, tc]
       KCHECK(tr(m, zc, H, m->xT, tc, tc, H));           // z^T [H, tc]
       KCHECK(run_gemm(m, nt(V, H, tc, m->yT, tc, m->xT, tc, gW, H, DT_F32, r0 == 0 ? EPI_STORE : EPI_ACCUM)));
@@ -696,11 +1033,13 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
                                                              m->rowloss_dev + r0, m->dlogits, dt, V, tc, V, s));
     KCHECK(run_gemm(m, gemm(tc, H, V, m->dlogits, V, false, wout, H, true, m->dn + (int64_t)r0 * H, H, dt, DT_F32,
                             EPI_STORE)));
-    KCHECK(run_gemm(m, gemm(V, H, tc, m->dlogits, V, true, zc, H, true, gW, H, dt, DT_F32,
-                            r0 == 0 ? EPI_STORE : EPI_ACCUM)));
+    if (ht)
+      KCHECK(run_gemm(m, gemm(V, H, tc, m->dlogits, V, true, zc, H, true, gW, H, dt, DT_F32,
+                              r0 == 0 ? EPI_STORE : EPI_ACCUM)));
   }
-  KCHECK(launch_fill_f32(m->head_gdev, 0.f, H, s));
-  KT(KC_RMSNORM, 0, 12.0 * T * H, launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, m->head_gdev, m->partial, T, H, s));
+  if (ht) KCHECK(launch_fill_f32(m->head_gdev, 0.f, H, s));
+  KT(KC_RMSNORM, 0, 12.0 * T * H, launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, ht ? m->head_gdev : nullptr,
+                                                      m->partial, T, H, s));
   return HOL_OK;
 }
 
@@ -993,7 +1332,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       STEP(head_forward_backward(m, ckpt_of(m->nblocks), T, loss));
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 5});
-      if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE) {
+      if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE && m->head_trainable) {
         // head gradient to the host (gradient-transfer stream)
         HSTEP(hipEventRecord(m->ev_gdone[0], sc));
         HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[0], 0));
@@ -1020,6 +1359,9 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     const int s = op_slot[j];
     const W w = bind(m, m->slot[s]);
     HSTEP(hipStreamWaitEvent(sc, m->ev_ready[s], 0));
+    // the next layer's weights go to the other slot while this op computes (issued first: a
+    // mixture-of-experts layer waits on the host for its routing counts mid-op)
+    STEP(prefetch());
     const int n_seq = B;
     if (op.kind == OP_FWD) {
       // h_in: checkpoint of the block for the block's first layer, else the previous output
@@ -1033,13 +1375,18 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       // The last block keeps its forward activations in the store, where the backward reads them
       // (the recompute of that block would reproduce them bit for bit).
       Act A = act_at(m, 0);
+      int pos = 0;
       if (l >= lb0) {
-        A = act_at(m, l - lb0);
+        pos = l - lb0;
+        A = act_at(m, pos);
         if (l > lb0) hin = A.hin;
-        if (l + 1 < L) hout = act_at(m, l - lb0 + 1).hin;
+        if (l + 1 < L) hout = act_at(m, pos + 1).hin;
       }
       HSTEP(hipEventRecord(ta, sc));
-      STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S));
+      STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S, pos));
+      if (m->NE > 0)  // routing of this forward pass, kept for hol_get_routing
+        HSTEP(hipMemcpyAsync(m->route_rec + (int64_t)l * T * m->topk, A.ids, (size_t)T * m->topk * 4,
+                             hipMemcpyDeviceToDevice, sc));
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 2});
     } else if (op.kind == OP_RECOMP) {
@@ -1048,7 +1395,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
       float* hout = (op.layer + 1 < l1) ? act_at(m, op.pos + 1).hin : m->hbuf[0];
       HSTEP(hipEventRecord(ta, sc));
-      STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S));
+      STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S, op.pos));
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 3});
     } else {  // OP_BWD
@@ -1056,7 +1403,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
       HSTEP(hipStreamWaitEvent(sc, m->ev_gfree[gi], 0));
       HSTEP(hipEventRecord(ta, sc));
-      STEP(layer_backward(m, w, A, hin, m->gdev[gi], T, n_seq, S));
+      STEP(layer_backward(m, w, A, hin, m->gdev[gi], T, n_seq, S, op.pos));
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 4});
       HSTEP(hipEventRecord(m->ev_gdone[gi], sc));
@@ -1083,10 +1430,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       gi ^= 1;
     }
     HSTEP(hipEventRecord(m->ev_free[s], sc));
-    STEP(prefetch());
   }
   // ---- first-layer gradient (embedding rows) and loss rows back to the host
-  if (m->V > 0) {
+  m->last_T = T;
+  if (m->embed_trainable) {
     HSTEP(hipMemcpyAsync(m->h_stage, m->dh, T64 * H * 4, hipMemcpyDeviceToHost, sc));
     m->stats.d2h_bytes += (double)T64 * H * 4;
   }
@@ -1097,7 +1444,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   m->stats.gpu_done_ms = now_ms() - t_start;
   HSTEP(hipGetLastError());
   // embedding gradient: rows added in token order (columns split over threads: deterministic)
-  if (m->V > 0) {
+  if (m->embed_trainable) {
     float* gE = m->grad + m->embed_flat0;
     parallel_for(H, 64, [&](int64_t lo, int64_t hi) {
       for (int64_t t = 0; t < T64; ++t) {
@@ -1203,6 +1550,20 @@ hol_status engine_step(hol_model* m) {
   // every trainable gradient was zeroed by its unit; frozen tensors never hold gradients
   m->grads_zero = true;
   m->stats.step_ms = now_ms() - t0;
+  return HOL_OK;
+}
+
+hol_status engine_get_routing(const hol_model* m, int layer, int32_t* ids, int64_t n) {
+  if (m->NE <= 0) {
+    set_error("hol_get_routing: the model has no mixture-of-experts layers");
+    return HOL_EINVAL;
+  }
+  if (layer < 0 || layer >= m->L || m->last_T <= 0 || n != (int64_t)m->last_T * m->topk) {
+    set_error("hol_get_routing: bad layer or n, or no forward_backward yet");
+    return HOL_EINVAL;
+  }
+  HCHECK(hipSetDevice(m->cfg.device));
+  HCHECK(hipMemcpy(ids, m->route_rec + (int64_t)layer * m->last_T * m->topk, (size_t)n * 4, hipMemcpyDeviceToHost));
   return HOL_OK;
 }
 

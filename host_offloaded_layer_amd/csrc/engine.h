@@ -22,7 +22,8 @@ struct TensorDesc {
   int64_t shape[4] = {0, 0, 0, 0};
   int64_t numel = 0;
   bool trainable = true;
-  int64_t flat = 0;      // offset (floats) in the flat host arrays (master / grad / m / v)
+  int64_t flat = 0;      // offset (floats) in the flat host arrays (master / grad / m / v); -1 for a
+                         // frozen tensor whose only copy is its image (frozen base under LoRA)
   int block = 0;         // image block: layer index, or -1 for the head block, -2 none (embed)
   int64_t img = -1;      // byte offset inside that image block
   bool img_f32 = false;  // kept fp32 in the image (norm gains)
@@ -41,6 +42,14 @@ struct Act {
   void* n2 = nullptr;    // [T,H]
   void* gu = nullptr;    // [T, 2F] (gate | up)
   void* a = nullptr;     // silu(gate)*up [T, F]
+  // mixture of experts (T k routed rows)
+  float* probs = nullptr;       // router softmax fp32 [T, E]
+  int32_t* ids = nullptr;       // [T, k] expert of each slot
+  float* w = nullptr;           // [T, k] renormalised routing weight
+  int32_t* slot_pos = nullptr;  // [T k] routed row of each slot
+  int32_t* perm_slot = nullptr; // [T k] slot of each routed row
+  void* gup = nullptr;          // [T k, 2 Fe] expert gate | up outputs
+  float* yp = nullptr;          // [T k, H] expert outputs (fp32)
 };
 
 enum OpKind { OP_FWD = 0, OP_RECOMP = 1, OP_BWD = 2, OP_HEAD = 3 };
@@ -75,6 +84,10 @@ struct hol_model {
   hol_config cfg{};
   // derived shape
   int L = 0, H = 0, nq = 0, nkv = 0, d = 0, F = 0, V = 0, QKV = 0, nqd = 0;
+  int NE = 0, topk = 0, Fe = 0;  // experts (NE == 0: dense MLP), experts per token, expert FFN width
+  int R = 0;                     // LoRA rank (0: full fine-tune)
+  bool base_trainable = true;    // false under LoRA: every base tensor is frozen
+  bool head_trainable = false, embed_trainable = false;
   int E = 4;  // bytes per compute element
   hol::DType dt = hol::DT_F32;
   int Tmax = 0, Smax = 0, K = 1, Kmax = 1, nblocks = 0, n_ckpt = 0;
@@ -88,9 +101,15 @@ struct hol_model {
   float* mom2 = nullptr;
   uint8_t* image = nullptr;  // low-precision copy, layer-contiguous, 4 KiB aligned (pinned)
   int64_t layer_img_bytes = 0, head_img_bytes = 0, image_bytes = 0;
-  int64_t o_wqkv = 0, o_wo = 0, o_wgu = 0, o_wd = 0, o_g1 = 0, o_g2 = 0;  // layer image offsets
+  // layer image offsets (bytes); MoE: router [E, H], expert gates [E, Fe, H], ups [E, Fe, H],
+  // downs [E, H, Fe]; LoRA factors fp32: A [r, in], B [out, r] for q, k, v, o
+  int64_t o_wqkv = 0, o_wo = 0, o_wgu = 0, o_wd = 0, o_g1 = 0, o_g2 = 0;
+  int64_t o_router = 0, o_egate = 0, o_eup = 0, o_edown = 0, o_lA[4] = {}, o_lB[4] = {};
   int64_t o_gf = 0, o_wout = 0;                                           // head image offsets
-  int64_t g_wqkv = 0, g_wo = 0, g_wgu = 0, g_wd = 0, g_g1 = 0, g_g2 = 0;  // layer grad offsets (floats)
+  // layer gradient block offsets (floats); -1 when the tensor is frozen
+  int64_t g_wqkv = -1, g_wo = -1, g_wgu = -1, g_wd = -1, g_g1 = -1, g_g2 = -1;
+  int64_t g_router = -1, g_egate = -1, g_eup = -1, g_edown = -1, g_lA[4] = {-1, -1, -1, -1}, g_lB[4] = {-1, -1, -1, -1};
+  int64_t wT_bytes = 0;  // bytes of the layer image the bf16 backward transposes
 
   // pinned host staging
   float* h_stage = nullptr;      // [Tmax, H] embedding rows up / first-layer gradient down
@@ -112,7 +131,18 @@ struct hol_model {
   uint8_t* act_mem = nullptr;
   int64_t act_stride = 0;
   int64_t ao_hin = 0, ao_r1 = 0, ao_n1 = 0, ao_qkv = 0, ao_o = 0, ao_lse = 0, ao_h1 = 0, ao_r2 = 0, ao_n2 = 0,
-          ao_gu = 0, ao_a = 0;
+          ao_gu = 0, ao_a = 0, ao_probs = 0, ao_ids = 0, ao_w = 0, ao_slot = 0, ao_perm = 0, ao_gup = 0, ao_yp = 0;
+  // mixture of experts: per activation-store position, the host copy of the expert row counts
+  std::vector<std::vector<int32_t>> act_counts;
+  float* mlogits = nullptr;                       // router logits fp32 [T, E]
+  int32_t *mcounts = nullptr, *moffsets = nullptr, *mcursor = nullptr;
+  int32_t* counts_stage = nullptr;                // pinned [E]
+  void *xp = nullptr, *ap = nullptr, *dyp = nullptr, *dap = nullptr, *dgup = nullptr, *dlogr = nullptr;
+  float *dxp = nullptr, *dwr = nullptr;
+  int32_t* route_rec = nullptr;                   // [L, T k] expert ids of the last forward pass
+  int last_T = 0;
+  // LoRA scratch: x A^T and dy B, fp32 [T, r]
+  float *lu = nullptr, *lg = nullptr;
   float* hbuf[2] = {nullptr, nullptr};
   float* dh = nullptr;
   float* dn = nullptr;
@@ -175,6 +205,9 @@ hol_status engine_zero_grad(hol_model* m);
 hol_status engine_set_k(hol_model* m, int k);
 hol_status engine_set_kernel_timing(hol_model* m, bool on);
 void refresh_image_tensor(hol_model* m, const TensorDesc& t);
+void write_image_tensor(hol_model* m, const TensorDesc& t, const float* src);
+void read_image_tensor(const hol_model* m, const TensorDesc& t, float* dst);
+hol_status engine_get_routing(const hol_model* m, int layer, int32_t* ids, int64_t n);
 std::string stats_json(const hol_model* m);
 void set_error(const std::string& s);
 }  // namespace hol

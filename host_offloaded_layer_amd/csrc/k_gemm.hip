@@ -18,13 +18,13 @@ namespace hol {
 // ------------------------------------------------------------------------------------------
 // generic fp32 / mixed tiled GEMM
 // ------------------------------------------------------------------------------------------
-template <typename TI, typename TO>
+template <typename TA, typename TB, typename TO>
 __global__ __launch_bounds__(256) void gemm_tiled(Gemm g) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
   const int z = blockIdx.z;
-  const TI* A = (const TI*)g.A + z * g.sA;
-  const TI* B = (const TI*)g.B + z * g.sB;
+  const TA* A = (const TA*)g.A + z * g.sA;
+  const TB* B = (const TB*)g.B + z * g.sB;
   const int M = g.M, N = g.N, K = g.K;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
@@ -465,21 +465,35 @@ int launch_gemm(const Gemm& g, hipStream_t s) {
   if (g.K <= 0) return (int)hipErrorInvalidValue;
   if (g.epi != EPI_STORE && g.c != DT_F32) return (int)hipErrorInvalidValue;
   if (g.epi == EPI_RESID && !g.R) return (int)hipErrorInvalidValue;
-  if (g.ab == DT_BF16) {
+  const DType tb = g.bt < 0 ? g.ab : (DType)g.bt;
+  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.batch);
+  if (g.ab == DT_BF16 && tb == DT_BF16) {
     // MFMA path: 16-byte rows need K, leading dimensions and base pointers 8-element aligned
     const bool aligned = (g.K % 8 == 0) && (g.lda % 8 == 0) && (g.ldb % 8 == 0) &&
                          (((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0) &&
                          (g.batch == 1 || (g.sA % 8 == 0 && g.sB % 8 == 0));
-    if (!aligned) return (int)hipErrorInvalidValue;
-    if (!g.a_km && !g.b_kn && g.K % N2_BK == 0) return launch_nt2(g, s);
-    if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
-    if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);
-    if (g.a_km && g.b_kn) return launch_mfma_l<true, true>(g, s);
-    return launch_mfma_l<true, false>(g, s);
+    if (aligned) {
+      if (!g.a_km && !g.b_kn && g.K % N2_BK == 0) return launch_nt2(g, s);
+      if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
+      if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);
+      if (g.a_km && g.b_kn) return launch_mfma_l<true, true>(g, s);
+      return launch_mfma_l<true, false>(g, s);
+    }
+    if (!g.any_align) return (int)hipErrorInvalidValue;
+    if (g.c == DT_BF16) hipLaunchKernelGGL((gemm_tiled<bf16, bf16, bf16>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((gemm_tiled<bf16, bf16, float>), grid, dim3(256), 0, s, g);
+    return (int)hipGetLastError();
   }
-  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.batch);
-  if (g.c == DT_BF16) hipLaunchKernelGGL((gemm_tiled<float, bf16>), grid, dim3(256), 0, s, g);
-  else hipLaunchKernelGGL((gemm_tiled<float, float>), grid, dim3(256), 0, s, g);
+  // fp32 and mixed operands (fp32 adapter factors against bf16 activations)
+#define GT(TA, TB)                                                                           \
+  do {                                                                                       \
+    if (g.c == DT_BF16) hipLaunchKernelGGL((gemm_tiled<TA, TB, bf16>), grid, dim3(256), 0, s, g); \
+    else hipLaunchKernelGGL((gemm_tiled<TA, TB, float>), grid, dim3(256), 0, s, g);          \
+  } while (0)
+  if (g.ab == DT_F32 && tb == DT_F32) GT(float, float);
+  else if (g.ab == DT_BF16) GT(bf16, float);
+  else GT(float, bf16);
+#undef GT
   return (int)hipGetLastError();
 }
 

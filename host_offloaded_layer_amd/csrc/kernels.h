@@ -32,6 +32,8 @@ struct Gemm {
   int epi = EPI_STORE;
   float alpha = 1.f;
   int batch = 1; int64_t sA = 0, sB = 0, sC = 0, sR = 0;
+  int bt = -1;             // dtype of B when it differs from ab (fp32 adapter factors); -1: ab
+  bool any_align = false;  // bf16 operands that miss the MFMA alignment take the tiled kernel
 };
 int launch_gemm(const Gemm& g, hipStream_t s);
 
@@ -93,6 +95,29 @@ int launch_attn_bwd(const Attn& a, hipStream_t s);
 int launch_ce_fwd_bwd(const float* logits, int64_t ld, const int32_t* labels, const float* w,
                       float* row_loss, void* dlogits, DType dt, int64_t ldd, int Tc, int V,
                       hipStream_t s);
+// Mixture-of-experts routing and permutation (k_moe.hip). logits / probs fp32 [T, E]; ids int32
+// and w fp32 [T, k]; counts / cursor int32 [E]; offsets int32 [E + 1]; perm_slot and slot_pos
+// int32 [T k]. E <= 512, k <= 16.
+int launch_fill_i32(int32_t* x, int32_t v, int64_t n, hipStream_t s);
+int launch_moe_route(const float* logits, int T, int E, int k, float* probs, int32_t* ids, float* w,
+                     int32_t* counts, hipStream_t s);
+int launch_moe_permute(const int32_t* ids, int T, int E, int k, const int32_t* counts, int32_t* offsets,
+                       int32_t* cursor, int32_t* perm_slot, int32_t* slot_pos, hipStream_t s);
+// Xp[p] = X[perm_slot[p] / k] for rows of H elements of type t
+int launch_moe_gather(const void* X, DType t, const int32_t* perm_slot, int k, int64_t n_rows, int H, void* Xp,
+                      hipStream_t s);
+// hout[t] = h1[t] + sum_i w[t, i] Yp[slot_pos[t k + i]]   (fp32)
+int launch_moe_combine(const float* h1, const float* Yp, const float* w, const int32_t* slot_pos, int T, int k, int H,
+                       float* hout, hipStream_t s);
+// dw[t, i] = <dh[t], Yp[p_i]>; dYp[p_i] = w[t, i] dh[t] (type t)
+int launch_moe_combine_bwd(const float* dh, const float* Yp, const float* w, const int32_t* slot_pos, int T, int k,
+                           int H, float* dw, void* dYp, DType t, hipStream_t s);
+// dn[t] = sum_i dXp[slot_pos[t k + i]]   (fp32, overwrites dn)
+int launch_moe_unpermute(const float* dXp, const int32_t* slot_pos, int T, int k, int H, float* dn, hipStream_t s);
+// d loss / d router logits from d loss / d w (type t output)
+int launch_moe_router_bwd(const float* probs, const int32_t* ids, const float* w, const float* dw, int T, int E, int k,
+                          void* dlogits, DType t, hipStream_t s);
+
 // Sum of squares: row_loss[t] = sum_j h^2, dh = 2h.
 int launch_sumsq(const float* h, float* row_loss, float* dh, int T, int H, hipStream_t s);
 

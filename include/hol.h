@@ -59,8 +59,16 @@ typedef struct {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn;
   int32_t vocab;              /* > 0: token input with untied embedding and LM head;
                                  0: hidden-state input, no embedding, no head */
-  int32_t n_experts, top_k, expert_ffn; /* n_experts == 0: dense SwiGLU (MoE: HOL_EUNSUPPORTED) */
-  int32_t lora_rank;          /* 0: full fine-tune (LoRA: HOL_EUNSUPPORTED in this build) */
+  int32_t n_experts, top_k, expert_ffn; /* n_experts == 0: dense SwiGLU MLP of width ffn.
+                                 n_experts in [1, 512]: mixture-of-experts MLP instead (ffn
+                                 unused): router logits n W_r^T (W_r [n_experts, hidden]),
+                                 softmax, the top_k (<= 16) largest probabilities with ties to the
+                                 lower expert index, weights renormalised over the kept experts,
+                                 no capacity limit; each kept expert is a SwiGLU of width
+                                 expert_ffn; outputs summed with those weights */
+  int32_t lora_rank;          /* 0: full fine-tune. 1..64: every base tensor is frozen and a
+                                 LoRA adapter y += lora_scale (x A^T) B^T (A [r, in], B [out, r],
+                                 fp32) on the q, k, v and output projections is trained */
   float lora_scale;
   float rope_base, rms_eps;   /* e.g. 10000, 1e-5 */
   int32_t ckpt_every_k;       /* keep h_0, h_K, h_2K, ... in HBM (MegaTrain: checkpoint every K) */
@@ -95,16 +103,24 @@ void hol_destroy(hol_model* m);
 hol_status hol_num_tensors(const hol_model* m, int32_t* n);
 hol_status hol_tensor_info(const hol_model* m, int32_t i, char* name, size_t cap, int64_t shape[4],
                            int32_t* ndim, int32_t* trainable);
-/* fp32 master <- src (numel floats, row-major) and refresh of the low-precision image. */
+/* fp32 master <- src (numel floats, row-major) and refresh of the low-precision image. A frozen
+ * tensor other than the embedding keeps no fp32 master: set writes its image (rounded to the
+ * compute dtype) and get returns the image's values. */
 hol_status hol_set_tensor(hol_model* m, int32_t i, const float* src, int64_t numel);
 hol_status hol_get_tensor(const hol_model* m, int32_t i, float* dst, int64_t numel);
 /* Accumulated gradient of a trainable tensor (zeros after hol_step / hol_zero_grad). */
 hol_status hol_get_grad(const hol_model* m, int32_t i, float* dst, int64_t numel);
-/* Adam moments and the step counter (number of hol_step calls so far); set restores them. */
+/* Adam moments and the step counter (number of hol_step calls so far) of a trainable tensor;
+ * set restores them. HOL_EINVAL for a frozen tensor. */
 hol_status hol_get_adam_state(const hol_model* m, int32_t i, float* mom1, float* mom2, int64_t numel,
                               int64_t* step);
 hol_status hol_set_adam_state(hol_model* m, int32_t i, const float* mom1, const float* mom2,
                               int64_t numel, int64_t step);
+
+/* Mixture-of-experts routing of the last forward_backward: the top_k expert ids chosen for each
+ * token of layer `layer` in slot order (ids[t * top_k + i]; t over batch*seq tokens, n =
+ * batch*seq*top_k). HOL_EINVAL for a dense model, a bad layer or n, or before any call. */
+hol_status hol_get_routing(const hol_model* m, int32_t layer, int32_t* ids, int64_t n);
 
 /* Checkpoint interval for later forward_backward calls: 1 <= k <= cfg.ckpt_every_k (the
  * activation store is planned for cfg.ckpt_every_k layers, the checkpoint store for k = 1).

@@ -112,10 +112,19 @@ def test_create_rejects_bad_config_before_touching_device(bad):
     assert not h.value
 
 
-def test_create_moe_lora_reports_unsupported():
+@pytest.mark.parametrize("bad", [dict(n_experts=4, top_k=5, expert_ffn=16, ffn=0),      # top_k > experts
+                                 dict(n_experts=600, top_k=2, expert_ffn=16, ffn=0),    # too many experts
+                                 dict(n_experts=40, top_k=17, expert_ffn=16, ffn=0),    # top_k above 16
+                                 dict(n_experts=4, top_k=0, expert_ffn=16, ffn=0),
+                                 dict(n_experts=4, top_k=2, expert_ffn=0, ffn=0),
+                                 dict(n_experts=4, top_k=2, expert_ffn=20, ffn=0, compute_dtype=hol.BF16,
+                                      vocab=0),
+                                 dict(lora_rank=65), dict(lora_rank=-1)])
+def test_create_rejects_bad_moe_lora_config(bad):
     h = C.c_void_p()
-    cfg = _tiny_cfg(n_experts=4, top_k=2, expert_ffn=16, ffn=0)
-    assert hol.lib.hol_create(C.byref(cfg), C.byref(h)) == hol.HOL_EUNSUPPORTED
+    cfg = _tiny_cfg(**bad)
+    assert hol.lib.hol_create(C.byref(cfg), C.byref(h)) == hol.HOL_EINVAL, hol.lib.hol_last_error()
+    assert not h.value
 
 
 def test_null_arguments_are_einval():
