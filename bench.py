@@ -60,12 +60,16 @@ def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int
     s = w.shape
     H, d, nq, nkv, F, V = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads, s.ffn, s.vocab
     T, S, M = w.tokens, w.seq, w.batch
-    p_layer = H * (nq * d) * 2 + H * (nkv * d) * 2 + 3 * H * F
+    p_attn = H * (nq * d) * 2 + H * (nkv * d) * 2
+    # parameters a token passes through: dense MLP, or the router plus its top_k experts
+    p_mlp = s.n_experts * H + s.top_k * 3 * H * s.expert_ffn if s.n_experts else 3 * H * F
+    p_layer = p_attn + p_mlp
     attn_fwd = 2.0 * d * nq * S * (S + 1) * M
     L, K = s.n_layers, w.ckpt_every_k
     n_recomp = L - (L - ((L + K - 1) // K - 1) * K)          # every block but the last is recomputed
     f_fwd = 2.0 * p_layer * T + attn_fwd
-    f_bwd = 2 * (2.0 * p_layer * T) + 2.5 * attn_fwd          # dX and dW; attention backward
+    # backward: dX, plus dW unless the base is frozen (LoRA adapters are negligible); attention 2.5x
+    f_bwd = (1 if s.lora_rank else 2) * (2.0 * p_layer * T) + 2.5 * attn_fwd
     f_layers = L * (f_fwd + f_bwd) + n_recomp * f_fwd
     f_head = 3 * 2.0 * H * V * T
     return dict(p_layer=p_layer, f_layer=f_layers / L, f_head=f_head, n_recomp=n_recomp,
@@ -94,12 +98,16 @@ def cpu_baseline(w: W.Workload):
     from oracle import adam as OA
     from oracle import decoder as D
     s = D.Shape.of(w.shape)
-    one = w.with_shape(n_layers=1).with_(batch=1)
+    # one sequence of at most 4096 tokens (2048 with experts); the layer time is scaled by tokens
+    S = min(w.seq, 2048 if s.n_experts else 4096)
+    one = w.with_shape(n_layers=1).with_(batch=1, seq=S, n_micro=1)
     P = W.make_params(one)
-    tok = W.make_tokens(one)
-    S = w.seq
     cos, sin = D.rope_tables(S, s.head_dim, s.rope_base, np.float32)
-    h = P["embed"][tok.reshape(-1)]
+    if s.vocab:
+        tok = W.make_tokens(one)
+        h = P["embed"][tok.reshape(-1)]
+    else:
+        h = W.make_hidden(one).reshape(S, -1)
     G = D.zero_grads(P, s)
     t0 = time.perf_counter()
     out, _ = D.layer_forward(P, 0, h, s, 1, cos, sin)
@@ -107,27 +115,29 @@ def cpu_baseline(w: W.Workload):
     D.layer_backward(P, 0, c, np.ones_like(out) * 1e-3, s, 1, cos, sin, G)
     t_layer = time.perf_counter() - t0
     del c
-    n_head = 512
-    z = h[:n_head]
-    t0 = time.perf_counter()
-    zz, rz = D.rmsnorm(z, P["final_norm"], s.rms_eps)
-    logits = zz @ P["lm_head"].T
-    lab = tok.reshape(-1)[1:n_head + 1]
-    _, dl = D.cross_entropy(logits, lab)
-    dz = dl @ P["lm_head"]
-    G["lm_head"] += dl.T @ zz
-    D.rmsnorm_bwd(dz, z, P["final_norm"], rz)
-    t_head = time.perf_counter() - t0
+    n_head, t_head = min(512, S - 1), 0.0
+    if s.vocab:
+        z = h[:n_head]
+        t0 = time.perf_counter()
+        zz, rz = D.rmsnorm(z, P["final_norm"], s.rms_eps)
+        logits = zz @ P["lm_head"].T
+        lab = tok.reshape(-1)[1:n_head + 1]
+        _, dl = D.cross_entropy(logits, lab)
+        dz = dl @ P["lm_head"]
+        if "lm_head" in G:
+            G["lm_head"] += dl.T @ zz
+        D.rmsnorm_bwd(dz, z, P["final_norm"], rz)
+        t_head = time.perf_counter() - t0
     n_adam = 1 << 24
-    th = P["lm_head"].reshape(-1)[:n_adam].copy()
-    g = G["lm_head"].reshape(-1)[:n_adam].copy()
+    th = np.random.default_rng(0).standard_normal(n_adam, dtype=np.float32)
+    g = th * 1e-3
     mm = np.zeros_like(th)
     vv = np.zeros_like(th)
     t0 = time.perf_counter()
     OA.adam_update(th, g, mm, vv, 1)
     t_adam = time.perf_counter() - t0
-    total_params = W.n_params(w.shape)
-    t_step = (w.batch * s.n_layers * t_layer + w.tokens / n_head * t_head
+    total_params = sum(int(np.prod(p.shape)) for p in W.param_specs(w.shape) if p.trainable)
+    t_step = (w.tokens / S * s.n_layers * t_layer + (w.tokens / n_head * t_head if s.vocab else 0.0)
               + total_params / n_adam * t_adam)
     try:
         import threadpoolctl
@@ -136,9 +146,10 @@ def cpu_baseline(w: W.Workload):
         cores = os.cpu_count()
     return {"value": w.tokens / t_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"NumPy fp32 oracle: 1 layer fwd+recompute+bwd on 1x{S} tokens ({t_layer:.2f} s), "
-                       f"loss anchor on {n_head} tokens ({t_head:.2f} s), Adam on 2^24 params "
-                       f"({t_adam:.2f} s); scaled to {w.batch}x{s.n_layers} layer passes, "
-                       f"{w.tokens} head tokens, {total_params} params: {t_step:.1f} s/step")}
+                       + (f"loss anchor on {n_head} tokens ({t_head:.2f} s), " if s.vocab else "")
+                       + f"Adam on 2^24 params ({t_adam:.2f} s); scaled linearly to {w.tokens} tokens x "
+                       f"{s.n_layers} layers" + (f", {w.tokens} head tokens" if s.vocab else "")
+                       + f", {total_params} trainable params: {t_step:.1f} s/step")}
 
 
 def main():
@@ -146,7 +157,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "qwen3_1p7b", "llama8b_16k", "tiny"])
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["llama8b", "qwen3_1p7b", "llama8b_16k", "qwen3_235b_slice", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (the reference for scaling "
@@ -163,10 +175,12 @@ def main():
     log(f"[bench] workload {w.name}: L={s.n_layers} H={s.hidden} tokens={w.tokens} K={w.ckpt_every_k}")
     t0 = time.perf_counter()
     params = W.make_params(w)
-    tokens = W.make_tokens(w)
+    batch = W.make_batch(w)
     log(f"[bench] params generated in {time.perf_counter() - t0:.1f} s")
     cfg = hol.make_config(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab,
-                          ckpt_every_k=w.ckpt_every_k,
+                          n_experts=s.n_experts, top_k=s.top_k, expert_ffn=s.expert_ffn,
+                          lora_rank=s.lora_rank, lora_scale=s.lora_scale, rope_base=s.rope_base,
+                          rms_eps=s.rms_eps, ckpt_every_k=w.ckpt_every_k,
                           compute_dtype=hol.BF16 if w.compute == "bf16" else hol.F32,
                           max_tokens=w.tokens, max_seq=w.seq, lr=w.lr)
     t0 = time.perf_counter()
@@ -187,7 +201,10 @@ def main():
     def one_step():
         # forward_backward + step, with each layer's host Adam overlapped with the rest of the
         # backward (bitwise the same as the two calls)
-        loss = m.forward_backward(w.n_micro, tokens=tokens, and_step=True)
+        if s.vocab:
+            loss = m.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        else:
+            loss = m.forward_backward(w.n_micro, hidden=batch["hidden"], loss=hol.LOSS_SUMSQ, and_step=True)
         st = m.stats()
         return loss, st, st["step_ms"]
 
@@ -242,7 +259,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.compute == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x {s.head_dim}, "
-                               f"ffn {s.ffn}, vocab {s.vocab}; {w.n_micro} micro-batches x {w.batch // w.n_micro} x {w.seq} tokens; K={w.ckpt_every_k}",
+                               + (f"{s.n_experts} experts x {s.expert_ffn} top-{s.top_k}" if s.n_experts else f"ffn {s.ffn}")
+                               + (f", LoRA r={s.lora_rank} on a frozen base" if s.lora_rank else "")
+                               + f", vocab {s.vocab}; {w.n_micro} micro-batches x {w.batch // w.n_micro} x {w.seq} tokens; K={w.ckpt_every_k}",
                    "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU, layer streaming)"},
         "roofline": {"bound": "mfma", "kernel": "gemm_mfma (all decoder and head GEMMs)",
                      "achieved": round(g["tflops"], 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
