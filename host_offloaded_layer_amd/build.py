@@ -23,6 +23,10 @@ CPP_SRCS = ["host_math.cpp", "engine.cpp", "api.cpp"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-result"]
+# Attention keeps its score and gradient accumulators in architectural VGPRs, where the softmax
+# arithmetic reads them; left to itself the compiler parks them in AGPRs and copies them back and
+# forth on every tile. (The GEMM's 256 accumulators per lane need the AGPRs.)
+PER_FILE_FLAGS = {"k_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-ffp-contract=off", "-fno-fast-math", "-fno-math-errno",
              "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-Wall", "-Wno-unused-variable",
              "-Wno-unused-but-set-variable", "-Wno-unused-result", "-pthread"]
@@ -42,7 +46,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for s in HIP_SRCS:
         o = os.path.join(OBJ, s + ".o")
-        jobs.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        jobs.append([hipcc, *HIPCC_FLAGS, *PER_FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o])
     for s in CPP_SRCS:
         o = os.path.join(OBJ, s + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])

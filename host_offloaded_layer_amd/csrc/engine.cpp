@@ -411,7 +411,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     m->mlogits = (float*)D(T * NE * 4);
     m->mcounts = (int32_t*)D((NE + 1) * 4);
     m->moffsets = (int32_t*)D((NE + 1) * 4);
-    m->mcursor = (int32_t*)D((NE + 1) * 4);
+    m->mperm = (int32_t*)D(moe_permute_scratch((int)T, (int)NE, m->topk) * 4);  // permutation scratch
     m->xp = D(Tk * H * E);
     m->ap = D(Tk * Fe * E);
     m->dyp = D(Tk * H * E);
@@ -684,7 +684,7 @@ static hol_status moe_forward(hol_model* m, const W& w, const Act& A, int T, flo
   hipStream_t s = m->sc;
   KCHECK(run_gemm(m, gemm(T, NE, H, A.n2, H, false, w.router, H, false, m->mlogits, NE, dt, DT_F32, EPI_STORE)));
   KT(KC_OTHER, 0, (double)T * NE * 8, launch_moe_route(m->mlogits, T, NE, k, A.probs, A.ids, A.w, m->mcounts, s));
-  KT(KC_OTHER, 0, (double)Tk * 16, launch_moe_permute(A.ids, T, NE, k, m->mcounts, m->moffsets, m->mcursor,
+  KT(KC_OTHER, 0, (double)Tk * 16, launch_moe_permute(A.ids, T, NE, k, m->mcounts, m->moffsets, m->mperm,
                                                       A.perm_slot, A.slot_pos, s));
   HCHECK(hipMemcpyAsync(m->counts_stage, m->mcounts, (size_t)NE * 4, hipMemcpyDeviceToHost, s));
   HCHECK(hipStreamSynchronize(s));

@@ -135,7 +135,7 @@ struct hol_model {
   // mixture of experts: per activation-store position, the host copy of the expert row counts
   std::vector<std::vector<int32_t>> act_counts;
   float* mlogits = nullptr;                       // router logits fp32 [T, E]
-  int32_t *mcounts = nullptr, *moffsets = nullptr, *mcursor = nullptr;
+  int32_t *mcounts = nullptr, *moffsets = nullptr, *mperm = nullptr;
   int32_t* counts_stage = nullptr;                // pinned [E]
   void *xp = nullptr, *ap = nullptr, *dyp = nullptr, *dap = nullptr, *dgup = nullptr, *dlogr = nullptr;
   float *dxp = nullptr, *dwr = nullptr;

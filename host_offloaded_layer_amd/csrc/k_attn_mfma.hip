@@ -105,6 +105,93 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   *(bf16x4*)p = v;
 }
 
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; ex2(-inf) = 0
+
+// Register-staged tiles: a thread's share of the next tile is fetched into registers while the
+// current tile is computed on, then written to LDS after the next barrier.
+// Natural layout, 16-byte chunks: chunk c = tid + 256 i is row c / (D/8), columns (c % (D/8)) * 8.
+template <int R, int D>
+struct NatTile {
+  static constexpr int N = R * D / 8 / 256;
+  static_assert(R * D / 8 % 256 == 0, "tile must split into whole chunks per thread");
+  u32x4 v[N];
+  __device__ __forceinline__ void load(const bf16* src, int64_t ld, int64_t row0, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c / (D / 8), k = (c % (D / 8)) * 8;
+      const int rr = r < nvalid ? r : nvalid - 1;
+      v[i] = *(const u32x4*)(src + (row0 + rr) * ld + k);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* dst, int P) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      *(u32x4*)(dst + (c / (D / 8)) * P + (c % (D / 8)) * 8) = v[i];
+    }
+  }
+};
+
+// Transposed layout dst[d][r]: 8 x 8 blocks b = t + NT j (t in [0, NT)), rows 8 (b % (R/8)) + 0..7,
+// columns 8 (b / (R/8)) + 0..7; a thread with t outside [0, NT) holds nothing.
+template <int R, int D, int NT>
+struct TrTile {
+  static constexpr int NB = (R / 8) * (D / 8);
+  static constexpr int N = (NB + NT - 1) / NT;
+  u32x4 v[N][8];
+  __device__ __forceinline__ void load(int t, const bf16* src, int64_t ld, int64_t row0, int nvalid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int b = t + NT * j;
+      if (t < 0 || t >= NT || b >= NB) continue;
+      const int rb = b % (R / 8), db = b / (R / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = rb * 8 + i;
+        const int rr = r < nvalid ? r : nvalid - 1;
+        v[j][i] = *(const u32x4*)(src + (row0 + rr) * ld + db * 8);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(int t, bf16* dst, int P) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int b = t + NT * j;
+      if (t < 0 || t >= NT || b >= NB) continue;
+      const int rb = b % (R / 8), db = b / (R / 8);
+      u32x4 out[8];
+      transpose8x8(v[j], out);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        bf16* q = dst + (db * 8 + c) * P + rb * 8;
+        *(u32x2*)q = u32x2{out[c][0], out[c][1]};
+        *(u32x2*)(q + 4) = u32x2{out[c][2], out[c][3]};
+      }
+    }
+  }
+};
+
+// dst[d][r] (pitch TP) = src[r][d] (pitch SP) for an R x D tile already in LDS; 8 x 8 blocks with
+// the column block varying fastest across lanes (conflict-free 16-byte reads of source rows).
+template <int R, int D>
+__device__ __forceinline__ void lds_transpose(const bf16* src, int SP, bf16* dst, int TP) {
+  constexpr int NB = (R / 8) * (D / 8);
+  for (int b = threadIdx.x; b < NB; b += 256) {
+    const int db = b % (D / 8), rb = b / (D / 8);
+    u32x4 in[8], out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) in[i] = *(const u32x4*)(src + (rb * 8 + i) * SP + db * 8);
+    transpose8x8(in, out);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      bf16* q = dst + (db * 8 + c) * TP + rb * 8;
+      *(u32x2*)q = u32x2{out[c][0], out[c][1]};
+      *(u32x2*)(q + 4) = u32x2{out[c][2], out[c][3]};
+    }
+  }
+}
+
 }  // namespace fa
 
 using namespace fa;
@@ -145,13 +232,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(Attn a) {
   const int nkt = qmax / BK + 1;
   const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
 
+  NatTile<BK, D> kreg;
+  TrTile<BK, D, 256> vreg;
+  kreg.load(K, a.ldk, base, min(BK, S));
+  vreg.load(threadIdx.x, V, a.ldv, base, min(BK, S));
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BK;
-    const int nk = min(BK, S - k0);
     __syncthreads();
-    load_rows<BK, D>(Ks, KP, K, a.ldk, base + k0, nk);
-    load_rows_t<BK, D>(Vt, VP, V, a.ldv, base + k0, nk);
+    kreg.store(Ks, KP);
+    vreg.store(threadIdx.x, Vt, VP);
     __syncthreads();
+    if (kt + 1 < nkt) {  // next tile in flight while this one is computed on
+      kreg.load(K, a.ldk, base + k0 + BK, min(BK, S - k0 - BK));
+      vreg.load(threadIdx.x, V, a.ldv, base + k0 + BK, min(BK, S - k0 - BK));
+    }
     if (k0 > wave_qmax) continue;  // every key of this tile is in this wave's future
     f32x16 s[2];
     zero(s[0]);
@@ -181,23 +275,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(Attn a) {
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mn = fmaxf(m, mx);
-    const float corr = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+    if (mn > m) {  // the running max moved: rescale (the whole wave skips this once maxima settle)
+      const float corr = ex2(m - mn);
+      l *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= corr;
+      m = mn;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = (s[kb][r] == -INFINITY) ? 0.f : exp2f(s[kb][r] - mn);
+        const float p = ex2(s[kb][r] - m);
         s[kb][r] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l = l * corr + ls;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= corr;
+    l += ls;
     // O^T[d][q] += V^T[d][key] P^T[key][q]
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -231,6 +328,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   __shared__ bf16 Qt[D * TP];
   __shared__ bf16 Gt[D * TP];
   __shared__ float lse2[BQ], dlt[BQ];
+  __shared__ bf16 Kb[BKV * KP];  // the block's keys and values (fragments read per use, which
+  __shared__ bf16 Vb[BKV * KP];  // leaves the registers to the accumulators and the prefetch)
   const int S = a.S;
   const int nkt = (S + BKV - 1) / BKV;
   const int kt = nkt - 1 - (int)blockIdx.x;  // early keys see the most queries: schedule them first
@@ -243,17 +342,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   const float sl2 = LOG2E / sqrtf((float)D);
   const float scale = 1.f / sqrtf((float)D);
 
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const int64_t row = base + min(kj, S - 1);
-    const bf16* kp = (const bf16*)a.k + row * a.ldk + (int64_t)kvh * D;
-    const bf16* vp = (const bf16*)a.v + row * a.ldv + (int64_t)kvh * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = *(const bf16x8*)(kp + 16 * kk + 8 * hh);
-      vf[kk] = *(const bf16x8*)(vp + 16 * kk + 8 * hh);
-    }
-  }
+  // (visible to every wave after the first iteration's barrier)
+  load_rows<BKV, D>(Kb, KP, (const bf16*)a.k + (int64_t)kvh * D, a.ldk, base + k0, min(BKV, S - k0));
+  load_rows<BKV, D>(Vb, KP, (const bf16*)a.v + (int64_t)kvh * D, a.ldv, base + k0, min(BKV, S - k0));
+  const bf16* kfp = Kb + (32 * w + lq) * KP + 8 * hh;
+  const bf16* vfp = Vb + (32 * w + lq) * KP + 8 * hh;
   f32x16 dv[D / 32], dk[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -262,58 +355,83 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   }
   const int wave_kmin = k0 + 32 * w;
   const int nqt = (S + BQ - 1) / BQ;
-  for (int hq = 0; hq < group; ++hq) {
-    const int h = kvh * group + hq;
+  const int qt0 = k0 / BQ, nper = nqt - qt0, nit = group * nper;
+  // iteration it: q head kvh * group + it / nper, query tile qt0 + it % nper
+  NatTile<BQ, D> qreg, greg;
+  float lse_r = 0.f, dl_r = 0.f;
+  auto fetch = [&](int it) {
+    const int h = kvh * group + it / nper, q0 = (qt0 + it % nper) * BQ, nq = min(BQ, S - q0);
     const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
     const bf16* G = (const bf16*)a.dO + (int64_t)h * D;
-    const float* L = a.lse + ((int64_t)seq * a.nq + h) * S;
-    const float* Dl = a.delta + ((int64_t)seq * a.nq + h) * S;
-    for (int qt = k0 / BQ; qt < nqt; ++qt) {
-      const int q0 = qt * BQ;
-      const int nq = min(BQ, S - q0);
+    qreg.load(Q, a.ldq, base + q0, nq);
+    greg.load(G, a.lddo, base + q0, nq);
+    if (threadIdx.x < BQ) {
+      const int qq = q0 + threadIdx.x;
+      const int64_t hrow = ((int64_t)seq * a.nq + h) * S;
+      lse_r = qq < S ? a.lse[hrow + qq] * LOG2E : 0.f;
+      dl_r = qq < S ? a.delta[hrow + qq] : 0.f;
+    }
+  };
+  fetch(0);
+  for (int it = 0; it < nit; ++it) {
+    const int q0 = (qt0 + it % nper) * BQ;
+    {
       __syncthreads();
-      load_rows<BQ, D>(Qs, KP, Q, a.ldq, base + q0, nq);
-      load_rows<BQ, D>(Gs, KP, G, a.lddo, base + q0, nq);
-      load_rows_t<BQ, D>(Qt, TP, Q, a.ldq, base + q0, nq);
-      load_rows_t<BQ, D>(Gt, TP, G, a.lddo, base + q0, nq);
+      qreg.store(Qs, KP);
+      greg.store(Gs, KP);
       if (threadIdx.x < BQ) {
-        const int qq = q0 + threadIdx.x;
-        lse2[threadIdx.x] = qq < S ? L[qq] * LOG2E : 0.f;
-        dlt[threadIdx.x] = qq < S ? Dl[qq] : 0.f;
+        lse2[threadIdx.x] = lse_r;
+        dlt[threadIdx.x] = dl_r;
       }
       __syncthreads();
+      lds_transpose<BQ, D>(Qs, KP, Qt, TP);
+      lds_transpose<BQ, D>(Gs, KP, Gt, TP);
+      if (it + 1 < nit) fetch(it + 1);  // next tile in flight while this one is computed on
+      __syncthreads();
       if (q0 + BQ - 1 < wave_kmin) continue;  // all queries before this wave's keys
-      // S[q][key], dP[q][key] for 2 blocks of 32 queries
-      f32x16 s[2], dp[2];
-      zero(s[0]); zero(s[1]); zero(dp[0]); zero(dp[1]);
+      // two 32-query halves in turn: S[q][key] and dP[q][key], then their dV / dK products
+      // (element r of a half qb: query q0 + 32 qb + 8 (r/4) + 4 hh + r%4, key kj)
+      const bool full = q0 >= wave_kmin + 31 && q0 + BQ <= S && kj < S;  // no masking in this tile
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = mfma(*(const bf16x8*)(Qs + (qb * 32 + lq) * KP + 16 * kk + 8 * hh), kf[kk], s[qb]);
-          dp[qb] = mfma(*(const bf16x8*)(Gs + (qb * 32 + lq) * KP + 16 * kk + 8 * hh), vf[kk], dp[qb]);
+        for (int kk = 0; kk < D / 16; ++kk) {
+          s = mfma(*(const bf16x8*)(Qs + (qb * 32 + lq) * KP + 16 * kk + 8 * hh), *(const bf16x8*)(kfp + 16 * kk), s);
+          dp = mfma(*(const bf16x8*)(Gs + (qb * 32 + lq) * KP + 16 * kk + 8 * hh), *(const bf16x8*)(vfp + 16 * kk), dp);
         }
-      // element r of block qb: query q0 + 32 qb + 8 (r/4) + 4 hh + r%4, key kj
+        if (full) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+          for (int r = 0; r < 16; ++r) {
+            const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const float p = ex2(fmaf(s[r], sl2, -lse2[qloc]));
+            s[r] = p;
+            dp[r] = p * (dp[r] - dlt[qloc]);
+          }
+        } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int qq = q0 + qloc;
-          const bool ok = qq < S && kj <= qq && kj < S;
-          const float p = ok ? exp2f(s[qb][r] * sl2 - lse2[qloc]) : 0.f;
-          s[qb][r] = p;
-          dp[qb][r] = p * (dp[qb][r] - dlt[qloc]);
+          for (int r = 0; r < 16; ++r) {
+            const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int qq = q0 + qloc;
+            const bool ok = qq < S && kj <= qq && kj < S;
+            const float p = ok ? ex2(fmaf(s[r], sl2, -lse2[qloc])) : 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - dlt[qloc]);
+          }
         }
-      // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
 #pragma unroll
-      for (int ks = 0; ks < BQ / 16; ++ks) {
-        const bf16x8 pb = acc_frag(s[ks >> 1], ks & 1);
-        const bf16x8 sb = acc_frag(dp[ks >> 1], ks & 1);
+        for (int ksp = 0; ksp < 2; ++ksp) {
+          const int ks = 2 * qb + ksp;
+          const bf16x8 pb = acc_frag(s, ksp);
+          const bf16x8 sb = acc_frag(dp, ksp);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = mfma(tfrag(Gt, TP, db * 32 + lq, ks, hh), pb, dv[db]);
-          dk[db] = mfma(tfrag(Qt, TP, db * 32 + lq, ks, hh), sb, dk[db]);
+          for (int db = 0; db < D / 32; ++db) {
+            dv[db] = mfma(tfrag(Gt, TP, db * 32 + lq, ks, hh), pb, dv[db]);
+            dk[db] = mfma(tfrag(Qt, TP, db * 32 + lq, ks, hh), sb, dk[db]);
+          }
         }
       }
     }
@@ -337,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
 // backward, dQ: block = 4 waves x 32 queries of one q head; key tiles of 64 up to the diagonal
 // ------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_dq_mfma(Attn a) {
+__global__ __launch_bounds__(256, 1) void attn_dq_mfma(Attn a) {
   constexpr int BQ = 128, BK = 64, KP = D + 8, TP = BK + 12;
   __shared__ bf16 Ks[BK * KP];
   __shared__ bf16 Vs[BK * KP];
@@ -376,13 +494,21 @@ __global__ __launch_bounds__(256, 2) void attn_dq_mfma(Attn a) {
   const int qmax = min(q0 + BQ, S) - 1;
   const int nkt = qmax / BK + 1;
   const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
+  NatTile<BK, D> kreg, vreg;
+  kreg.load(K, a.ldk, base, min(BK, S));
+  vreg.load(V, a.ldv, base, min(BK, S));
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BK;
-    const int nk = min(BK, S - k0);
     __syncthreads();
-    load_rows<BK, D>(Ks, KP, K, a.ldk, base + k0, nk);
-    load_rows<BK, D>(Vs, KP, V, a.ldv, base + k0, nk);
-    load_rows_t<BK, D>(Kt, TP, K, a.ldk, base + k0, nk);
+    kreg.store(Ks, KP);
+    vreg.store(Vs, KP);
+    __syncthreads();
+    lds_transpose<BK, D>(Ks, KP, Kt, TP);
+    if (kt + 1 < nkt) {  // next tile in flight while this one is computed on
+      const int n1 = min(BK, S - k0 - BK);
+      kreg.load(K, a.ldk, base + k0 + BK, n1);
+      vreg.load(V, a.ldv, base + k0 + BK, n1);
+    }
     __syncthreads();
     if (k0 > wave_qmax) continue;
     f32x16 s[2], dp[2];
@@ -401,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_mfma(Attn a) {
       for (int r = 0; r < 16; ++r) {
         const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
         const bool ok = qv && kk <= qi && kk < S;
-        const float p = ok ? exp2f(s[kb][r] * sl2 - lse_q) : 0.f;
+        const float p = ok ? ex2(s[kb][r] * sl2 - lse_q) : 0.f;
         dp[kb][r] = p * (dp[kb][r] - dl_q);
       }
     // dQ^T[d][q] += K^T[d][key] dS^T[key][q]

@@ -9,9 +9,8 @@
 // Layout: logits / probs fp32 [T, E]; ids int32 and w fp32 [T, k] (slot i of token t at t*k+i).
 // A routed row p in [0, T*k) belongs to expert e when offsets[e] <= p < offsets[e+1];
 // perm_slot[p] = t*k+i names the slot it came from and slot_pos[t*k+i] = p is the inverse. The
-// row order inside an expert comes from atomics and varies from call to call; every result is
-// independent of it (each row of an expert GEMM is computed on its own and every per-token sum
-// runs over the slots in order i = 0..k-1).
+// rows of an expert keep the order of their slots, so the permutation (and every sum over an
+// expert's rows) is the same on every call and in the recompute.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -93,28 +92,56 @@ __global__ __launch_bounds__(256) void moe_route_k(const float* __restrict__ log
   }
 }
 
-// offsets[e] = sum_{e' < e} counts[e'], offsets[E] = total; cursor[e] = 0. One thread.
-__global__ void moe_offsets_k(const int32_t* __restrict__ counts, int E, int32_t* __restrict__ offsets,
-                              int32_t* __restrict__ cursor) {
+// offsets[e] = sum_{e' < e} counts[e'], offsets[E] = total. One thread.
+__global__ void moe_offsets_k(const int32_t* __restrict__ counts, int E, int32_t* __restrict__ offsets) {
   if (blockIdx.x != 0 || threadIdx.x != 0) return;
   int32_t acc = 0;
   for (int e = 0; e < E; ++e) {
     offsets[e] = acc;
     acc += counts[e];
-    cursor[e] = 0;
   }
   offsets[E] = acc;
 }
 
-__global__ void moe_scatter_k(const int32_t* __restrict__ ids, int64_t n, const int32_t* __restrict__ offsets,
-                              int32_t* __restrict__ cursor, int32_t* __restrict__ perm_slot,
-                              int32_t* __restrict__ slot_pos) {
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= n) return;
-  const int e = ids[q];
-  const int p = offsets[e] + atomicAdd(&cursor[e], 1);
-  perm_slot[p] = (int32_t)q;
-  slot_pos[q] = p;
+// Stable permutation: inside an expert, routed rows keep the order of their slots (t k + i), so
+// every sum over an expert's rows (its weight gradients) is taken in one fixed order.
+// Pass 1: per chunk of MOE_CH slots, how many go to each expert (cc [n_chunks, E]).
+constexpr int MOE_CH = 256;
+__global__ __launch_bounds__(256) void moe_chunk_count_k(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                         int32_t* __restrict__ cc) {
+  __shared__ int32_t hist[MOE_MAX_E];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t q = (int64_t)blockIdx.x * MOE_CH + threadIdx.x;
+  if (threadIdx.x < MOE_CH && q < n) atomicAdd(&hist[ids[q]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cc[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+// Pass 2: first position of each (chunk, expert): co[c][e] = offsets[e] + sum_{c' < c} cc[c'][e].
+__global__ void moe_chunk_offsets_k(const int32_t* __restrict__ cc, int nch, int E, const int32_t* __restrict__ offsets,
+                                    int32_t* __restrict__ co) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  int32_t acc = offsets[e];
+  for (int c = 0; c < nch; ++c) {
+    co[(int64_t)c * E + e] = acc;
+    acc += cc[(int64_t)c * E + e];
+  }
+}
+// Pass 3: one thread per chunk walks its slots in order.
+__global__ __launch_bounds__(64) void moe_chunk_scatter_k(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                          const int32_t* __restrict__ co, int32_t* __restrict__ perm_slot,
+                                                          int32_t* __restrict__ slot_pos) {
+  __shared__ int32_t cur[MOE_MAX_E];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cur[e] = co[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const int64_t q0 = (int64_t)blockIdx.x * MOE_CH, q1 = q0 + MOE_CH < n ? q0 + MOE_CH : n;
+  for (int64_t q = q0; q < q1; ++q) {
+    const int p = cur[ids[q]]++;
+    perm_slot[p] = (int32_t)q;
+    slot_pos[q] = p;
+  }
 }
 
 // Xp[p, :] = X[perm_slot[p] / k, :]; rows of H elements (H * sizeof(T) a multiple of 16 bytes).
@@ -236,13 +263,23 @@ int launch_moe_route(const float* logits, int T, int E, int k, float* probs, int
   return (int)hipGetLastError();
 }
 
-int launch_moe_permute(const int32_t* ids, int T, int E, int k, const int32_t* counts, int32_t* offsets,
-                       int32_t* cursor, int32_t* perm_slot, int32_t* slot_pos, hipStream_t s) {
-  if (T <= 0) return 0;
-  hipLaunchKernelGGL(moe_offsets_k, dim3(1), dim3(64), 0, s, counts, E, offsets, cursor);
+int64_t moe_permute_scratch(int T, int E, int k) {
   const int64_t n = (int64_t)T * k;
-  hipLaunchKernelGGL(moe_scatter_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids, n, offsets, cursor,
-                     perm_slot, slot_pos);
+  return 2 * ((n + MOE_CH - 1) / MOE_CH) * E;
+}
+
+int launch_moe_permute(const int32_t* ids, int T, int E, int k, const int32_t* counts, int32_t* offsets,
+                       int32_t* scratch, int32_t* perm_slot, int32_t* slot_pos, hipStream_t s) {
+  if (T <= 0) return 0;
+  if (E < 1 || E > MOE_MAX_E) return (int)hipErrorInvalidValue;
+  const int64_t n = (int64_t)T * k;
+  const int nch = (int)((n + MOE_CH - 1) / MOE_CH);
+  int32_t* cc = scratch;
+  int32_t* co = scratch + (int64_t)nch * E;
+  hipLaunchKernelGGL(moe_offsets_k, dim3(1), dim3(64), 0, s, counts, E, offsets);
+  hipLaunchKernelGGL(moe_chunk_count_k, dim3(nch), dim3(256), 0, s, ids, n, E, cc);
+  hipLaunchKernelGGL(moe_chunk_offsets_k, dim3((E + 255) / 256), dim3(256), 0, s, cc, nch, E, offsets, co);
+  hipLaunchKernelGGL(moe_chunk_scatter_k, dim3(nch), dim3(64), 0, s, ids, n, E, co, perm_slot, slot_pos);
   return (int)hipGetLastError();
 }
 

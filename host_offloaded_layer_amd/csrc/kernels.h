@@ -96,13 +96,16 @@ int launch_ce_fwd_bwd(const float* logits, int64_t ld, const int32_t* labels, co
                       float* row_loss, void* dlogits, DType dt, int64_t ldd, int Tc, int V,
                       hipStream_t s);
 // Mixture-of-experts routing and permutation (k_moe.hip). logits / probs fp32 [T, E]; ids int32
-// and w fp32 [T, k]; counts / cursor int32 [E]; offsets int32 [E + 1]; perm_slot and slot_pos
+// and w fp32 [T, k]; counts int32 [E]; offsets int32 [E + 1]; perm_slot and slot_pos
 // int32 [T k]. E <= 512, k <= 16.
 int launch_fill_i32(int32_t* x, int32_t v, int64_t n, hipStream_t s);
 int launch_moe_route(const float* logits, int T, int E, int k, float* probs, int32_t* ids, float* w,
                      int32_t* counts, hipStream_t s);
+// Stable permutation (rows of an expert in slot order); scratch holds moe_permute_scratch(T, E, k)
+// int32.
+int64_t moe_permute_scratch(int T, int E, int k);
 int launch_moe_permute(const int32_t* ids, int T, int E, int k, const int32_t* counts, int32_t* offsets,
-                       int32_t* cursor, int32_t* perm_slot, int32_t* slot_pos, hipStream_t s);
+                       int32_t* scratch, int32_t* perm_slot, int32_t* slot_pos, hipStream_t s);
 // Xp[p] = X[perm_slot[p] / k] for rows of H elements of type t
 int launch_moe_gather(const void* X, DType t, const int32_t* perm_slot, int k, int64_t n_rows, int H, void* Xp,
                       hipStream_t s);
