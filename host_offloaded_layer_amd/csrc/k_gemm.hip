@@ -296,39 +296,45 @@ __device__ __forceinline__ int n2_off(int r, int c) { return (r >> 1) * 64 + (((
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
 
-// Issue this wave's share of one stage: LDS rows [8 q, 8 q + 8) (tile rows [16 q, 16 q + 16)) of
-// the A tile, q = wave, wave+4, wave+8, wave+12, and the same of the B tile. Lane i fills LDS row
-// 8 q + i / 8 at physical chunk i % 8, so it fetches the logical (row, chunk) stored there.
+// Issue this wave's share of one stage (NW waves): LDS rows [8 q, 8 q + 8) (tile rows
+// [16 q, 16 q + 16)) of the A tile for q = wave + NW i, and the same of the B tile. Lane i fills
+// LDS row 8 q + i / 8 at physical chunk i % 8, so it fetches the logical (row, chunk) stored there.
+template <int NW>
 __device__ __forceinline__ void n2_issue(bf16* stage, const bf16* __restrict__ A, int64_t lda, int m0, int M,
                                          const bf16* __restrict__ B, int64_t ldb, int n0, int N, int k0) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = (w + 4 * i) * 8 + (lane >> 3);  // LDS row
-    const int lc = (lane & 7) ^ n2_sw(R);         // logical 8-chunk index: (odd row?) * 4 + chunk
-    const int r = 2 * R + (lc >> 2);              // tile row
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int R = (w + NW * i) * 8 + (lane >> 3);  // LDS row
+    const int lc = (lane & 7) ^ n2_sw(R);          // logical 8-chunk index: (odd row?) * 4 + chunk
+    const int r = 2 * R + (lc >> 2);               // tile row
     const int c = lc & 3;
     int gr = m0 + r;
     gr = gr < M ? gr : M - 1;
     const bf16* src = A + (int64_t)gr * lda + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + (w + 4 * i) * 16 * N2_BK), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + (w + NW * i) * 16 * N2_BK), 16, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = (w + 4 * i) * 8 + (lane >> 3);
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int R = (w + NW * i) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ n2_sw(R);
     const int r = 2 * R + (lc >> 2);
     const int c = lc & 3;
     int gr = n0 + r;
     gr = gr < N ? gr : N - 1;
     const bf16* src = B + (int64_t)gr * ldb + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + N2_BM * N2_BK + (w + 4 * i) * 16 * N2_BK),
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + N2_BM * N2_BK + (w + NW * i) * 16 * N2_BK),
                                      16, 0, 0);
   }
 }
 
-template <int EPI, typename TO>
-__global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
+// NW = 4: waves in a 2 x 2 grid, 128 x 128 each (one wave per SIMD, 256 accumulators a lane).
+// NW = 8: waves in a 2 x 4 grid, 128 x 64 each (two waves per SIMD, one's MFMAs cover the other's
+// waits).
+template <int EPI, typename TO, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_nt2(Gemm g) {
+  constexpr int WJ = NW == 4 ? 4 : 2;           // 32-column blocks per wave
+  constexpr int LOADS = 2 * 16 / NW;            // loads per wave per stage
   __shared__ __attribute__((aligned(1024))) bf16 lds[N2_ST * N2_TILE];
   const int M = g.M, N = g.N, K = g.K;
   const int z = blockIdx.y;
@@ -346,12 +352,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
   const int tn = (pid % group) / gsz;
   const int m0 = tm * N2_BM, n0 = tn * N2_BN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  f32x16 acc[4][4];
+  const int wm = w / (NW / 2), wn = w % (NW / 2);
+  f32x16 acc[4][WJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -360,11 +366,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
   // with stage kt + N2_ST once stage kt is in registers
 #pragma unroll
   for (int s = 0; s < N2_ST; ++s)
-    if (s < nk) n2_issue(lds + s * N2_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, s * N2_BK);
+    if (s < nk) n2_issue<NW>(lds + s * N2_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, s * N2_BK);
 
   // Fragments: F0 = k-step 0 of the current stage, F1 = k-step 1. Each k-step's 16 MFMAs run
   // while the next k-step's 8 fragments are being read from LDS.
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
   auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
     const bf16* As = st;
     const bf16* Bs = st + N2_BM * N2_BK;
@@ -372,13 +378,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(As + n2_off(wm * 128 + i * 32 + (lane & 31), c));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(Bs + n2_off(wn * 128 + j * 32 + (lane & 31), c));
+    for (int j = 0; j < WJ; ++j) b[j] = *(const bf16x8*)(Bs + n2_off(wn * 32 * WJ + j * 32 + (lane & 31), c));
   };
+  // C^T blocks (B fragment as the MFMA's A operand): a lane then holds one row of C and, per
+  // accumulator quad, 4 consecutive columns, so the epilogue moves 16-byte pieces
   auto mma = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < WJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
   // Stage t is ready for everyone once this wave's loads of it are done (at most `later` later
   // stages of 8 loads each may still be in flight) and every wave has passed the barrier; the
@@ -388,10 +396,18 @@ __global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
   // the prologue).
   auto stage_ready = [&](int t) {
     const int later = min(t == 0 ? N2_ST - 1 : N2_ST - 2, nk - 1 - t);
-    if (later >= 3) asm volatile("s_waitcnt vmcnt(24)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (later == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (LOADS == 8) {
+      if (later >= 3) asm volatile("s_waitcnt vmcnt(24)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (later == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      static_assert(LOADS == 4, "4 or 8 loads per wave per stage");
+      if (later >= 3) asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (later == 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   };
   stage_ready(0);
   frags(lds, 0, a0, b0);
@@ -402,37 +418,68 @@ __global__ __launch_bounds__(256, 1) void gemm_nt2(Gemm g) {
     if (kt + 1 < nk) {
       stage_ready(kt + 1);  // stage kt is fully in registers now: its slot can be refilled
       if (kt + N2_ST < nk)
-        n2_issue(lds + (kt % N2_ST) * N2_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, (kt + N2_ST) * N2_BK);
+        n2_issue<NW>(lds + (kt % N2_ST) * N2_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, (kt + N2_ST) * N2_BK);
       frags(lds + ((kt + 1) % N2_ST) * N2_TILE, 0, a0, b0);
     }
     mma(a1, b1);
   }
 
+  // epilogue: acc[i][j][4 q + e] is C[row][col + e], row = m0 + 128 wm + 32 i + lane % 32,
+  // col = n0 + 32 WJ wn + 32 j + 8 q + 4 (lane / 32)
   TO* C = (TO*)g.C + z * g.sC;
   const float* R = g.R ? g.R + z * g.sR : nullptr;
+  constexpr int VB = 4 * (int)sizeof(TO);  // bytes of 4 outputs
+  const bool vec = g.ldc % 4 == 0 && (uintptr_t)C % VB == 0 &&
+                   (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (row >= M) continue;
+    TO* crow = C + (int64_t)row * g.ldc;
+    const float* rrow = EPI == EPI_RESID ? R + (int64_t)row * g.ldr : nullptr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= N) continue;
+    for (int j = 0; j < WJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= M) continue;
-        float v = g.alpha * acc[i][j][r];
-        TO* c = C + (int64_t)row * g.ldc + col;
-        if constexpr (EPI == EPI_ACCUM) v += to_f(*c);
-        if constexpr (EPI == EPI_RESID) v += R[(int64_t)row * g.ldr + col];
-        *c = from_f<TO>(v);
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * 32 * WJ + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = g.alpha * acc[i][j][4 * q + e];
+        if (vec && col + 4 <= N) {
+          if constexpr (EPI == EPI_RESID) {
+            const float4 rv = *(const float4*)(rrow + col);
+            v[0] += rv.x; v[1] += rv.y; v[2] += rv.z; v[3] += rv.w;
+          }
+          if constexpr (sizeof(TO) == 4) {
+            if constexpr (EPI == EPI_ACCUM) {
+              const float4 cv = *(const float4*)(crow + col);
+              v[0] += cv.x; v[1] += cv.y; v[2] += cv.z; v[3] += cv.w;
+            }
+            *(float4*)(crow + col) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            *(bf16x4*)(crow + col) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= N) break;
+            float x = v[e];
+            if constexpr (EPI == EPI_ACCUM) x += to_f(crow[col + e]);
+            if constexpr (EPI == EPI_RESID) x += rrow[col + e];
+            crow[col + e] = from_f<TO>(x);
+          }
+        }
       }
-    }
+  }
 }
 
+constexpr int NT2_WAVES = 8;
 template <int EPI, typename TO>
 static int launch_nt2_t(const Gemm& g, hipStream_t s) {
   const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
-  hipLaunchKernelGGL((gemm_nt2<EPI, TO>), dim3(tiles, g.batch), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((gemm_nt2<EPI, TO, NT2_WAVES>), dim3(tiles, g.batch), dim3(64 * NT2_WAVES), 0, s, g);
   return (int)hipGetLastError();
 }
 
