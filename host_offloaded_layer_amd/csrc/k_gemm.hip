@@ -475,6 +475,182 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt2(Gemm g) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// NT3: the same 256 x 256 block and 8-wave grid with 64-deep stages in a 2-slot ring, so one block
+// barrier covers twice the MFMA work. A tile row (64 bf16) is one 128-byte LDS row; physical
+// 16-byte chunk = logical chunk ^ ((row / 2) % 8) (16 consecutive rows read conflict-free).
+// ------------------------------------------------------------------------------------------
+constexpr int N3_BK = 64;
+constexpr int N3_TILE = (N2_BM + N2_BN) * N3_BK;  // bf16 elements per stage
+
+__device__ __forceinline__ int n3_off(int r, int c) { return r * N3_BK + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// this wave's 64 / NW loads of one stage: LDS rows [8 q, 8 q + 8) for q = wave + NW i of A, then
+// of B
+template <int NW>
+__device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A, int64_t lda, int m0, int M,
+                                         const bf16* __restrict__ B, int64_t ldb, int n0, int N, int k0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int R = (w + NW * i) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ ((R >> 1) & 7);
+    int gr = m0 + R;
+    gr = gr < M ? gr : M - 1;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(A + (int64_t)gr * lda + k0 + lc * 8),
+                                     (lds_ptr_t)(stage + (w + NW * i) * 8 * N3_BK), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int R = (w + NW * i) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ ((R >> 1) & 7);
+    int gr = n0 + R;
+    gr = gr < N ? gr : N - 1;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(B + (int64_t)gr * ldb + k0 + lc * 8),
+                                     (lds_ptr_t)(stage + N2_BM * N3_BK + (w + NW * i) * 8 * N3_BK), 16, 0, 0);
+  }
+}
+
+// NW = 8: 2 x 4 waves of 128 x 64 (two per SIMD); NW = 4: 2 x 2 waves of 128 x 128 (one per SIMD,
+// a third fewer LDS fragment reads per MFMA).
+template <int EPI, typename TO, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
+  constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * N3_TILE];
+  const int M = g.M, N = g.N, K = g.K;
+  const int z = blockIdx.y;
+  const bf16* __restrict__ A = (const bf16*)g.A + z * g.sA;
+  const bf16* __restrict__ B = (const bf16*)g.B + z * g.sB;
+  const int tiles_m = (M + N2_BM - 1) / N2_BM, tiles_n = (N + N2_BN - 1) / N2_BN;
+  const int ntiles = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+  const int GM = 4;
+  const int group = GM * tiles_n;
+  const int first_m = (pid / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % group) % gsz;
+  const int tn = (pid % group) / gsz;
+  const int m0 = tm * N2_BM, n0 = tn * N2_BN;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / (NW / 2), wn = w % (NW / 2);
+  f32x16 acc[4][WJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / N3_BK;
+  n3_issue<NW>(lds, A, g.lda, m0, M, B, g.ldb, n0, N, 0);
+  if (nk > 1) n3_issue<NW>(lds + N3_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, N3_BK);
+  bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
+  auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
+    const bf16* Bs = st + N2_BM * N3_BK;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + n3_off(wm * 128 + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) b[j] = *(const bf16x8*)(Bs + n3_off(wn * 32 * WJ + j * 32 + (lane & 31), c));
+  };
+  auto mma = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  // stage 0 ready (stage 1's 64 / NW loads may still be in flight)
+  if (nk > 1) {
+    if constexpr (NW == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  frags(lds, 0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const bf16* st = lds + (kt & 1) * N3_TILE;
+    frags(st, 1, a1, b1);
+    mma(a0, b0);
+    frags(st, 2, a0, b0);
+    mma(a1, b1);
+    frags(st, 3, a1, b1);
+    mma(a0, b0);
+    if (kt + 1 < nk) {
+      // stage kt + 1 is the only load in flight; once every wave has also finished reading this
+      // slot, it takes stage kt + 2
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + 2 < nk) n3_issue<NW>(lds + (kt & 1) * N3_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, (kt + 2) * N3_BK);
+      frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
+    }
+    mma(a1, b1);
+  }
+
+  // epilogue: acc[i][j][4 q + e] is C[row][col + e], row = m0 + 128 wm + 32 i + lane % 32,
+  // col = n0 + 32 WJ wn + 32 j + 8 q + 4 (lane / 32)
+  TO* C = (TO*)g.C + z * g.sC;
+  const float* R = g.R ? g.R + z * g.sR : nullptr;
+  constexpr int VB = 4 * (int)sizeof(TO);
+  const bool vec = g.ldc % 4 == 0 && (uintptr_t)C % VB == 0 &&
+                   (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (row >= M) continue;
+    TO* crow = C + (int64_t)row * g.ldc;
+    const float* rrow = EPI == EPI_RESID ? R + (int64_t)row * g.ldr : nullptr;
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * 32 * WJ + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = g.alpha * acc[i][j][4 * q + e];
+        if (vec && col + 4 <= N) {
+          if constexpr (EPI == EPI_RESID) {
+            const float4 rv = *(const float4*)(rrow + col);
+            v[0] += rv.x; v[1] += rv.y; v[2] += rv.z; v[3] += rv.w;
+          }
+          if constexpr (sizeof(TO) == 4) {
+            if constexpr (EPI == EPI_ACCUM) {
+              const float4 cv = *(const float4*)(crow + col);
+              v[0] += cv.x; v[1] += cv.y; v[2] += cv.z; v[3] += cv.w;
+            }
+            *(float4*)(crow + col) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            *(bf16x4*)(crow + col) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= N) break;
+            float x = v[e];
+            if constexpr (EPI == EPI_ACCUM) x += to_f(crow[col + e]);
+            if constexpr (EPI == EPI_RESID) x += rrow[col + e];
+            crow[col + e] = from_f<TO>(x);
+          }
+        }
+      }
+  }
+}
+
+constexpr int NT3_WAVES = 8;
+template <int EPI, typename TO>
+static int launch_nt3_t(const Gemm& g, hipStream_t s) {
+  const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
+  hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
+  return (int)hipGetLastError();
+}
+
+static int launch_nt3(const Gemm& g, hipStream_t s) {
+  if (g.epi == EPI_STORE) return g.c == DT_BF16 ? launch_nt3_t<EPI_STORE, bf16>(g, s) : launch_nt3_t<EPI_STORE, float>(g, s);
+  if (g.epi == EPI_ACCUM) return launch_nt3_t<EPI_ACCUM, float>(g, s);
+  return launch_nt3_t<EPI_RESID, float>(g, s);
+}
+
 constexpr int NT2_WAVES = 8;
 template <int EPI, typename TO>
 static int launch_nt2_t(const Gemm& g, hipStream_t s) {
@@ -520,6 +696,7 @@ int launch_gemm(const Gemm& g, hipStream_t s) {
                          (((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0) &&
                          (g.batch == 1 || (g.sA % 8 == 0 && g.sB % 8 == 0));
     if (aligned) {
+      if (!g.a_km && !g.b_kn && g.K % N3_BK == 0) return launch_nt3(g, s);
       if (!g.a_km && !g.b_kn && g.K % N2_BK == 0) return launch_nt2(g, s);
       if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
       if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);

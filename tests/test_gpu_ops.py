@@ -72,7 +72,7 @@ def gemm_case(M, N, K, a_km, b_kn, dt, epi, seed=0, out_bf16=False):
 
 
 @pytest.mark.parametrize("a_km,b_kn", [(0, 0), (0, 1), (1, 1), (1, 0)])
-@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (512, 384, 256), (37, 129, 8)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (512, 384, 256), (37, 129, 8), (300, 520, 96), (600, 520, 320)])
 def test_gemm_bf16_mfma_layouts(M, N, K, a_km, b_kn):
     got, ref = gemm_case(M, N, K, a_km, b_kn, hol.BF16, 0)
     # fp32 accumulation of exact bf16 products: error well below 1e-5 of the typical magnitude
@@ -83,6 +83,18 @@ def test_gemm_bf16_mfma_layouts(M, N, K, a_km, b_kn):
 def test_gemm_bf16_epilogues(epi):
     got, ref = gemm_case(260, 140, 64, 1, 1, hol.BF16, epi, seed=3)
     assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < 1e-5
+
+
+# the NT kernels (K a multiple of 64: 64-deep stages; of 32: 32-deep) with every epilogue, ragged
+# M and N over several 256 x 256 tiles
+# (N = 300: 16-byte epilogue stores; N = 302: row stride not a multiple of 4, element stores)
+@pytest.mark.parametrize("K", [192, 96])
+@pytest.mark.parametrize("N", [300, 302])
+@pytest.mark.parametrize("epi,out_bf16", [(0, False), (0, True), (1, False), (2, False)])
+def test_gemm_bf16_nt_epilogues(K, N, epi, out_bf16):
+    got, ref = gemm_case(530, N, K, 0, 0, hol.BF16, epi, seed=K + epi, out_bf16=out_bf16)
+    tol = 2 ** -8 if out_bf16 else 1e-5
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < tol
 
 
 def test_gemm_bf16_output_rounding():
