@@ -1059,6 +1059,7 @@ static void host_accumulate(void* p) {
 }
 
 static void adam_unit(hol_model* m, int u, const AdamConsts& k);
+static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k);
 
 // Host worker of the fused forward_backward + step: runs the optimiser on each unit as soon as
 // that unit's gradient copy (enqueued by the main thread, in backward order) has completed.
@@ -1089,12 +1090,15 @@ struct FusedWorker {
           u = m->unit_queue[next++];
         }
         if (u < 0) return;  // every unit handed over
-        if (hipEventSynchronize(m->ev_unit[u]) != hipSuccess) {
+        // unit L + 2: embedding rows no token of this call touches (their gradient is zero and
+        // known from the start)
+        if (u != m->L + 2 && hipEventSynchronize(m->ev_unit[u]) != hipSuccess) {
           failed = true;
           return;
         }
         const double t0 = now_ms();
-        adam_unit(m, u, kc);
+        if (u == m->L + 2) adam_embed_rows(m, m->emb_untouched, kc);
+        else adam_unit(m, u, kc);
         const double t1 = now_ms();
         busy_ms += t1 - t0;
         m->stats.units.push_back({(double)u, t0 - t_call, t1 - t_call});
@@ -1185,17 +1189,20 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     }
   }
   // ---- h_0: embedding rows gathered on the host from the fp32 masters, or the given hidden states
-  const double te = now_ms();
-  if (m->V > 0) {
-    const float* emb = m->master + m->embed_flat0;
-    parallel_for(T64, 256, [&](int64_t lo, int64_t hi) {
-      for (int64_t t = lo; t < hi; ++t) memcpy(m->h_stage + t * H, emb + (int64_t)b->tokens[t] * H, (size_t)H * 4);
-    });
-  } else {
-    parallel_for(T64 * H, 1 << 20,
-                 [&](int64_t lo, int64_t hi) { memcpy(m->h_stage + lo, b->hidden_in + lo, (size_t)(hi - lo) * 4); });
-  }
-  m->stats.host_embed_ms = now_ms() - te;
+  // (run while the first layer's weights stream in)
+  auto gather_h0 = [&]() {
+    const double te = now_ms();
+    if (m->V > 0) {
+      const float* emb = m->master + m->embed_flat0;
+      parallel_for(T64, 256, [&](int64_t lo, int64_t hi) {
+        for (int64_t t = lo; t < hi; ++t) memcpy(m->h_stage + t * H, emb + (int64_t)b->tokens[t] * H, (size_t)H * 4);
+      });
+    } else {
+      parallel_for(T64 * H, 1 << 20,
+                   [&](int64_t lo, int64_t hi) { memcpy(m->h_stage + lo, b->hidden_in + lo, (size_t)(hi - lo) * 4); });
+    }
+    m->stats.host_embed_ms = now_ms() - te;
+  };
 
   hol_status st = HOL_OK;
   auto fail = [&](hol_status s) {
@@ -1237,9 +1244,6 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     HSTEP(hipMemcpyAsync(m->labels_dev, m->lab_stage, T64 * 4, hipMemcpyHostToDevice, sc));
     HSTEP(hipMemcpyAsync(m->w_dev, m->w_stage, T64 * 4, hipMemcpyHostToDevice, sc));
   }
-  HSTEP(hipMemcpyAsync(m->ckpt, m->h_stage, T64 * H * 4, hipMemcpyHostToDevice, sc));
-  m->stats.h2d_bytes += (double)T64 * H * 4;
-
   // ---- op list
   std::vector<Op> ops;
   for (int l = 0; l < L; ++l) ops.push_back({OP_FWD, l, l / K, l % K});
@@ -1305,6 +1309,30 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   };
 
   STEP(ensure_loaded(0));
+  gather_h0();
+  HSTEP(hipMemcpyAsync(m->ckpt, m->h_stage, T64 * H * 4, hipMemcpyHostToDevice, sc));
+  m->stats.h2d_bytes += (double)T64 * H * 4;
+  // embedding rows by token: occurrences of each token id in order of position (the scatter-add of
+  // the first-layer gradient sums them in that order), and the rows no token touches
+  std::vector<int32_t> tok_order;
+  if (m->embed_trainable) {
+    tok_order.resize(T64);
+    for (int64_t t = 0; t < T64; ++t) tok_order[t] = (int32_t)t;
+    std::stable_sort(tok_order.begin(), tok_order.end(),
+                     [&](int32_t x, int32_t y) { return b->tokens[x] < b->tokens[y]; });
+    m->emb_touched.clear();
+    for (int64_t i = 0; i < T64; ++i)
+      if (i == 0 || b->tokens[tok_order[i]] != b->tokens[tok_order[i - 1]]) m->emb_touched.push_back(b->tokens[tok_order[i]]);
+    if (fused) {
+      m->emb_untouched.clear();
+      size_t q = 0;
+      for (int32_t r = 0; r < m->V; ++r) {
+        if (q < m->emb_touched.size() && m->emb_touched[q] == r) ++q;
+        else m->emb_untouched.push_back(r);
+      }
+      worker.push(m->L + 2);  // their Adam overlaps the forward
+    }
+  }
   int gi = 0;  // grad buffer ping-pong
   for (size_t j = 0; j < ops.size(); ++j) {
     const Op& op = ops[j];
@@ -1443,14 +1471,21 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   HSTEP(hipStreamSynchronize(sd));
   m->stats.gpu_done_ms = now_ms() - t_start;
   HSTEP(hipGetLastError());
-  // embedding gradient: rows added in token order (columns split over threads: deterministic)
+  // embedding gradient: each touched row adds its tokens' first-layer gradients in position order
+  // (rows split over threads: deterministic)
   if (m->embed_trainable) {
     float* gE = m->grad + m->embed_flat0;
-    parallel_for(H, 64, [&](int64_t lo, int64_t hi) {
-      for (int64_t t = 0; t < T64; ++t) {
-        float* dst = gE + (int64_t)b->tokens[t] * H;
-        const float* src = m->h_stage + t * H;
-        for (int64_t c = lo; c < hi; ++c) dst[c] += src[c];
+    std::vector<int64_t> starts;
+    for (int64_t i = 0; i < T64; ++i)
+      if (i == 0 || b->tokens[tok_order[i]] != b->tokens[tok_order[i - 1]]) starts.push_back(i);
+    starts.push_back(T64);
+    parallel_for((int64_t)starts.size() - 1, 8, [&](int64_t lo, int64_t hi) {
+      for (int64_t gi = lo; gi < hi; ++gi) {
+        float* dst = gE + (int64_t)b->tokens[tok_order[starts[gi]]] * H;
+        for (int64_t i = starts[gi]; i < starts[gi + 1]; ++i) {
+          const float* src = m->h_stage + (int64_t)tok_order[i] * H;
+          for (int64_t c = 0; c < H; ++c) dst[c] += src[c];
+        }
       }
     });
   }
@@ -1467,7 +1502,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
       return fail(HOL_EDEVICE);
     }
-    adam_unit(m, 0, kc);  // the embedding gradient is complete only after the host scatter-add
+    // the touched embedding rows are complete only after the host scatter-add
+    adam_embed_rows(m, m->emb_touched, kc);
     m->step_t += 1;
     m->grads_zero = true;
     m->stats.step_ms = now_ms() - t_gpu_done;  // optimiser time not hidden under the GPU work
@@ -1535,6 +1571,20 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k) {
       }
     });
   }
+}
+
+// Adam on the given rows of the embedding (and zeroing of their gradients): the same per-element
+// arithmetic as adam_unit, split by rows.
+static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k) {
+  if (!m->embed_trainable || rows.empty()) return;
+  const int64_t H = m->H, f0 = m->embed_flat0;
+  parallel_for((int64_t)rows.size(), 16, [&](int64_t lo, int64_t hi) {
+    for (int64_t q = lo; q < hi; ++q) {
+      const int64_t o = f0 + (int64_t)rows[q] * H;
+      adam_range(m->master + o, m->grad + o, m->mom1 + o, m->mom2 + o, H, k);
+      memset(m->grad + o, 0, (size_t)H * 4);
+    }
+  });
 }
 
 hol_status engine_step(hol_model* m) {

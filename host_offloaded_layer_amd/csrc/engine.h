@@ -191,6 +191,7 @@ struct hol_model {
   std::mutex fmu;
   std::condition_variable fcv;
   std::vector<int> unit_queue;         // units whose gradient copy has been enqueued, in order
+  std::vector<int32_t> emb_touched, emb_untouched;  // embedding rows the call's tokens use / do not
   bool fused_abort = false;
   double fused_overlap_ms = 0, fused_tail_ms = 0;
 };
