@@ -513,7 +513,40 @@ __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A
 
 // NW = 8: 2 x 4 waves of 128 x 64 (two per SIMD); NW = 4: 2 x 2 waves of 128 x 128 (one per SIMD,
 // a third fewer LDS fragment reads per MFMA).
-template <int EPI, typename TO, int NW>
+// The same loads through buffer resources: a lane's byte offset into A (B) is fixed for the whole
+// tile (rows clamped as above), the stage's k offset is a scalar, so no per-load address arithmetic.
+template <int NW>
+struct N3Buf {
+  uint32_t va[32 / NW], vb[32 / NW];
+  __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int R = (w + NW * i) * 8 + (lane >> 3);
+      const int lc = (lane & 7) ^ ((R >> 1) & 7);
+      va[i] = (uint32_t)(min(m0 + R, M - 1) * lda * 2 + lc * 16);
+      vb[i] = (uint32_t)(min(n0 + R, N - 1) * ldb * 2 + lc * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int k0) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + (w + NW * i) * 8 * N3_BK), 16, va[i], k0 * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + N2_BM * N3_BK + (w + NW * i) * 8 * N3_BK), 16,
+                                               vb[i], k0 * 2, 0, 0);
+  }
+};
+
+// Whether every byte of A and B lies within an unsigned 32-bit offset of its base (the buffer path).
+static bool n3_buffer_ok(const Gemm& g) {
+  const uint64_t ea = (uint64_t)g.M * (uint64_t)g.lda * 2, eb = (uint64_t)g.N * (uint64_t)g.ldb * 2;
+  return g.batch == 1 && ea < (1ull << 32) && eb < (1ull << 32);
+}
+
+template <int EPI, typename TO, int NW, bool BUF>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * N3_TILE];
@@ -543,8 +576,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = K / N3_BK;
-  n3_issue<NW>(lds, A, g.lda, m0, M, B, g.ldb, n0, N, 0);
-  if (nk > 1) n3_issue<NW>(lds + N3_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, N3_BK);
+  N3Buf<NW> nb;
+  if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)M * g.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)N * g.ldb * 2), 0x00020000);
+  auto issue = [&](bf16* stage, int k0) {
+    if constexpr (BUF) nb.issue(stage, ra, rb, k0);
+    else n3_issue<NW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, k0);
+  };
+  issue(lds, 0);
+  if (nk > 1) issue(lds + N3_TILE, N3_BK);
   bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
   auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
     const bf16* Bs = st + N2_BM * N3_BK;
@@ -580,7 +623,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       // stage kt + 1 is the only load in flight; once every wave has also finished reading this
       // slot, it takes stage kt + 2
       asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (kt + 2 < nk) n3_issue<NW>(lds + (kt & 1) * N3_TILE, A, g.lda, m0, M, B, g.ldb, n0, N, (kt + 2) * N3_BK);
+      if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
       frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
     }
     mma(a1, b1);
@@ -638,10 +681,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 }
 
 constexpr int NT3_WAVES = 8;
+// (explicit instantiations: the host pass does not always emit the launch stubs of the
+// buffer-path instantiations on its own)
+template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true>(Gemm);
+template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, true>(Gemm);
+template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, false>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false>(Gemm);
+template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, false>(Gemm);
+template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, false>(Gemm);
 template <int EPI, typename TO>
 static int launch_nt3_t(const Gemm& g, hipStream_t s) {
   const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
-  hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
+  if (n3_buffer_ok(g))
+    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, false>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
   return (int)hipGetLastError();
 }
 
