@@ -223,6 +223,8 @@ def main():
         u = fb.get("units") or []
         if u:
             lag = [e - a for _, a, e in u]
+            log(f"[bench]   device: compute from {fb['first_compute_ms']:.1f} to {fb['last_compute_end_ms']:.1f} ms after the "
+                f"first weight copy, busy {fb['compute_busy_ms']:.0f} ms")
             log(f"[bench]   host: gpu done at {fb['gpu_done_ms']:.0f} ms, scatter done {fb['scatter_done_ms']:.0f} ms, "
                 f"optimiser busy {fb['worker_busy_ms']:.0f} ms over {len(u)} units (first start {u[0][1]:.0f}, "
                 f"last end {u[-1][2]:.0f}, max unit {max(lag):.0f} ms); starts "

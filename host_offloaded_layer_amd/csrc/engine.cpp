@@ -1513,6 +1513,21 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     return engine_step(m);
   }
   // ---- stats
+  {
+    // device timeline from the first weight copy: when compute starts and ends
+    int f = -1, l = -1;
+    for (int i = 0; i < (int)spans.size(); ++i)
+      if (spans[i].cls >= 2) {
+        if (f < 0) f = i;
+        l = i;
+      }
+    float a = 0.f, b2 = 0.f;
+    if (!spans.empty() && f >= 0 && hipEventElapsedTime(&a, spans[0].a, spans[f].a) == hipSuccess &&
+        hipEventElapsedTime(&b2, spans[0].a, spans[l].b) == hipSuccess) {
+      m->stats.first_compute_ms = a;
+      m->stats.last_compute_end_ms = b2;
+    }
+  }
   for (auto& sp : spans) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, sp.a, sp.b) != hipSuccess) continue;
@@ -1659,7 +1674,8 @@ std::string stats_json(const hol_model* m) {
     << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
     << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads()
     << ",\"gpu_done_ms\":" << s.gpu_done_ms << ",\"scatter_done_ms\":" << s.scatter_done_ms
-    << ",\"worker_busy_ms\":" << s.worker_busy_ms << ",\"units\":[";
+    << ",\"worker_busy_ms\":" << s.worker_busy_ms << ",\"first_compute_ms\":" << s.first_compute_ms
+    << ",\"last_compute_end_ms\":" << s.last_compute_end_ms << ",\"units\":[";
   for (size_t i = 0; i < s.units.size(); ++i)
     o << (i ? "," : "") << "[" << (int)s.units[i][0] << "," << s.units[i][1] << "," << s.units[i][2] << "]";
   o << "]";

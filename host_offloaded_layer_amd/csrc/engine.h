@@ -72,6 +72,8 @@ struct Stats {
   // host timeline of a fused call (ms from the call's start): GPU work drained, embedding
   // scatter-add done; per optimiser unit: gradient arrived on the host, Adam done
   double gpu_done_ms = 0, scatter_done_ms = 0, worker_busy_ms = 0;
+  // device timeline (ms after the first weight copy starts): first compute op starts, last ends
+  double first_compute_ms = 0, last_compute_end_ms = 0;
   std::vector<std::array<double, 3>> units;  // {unit, arrived, done}
   int n_weight_streams = 0;
   int tokens = 0;
