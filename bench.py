@@ -78,10 +78,10 @@ def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int
 
 
 def profiled_traffic(workload: str):
-    """HBM bytes per gemm_nt2 launch from the committed rocprofv3 counter summary, or None when
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, or None when
     there is none for this workload or the GEMM source changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"gemm_nt2_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and " " not in l.strip())

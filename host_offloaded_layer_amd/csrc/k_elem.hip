@@ -5,6 +5,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <initializer_list>
+
 namespace hol {
 
 // ------------------------------------------------------------------------------------------
@@ -251,6 +253,18 @@ int launch_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int T,
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// Contraction is off in these two so that every kernel below that calls them rounds the same way.
+__device__ __forceinline__ float swiglu_f(float g, float u) {
+#pragma clang fp contract(off)
+  return g * sigm(g) * u;
+}
+__device__ __forceinline__ void swiglu_b(float d, float g, float u, float& dg, float& du) {
+#pragma clang fp contract(off)
+  const float sg = sigm(g);
+  dg = d * u * sg * (1.f + g * (1.f - sg));
+  du = d * g * sg;
+}
+
 template <typename T>
 __global__ void swiglu_fwd_k(const T* __restrict__ gu, T* __restrict__ a, int Tn, int F) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -258,7 +272,7 @@ __global__ void swiglu_fwd_k(const T* __restrict__ gu, T* __restrict__ a, int Tn
   const int64_t t = i / F;
   const int f = (int)(i % F);
   const float g = to_f(gu[t * 2 * F + f]), u = to_f(gu[t * 2 * F + F + f]);
-  a[i] = from_f<T>(g * sigm(g) * u);
+  a[i] = from_f<T>(swiglu_f(g, u));
 }
 
 template <typename T>
@@ -268,15 +282,84 @@ __global__ void swiglu_bwd_k(const T* __restrict__ da, const T* __restrict__ gu,
   const int64_t t = i / F;
   const int f = (int)(i % F);
   const float g = to_f(gu[t * 2 * F + f]), u = to_f(gu[t * 2 * F + F + f]);
-  const float d = to_f(da[i]);
-  const float sg = sigm(g);
-  dgu[t * 2 * F + f] = from_f<T>(d * u * sg * (1.f + g * (1.f - sg)));
-  dgu[t * 2 * F + F + f] = from_f<T>(d * g * sg);
+  float dg, du;
+  swiglu_b(to_f(da[i]), g, u, dg, du);
+  dgu[t * 2 * F + f] = from_f<T>(dg);
+  dgu[t * 2 * F + F + f] = from_f<T>(du);
+}
+
+// Eight consecutive elements per thread (16-byte bf16 / 2 x 16-byte fp32 accesses). Each element
+// goes through the same uncontracted expressions as in the one-element kernels above, so both give
+// identical bits; these are taken when F % 8 == 0, the pointers are 16-byte aligned and T * F / 8 < 2^31.
+__device__ __forceinline__ void ld8(const bf16* p, float* v) {
+  const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (float)x[j];
+}
+__device__ __forceinline__ void ld8(const float* p, float* v) {
+  const float4 x = *(const float4*)p, y = *(const float4*)(p + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+__device__ __forceinline__ void st8(bf16* p, const float* v) {
+  bf16x8 x;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (bf16)v[j];
+  *(bf16x8*)p = x;
+}
+__device__ __forceinline__ void st8(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_fwd8_k(const T* __restrict__ gu, T* __restrict__ a, uint32_t units,
+                                                     uint32_t nv) {
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= units) return;
+  const uint32_t t = u / nv, c = u - t * nv;
+  const T* gr = gu + (int64_t)t * 16 * nv + c * 8;
+  float g[8], up[8], o[8];
+  ld8(gr, g);
+  ld8(gr + 8 * nv, up);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = swiglu_f(g[j], up[j]);
+  st8(a + (int64_t)u * 8, o);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd8_k(const T* __restrict__ da, const T* __restrict__ gu,
+                                                     T* __restrict__ dgu, uint32_t units, uint32_t nv) {
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= units) return;
+  const uint32_t t = u / nv, c = u - t * nv;
+  const int64_t base = (int64_t)t * 16 * nv + c * 8;
+  float g[8], up[8], d[8], dg[8], du[8];
+  ld8(gu + base, g);
+  ld8(gu + base + 8 * nv, up);
+  ld8(da + (int64_t)u * 8, d);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) swiglu_b(d[j], g[j], up[j], dg[j], du[j]);
+  st8(dgu + base, dg);
+  st8(dgu + base + 8 * nv, du);
+}
+
+static bool vec8_ok(int64_t units, std::initializer_list<const void*> ptrs) {
+  if (units >= (int64_t(1) << 31)) return false;
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return false;
+  return true;
 }
 
 int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_t s) {
   const int64_t n = (int64_t)T * F;
   if (n <= 0) return 0;
+  if (F % 8 == 0 && vec8_ok(n / 8, {gu, a})) {
+    const uint32_t units = (uint32_t)(n / 8), nv = (uint32_t)(F / 8);
+    dim3 grid((units + 255) / 256);
+    if (t == DT_BF16) hipLaunchKernelGGL(swiglu_fwd8_k<bf16>, grid, dim3(256), 0, s, (const bf16*)gu, (bf16*)a, units, nv);
+    else hipLaunchKernelGGL(swiglu_fwd8_k<float>, grid, dim3(256), 0, s, (const float*)gu, (float*)a, units, nv);
+    return (int)hipGetLastError();
+  }
   dim3 grid((unsigned)((n + 255) / 256));
   if (t == DT_BF16) hipLaunchKernelGGL(swiglu_fwd_k<bf16>, grid, dim3(256), 0, s, (const bf16*)gu, (bf16*)a, T, F);
   else hipLaunchKernelGGL(swiglu_fwd_k<float>, grid, dim3(256), 0, s, (const float*)gu, (float*)a, T, F);
@@ -286,6 +369,15 @@ int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_
 int launch_swiglu_bwd(const void* da, const void* gu, void* dgu, DType t, int T, int F, hipStream_t s) {
   const int64_t n = (int64_t)T * F;
   if (n <= 0) return 0;
+  if (F % 8 == 0 && vec8_ok(n / 8, {da, gu, dgu})) {
+    const uint32_t units = (uint32_t)(n / 8), nv = (uint32_t)(F / 8);
+    dim3 grid((units + 255) / 256);
+    if (t == DT_BF16)
+      hipLaunchKernelGGL(swiglu_bwd8_k<bf16>, grid, dim3(256), 0, s, (const bf16*)da, (const bf16*)gu, (bf16*)dgu, units, nv);
+    else
+      hipLaunchKernelGGL(swiglu_bwd8_k<float>, grid, dim3(256), 0, s, (const float*)da, (const float*)gu, (float*)dgu, units, nv);
+    return (int)hipGetLastError();
+  }
   dim3 grid((unsigned)((n + 255) / 256));
   if (t == DT_BF16) hipLaunchKernelGGL(swiglu_bwd_k<bf16>, grid, dim3(256), 0, s, (const bf16*)da, (const bf16*)gu, (bf16*)dgu, T, F);
   else hipLaunchKernelGGL(swiglu_bwd_k<float>, grid, dim3(256), 0, s, (const float*)da, (const float*)gu, (float*)dgu, T, F);
@@ -394,6 +486,14 @@ __global__ void cast_k(const float* __restrict__ x, T* __restrict__ y, int64_t n
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = from_f<T>(x[i]);
 }
+template <typename T>
+__global__ __launch_bounds__(256) void cast8_k(const float* __restrict__ x, T* __restrict__ y, uint32_t units) {
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= units) return;
+  float v[8];
+  ld8(x + (int64_t)u * 8, v);
+  st8(y + (int64_t)u * 8, v);
+}
 __global__ void fill_k(float* x, float v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) x[i] = v;
@@ -405,6 +505,13 @@ __global__ void scale_k(const float* x, float a, float* y, int64_t n) {
 
 int launch_cast_f32(const float* x, void* y, DType yt, int64_t n, hipStream_t s) {
   if (n <= 0) return 0;
+  if (n % 8 == 0 && vec8_ok(n / 8, {x, y})) {
+    const uint32_t units = (uint32_t)(n / 8);
+    dim3 grid((units + 255) / 256);
+    if (yt == DT_BF16) hipLaunchKernelGGL(cast8_k<bf16>, grid, dim3(256), 0, s, x, (bf16*)y, units);
+    else hipLaunchKernelGGL(cast8_k<float>, grid, dim3(256), 0, s, x, (float*)y, units);
+    return (int)hipGetLastError();
+  }
   dim3 grid((unsigned)((n + 255) / 256));
   if (yt == DT_BF16) hipLaunchKernelGGL(cast_k<bf16>, grid, dim3(256), 0, s, x, (bf16*)y, n);
   else hipLaunchKernelGGL(cast_k<float>, grid, dim3(256), 0, s, x, (float*)y, n);

@@ -201,9 +201,10 @@ def test_rope_fwd_and_inverse(dt):
 
 
 # ------------------------------------------------------------------ SwiGLU
+@pytest.mark.parametrize("F", [344, 342])   # 8-wide kernel / one-element kernel
 @pytest.mark.parametrize("dt", [hol.F32, hol.BF16])
-def test_swiglu_fwd_bwd(dt):
-    T, F = 77, 344
+def test_swiglu_fwd_bwd(dt, F):
+    T = 77
     r = np.random.default_rng(2)
     gu = r.standard_normal((T, 2 * F)).astype(np.float32) * 2
     da = r.standard_normal((T, F)).astype(np.float32)
@@ -220,6 +221,32 @@ def test_swiglu_fwd_bwd(dt):
     dg, du = D.swiglu_bwd(da64, g64, u64)
     np.testing.assert_allclose(host(dgu), np.concatenate([dg, du], 1), rtol=tol, atol=tol)
 
+
+
+@pytest.mark.parametrize("dt", [hol.F32, hol.BF16])
+def test_swiglu_vector_and_scalar_kernels_agree_bitwise(dt):
+    """Buffers shifted by one element are not 16-byte aligned, which routes the call to the
+    one-element kernels; both kernels must give the same bits."""
+    T, F = 45, 96
+    r = np.random.default_rng(3)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    gu0 = dev(r.standard_normal((T * 2 * F,)).astype(np.float32) * 3, tdt)
+    da0 = dev(r.standard_normal((T * F,)).astype(np.float32), tdt)
+    outs = []
+    for off in (0, 1):
+        gu = torch.zeros(T * 2 * F + 1, dtype=tdt, device=DEV)
+        da = torch.zeros(T * F + 1, dtype=tdt, device=DEV)
+        g, d = gu[off:off + T * 2 * F], da[off:off + T * F]
+        g.copy_(gu0)
+        d.copy_(da0)
+        a = torch.zeros(T * F + 1, dtype=tdt, device=DEV)
+        dgu = torch.zeros(T * 2 * F + 1, dtype=tdt, device=DEV)
+        hol.check(hol.lib.hol_op_swiglu_fwd(g.data_ptr(), a[off:].data_ptr(), dt, T, F, None))
+        hol.check(hol.lib.hol_op_swiglu_bwd(d.data_ptr(), g.data_ptr(), dgu[off:].data_ptr(), dt, T, F, None))
+        sync()
+        outs.append((host(a[off:off + T * F]), host(dgu[off:off + T * 2 * F])))
+    for x, y in zip(outs[0], outs[1]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("dt,S,nseq,nq,nkv,d", [
