@@ -224,6 +224,14 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     m->o_wd = o;   o = align_up(o + H * F_ * E, 4096);
     m->wT_bytes = o;
   }
+  m->moe_grp = NE > 0 && m->dt == DT_BF16 && H % 64 == 0 && Fe % 64 == 0;
+  if (m->moe_grp) {
+    int64_t t = m->wT_bytes;
+    m->t_egate = t; t = align_up(t + NE * Fe * H * E, 4096);
+    m->t_eup = t;   t = align_up(t + NE * Fe * H * E, 4096);
+    m->t_edown = t; t = align_up(t + NE * H * Fe * E, 4096);
+    m->wT_bytes = t;
+  }
   m->o_g1 = o;   o = align_up(o + H * 4, 4096);
   m->o_g2 = o;   o = align_up(o + H * 4, 4096);
   // LoRA factors (fp32): q, k, v on the attention-norm output, o on the attention output
@@ -379,6 +387,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     m->ao_perm = A(Tk * 4);
     m->ao_gup = A(Tk * 2 * Fe * E);
     m->ao_yp = A(Tk * H * 4);
+    m->ao_mtab = A((2 * NE + 2) * 4);
   }
   m->act_stride = a;
   m->act_counts.assign(m->Kmax, std::vector<int32_t>(std::max<int64_t>(NE, 1), 0));
@@ -598,6 +607,7 @@ static Act act_at(const hol_model* m, int j) {
   a.perm_slot = (int32_t*)(b + m->ao_perm);
   a.gup = b + m->ao_gup;
   a.yp = (float*)(b + m->ao_yp);
+  a.mtab = (int32_t*)(b + m->ao_mtab);
   return a;
 }
 
@@ -674,9 +684,29 @@ static hol_status lora_bwd(hol_model* m, const void* dy, int64_t lddy, const voi
   return HOL_OK;
 }
 
-// Mixture-of-experts MLP: hout = h1 + sum_i w_i SwiGLU_{e_i}(n2). Routing, the permutation and the
-// expert outputs go to the activation store; the expert row counts to act_counts[pos] (the host
-// reads them to launch one pair of GEMMs per expert).
+// One product over every expert's rows (grouped launch): C[rows of e] = A[rows of e] B_e^T with
+// B_e = B + e sB elements; the group table of the activation-store position gives the rows.
+static Gemm grouped(const hol_model* m, const Act& A, int64_t rows, int N, int K, const void* a, int64_t lda,
+                    const void* b, int64_t ldb, int64_t sB, void* c, int64_t ldc, DType ct, int epi) {
+  Gemm g = gemm((int)rows, N, K, a, lda, false, b, ldb, false, c, ldc, DT_BF16, ct, epi);
+  g.grp = A.mtab;
+  g.ngroups = m->NE;
+  g.sB = sB;
+  g.grp_max_rt = (int)((rows + (int64_t)m->NE * (GEMM_GROUP_BM - 1)) / GEMM_GROUP_BM);
+  return g;
+}
+
+static int run_grouped(hol_model* m, const Gemm& g) {
+  const double bytes = 2.0 * ((double)g.M * g.K + (double)g.ngroups * g.N * g.K) +
+                       (g.c == DT_BF16 ? 2.0 : 4.0) * (double)g.M * g.N * (g.epi == EPI_STORE ? 1 : 2);
+  return timed(m, KC_GEMM, 2.0 * g.M * g.N * g.K, bytes, [&] { return launch_gemm_grouped(g, m->sc); });
+}
+
+// Mixture-of-experts MLP: hout = h1 + sum_i w_i SwiGLU_{e_i}(n2). Routing, the permutation, the
+// group table and the expert outputs go to the activation store. The expert products are grouped
+// launches (bf16, 64-aligned widths) that read the row counts on the device; otherwise the host
+// reads the counts into act_counts[pos] and launches one pair of products per expert, as it also
+// does for the expert weight gradients.
 static hol_status moe_forward(hol_model* m, const W& w, const Act& A, int T, float* hout, int pos) {
   const int H = m->H, NE = m->NE, k = m->topk, Fe = m->Fe;
   const DType dt = m->dt;
@@ -686,11 +716,23 @@ static hol_status moe_forward(hol_model* m, const W& w, const Act& A, int T, flo
   KT(KC_OTHER, 0, (double)T * NE * 8, launch_moe_route(m->mlogits, T, NE, k, A.probs, A.ids, A.w, m->mcounts, s));
   KT(KC_OTHER, 0, (double)Tk * 16, launch_moe_permute(A.ids, T, NE, k, m->mcounts, m->moffsets, m->mperm,
                                                       A.perm_slot, A.slot_pos, s));
-  HCHECK(hipMemcpyAsync(m->counts_stage, m->mcounts, (size_t)NE * 4, hipMemcpyDeviceToHost, s));
-  HCHECK(hipStreamSynchronize(s));
-  std::vector<int32_t>& cnt = m->act_counts[pos];
-  memcpy(cnt.data(), m->counts_stage, (size_t)NE * 4);
+  if (m->moe_grp) KT(KC_OTHER, 0, (double)NE * 12, launch_gemm_group_table(m->mcounts, NE, A.mtab, s));
+  if (!m->moe_grp || m->base_trainable) {
+    HCHECK(hipMemcpyAsync(m->counts_stage, m->mcounts, (size_t)NE * 4, hipMemcpyDeviceToHost, s));
+    HCHECK(hipStreamSynchronize(s));
+    memcpy(m->act_counts[pos].data(), m->counts_stage, (size_t)NE * 4);
+  }
+  const std::vector<int32_t>& cnt = m->act_counts[pos];
   KT(KC_OTHER, 0, 2.0 * Tk * H * E, launch_moe_gather(A.n2, dt, A.perm_slot, k, Tk, H, m->xp, s));
+  if (m->moe_grp) {
+    KCHECK(run_grouped(m, grouped(m, A, Tk, Fe, H, m->xp, H, w.egate, H, (int64_t)Fe * H, A.gup, 2 * Fe, dt, EPI_STORE)));
+    KCHECK(run_grouped(m, grouped(m, A, Tk, Fe, H, m->xp, H, w.eup, H, (int64_t)Fe * H, (uint8_t*)A.gup + Fe * E, 2 * Fe,
+                                  dt, EPI_STORE)));
+    KT(KC_SWIGLU, 0, 3.0 * Tk * Fe * E, launch_swiglu_fwd(A.gup, m->ap, dt, (int)Tk, Fe, s));
+    KCHECK(run_grouped(m, grouped(m, A, Tk, H, Fe, m->ap, Fe, w.edown, Fe, (int64_t)H * Fe, A.yp, H, DT_F32, EPI_STORE)));
+    KT(KC_OTHER, 0, (double)T * H * 8 + (double)Tk * H * 4, launch_moe_combine(A.h1, A.yp, A.w, A.slot_pos, T, k, H, hout, s));
+    return HOL_OK;
+  }
   int64_t off = 0;
   for (int e = 0; e < NE; ++e) {
     const int me = cnt[e];
@@ -726,15 +768,20 @@ static hol_status moe_backward(hol_model* m, const W& w, const Act& A, int T, fl
   const int64_t E = m->E, Tk = (int64_t)T * k;
   hipStream_t s = m->sc;
   const std::vector<int32_t>& cnt = m->act_counts[pos];
-  const bool tr_w = m->base_trainable;
+  const bool tr_w = m->base_trainable, grp = m->moe_grp;
+  const uint8_t* wt = (const uint8_t*)m->wT;
   KT(KC_OTHER, 0, (double)Tk * H * (4 + 4 + E), launch_moe_combine_bwd(m->dh, A.yp, A.w, A.slot_pos, T, k, H, m->dwr, m->dyp, dt, s));
   if (tr_w) KT(KC_SWIGLU, 0, 3.0 * Tk * Fe * E, launch_swiglu_fwd(A.gup, m->ap, dt, (int)Tk, Fe, s));
+  // dA = dY W_down,e: B_e = (W_down,e)^T, columns e H .. e H + H - 1 of the stacked transpose
+  if (grp)
+    KCHECK(run_grouped(m, grouped(m, A, Tk, Fe, H, m->dyp, H, wt + m->t_edown, (int64_t)NE * H, H, m->dap, Fe, dt, EPI_STORE)));
   int64_t off = 0;
   for (int e = 0; e < NE; ++e) {
-    const int me = cnt[e];
+    const int me = grp && !tr_w ? 0 : cnt[e];
     const uint8_t* dY = (const uint8_t*)m->dyp + off * H * E;
     const uint8_t* Wd = (const uint8_t*)w.edown + (int64_t)e * H * Fe * E;
-    if (me > 0) KCHECK(run_gemm(m, gemm(me, Fe, H, dY, H, false, Wd, Fe, true, (uint8_t*)m->dap + off * Fe * E, Fe, dt, dt, EPI_STORE)));
+    if (me > 0 && !grp)
+      KCHECK(run_gemm(m, gemm(me, Fe, H, dY, H, false, Wd, Fe, true, (uint8_t*)m->dap + off * Fe * E, Fe, dt, dt, EPI_STORE)));
     if (tr_w) {
       float* gWd = G + m->g_edown + (int64_t)e * H * Fe;
       if (me > 0) {
@@ -749,12 +796,19 @@ static hol_status moe_backward(hol_model* m, const W& w, const Act& A, int T, fl
   }
   KT(KC_SWIGLU, 0, 5.0 * Tk * Fe * E, launch_swiglu_bwd(m->dap, A.gup, m->dgup, dt, (int)Tk, Fe, s));
   if (tr_w) KT(KC_OTHER, 0, 2.0 * Tk * H * E, launch_moe_gather(A.n2, dt, A.perm_slot, k, Tk, H, m->xp, s));
+  // dX = dG W_gate,e + dU W_up,e: B_e = (W_gate,e)^T, columns e Fe .. e Fe + Fe - 1 of [H, E Fe]
+  if (grp) {
+    KCHECK(run_grouped(m, grouped(m, A, Tk, H, Fe, m->dgup, 2 * Fe, wt + m->t_egate, (int64_t)NE * Fe, Fe, m->dxp, H,
+                                  DT_F32, EPI_STORE)));
+    KCHECK(run_grouped(m, grouped(m, A, Tk, H, Fe, (const uint8_t*)m->dgup + Fe * E, 2 * Fe, wt + m->t_eup, (int64_t)NE * Fe,
+                                  Fe, m->dxp, H, DT_F32, EPI_ACCUM)));
+  }
   off = 0;
   for (int e = 0; e < NE; ++e) {
-    const int me = cnt[e];
+    const int me = grp && !tr_w ? 0 : cnt[e];
     const uint8_t* dGU = (const uint8_t*)m->dgup + off * 2 * Fe * E;
     const int64_t wo = (int64_t)e * Fe * H * E;
-    if (me > 0) {
+    if (me > 0 && !grp) {
       KCHECK(run_gemm(m, gemm(me, H, Fe, dGU, 2 * Fe, false, (const uint8_t*)w.egate + wo, H, true, m->dxp + off * H, H, dt,
                               DT_F32, EPI_STORE)));
       KCHECK(run_gemm(m, gemm(me, H, Fe, dGU + Fe * E, 2 * Fe, false, (const uint8_t*)w.eup + wo, H, true, m->dxp + off * H,
@@ -853,6 +907,12 @@ static hol_status transpose_layer_weights(hol_model* m, const W& w) {
   uint8_t* t = (uint8_t*)m->wT;
   KCHECK(tr(m, w.wqkv, H, t + m->o_wqkv, QKV, QKV, H));
   KCHECK(tr(m, w.wo, nqd, t + m->o_wo, H, H, nqd));
+  if (m->moe_grp) {
+    const int NE = m->NE, Fe = m->Fe;
+    KCHECK(tr(m, w.egate, H, t + m->t_egate, NE * Fe, NE * Fe, H));  // [E Fe, H] -> [H, E Fe]
+    KCHECK(tr(m, w.eup, H, t + m->t_eup, NE * Fe, NE * Fe, H));
+    KCHECK(tr(m, w.edown, Fe, t + m->t_edown, NE * H, NE * H, Fe));  // [E H, Fe] -> [Fe, E H]
+  }
   if (m->NE > 0) return HOL_OK;
   KCHECK(tr(m, w.wgu, H, t + m->o_wgu, 2 * F, 2 * F, H));
   KCHECK(tr(m, w.wd, F, t + m->o_wd, H, H, F));

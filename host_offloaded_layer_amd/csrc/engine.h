@@ -50,6 +50,7 @@ struct Act {
   int32_t* perm_slot = nullptr; // [T k] slot of each routed row
   void* gup = nullptr;          // [T k, 2 Fe] expert gate | up outputs
   float* yp = nullptr;          // [T k, H] expert outputs (fp32)
+  int32_t* mtab = nullptr;      // [2 E + 2] expert row offsets and 256-row tile offsets
 };
 
 enum OpKind { OP_FWD = 0, OP_RECOMP = 1, OP_BWD = 2, OP_HEAD = 3 };
@@ -112,6 +113,10 @@ struct hol_model {
   int64_t g_wqkv = -1, g_wo = -1, g_wgu = -1, g_wd = -1, g_g1 = -1, g_g2 = -1;
   int64_t g_router = -1, g_egate = -1, g_eup = -1, g_edown = -1, g_lA[4] = {-1, -1, -1, -1}, g_lB[4] = {-1, -1, -1, -1};
   int64_t wT_bytes = 0;  // bytes of the layer image the bf16 backward transposes
+  // bf16 MoE with 64-aligned widths: one grouped launch per expert product; the backward's data
+  // gradients read the experts transposed, stacked: gate and up [H, E Fe], down [Fe, E H]
+  bool moe_grp = false;
+  int64_t t_egate = 0, t_eup = 0, t_edown = 0;  // byte offsets of those in wT
 
   // pinned host staging
   float* h_stage = nullptr;      // [Tmax, H] embedding rows up / first-layer gradient down
@@ -133,8 +138,10 @@ struct hol_model {
   uint8_t* act_mem = nullptr;
   int64_t act_stride = 0;
   int64_t ao_hin = 0, ao_r1 = 0, ao_n1 = 0, ao_qkv = 0, ao_o = 0, ao_lse = 0, ao_h1 = 0, ao_r2 = 0, ao_n2 = 0,
-          ao_gu = 0, ao_a = 0, ao_probs = 0, ao_ids = 0, ao_w = 0, ao_slot = 0, ao_perm = 0, ao_gup = 0, ao_yp = 0;
+          ao_gu = 0, ao_a = 0, ao_probs = 0, ao_ids = 0, ao_w = 0, ao_slot = 0, ao_perm = 0, ao_gup = 0, ao_yp = 0,
+          ao_mtab = 0;
   // mixture of experts: per activation-store position, the host copy of the expert row counts
+  // (read only where per-expert launches need them: fp32 compute, expert weight gradients)
   std::vector<std::vector<int32_t>> act_counts;
   float* mlogits = nullptr;                       // router logits fp32 [T, E]
   int32_t *mcounts = nullptr, *moffsets = nullptr, *mperm = nullptr;

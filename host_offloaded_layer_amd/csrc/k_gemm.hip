@@ -546,25 +546,62 @@ static bool n3_buffer_ok(const Gemm& g) {
   return g.batch == 1 && ea < (1ull << 32) && eb < (1ull << 32);
 }
 
-template <int EPI, typename TO, int NW, bool BUF>
+// GRP: one launch over groups of rows (the experts of a mixture-of-experts layer). The table gives
+// each group's first row and first row tile; the grid is an upper bound, the real tile count is
+// read from the table, dealt in 8 equal contiguous ranges (one per XCD) with the surplus blocks
+// leaving at once, and a block finds its group by binary search over the row-tile offsets.
+template <int EPI, typename TO, int NW, bool BUF, bool GRP>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * N3_TILE];
-  const int M = g.M, N = g.N, K = g.K;
+  int M = g.M;
+  const int N = g.N, K = g.K;
   const int z = blockIdx.y;
   const bf16* __restrict__ A = (const bf16*)g.A + z * g.sA;
   const bf16* __restrict__ B = (const bf16*)g.B + z * g.sB;
-  const int tiles_m = (M + N2_BM - 1) / N2_BM, tiles_n = (N + N2_BN - 1) / N2_BN;
-  const int ntiles = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-  const int GM = 4;
-  const int group = GM * tiles_n;
-  const int first_m = (pid / group) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (pid % group) % gsz;
-  const int tn = (pid % group) / gsz;
-  const int m0 = tm * N2_BM, n0 = tn * N2_BN;
+  TO* C = (TO*)g.C + z * g.sC;
+  const float* R = g.R ? g.R + z * g.sR : nullptr;
+  const int tiles_n = (N + N2_BN - 1) / N2_BN;
+  int m0, n0;
+  if constexpr (GRP) {
+    const int G = g.ngroups;
+    const int32_t* roff = g.grp;
+    const int32_t* toff = g.grp + G + 1;
+    const int total = toff[G] * tiles_n;
+    const int per = (total + 7) >> 3;
+    const int i = blockIdx.x >> 3;
+    if (i >= per) return;
+    const int lp = (blockIdx.x & 7) * per + i;
+    if (lp >= total) return;
+    const int rt = lp / tiles_n, tn = lp - rt * tiles_n;
+    int lo = 0, hi = G;  // toff[lo] <= rt < toff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (toff[mid] <= rt) lo = mid;
+      else hi = mid;
+    }
+    const int r0 = roff[lo];
+    M = roff[lo + 1] - r0;
+    A += (int64_t)r0 * g.lda;
+    B = (const bf16*)g.B + (int64_t)lo * g.sB;
+    C += (int64_t)r0 * g.ldc;
+    if (R) R += (int64_t)r0 * g.ldr;
+    m0 = (rt - toff[lo]) * N2_BM;
+    n0 = tn * N2_BN;
+  } else {
+    const int tiles_m = (M + N2_BM - 1) / N2_BM;
+    const int ntiles = tiles_m * tiles_n;
+    int pid = blockIdx.x;
+    if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+    const int GM = 4;
+    const int group = GM * tiles_n;
+    const int first_m = (pid / group) * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int tm = first_m + (pid % group) % gsz;
+    const int tn = (pid % group) / gsz;
+    m0 = tm * N2_BM;
+    n0 = tn * N2_BN;
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w / (NW / 2), wn = w % (NW / 2);
   f32x16 acc[4][WJ];
@@ -631,8 +668,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 
   // epilogue: acc[i][j][4 q + e] is C[row][col + e], row = m0 + 128 wm + 32 i + lane % 32,
   // col = n0 + 32 WJ wn + 32 j + 8 q + 4 (lane / 32)
-  TO* C = (TO*)g.C + z * g.sC;
-  const float* R = g.R ? g.R + z * g.sR : nullptr;
   constexpr int VB = 4 * (int)sizeof(TO);
   const bool vec = g.ldc % 4 == 0 && (uintptr_t)C % VB == 0 &&
                    (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
@@ -683,28 +718,81 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 constexpr int NT3_WAVES = 8;
 // (explicit instantiations: the host pass does not always emit the launch stubs of the
 // buffer-path instantiations on its own)
-template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true>(Gemm);
-template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true>(Gemm);
-template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, true>(Gemm);
-template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, true>(Gemm);
-template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, false>(Gemm);
-template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false>(Gemm);
-template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, false>(Gemm);
-template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, false>(Gemm);
-template <int EPI, typename TO>
+#define HOL_NT3_INST(GRP)                                                           \
+  template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, GRP>(Gemm);  \
+  template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, GRP>(Gemm);   \
+  template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, true, GRP>(Gemm);  \
+  template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, true, GRP>(Gemm);  \
+  template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, false, GRP>(Gemm); \
+  template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, GRP>(Gemm);  \
+  template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, false, GRP>(Gemm); \
+  template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, false, GRP>(Gemm);
+HOL_NT3_INST(false)
+HOL_NT3_INST(true)
+#undef HOL_NT3_INST
+
+template <int EPI, typename TO, bool GRP>
 static int launch_nt3_t(const Gemm& g, hipStream_t s) {
-  const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
+  const int tn = (g.N + N2_BN - 1) / N2_BN;
+  // grouped: an upper bound of the tile count rounded up to the 8 XCD ranges
+  const int tiles = GRP ? (int)((((int64_t)g.grp_max_rt * tn) + 7) / 8 * 8) : ((g.M + N2_BM - 1) / N2_BM) * tn;
+  if (tiles <= 0) return 0;
   if (n3_buffer_ok(g))
-    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
+    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true, GRP>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, false>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
+    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, false, GRP>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
   return (int)hipGetLastError();
 }
 
+template <bool GRP>
 static int launch_nt3(const Gemm& g, hipStream_t s) {
-  if (g.epi == EPI_STORE) return g.c == DT_BF16 ? launch_nt3_t<EPI_STORE, bf16>(g, s) : launch_nt3_t<EPI_STORE, float>(g, s);
-  if (g.epi == EPI_ACCUM) return launch_nt3_t<EPI_ACCUM, float>(g, s);
-  return launch_nt3_t<EPI_RESID, float>(g, s);
+  if (g.epi == EPI_STORE)
+    return g.c == DT_BF16 ? launch_nt3_t<EPI_STORE, bf16, GRP>(g, s) : launch_nt3_t<EPI_STORE, float, GRP>(g, s);
+  if (g.epi == EPI_ACCUM) return launch_nt3_t<EPI_ACCUM, float, GRP>(g, s);
+  return launch_nt3_t<EPI_RESID, float, GRP>(g, s);
+}
+
+int launch_gemm_grouped(const Gemm& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.grp_max_rt <= 0) return 0;
+  if (!g.grp || g.ngroups <= 0 || g.batch != 1 || g.ab != DT_BF16 || (g.bt >= 0 && g.bt != DT_BF16) || g.a_km ||
+      g.b_kn || g.K <= 0 || g.K % N3_BK != 0 || g.lda % 8 || g.ldb % 8 || g.sB % 8 ||
+      (((uintptr_t)g.A | (uintptr_t)g.B) % 16))
+    return (int)hipErrorInvalidValue;
+  if (g.epi != EPI_STORE && g.c != DT_F32) return (int)hipErrorInvalidValue;
+  if (g.epi == EPI_RESID && !g.R) return (int)hipErrorInvalidValue;
+  return launch_nt3<true>(g, s);
+}
+
+// Exclusive prefix sums of the group sizes and of their 256-row tile counts (one block).
+__global__ __launch_bounds__(512) void gemm_group_table_k(const int32_t* __restrict__ counts, int G,
+                                                          int32_t* __restrict__ tab) {
+  __shared__ int32_t sr[512], st[512];
+  const int t = threadIdx.x;
+  const int c = t < G ? counts[t] : 0;
+  sr[t] = c;
+  st[t] = (c + GEMM_GROUP_BM - 1) / GEMM_GROUP_BM;
+  __syncthreads();
+  for (int o = 1; o < 512; o <<= 1) {
+    const int a = t >= o ? sr[t - o] : 0, b = t >= o ? st[t - o] : 0;
+    __syncthreads();
+    sr[t] += a;
+    st[t] += b;
+    __syncthreads();
+  }
+  if (t < G) {
+    tab[t + 1] = sr[t];
+    tab[G + 2 + t] = st[t];
+  }
+  if (t == 0) {
+    tab[0] = 0;
+    tab[G + 1] = 0;
+  }
+}
+
+int launch_gemm_group_table(const int32_t* counts, int G, int32_t* tab, hipStream_t s) {
+  if (G <= 0 || G > 512) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_group_table_k, dim3(1), dim3(512), 0, s, counts, G, tab);
+  return (int)hipGetLastError();
 }
 
 constexpr int NT2_WAVES = 8;
@@ -752,7 +840,7 @@ int launch_gemm(const Gemm& g, hipStream_t s) {
                          (((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0) &&
                          (g.batch == 1 || (g.sA % 8 == 0 && g.sB % 8 == 0));
     if (aligned) {
-      if (!g.a_km && !g.b_kn && g.K % N3_BK == 0) return launch_nt3(g, s);
+      if (!g.a_km && !g.b_kn && g.K % N3_BK == 0) return launch_nt3<false>(g, s);
       if (!g.a_km && !g.b_kn && g.K % N2_BK == 0) return launch_nt2(g, s);
       if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
       if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);

@@ -34,8 +34,20 @@ struct Gemm {
   int batch = 1; int64_t sA = 0, sB = 0, sC = 0, sR = 0;
   int bt = -1;             // dtype of B when it differs from ab (fp32 adapter factors); -1: ab
   bool any_align = false;  // bf16 operands that miss the MFMA alignment take the tiled kernel
+  // grouped product (launch_gemm_grouped): `grp` is a device table from launch_gemm_group_table
+  // over `ngroups` groups; group e owns rows [grp[e], grp[e+1]) of A, C and R and uses B + e * sB.
+  // M bounds the total rows; grp_max_rt bounds the total 256-row tiles (sizes the grid).
+  const int32_t* grp = nullptr;
+  int ngroups = 0, grp_max_rt = 0;
 };
 int launch_gemm(const Gemm& g, hipStream_t s);
+// Row tile of the grouped product.
+constexpr int GEMM_GROUP_BM = 256;
+// Grouped bf16 NT product (K % 64 == 0, 16-byte aligned operands and leading dimensions).
+int launch_gemm_grouped(const Gemm& g, hipStream_t s);
+// tab[0..G]: exclusive prefix of counts (tab[G] = all rows); tab[G+1+e]: exclusive prefix of
+// ceil(counts / GEMM_GROUP_BM) (tab[2G+1] = all row tiles). G <= 512.
+int launch_gemm_group_table(const int32_t* counts, int G, int32_t* tab, hipStream_t s);
 
 // RMSNorm forward: y = x * rstd * gamma, rstd = 1/sqrt(mean(x^2)+eps). x fp32 [T,H].
 int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, DType yt,

@@ -40,6 +40,11 @@ MOE_LORA_BF16 = W.Workload("moe_lora_bf16",
                            batch=1, seq=256, n_micro=1, ckpt_every_k=2, compute="bf16", loss="sumsq",
                            weight_seed=68, token_seed=69, hidden_seed=70)
 
+MOE_FULL_BF16 = W.Workload("moe_full_bf16",
+                           W.ModelShape(2, 256, 4, 2, 64, vocab=512, n_experts=16, top_k=4, expert_ffn=128),
+                           batch=2, seq=128, n_micro=2, ckpt_every_k=2, compute="bf16", loss="ce",
+                           weight_seed=71, token_seed=72)
+
 
 def bf16_weights(params):
     """The low-precision copy the bf16 path computes with: base matrices rounded to bf16 (RNE);
@@ -123,6 +128,12 @@ def test_moe_lora_bf16_small_matches_oracle():
     run_parity(MOE_LORA_BF16, 1e-2, 2e-2, 0.05, ref_weights=bf16_weights)
 
 
+def test_moe_full_finetune_bf16_matches_oracle():
+    """bf16 full fine-tune: grouped expert products for the data gradients, per-expert launches
+    for the expert weight gradients."""
+    run_parity(MOE_FULL_BF16, 1e-2, 2e-2, 0.05, ref_weights=bf16_weights)
+
+
 def test_moe_lora_real_layer_shapes_matches_oracle():
     """The 235B-A22B layer (64/4 heads, 128 experts x 1536, top-8, LoRA r=16) with 2 layers and 256
     tokens: every kernel in the launch shape of the full slice."""
@@ -130,7 +141,7 @@ def test_moe_lora_real_layer_shapes_matches_oracle():
     run_parity(w, 1e-2, 2e-2, 0.05, ref_weights=bf16_weights)
 
 
-@pytest.mark.parametrize("w", [MOE_LORA_TINY, MOE_FULL_TINY, MOE_LORA_BF16], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [MOE_LORA_TINY, MOE_FULL_TINY, MOE_LORA_BF16, MOE_FULL_BF16], ids=lambda w: w.name)
 def test_moe_results_independent_of_k_bitwise(w):
     """The recompute permutes routed rows in a different order (atomics); every result must be
     bitwise the same for any checkpoint interval."""
