@@ -288,6 +288,16 @@ hol_status hol_op_rope(void* x, hol_dtype t, int64_t ld, int32_t T, int32_t head
                               (hipStream_t)stream), "hol_op_rope");
 }
 
+hol_status hol_op_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int32_t T, int32_t nq,
+                           int32_t nkv, int32_t d, int32_t S, const float* cos_t, const float* sin_t,
+                           void* stream) {
+  if (d % 2 || d <= 0 || nq < 0 || nkv < 0 || S <= 0) return einval("hol_op_rope_qkv", "bad head shape");
+  if (ldi < (int64_t)(nq + 2 * nkv) * d || ldo < (int64_t)(nq + 2 * nkv) * d)
+    return einval("hol_op_rope_qkv", "row stride below the projection width");
+  return launched(launch_rope_qkv(in, ldi, out, ldo, T, nq, nkv, d, S, cos_t, sin_t, (hipStream_t)stream),
+                  "hol_op_rope_qkv");
+}
+
 hol_status hol_op_swiglu_fwd(const void* gu, void* a, hol_dtype t, int32_t T, int32_t F, void* stream) {
   return launched(launch_swiglu_fwd(gu, a, t == HOL_BF16 ? DT_BF16 : DT_F32, T, F, (hipStream_t)stream),
                   "hol_op_swiglu_fwd");

@@ -94,8 +94,71 @@ int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, D
   return (int)hipGetLastError();
 }
 
-constexpr int RMS_BWD_BLOCKS = 256;
+constexpr int RMS_BWD_BLOCKS = 1024;
 int rmsnorm_bwd_blocks(int T) { return T < RMS_BWD_BLOCKS * 4 ? (T + 3) / 4 : RMS_BWD_BLOCKS; }
+
+// Wide rows (H >= 1024): one block of 256 threads per row, 4 NV columns a thread (columns
+// 4 t + 1024 i), so a thread holds few registers and many waves share a CU; the row's dot
+// product is a block reduction through a double-buffered 4-float LDS array (one barrier a row).
+// A thread owns the same columns on every row, so its gain-gradient sums need no reduction.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_row_k(const float* __restrict__ dy, const float* __restrict__ x,
+                                                         const float* __restrict__ g, const float* __restrict__ rstd,
+                                                         float* __restrict__ dx, int accumulate,
+                                                         float* __restrict__ partial, int T, int H) {
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float4 dg[NV], gv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid * 4 + i * 1024;
+    dg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    gv[i] = j < H ? *(const float4*)(g + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  int par = 0;
+  for (int row = blockIdx.x; row < T; row += gridDim.x, par ^= 1) {
+    const float r = rstd[row];
+    const float* xr = x + (int64_t)row * H;
+    const float* dyr = dy + (int64_t)row * H;
+    float* dxr = dx + (int64_t)row * H;
+    float4 xv[NV], dv[NV], pv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tid * 4 + i * 1024;
+      const bool in = j < H;
+      xv[i] = in ? *(const float4*)(xr + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      dv[i] = in ? *(const float4*)(dyr + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pv[i] = in && accumulate ? *(const float4*)(dxr + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      dg[i].x += dv[i].x * xv[i].x * r; dg[i].y += dv[i].y * xv[i].y * r;
+      dg[i].z += dv[i].z * xv[i].z * r; dg[i].w += dv[i].w * xv[i].w * r;
+      dv[i].x *= gv[i].x; dv[i].y *= gv[i].y; dv[i].z *= gv[i].z; dv[i].w *= gv[i].w;
+      dot += (dv[i].x * xv[i].x + dv[i].y * xv[i].y + dv[i].z * xv[i].z + dv[i].w * xv[i].w) * r;
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) red[par][w] = dot;
+    __syncthreads();
+    dot = ((red[par][0] + red[par][1]) + (red[par][2] + red[par][3])) / (float)H;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tid * 4 + i * 1024;
+      if (j < H) {
+        float4 o;
+        o.x = r * (dv[i].x - xv[i].x * r * dot) + pv[i].x; o.y = r * (dv[i].y - xv[i].y * r * dot) + pv[i].y;
+        o.z = r * (dv[i].z - xv[i].z * r * dot) + pv[i].z; o.w = r * (dv[i].w - xv[i].w * r * dot) + pv[i].w;
+        *(float4*)(dxr + j) = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid * 4 + i * 1024;
+    if (j < H) *(float4*)(partial + (int64_t)blockIdx.x * H + j) = dg[i];
+  }
+}
 
 // Each block handles rows blockIdx.x*4 + wave, stepping by gridDim.x*4; NV = float4s per lane.
 template <int NV>
@@ -112,6 +175,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ d
     const float r = rstd[row];
     const float* xr = x + (int64_t)row * H;
     const float* dyr = dy + (int64_t)row * H;
+    float* dxr = dx + (int64_t)row * H;
     float4 xv[NV], dv[NV];
     float dot = 0.f;
 #pragma unroll
@@ -129,7 +193,6 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ d
       }
     }
     dot = wave_sum(dot) / (float)H;
-    float* dxr = dx + (int64_t)row * H;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int j = lane * 4 + i * 256;
@@ -152,12 +215,24 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ d
     partial[(int64_t)blockIdx.x * H + j] = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
 }
 
-__global__ void reduce_cols_add_k(const float* __restrict__ partial, int nb, int H, float* __restrict__ out) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= H) return;
+// out[j] += sum_b partial[b][j]: a block of 16 waves owns 64 columns (one per lane); wave w sums
+// rows w, w + 16, ..., then the 16 wave sums are added in a fixed order.
+__global__ __launch_bounds__(1024) void reduce_cols_add_k(const float* __restrict__ partial, int nb, int H,
+                                                          float* __restrict__ out) {
+  __shared__ float red[16][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += partial[(int64_t)b * H + j];
-  out[j] += s;
+  if (j < H)
+    for (int b = w; b < nb; b += 16) s += partial[(int64_t)b * H + j];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && j < H) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += red[i][lane];
+    out[j] += t;
+  }
 }
 
 int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd, float* dx_out,
@@ -165,6 +240,16 @@ int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, cons
   if (T <= 0) return 0;
   if (H % 4 || H > 4096) return (int)hipErrorInvalidValue;
   const int nb = rmsnorm_bwd_blocks(T);
+  if (H >= 1024) {
+#define RR(NVV)                                                                                       \
+  hipLaunchKernelGGL(rmsnorm_bwd_row_k<NVV>, dim3(nb), dim3(256), 0, s, dy, x, gamma, rstd, dx_out, \
+                     (int)accumulate, partial, T, H)
+    if (H <= 2048) RR(2);
+    else RR(4);
+#undef RR
+    if (dgamma_acc) hipLaunchKernelGGL(reduce_cols_add_k, dim3((H + 63) / 64), dim3(1024), 0, s, partial, nb, H, dgamma_acc);
+    return (int)hipGetLastError();
+  }
   const int nv = (H + 255) / 256;
 #define RB(NVV)                                                                                   \
   hipLaunchKernelGGL(rmsnorm_bwd_k<NVV>, dim3(nb), dim3(256), 0, s, dy, x, gamma, rstd, dx_out, \
@@ -175,7 +260,7 @@ int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, cons
   else if (nv <= 8) RB(8);
   else RB(16);
 #undef RB
-  if (dgamma_acc) hipLaunchKernelGGL(reduce_cols_add_k, dim3((H + 255) / 256), dim3(256), 0, s, partial, nb, H, dgamma_acc);
+  if (dgamma_acc) hipLaunchKernelGGL(reduce_cols_add_k, dim3((H + 63) / 64), dim3(1024), 0, s, partial, nb, H, dgamma_acc);
   return (int)hipGetLastError();
 }
 
@@ -214,6 +299,13 @@ int launch_rope(void* x, DType xt, int64_t ld, int T, int heads, int d, int S, c
 
 // RoPE fused with the cast of the projection output: in = fp32 [T, QKV] rows (q heads, k heads,
 // v heads), out = bf16 rows with q and k rotated; one rounding per element. One thread per pair.
+// One rotated pair, contraction off so that every RoPE kernel that calls it rounds the same way.
+__device__ __forceinline__ void rot_pair(float a, float b, float c, float s, float& x, float& y) {
+#pragma clang fp contract(off)
+  x = a * c - b * s;
+  y = b * c + a * s;
+}
+
 __global__ void rope_qkv_k(const float* __restrict__ in, int64_t ldi, bf16* __restrict__ out, int64_t ldo, int Tn,
                            int nq, int nkv, int d, int S, const float* __restrict__ cs, const float* __restrict__ sn) {
   const int half = d >> 1;
@@ -230,19 +322,60 @@ __global__ void rope_qkv_k(const float* __restrict__ in, int64_t ldi, bf16* __re
   const float a = r[j], b = r[j + half];
   if (h < nq + nkv) {
     const int p = (int)(t % S);
-    const float c = cs[(int64_t)p * half + j], s_ = sn[(int64_t)p * half + j];
-    o[j] = (bf16)(a * c - b * s_);
-    o[j + half] = (bf16)(b * c + a * s_);
+    float x, y;
+    rot_pair(a, b, cs[(int64_t)p * half + j], sn[(int64_t)p * half + j], x, y);
+    o[j] = (bf16)x;
+    o[j + half] = (bf16)y;
   } else {
     o[j] = (bf16)a;
     o[j + half] = (bf16)b;
   }
 }
 
+// Four consecutive pairs per thread (16-byte fp32 loads, 8-byte bf16 stores); the same rounding
+// as the one-pair kernel. Needs half % 4 == 0, 16-byte aligned input rows, 8-byte aligned output
+// rows and fewer than 2^31 units.
+__global__ __launch_bounds__(256) void rope_qkv4_k(const float* __restrict__ in, int64_t ldi, bf16* __restrict__ out,
+                                                   int64_t ldo, uint32_t units, uint32_t h4, uint32_t heads, int nrot,
+                                                   int d, int S, const float* __restrict__ cs,
+                                                   const float* __restrict__ sn) {
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= units) return;
+  const int half = d >> 1;
+  const uint32_t th = u / h4, j = (u - th * h4) * 4;
+  const uint32_t t = th / heads, h = th - t * heads;
+  const float* r = in + (int64_t)t * ldi + (int64_t)h * d;
+  bf16* o = out + (int64_t)t * ldo + (int64_t)h * d;
+  const float4 a = *(const float4*)(r + j), b = *(const float4*)(r + j + half);
+  bf16x4 x, y;
+  if ((int)h < nrot) {
+    const int64_t pc = (int64_t)(t % (uint32_t)S) * half + j;
+    const float4 c = *(const float4*)(cs + pc), s_ = *(const float4*)(sn + pc);
+    float xx, yy;
+    rot_pair(a.x, b.x, c.x, s_.x, xx, yy); x[0] = (bf16)xx; y[0] = (bf16)yy;
+    rot_pair(a.y, b.y, c.y, s_.y, xx, yy); x[1] = (bf16)xx; y[1] = (bf16)yy;
+    rot_pair(a.z, b.z, c.z, s_.z, xx, yy); x[2] = (bf16)xx; y[2] = (bf16)yy;
+    rot_pair(a.w, b.w, c.w, s_.w, xx, yy); x[3] = (bf16)xx; y[3] = (bf16)yy;
+  } else {
+    x[0] = (bf16)a.x; x[1] = (bf16)a.y; x[2] = (bf16)a.z; x[3] = (bf16)a.w;
+    y[0] = (bf16)b.x; y[1] = (bf16)b.y; y[2] = (bf16)b.z; y[3] = (bf16)b.w;
+  }
+  *(bf16x4*)(o + j) = x;
+  *(bf16x4*)(o + j + half) = y;
+}
+
 int launch_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int T, int nq, int nkv, int d, int S,
                     const float* cos_t, const float* sin_t, hipStream_t s) {
   const int64_t total = (int64_t)T * (nq + 2 * nkv) * (d / 2);
   if (total <= 0) return 0;
+  const int half = d / 2;
+  if (half % 4 == 0 && ldi % 4 == 0 && ldo % 4 == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 8 == 0 &&
+      (uintptr_t)cos_t % 16 == 0 && (uintptr_t)sin_t % 16 == 0 && total / 4 < (int64_t(1) << 31)) {
+    const uint32_t units = (uint32_t)(total / 4);
+    hipLaunchKernelGGL(rope_qkv4_k, dim3((units + 255) / 256), dim3(256), 0, s, in, ldi, (bf16*)out, ldo, units,
+                       (uint32_t)(half / 4), (uint32_t)(nq + 2 * nkv), nq + nkv, d, S, cos_t, sin_t);
+    return (int)hipGetLastError();
+  }
   hipLaunchKernelGGL(rope_qkv_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in, ldi, (bf16*)out, ldo, T,
                      nq, nkv, d, S, cos_t, sin_t);
   return (int)hipGetLastError();

@@ -48,6 +48,14 @@ hol_status hol_op_rope(void* x, hol_dtype t, int64_t ld, int32_t T, int32_t head
                        int32_t S, const float* cos_t, const float* sin_t, int32_t inverse,
                        void* stream);
 
+/* RoPE of the fused q | k | v projection output (the bf16 forward, MegaTrain summary page, the
+ * Attention block of the layer template): in is fp32 [T, (nq + 2 nkv) d] at row stride ldi;
+ * out (bf16, row stride ldo) receives q and k rotated at position t % S and v unchanged, each
+ * value rounded to bf16 once. d even; tables as for hol_op_rope. */
+hol_status hol_op_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int32_t T, int32_t nq,
+                           int32_t nkv, int32_t d, int32_t S, const float* cos_t, const float* sin_t,
+                           void* stream);
+
 /* SwiGLU: gu = [g | u] ([T, 2F]); a = silu(g) u ([T, F]). Backward: dgu = [dg | du]. */
 hol_status hol_op_swiglu_fwd(const void* gu, void* a, hol_dtype t, int32_t T, int32_t F, void* stream);
 hol_status hol_op_swiglu_bwd(const void* da, const void* gu, void* dgu, hol_dtype t, int32_t T,

@@ -13,6 +13,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import host_offloaded_layer_amd as hol  # noqa: E402
+from oracle import adam as OA  # noqa: E402
 from oracle import decoder as D  # noqa: E402
 
 DEV = "cuda"
@@ -139,9 +140,9 @@ def test_transpose_rejects_misaligned():
 
 
 # ------------------------------------------------------------------ RMSNorm
-@pytest.mark.parametrize("H,T,yt", [(64, 37, hol.F32), (4096, 300, hol.BF16), (2048, 1100, hol.F32),
-                                    (5000, 70, hol.BF16)])
-def test_rmsnorm_fwd_bwd(H, T, yt):
+@pytest.mark.parametrize("H,T,yt,acc", [(64, 37, hol.F32, 1), (4096, 300, hol.BF16, 1), (2048, 1100, hol.F32, 1),
+                                        (1540, 2500, hol.F32, 0), (3072, 5000, hol.BF16, 1), (5000, 70, hol.BF16, 1)])
+def test_rmsnorm_fwd_bwd(H, T, yt, acc):
     r = np.random.default_rng(H + T)
     x = r.standard_normal((T, H)).astype(np.float32) * 3
     g = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
@@ -163,13 +164,13 @@ def test_rmsnorm_fwd_bwd(H, T, yt):
         np.testing.assert_allclose(host(rs), rr, rtol=1e-6)
         np.testing.assert_allclose(host(y), ry, rtol=tol, atol=tol)
         return
-    hol.check(hol.lib.hol_op_rmsnorm_bwd(dyd.data_ptr(), xd.data_ptr(), gd.data_ptr(), rs.data_ptr(), dx.data_ptr(), 1,
+    hol.check(hol.lib.hol_op_rmsnorm_bwd(dyd.data_ptr(), xd.data_ptr(), gd.data_ptr(), rs.data_ptr(), dx.data_ptr(), acc,
                                          dgam.data_ptr(), ws.data_ptr(), T, H, None))
     sync()
     rdx, rdg = D.rmsnorm_bwd(dy.astype(np.float64), x.astype(np.float64), g.astype(np.float64), rr)
     np.testing.assert_allclose(host(rs), rr, rtol=1e-6)
     np.testing.assert_allclose(host(y), ry, rtol=tol, atol=tol)
-    np.testing.assert_allclose(host(dx), rdx + dx0, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(host(dx), rdx + (dx0 if acc else 0), rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(host(dgam), rdg + 0.5, rtol=1e-5, atol=1e-4)
 
 
@@ -199,6 +200,38 @@ def test_rope_fwd_and_inverse(dt):
         sync()
         np.testing.assert_allclose(host(xd), xin, atol=1e-5)
 
+
+
+@pytest.mark.parametrize("d,ldx", [(128, 0), (64, 8), (20, 4)])   # 4-pair kernel / one-pair kernel
+def test_rope_qkv_fused(d, ldx):
+    """q and k rotated, v copied, all rounded to bf16 once; with an input shifted by one float (not
+    16-byte aligned) the one-pair kernel runs and must give the same bits."""
+    S, nseq, nq, nkv = 37, 3, 4, 2
+    W_ = (nq + 2 * nkv) * d
+    ldi = W_ + ldx
+    T = nseq * S
+    r = np.random.default_rng(d)
+    x = (r.standard_normal((T, ldi)) * 2).astype(np.float32)
+    cos, sin = D.rope_tables(S, d, 10000.0, np.float32)
+    cd, sd = dev(cos), dev(sin)
+    outs = []
+    for shift in (0, 1):
+        buf = torch.zeros(T * ldi + 1, device=DEV)
+        buf[shift:shift + T * ldi].copy_(torch.as_tensor(x.reshape(-1)))
+        out = torch.zeros((T, W_), dtype=torch.bfloat16, device=DEV)
+        hol.check(hol.lib.hol_op_rope_qkv(buf[shift:].data_ptr(), ldi, out.data_ptr(), W_, T, nq, nkv, d, S,
+                                          cd.data_ptr(), sd.data_ptr(), None))
+        sync()
+        outs.append(out.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    got = OA.bf16_to_f32(outs[0].view(np.uint16)).reshape(T, W_).astype(np.float64)
+    for b in range(nseq):
+        blk = x[b * S:(b + 1) * S, :W_].astype(np.float64)
+        qk = blk[:, :(nq + nkv) * d].reshape(S, nq + nkv, d)
+        ref = D.rope(qk, cos.astype(np.float64), sin.astype(np.float64)).reshape(S, -1)
+        np.testing.assert_allclose(got[b * S:(b + 1) * S, :(nq + nkv) * d], ref, rtol=2 ** -8, atol=2 ** -8)
+        np.testing.assert_array_equal(got[b * S:(b + 1) * S, (nq + nkv) * d:],
+                                      OA.bf16_to_f32(OA.bf16_round(blk[:, (nq + nkv) * d:].astype(np.float32))).reshape(S, -1))
 
 # ------------------------------------------------------------------ SwiGLU
 @pytest.mark.parametrize("F", [344, 342])   # 8-wide kernel / one-element kernel
