@@ -107,6 +107,18 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; ex2(-inf) = 0
 
+// Block order: the grid is `per` units for each (sequence, kv head) pair, unit 0 of a pair the
+// longest. Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8); when the pairs split
+// evenly over the XCDs, each XCD takes a contiguous range of whole pairs, so the blocks it runs at
+// once stream the same tiles of one pair through its L2.
+__device__ __forceinline__ void pair_unit(int per, int npairs, int& pair, int& unit) {
+  const int nb = per * npairs;
+  int u = blockIdx.x;
+  if ((npairs & 7) == 0) u = (u & 7) * (nb >> 3) + (u >> 3);
+  pair = u / per;
+  unit = u - pair * per;
+}
+
 // Register-staged tiles: a thread's share of the next tile is fetched into registers while the
 // current tile is computed on, then written to LDS after the next barrier.
 // Natural layout, 16-byte chunks: chunk c = tid + 256 i is row c / (D/8), columns (c % (D/8)) * 8.
@@ -206,9 +218,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(Attn a) {
   __shared__ bf16 Vt[D * VP];
   const int S = a.S;
   const int nqt = (S + BQ - 1) / BQ;
-  const int qt = nqt - 1 - (int)blockIdx.x;  // longest (latest) query tiles first
-  const int h = blockIdx.y, seq = blockIdx.z;
-  const int kvh = h / (a.nq / a.nkv);
+  const int group = a.nq / a.nkv;
+  int pair, unit;
+  pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit);
+  const int qt = nqt - 1 - unit / group;  // longest (latest) query tiles first, the group's heads together
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
+  const int h = kvh * group + unit % group;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
   const int q0 = qt * BQ;
   const int qi = q0 + 32 * w + lq;  // this lane's query (column of every accumulator)
@@ -332,8 +347,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   __shared__ bf16 Vb[BKV * KP];  // leaves the registers to the accumulators and the prefetch)
   const int S = a.S;
   const int nkt = (S + BKV - 1) / BKV;
-  const int kt = nkt - 1 - (int)blockIdx.x;  // early keys see the most queries: schedule them first
-  const int kvh = blockIdx.y, seq = blockIdx.z;
+  int pair, kt;  // early keys see the most queries: key tile 0 of a pair first
+  pair_unit(nkt, a.nkv * a.n_seq, pair, kt);
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int group = a.nq / a.nkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
   const int k0 = kt * BKV;
@@ -356,11 +372,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   const int wave_kmin = k0 + 32 * w;
   const int nqt = (S + BQ - 1) / BQ;
   const int qt0 = k0 / BQ, nper = nqt - qt0, nit = group * nper;
-  // iteration it: q head kvh * group + it / nper, query tile qt0 + it % nper
+  // iteration it: query tile nqt - 1 - it / group (from the last down to the diagonal), q head
+  // kvh * group + it % group; every key tile of a pair walks the query tiles in the same order
   NatTile<BQ, D> qreg, greg;
   float lse_r = 0.f, dl_r = 0.f;
   auto fetch = [&](int it) {
-    const int h = kvh * group + it / nper, q0 = (qt0 + it % nper) * BQ, nq = min(BQ, S - q0);
+    const int h = kvh * group + it % group, q0 = (nqt - 1 - it / group) * BQ, nq = min(BQ, S - q0);
     const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
     const bf16* G = (const bf16*)a.dO + (int64_t)h * D;
     qreg.load(Q, a.ldq, base + q0, nq);
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   };
   fetch(0);
   for (int it = 0; it < nit; ++it) {
-    const int q0 = (qt0 + it % nper) * BQ;
+    const int q0 = (nqt - 1 - it / group) * BQ;
     {
       __syncthreads();
       qreg.store(Qs, KP);
@@ -462,9 +479,12 @@ __global__ __launch_bounds__(256, 1) void attn_dq_mfma(Attn a) {
   __shared__ bf16 Kt[D * TP];
   const int S = a.S;
   const int nqt = (S + BQ - 1) / BQ;
-  const int qt = nqt - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y, seq = blockIdx.z;
-  const int kvh = h / (a.nq / a.nkv);
+  const int group = a.nq / a.nkv;
+  int pair, unit;
+  pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit);
+  const int qt = nqt - 1 - unit / group;  // longest first, the group's heads together
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
+  const int h = kvh * group + unit % group;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
   const int q0 = qt * BQ;
   const int qi = q0 + 32 * w + lq;
@@ -579,7 +599,7 @@ bool attn_mfma_bwd_supported(const Attn& a) {
 }
 
 int launch_attn_fwd_mfma(const Attn& a, hipStream_t s) {
-  dim3 grid((a.S + 127) / 128, a.nq, a.n_seq);
+  dim3 grid((unsigned)(((a.S + 127) / 128) * a.nq * a.n_seq));
   if (a.d == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, a);
   return (int)hipGetLastError();
@@ -588,7 +608,7 @@ int launch_attn_fwd_mfma(const Attn& a, hipStream_t s) {
 int launch_attn_bwd_mfma(const Attn& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.n_seq * a.S * a.nq;
   hipLaunchKernelGGL(attn_delta_bf16, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  dim3 gk((a.S + 127) / 128, a.nkv, a.n_seq), gq((a.S + 127) / 128, a.nq, a.n_seq);
+  dim3 gk((unsigned)(((a.S + 127) / 128) * a.nkv * a.n_seq)), gq((unsigned)(((a.S + 127) / 128) * a.nq * a.n_seq));
   if (a.d == 128) {
     hipLaunchKernelGGL(attn_dkdv_mfma<128>, gk, dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_dq_mfma<128>, gq, dim3(256), 0, s, a);

@@ -287,6 +287,8 @@ def test_swiglu_vector_and_scalar_kernels_agree_bitwise(dt):
     (hol.F32, 100, 2, 4, 2, 64),
     (hol.BF16, 200, 1, 8, 2, 128),
     (hol.BF16, 130, 2, 4, 1, 128),
+    (hol.BF16, 260, 2, 16, 4, 128),   # 8 (sequence, kv head) pairs: whole pairs dealt to each XCD
+    (hol.BF16, 192, 8, 8, 1, 64),
 ])
 def test_attention_fwd_bwd(dt, S, nseq, nq, nkv, d):
     r = np.random.default_rng(S + nq)
