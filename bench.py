@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "qwen3_1p7b", "llama8b_16k", "qwen3_235b_slice", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats-out", default=None,
+                    help="write the library's statistics of the last timed step (device timeline included) "
+                         "to this JSON file")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -237,6 +240,9 @@ def main():
     fb_ms = float(np.mean([r[1]["fb_ms"] for r in recs]))
     step_ms = float(np.mean([r[2] for r in recs]))
     fb0 = recs[-1][1]
+    if args.stats_out:
+        with open(args.stats_out, "w") as f:
+            json.dump(fb0, f)
     kern = {}
     for c in fb0["kernels"]:
         ms = sum(r[1]["kernels"][c]["ms"] for r in recs)

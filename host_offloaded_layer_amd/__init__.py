@@ -40,7 +40,8 @@ class Config(C.Structure):
                 ("rope_base", C.c_float), ("rms_eps", C.c_float), ("ckpt_every_k", C.c_int32),
                 ("compute_dtype", C.c_int32), ("lr", C.c_float), ("beta1", C.c_float),
                 ("beta2", C.c_float), ("adam_eps", C.c_float), ("weight_decay", C.c_float),
-                ("device", C.c_int32), ("max_tokens", C.c_int32), ("max_seq", C.c_int32)]
+                ("device", C.c_int32), ("max_tokens", C.c_int32), ("max_seq", C.c_int32),
+                ("weight_slots", C.c_int32), ("grad_buffers", C.c_int32)]
 
 
 class Batch(C.Structure):
@@ -248,10 +249,10 @@ class Model:
 def make_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, *, ckpt_every_k=1,
                 compute_dtype=F32, max_tokens, max_seq, n_experts=0, top_k=0, expert_ffn=0,
                 lora_rank=0, lora_scale=1.0, rope_base=10000.0, rms_eps=1e-5, lr=1e-3, beta1=0.9,
-                beta2=0.999, adam_eps=1e-8, device=0) -> Config:
+                beta2=0.999, adam_eps=1e-8, device=0, weight_slots=0, grad_buffers=0) -> Config:
     return Config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_experts, top_k,
                   expert_ffn, lora_rank, lora_scale, rope_base, rms_eps, ckpt_every_k, compute_dtype,
-                  lr, beta1, beta2, adam_eps, 0.0, device, max_tokens, max_seq)
+                  lr, beta1, beta2, adam_eps, 0.0, device, max_tokens, max_seq, weight_slots, grad_buffers)
 
 
 # ------------------------------------------------------------------------------------------

@@ -103,6 +103,8 @@ static hol_status validate_config(const hol_config& c) {
   if (c.weight_decay != 0.f) return bad("weight_decay must be 0");
   if (c.max_tokens <= 0 || c.max_seq <= 0 || c.max_seq > c.max_tokens) return bad("max_tokens / max_seq");
   if (!(c.rms_eps > 0) || !(c.rope_base > 0)) return bad("rms_eps / rope_base");
+  if (c.weight_slots != 0 && (c.weight_slots < 2 || c.weight_slots > 8)) return bad("weight_slots must be 0 or 2..8");
+  if (c.grad_buffers != 0 && (c.grad_buffers < 2 || c.grad_buffers > 4)) return bad("grad_buffers must be 0 or 2..4");
   return HOL_OK;
 }
 
@@ -353,11 +355,11 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
 
   // ---- device plan
   auto D = [&](int64_t bytes) { return dev_alloc(m, align_up(bytes, 256), &st); };
-  m->slot[0] = (uint8_t*)D(m->layer_img_bytes);
-  m->slot[1] = (uint8_t*)D(m->layer_img_bytes);
+  m->nslots = c.weight_slots ? c.weight_slots : 4;
+  m->ngbuf = c.grad_buffers ? c.grad_buffers : 3;
+  for (int i = 0; i < m->nslots; ++i) m->slot[i] = (uint8_t*)D(m->layer_img_bytes);
   if (V > 0) m->head_dev = (uint8_t*)D(m->head_img_bytes);
-  m->gdev[0] = (float*)D(m->layer_flat_n * 4);
-  m->gdev[1] = (float*)D(m->layer_flat_n * 4);
+  for (int i = 0; i < m->ngbuf; ++i) m->gdev[i] = (float*)D(m->layer_flat_n * 4);
   if (V > 0) m->head_gdev = (float*)D(m->head_flat_n * 4);
   m->ckpt = (float*)D((int64_t)m->n_ckpt * T * H * 4);
   // activation block: K layers
@@ -466,13 +468,16 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking));
   HCHECK(hipStreamCreateWithFlags(&m->sh2d, hipStreamNonBlocking));
   HCHECK(hipStreamCreateWithFlags(&m->sd2h, hipStreamNonBlocking));
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < m->nslots; ++i) {
     HCHECK(hipEventCreateWithFlags(&m->ev_ready[i], hipEventDisableTiming));
     HCHECK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
+  }
+  for (int i = 0; i < m->ngbuf; ++i) {
     HCHECK(hipEventCreateWithFlags(&m->ev_gdone[i], hipEventDisableTiming));
     HCHECK(hipEventCreateWithFlags(&m->ev_gfree[i], hipEventDisableTiming));
   }
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   m->unit_tensors.assign(m->L + 2, {});
   for (int i = 0; i < (int)m->tensors.size(); ++i) {
     const TensorDesc& t = m->tensors[i];
@@ -494,13 +499,16 @@ void engine_destroy(hol_model* m) {
   if (m->sc) hipStreamSynchronize(m->sc);
   if (m->sh2d) hipStreamSynchronize(m->sh2d);
   if (m->sd2h) hipStreamSynchronize(m->sd2h);
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < hol_model::MAX_SLOTS; ++i) {
     if (m->ev_ready[i]) hipEventDestroy(m->ev_ready[i]);
     if (m->ev_free[i]) hipEventDestroy(m->ev_free[i]);
+  }
+  for (int i = 0; i < hol_model::MAX_GBUF; ++i) {
     if (m->ev_gdone[i]) hipEventDestroy(m->ev_gdone[i]);
     if (m->ev_gfree[i]) hipEventDestroy(m->ev_gfree[i]);
   }
   if (m->ev_head) hipEventDestroy(m->ev_head);
+  if (m->ev_h0) hipEventDestroy(m->ev_h0);
   for (auto e : m->tev)
     if (e) hipEventDestroy(e);
   for (auto e : m->kev)
@@ -1289,11 +1297,11 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   HSTEP(hipSetDevice(m->cfg.device));
   hipStream_t sc = m->sc, sh = m->sh2d, sd = m->sd2h;
   // initial event states: every buffer free
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < m->nslots; ++i) {
     HSTEP(hipEventRecord(m->ev_free[i], sc));
-    HSTEP(hipEventRecord(m->ev_gfree[i], sd));
+    m->slot_layer[i] = -1;
   }
-  m->slot_layer[0] = m->slot_layer[1] = -1;
+  for (int i = 0; i < m->ngbuf; ++i) HSTEP(hipEventRecord(m->ev_gfree[i], sd));
   m->tev_used = 0;
   m->krec.clear();
   auto tev = [&]() -> hipEvent_t { return m->tev[std::min<int>(m->tev_used++, (int)m->tev.size() - 1)]; };
@@ -1324,35 +1332,52 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   FusedWorker worker{m};
   if (fused) worker.start(kc, t_start);
 
-  // ---- weight streaming helpers
-  int last_slot = 1;  // so the first load goes to slot 0
-  std::vector<int> op_slot(ops.size(), -1);
-  auto ensure_loaded = [&](size_t j) -> hol_status {
-    const Op& op = ops[j];
-    if (op.kind == OP_HEAD) return HOL_OK;
-    for (int s = 0; s < 2; ++s)
-      if (m->slot_layer[s] == op.layer) {
-        op_slot[j] = s;
-        return HOL_OK;
+  // ---- weight streaming: the layer of each op sits in one of the nslots HBM slots. After binding
+  // op j, the transfer stream fills slots with the layers of the next nslots - 1 ops; a slot is
+  // reused only when no op from j up to the one being loaded needs its layer, and among those the
+  // one whose layer is needed furthest ahead (or never) goes first.
+  const int NS = m->nslots;
+  auto slot_of = [&](int layer) -> int {
+    for (int s = 0; s < NS; ++s)
+      if (m->slot_layer[s] == layer) return s;
+    return -1;
+  };
+  auto next_use = [&](int layer, size_t from) -> size_t {
+    for (size_t i = from; i < ops.size(); ++i)
+      if (ops[i].kind != OP_HEAD && ops[i].layer == layer) return i;
+    return ops.size();
+  };
+  // makes op k's layer resident while op j is the current op; *placed = false when no slot can
+  // be reused yet
+  auto ensure = [&](size_t j, size_t k, bool* placed = nullptr) -> hol_status {
+    const int layer = ops[k].layer;
+    if (placed) *placed = true;
+    if (slot_of(layer) >= 0) return HOL_OK;
+    int best = -1;
+    size_t best_use = 0;
+    for (int s = 0; s < NS; ++s) {
+      const size_t u = m->slot_layer[s] < 0 ? ops.size() + 1 : next_use(m->slot_layer[s], j);
+      if (u <= k) continue;
+      if (best < 0 || u > best_use) {
+        best = s;
+        best_use = u;
       }
-    const int s = last_slot ^ 1;
-    HCHECK(hipStreamWaitEvent(sh, m->ev_free[s], 0));
+    }
+    if (best < 0) {
+      if (placed) *placed = false;
+      return HOL_OK;
+    }
+    HCHECK(hipStreamWaitEvent(sh, m->ev_free[best], 0));
     hipEvent_t a = tev(), e = tev();
     HCHECK(hipEventRecord(a, sh));
-    HCHECK(hipMemcpyAsync(m->slot[s], image_block(m, op.layer), m->layer_img_bytes, hipMemcpyHostToDevice, sh));
+    HCHECK(hipMemcpyAsync(m->slot[best], image_block(m, layer), m->layer_img_bytes, hipMemcpyHostToDevice, sh));
     HCHECK(hipEventRecord(e, sh));
     spans.push_back({a, e, 0});
-    HCHECK(hipEventRecord(m->ev_ready[s], sh));
-    m->slot_layer[s] = op.layer;
-    op_slot[j] = s;
+    HCHECK(hipEventRecord(m->ev_ready[best], sh));
+    m->slot_layer[best] = layer;
     m->stats.h2d_bytes += (double)m->layer_img_bytes;
     m->stats.n_weight_streams++;
     return HOL_OK;
-  };
-  auto next_layer_op = [&](size_t j) -> size_t {
-    size_t k = j + 1;
-    while (k < ops.size() && ops[k].kind == OP_HEAD) ++k;
-    return k;
   };
   bool head_loaded = false;
   auto load_head = [&]() -> hol_status {
@@ -1368,10 +1393,13 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     return HOL_OK;
   };
 
-  STEP(ensure_loaded(0));
+  STEP(ensure(0, 0));
   gather_h0();
   HSTEP(hipMemcpyAsync(m->ckpt, m->h_stage, T64 * H * 4, hipMemcpyHostToDevice, sc));
   m->stats.h2d_bytes += (double)T64 * H * 4;
+  // further weight copies start after h0 is up: the first layer needs both
+  HSTEP(hipEventRecord(m->ev_h0, sc));
+  HSTEP(hipStreamWaitEvent(sh, m->ev_h0, 0));
   // embedding rows by token: occurrences of each token id in order of position (the scatter-add of
   // the first-layer gradient sums them in that order), and the rows no token touches
   std::vector<int32_t> tok_order;
@@ -1397,19 +1425,23 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   for (size_t j = 0; j < ops.size(); ++j) {
     const Op& op = ops[j];
     // bind
-    if (op.kind != OP_HEAD) {
-      if (op_slot[j] < 0) STEP(ensure_loaded(j));
-      last_slot = op_slot[j];
-    }
-    // prefetch the next layer's weights into the other slot (overlaps this op's compute)
+    if (op.kind != OP_HEAD && slot_of(op.layer) < 0) STEP(ensure(j, j));
+    // prefetch the layers of the next ops (overlaps this op's compute); the head's weights go up
+    // when the window reaches the head
     auto prefetch = [&]() -> hol_status {
-      const size_t k = next_layer_op(j);
-      if (k < ops.size()) {
-        hol_status r = ensure_loaded(k);
+      int ahead = 0;
+      for (size_t k = j + 1; k < ops.size() && ahead < NS - 1; ++k) {
+        if (ops[k].kind == OP_HEAD) {
+          const hol_status r = load_head();
+          if (r != HOL_OK) return r;
+          continue;
+        }
+        ++ahead;
+        bool placed = true;
+        const hol_status r = ensure(j, k, &placed);
         if (r != HOL_OK) return r;
+        if (!placed) break;
       }
-      // the head follows the last forward layer's prefetch on the transfer stream
-      if (op.kind == OP_FWD && op.layer >= L - 2) return load_head();
       return HOL_OK;
     };
     hipEvent_t ta = tev(), tb = tev();
@@ -1444,7 +1476,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       STEP(prefetch());
       continue;
     }
-    const int s = op_slot[j];
+    const int s = slot_of(op.layer);
     const W w = bind(m, m->slot[s]);
     HSTEP(hipStreamWaitEvent(sc, m->ev_ready[s], 0));
     // the next layer's weights go to the other slot while this op computes (issued first: a
@@ -1515,7 +1547,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
         worker.push(1 + op.layer);
       }
       m->stats.d2h_bytes += (double)m->layer_flat_n * 4;
-      gi ^= 1;
+      gi = (gi + 1) % m->ngbuf;
     }
     HSTEP(hipEventRecord(m->ev_free[s], sc));
   }
@@ -1588,9 +1620,11 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       m->stats.last_compute_end_ms = b2;
     }
   }
+  m->stats.timeline.clear();
   for (auto& sp : spans) {
-    float ms = 0.f;
+    float ms = 0.f, t0 = 0.f;
     if (hipEventElapsedTime(&ms, sp.a, sp.b) != hipSuccess) continue;
+    if (hipEventElapsedTime(&t0, spans[0].a, sp.a) == hipSuccess) m->stats.timeline.push_back({(float)sp.cls, t0, t0 + ms});
     switch (sp.cls) {
       case 0: m->stats.h2d_busy_ms += ms; break;
       case 1: m->stats.d2h_busy_ms += ms; break;
@@ -1738,6 +1772,9 @@ std::string stats_json(const hol_model* m) {
     << ",\"last_compute_end_ms\":" << s.last_compute_end_ms << ",\"units\":[";
   for (size_t i = 0; i < s.units.size(); ++i)
     o << (i ? "," : "") << "[" << (int)s.units[i][0] << "," << s.units[i][1] << "," << s.units[i][2] << "]";
+  o << "],\"timeline\":[";
+  for (size_t i = 0; i < s.timeline.size(); ++i)
+    o << (i ? "," : "") << "[" << (int)s.timeline[i][0] << "," << s.timeline[i][1] << "," << s.timeline[i][2] << "]";
   o << "]";
   static const char* names[KC_N] = {"gemm", "attn_fwd", "attn_bwd", "rmsnorm", "rope", "swiglu", "ce", "transpose", "other"};
   o << ",\"kernels\":{";

@@ -76,6 +76,9 @@ struct Stats {
   // device timeline (ms after the first weight copy starts): first compute op starts, last ends
   double first_compute_ms = 0, last_compute_end_ms = 0;
   std::vector<std::array<double, 3>> units;  // {unit, arrived, done}
+  // device spans of the call: {class (0 h2d, 1 d2h, 2 fwd, 3 recompute, 4 bwd, 5 head), start, end}
+  // in ms after the first weight copy starts
+  std::vector<std::array<float, 3>> timeline;
   int n_weight_streams = 0;
   int tokens = 0;
   KStat k[KC_N];
@@ -128,11 +131,14 @@ struct hol_model {
 
   // device
   hipStream_t sc = nullptr, sh2d = nullptr, sd2h = nullptr;
-  uint8_t* slot[2] = {nullptr, nullptr};
-  int slot_layer[2] = {-1, -1};
-  hipEvent_t ev_ready[2] = {}, ev_free[2] = {}, ev_gdone[2] = {}, ev_gfree[2] = {}, ev_head = nullptr;
+  static constexpr int MAX_SLOTS = 8, MAX_GBUF = 4;
+  int nslots = 2, ngbuf = 2;
+  uint8_t* slot[MAX_SLOTS] = {};
+  int slot_layer[MAX_SLOTS] = {};
+  hipEvent_t ev_ready[MAX_SLOTS] = {}, ev_free[MAX_SLOTS] = {}, ev_gdone[MAX_GBUF] = {}, ev_gfree[MAX_GBUF] = {},
+             ev_head = nullptr, ev_h0 = nullptr;
   uint8_t* head_dev = nullptr;
-  float* gdev[2] = {nullptr, nullptr};
+  float* gdev[MAX_GBUF] = {};
   float* head_gdev = nullptr;
   float* ckpt = nullptr;
   uint8_t* act_mem = nullptr;

@@ -107,16 +107,37 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; ex2(-inf) = 0
 
-// Block order: the grid is `per` units for each (sequence, kv head) pair, unit 0 of a pair the
-// longest. Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8); when the pairs split
-// evenly over the XCDs, each XCD takes a contiguous range of whole pairs, so the blocks it runs at
-// once stream the same tiles of one pair through its L2.
-__device__ __forceinline__ void pair_unit(int per, int npairs, int& pair, int& unit) {
-  const int nb = per * npairs;
-  int u = blockIdx.x;
-  if ((npairs & 7) == 0) u = (u & 7) * (nb >> 3) + (u >> 3);
-  pair = u / per;
-  unit = u - pair * per;
+// Block order: `per` units for each (sequence, kv head) pair, unit 0 of a pair the longest.
+// Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8), so that the blocks an XCD runs
+// at once stream the tiles of one pair through its L2:
+//   pairs a multiple of 8: each XCD takes a contiguous range of whole pairs;
+//   pairs dividing 8 (r = 8 / pairs XCDs a pair): XCD x serves pair x / r, units x % r + r j;
+//   otherwise: plain order.
+// Returns false for the surplus blocks of the second case (the grid is rounded up to 8 r units).
+__host__ __device__ __forceinline__ unsigned pair_grid(int per, int npairs) {
+  if (npairs % 8 != 0 && 8 % npairs == 0) {
+    const int r = 8 / npairs;
+    return 8u * (unsigned)((per + r - 1) / r);
+  }
+  return (unsigned)(per * npairs);
+}
+__device__ __forceinline__ bool pair_unit(int per, int npairs, int& pair, int& unit) {
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  if ((npairs & 7) == 0) {
+    const int u = x * ((per * npairs) >> 3) + j;
+    pair = u / per;
+    unit = u - pair * per;
+    return true;
+  }
+  if (8 % npairs == 0) {
+    const int r = 8 / npairs;
+    pair = x / r;
+    unit = x % r + r * j;
+    return unit < per;
+  }
+  pair = blockIdx.x / per;
+  unit = blockIdx.x - pair * per;
+  return true;
 }
 
 // Register-staged tiles: a thread's share of the next tile is fetched into registers while the
@@ -220,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(Attn a) {
   const int nqt = (S + BQ - 1) / BQ;
   const int group = a.nq / a.nkv;
   int pair, unit;
-  pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit);
+  if (!pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit)) return;
   const int qt = nqt - 1 - unit / group;  // longest (latest) query tiles first, the group's heads together
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int h = kvh * group + unit % group;
@@ -348,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
   const int S = a.S;
   const int nkt = (S + BKV - 1) / BKV;
   int pair, kt;  // early keys see the most queries: key tile 0 of a pair first
-  pair_unit(nkt, a.nkv * a.n_seq, pair, kt);
+  if (!pair_unit(nkt, a.nkv * a.n_seq, pair, kt)) return;
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int group = a.nq / a.nkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
@@ -481,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_mfma(Attn a) {
   const int nqt = (S + BQ - 1) / BQ;
   const int group = a.nq / a.nkv;
   int pair, unit;
-  pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit);
+  if (!pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit)) return;
   const int qt = nqt - 1 - unit / group;  // longest first, the group's heads together
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int h = kvh * group + unit % group;
@@ -599,7 +620,7 @@ bool attn_mfma_bwd_supported(const Attn& a) {
 }
 
 int launch_attn_fwd_mfma(const Attn& a, hipStream_t s) {
-  dim3 grid((unsigned)(((a.S + 127) / 128) * a.nq * a.n_seq));
+  dim3 grid(pair_grid(((a.S + 127) / 128) * (a.nq / a.nkv), a.nkv * a.n_seq));
   if (a.d == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, a);
   return (int)hipGetLastError();
@@ -608,7 +629,8 @@ int launch_attn_fwd_mfma(const Attn& a, hipStream_t s) {
 int launch_attn_bwd_mfma(const Attn& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.n_seq * a.S * a.nq;
   hipLaunchKernelGGL(attn_delta_bf16, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  dim3 gk((unsigned)(((a.S + 127) / 128) * a.nkv * a.n_seq)), gq((unsigned)(((a.S + 127) / 128) * a.nq * a.n_seq));
+  dim3 gk(pair_grid((a.S + 127) / 128, a.nkv * a.n_seq)),
+      gq(pair_grid(((a.S + 127) / 128) * (a.nq / a.nkv), a.nkv * a.n_seq));
   if (a.d == 128) {
     hipLaunchKernelGGL(attn_dkdv_mfma<128>, gk, dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_dq_mfma<128>, gq, dim3(256), 0, s, a);

@@ -77,6 +77,12 @@ typedef struct {
   int32_t device;             /* HIP device ordinal */
   int32_t max_tokens;         /* largest batch*seq passed to forward_backward (sizes the HBM plan) */
   int32_t max_seq;            /* longest sequence (sizes the RoPE table) */
+  int32_t weight_slots;       /* HBM slots of the weight ring, 2..8; 0: 4. Two is the pages'
+                               * double buffer; more let the transfer stream run ahead of the
+                               * compute where the compute is the longer of the two. Results do
+                               * not depend on it. */
+  int32_t grad_buffers;       /* HBM layer-gradient buffers awaiting the device->host copy, 2..4;
+                               * 0: 3. Results do not depend on it. */
 } hol_config;
 
 /* One forward_backward input. tokens: int32 [batch*seq] (vocab > 0); labels: int32

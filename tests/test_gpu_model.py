@@ -183,3 +183,24 @@ def test_fused_forward_backward_step_is_bitwise_fb_then_step(wname):
             for x, y in zip(sa[n], sb[n]):
                 assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
             assert not np.any(b.get_grad(n))
+
+
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
+def test_results_independent_of_weight_slots_and_grad_buffers_bitwise(wname):
+    """The weight ring depth and the number of gradient buffers only change when copies run:
+    two fused steps give the same loss, weights and Adam moments bit for bit."""
+    w = TINY if wname == "tiny" else BF16_SMALL
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+    runs = []
+    for slots, gbufs in ((2, 2), (3, 4), (8, 3), (0, 0)):
+        with lib_model(w, params, slots=slots, gbufs=gbufs) as m:
+            losses = [m.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True) for _ in range(2)]
+            st = m.stats()
+            runs.append((losses, _state(m), st["n_weight_streams"]))
+    print(wname, "weight streams per call by ring depth", [r[2] for r in runs])
+    for losses, state, _ in runs[1:]:
+        assert losses == runs[0][0]
+        for n in state:
+            for x, y in zip(state[n], runs[0][1][n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n

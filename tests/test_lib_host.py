@@ -103,7 +103,9 @@ def _tiny_cfg(**kw):
 
 @pytest.mark.parametrize("bad", [dict(n_q_heads=3, n_kv_heads=2), dict(head_dim=15), dict(hidden=60),
                                  dict(ffn=170, compute_dtype=hol.BF16), dict(ckpt_every_k=0),
-                                 dict(max_seq=100), dict(vocab=250, compute_dtype=hol.BF16), dict(ffn=0)])
+                                 dict(max_seq=100), dict(vocab=250, compute_dtype=hol.BF16), dict(ffn=0),
+                                 dict(weight_slots=1), dict(weight_slots=9), dict(grad_buffers=1),
+                                 dict(grad_buffers=5)])
 def test_create_rejects_bad_config_before_touching_device(bad):
     h = C.c_void_p()
     cfg = _tiny_cfg(**bad)
