@@ -77,10 +77,12 @@ typedef struct {
   int32_t device;             /* HIP device ordinal */
   int32_t max_tokens;         /* largest batch*seq passed to forward_backward (sizes the HBM plan) */
   int32_t max_seq;            /* longest sequence (sizes the RoPE table) */
-  int32_t weight_slots;       /* HBM slots of the weight ring, 2..8; 0: 4. Two is the pages'
-                               * double buffer; more let the transfer stream run ahead of the
-                               * compute where the compute is the longer of the two. Results do
-                               * not depend on it. */
+  int32_t weight_slots;       /* HBM slots of the weight ring, 2..8; 0: min(8, max(4, K + 2)) for
+                               * K = ckpt_every_k. Two is the pages' double buffer; with K or more
+                               * a block's layers stay resident from its recompute through its
+                               * backward, and further slots let the transfer stream run ahead
+                               * where the compute is the longer of the two. Results do not
+                               * depend on it. */
   int32_t grad_buffers;       /* HBM layer-gradient buffers awaiting the device->host copy, 2..4;
                                * 0: 3. Results do not depend on it. */
 } hol_config;
