@@ -442,6 +442,8 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   if (m->dt == DT_BF16) {
     m->wT = D(m->wT_bytes);
     const int64_t Tc64 = V > 0 ? m->Tc : 0;
+    // the dW products read the upstream gradient and the activation transposed (the NT kernel
+    // with transposes measured as fast as the TN kernel reading them as stored, at these shapes)
     m->yT = D(std::max<int64_t>(T * std::max<int64_t>(2 * F, std::max<int64_t>(QKV, H)), Tc64 * V) * 2);
     m->xT = D(std::max<int64_t>(T * std::max<int64_t>(F, std::max<int64_t>(nqd, H)), Tc64 * H) * 2);
     if (V > 0) m->woutT = D(V * H * 2);
@@ -480,6 +482,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   }
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
+  for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   m->unit_tensors.assign(m->L + 2, {});
   for (int i = 0; i < (int)m->tensors.size(); ++i) {
     const TensorDesc& t = m->tensors[i];
@@ -511,6 +514,8 @@ void engine_destroy(hol_model* m) {
   }
   if (m->ev_head) hipEventDestroy(m->ev_head);
   if (m->ev_h0) hipEventDestroy(m->ev_h0);
+  for (auto e : m->ev_tail)
+    if (e) hipEventDestroy(e);
   for (auto e : m->tev)
     if (e) hipEventDestroy(e);
   for (auto e : m->kev)
@@ -1128,7 +1133,7 @@ static void host_accumulate(void* p) {
   });
 }
 
-static void adam_unit(hol_model* m, int u, const AdamConsts& k);
+static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1, int64_t hi = -1);
 static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k);
 
 // Host worker of the fused forward_backward + step: runs the optimiser on each unit as soon as
@@ -1160,15 +1165,24 @@ struct FusedWorker {
           u = m->unit_queue[next++];
         }
         if (u < 0) return;  // every unit handed over
+        const bool piece = u >= hol_model::TAIL_CODE;
         // unit L + 2: embedding rows no token of this call touches (their gradient is zero and
         // known from the start)
-        if (u != m->L + 2 && hipEventSynchronize(m->ev_unit[u]) != hipSuccess) {
+        hipEvent_t ev = piece ? m->ev_tail[u - hol_model::TAIL_CODE] : (u != m->L + 2 ? m->ev_unit[u] : nullptr);
+        if (ev && hipEventSynchronize(ev) != hipSuccess) {
           failed = true;
           return;
         }
         const double t0 = now_ms();
-        if (u == m->L + 2) adam_embed_rows(m, m->emb_untouched, kc);
-        else adam_unit(m, u, kc);
+        if (piece) {
+          const int c = u - hol_model::TAIL_CODE;
+          const int64_t n = m->layer_flat_n, f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * n;
+          adam_unit(m, m->tail_unit, kc, f0 + n * c / hol_model::N_TAIL, f0 + n * (c + 1) / hol_model::N_TAIL);
+        } else if (u == m->L + 2) {
+          adam_embed_rows(m, m->emb_untouched, kc);
+        } else {
+          adam_unit(m, u, kc);
+        }
         const double t1 = now_ms();
         busy_ms += t1 - t0;
         m->stats.units.push_back({(double)u, t0 - t_call, t1 - t_call});
@@ -1532,9 +1546,22 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       // gradient offload on the gradient-transfer stream
       HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
       float* lg = m->grad + m->layer_flat0 + (int64_t)op.layer * m->layer_flat_n;
+      const bool tail = fused && j + 1 == ops.size();
       hipEvent_t a = tev(), e = tev();
       HSTEP(hipEventRecord(a, sd));
-      HSTEP(hipMemcpyAsync(direct ? lg : m->grad_stage, m->gdev[gi], m->layer_flat_n * 4, hipMemcpyDeviceToHost, sd));
+      if (tail) {
+        // the call's last gradient: in pieces, each handed to the optimiser as it lands
+        m->tail_unit = 1 + op.layer;
+        const int64_t n = m->layer_flat_n;
+        for (int c = 0; c < hol_model::N_TAIL; ++c) {
+          const int64_t c0 = n * c / hol_model::N_TAIL, c1 = n * (c + 1) / hol_model::N_TAIL;
+          HSTEP(hipMemcpyAsync(lg + c0, m->gdev[gi] + c0, (size_t)(c1 - c0) * 4, hipMemcpyDeviceToHost, sd));
+          HSTEP(hipEventRecord(m->ev_tail[c], sd));
+          worker.push(hol_model::TAIL_CODE + c);
+        }
+      } else {
+        HSTEP(hipMemcpyAsync(direct ? lg : m->grad_stage, m->gdev[gi], m->layer_flat_n * 4, hipMemcpyDeviceToHost, sd));
+      }
       HSTEP(hipEventRecord(e, sd));
       spans.push_back({a, e, 1});
       if (!direct) {
@@ -1544,7 +1571,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
         HSTEP(hipLaunchHostFunc(sd, host_accumulate, &jobs[op.layer]));
       }
       HSTEP(hipEventRecord(m->ev_gfree[gi], sd));
-      if (fused) {
+      if (fused && !tail) {
         HSTEP(hipEventRecord(m->ev_unit[1 + op.layer], sd));
         worker.push(1 + op.layer);
       }
@@ -1560,10 +1587,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     m->stats.d2h_bytes += (double)T64 * H * 4;
   }
   HSTEP(hipMemcpyAsync(m->loss_stage, m->rowloss_dev, T64 * 4, hipMemcpyDeviceToHost, sc));
+  // the scatter-add below needs only the compute stream's copies; the last gradient copy may
+  // still run
   HSTEP(hipStreamSynchronize(sc));
   HSTEP(hipStreamSynchronize(sh));
-  HSTEP(hipStreamSynchronize(sd));
-  m->stats.gpu_done_ms = now_ms() - t_start;
   HSTEP(hipGetLastError());
   // embedding gradient: each touched row adds its tokens' first-layer gradients in position order
   // (rows split over threads: deterministic)
@@ -1588,6 +1615,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   *out = total;
   m->grads_zero = false;
   m->stats.scatter_done_ms = now_ms() - t_start;
+  HSTEP(hipStreamSynchronize(sd));
+  m->stats.gpu_done_ms = now_ms() - t_start;
   if (fused) {
     const double t_gpu_done = now_ms();
     worker.stop(false);
@@ -1659,17 +1688,23 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 // ------------------------------------------------------------------------------------------
 // Adam on every trainable tensor of optimiser unit u, refresh of its low-precision image, and
 // zeroing of its gradients.
-static void adam_unit(hol_model* m, int u, const AdamConsts& k) {
+// Adam (and the image refresh) on the trainable tensors of unit u, restricted to the flat
+// parameter range [lo, hi) when lo >= 0 (the same per-element arithmetic either way).
+static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int64_t hi) {
   for (int ti : m->unit_tensors[u]) {
     const TensorDesc& t = m->tensors[ti];
     if (!t.trainable) continue;
-    float* th = m->master + t.flat;
-    float* g = m->grad + t.flat;
-    float* m1 = m->mom1 + t.flat;
-    float* m2 = m->mom2 + t.flat;
+    const int64_t a0 = lo < 0 ? 0 : std::max<int64_t>(0, lo - t.flat);
+    const int64_t a1 = lo < 0 ? t.numel : std::min<int64_t>(t.numel, hi - t.flat);
+    if (a1 <= a0) continue;
+    float* th = m->master + t.flat + a0;
+    float* g = m->grad + t.flat + a0;
+    float* m1 = m->mom1 + t.flat + a0;
+    float* m2 = m->mom2 + t.flat + a0;
     const bool to_bf16 = !(t.img_f32 || m->dt == DT_F32) && t.img >= 0 && t.block != -2;
-    uint8_t* dst = (t.block == -2 || t.img < 0) ? nullptr : image_block(m, t.block) + t.img;
-    parallel_for(t.numel, 1 << 16, [&](int64_t lo, int64_t hi) {
+    uint8_t* dst = (t.block == -2 || t.img < 0) ? nullptr
+                                                : image_block(m, t.block) + t.img + a0 * (to_bf16 ? 2 : 4);
+    parallel_for(a1 - a0, 1 << 16, [&](int64_t lo, int64_t hi) {
       // chunked so the refreshed values are still in cache when converted
       for (int64_t a = lo; a < hi; a += 4096) {
         const int64_t n = std::min<int64_t>(4096, hi - a);

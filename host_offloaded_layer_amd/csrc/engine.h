@@ -206,6 +206,11 @@ struct hol_model {
   std::mutex fmu;
   std::condition_variable fcv;
   std::vector<int> unit_queue;         // units whose gradient copy has been enqueued, in order
+  // the last layer of a fused call copies its gradient in N_TAIL pieces, each handed to the
+  // worker on its own (queue code TAIL_CODE + piece), so its Adam overlaps the rest of the copy
+  static constexpr int N_TAIL = 4, TAIL_CODE = 1 << 20;
+  hipEvent_t ev_tail[N_TAIL] = {};
+  int tail_unit = -1;
   std::vector<int32_t> emb_touched, emb_untouched;  // embedding rows the call's tokens use / do not
   bool fused_abort = false;
   double fused_overlap_ms = 0, fused_tail_ms = 0;

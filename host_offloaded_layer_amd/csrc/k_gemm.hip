@@ -550,6 +550,59 @@ static bool n3_buffer_ok(const Gemm& g) {
 // each group's first row and first row tile; the grid is an upper bound, the real tile count is
 // read from the table, dealt in 8 equal contiguous ranges (one per XCD) with the surplus blocks
 // leaving at once, and a block finds its group by binary search over the row-tile offsets.
+// Epilogue of the 256 x 256 tiles: acc[i][j][4 q + e] is C[row][col + e], row = m0 + 128 wm +
+// 32 i + lane % 32, col = n0 + 32 WJ wn + 32 j + 8 q + 4 (lane / 32) (Cᵀ blocks, so a lane holds
+// 4 consecutive columns of one row per quad).
+template <int EPI, typename TO, int WJ>
+__device__ __forceinline__ void n3_store(const Gemm& g, const f32x16 (&acc)[4][WJ], TO* C, const float* R, int M,
+                                         int N, int m0, int n0, int wm, int wn, int lane) {
+  constexpr int VB = 4 * (int)sizeof(TO);
+  const bool vec = g.ldc % 4 == 0 && (uintptr_t)C % VB == 0 &&
+                   (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (row >= M) continue;
+    TO* crow = C + (int64_t)row * g.ldc;
+    const float* rrow = EPI == EPI_RESID ? R + (int64_t)row * g.ldr : nullptr;
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * 32 * WJ + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = g.alpha * acc[i][j][4 * q + e];
+        if (vec && col + 4 <= N) {
+          if constexpr (EPI == EPI_RESID) {
+            const float4 rv = *(const float4*)(rrow + col);
+            v[0] += rv.x; v[1] += rv.y; v[2] += rv.z; v[3] += rv.w;
+          }
+          if constexpr (sizeof(TO) == 4) {
+            if constexpr (EPI == EPI_ACCUM) {
+              const float4 cv = *(const float4*)(crow + col);
+              v[0] += cv.x; v[1] += cv.y; v[2] += cv.z; v[3] += cv.w;
+            }
+            *(float4*)(crow + col) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            *(bf16x4*)(crow + col) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= N) break;
+            float x = v[e];
+            if constexpr (EPI == EPI_ACCUM) x += to_f(crow[col + e]);
+            if constexpr (EPI == EPI_RESID) x += rrow[col + e];
+            crow[col + e] = from_f<TO>(x);
+          }
+        }
+      }
+  }
+}
+
 template <int EPI, typename TO, int NW, bool BUF, bool GRP>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
@@ -666,53 +719,181 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
     mma(a1, b1);
   }
 
-  // epilogue: acc[i][j][4 q + e] is C[row][col + e], row = m0 + 128 wm + 32 i + lane % 32,
-  // col = n0 + 32 WJ wn + 32 j + 8 q + 4 (lane / 32)
-  constexpr int VB = 4 * (int)sizeof(TO);
-  const bool vec = g.ldc % 4 == 0 && (uintptr_t)C % VB == 0 &&
-                   (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
+  n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, m0, n0, wm, wn, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// TN3: C = Aᵀ B with both operands stored K-major (A [K][M], B [K][N], row strides lda, ldb), the
+// layout of the weight-gradient products dW = dYᵀ X over saved activations, read as stored (no
+// transposes). The 256 x 256 x 64 block, 8 waves and 2-slot ring of NT3. A stage holds 64 k-rows
+// of 256 values (512 B) per operand, 16-byte chunk c of row k at physical chunk c ^ 4 (k mod 4).
+// An MFMA fragment (8 consecutive k of one m) is two ds_read_b64_tr_b16: within each 16-lane
+// group, lane 16 g + 4 a + b receives element b of the 8-byte pieces addressed by lanes
+// 16 g + a + 4 j (j = 0..3), so lane 16 g + a + 4 j addresses row k0 + j, columns
+// m0 + 16 (g mod 2) + 4 a .. + 3, and lane l ends with m = m0 + l mod 32, k = k0 + 0..3. The
+// swizzle keeps each half-wave's 4 rows x 64 bytes on distinct banks.
+// ------------------------------------------------------------------------------------------
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+
+typedef short tr8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ tr4_t tr_read(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr4_t*)p);
+}
+
+// fragment of 8 consecutive k: rows k0 .. k0 + 3 at p, k0 + 4 .. k0 + 7 four rows further
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* p) {
+  const tr4_t lo = tr_read(p), hi = tr_read(p + 4 * 256);
+  const tr8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// element offset, inside one operand's stage region, of this lane's transposed-read piece for
+// the 32-wide block at column c0, k-row offset 0 (add 256 k for row k)
+__device__ __forceinline__ int t3_frag_off(int c0, int lane) {
+  const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+  const int col = c0 + 16 * (g & 1) + 4 * a;
+  const int pc = (col >> 3) ^ (4 * j);
+  return (8 * (g >> 1) + j) * 256 + pc * 8 + (col & 4);
+}
+
+// Stage loads: instruction q = w + NW i fills stage rows 2 q, 2 q + 1 (1 KB) of an operand;
+// lane: row 2 q + lane / 32, physical chunk lane % 32 = logical chunk (lane % 32) ^ 4 (row % 4).
+// Columns past M (N) are clamped (their products land in rows that are not stored).
+template <int NW>
+struct T3Buf {
+  uint32_t va[32 / NW], vb[32 / NW];
+  __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
-    if (row >= M) continue;
-    TO* crow = C + (int64_t)row * g.ldc;
-    const float* rrow = EPI == EPI_RESID ? R + (int64_t)row * g.ldr : nullptr;
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int r = 2 * (w + NW * i) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (r & 3));
+      va[i] = (uint32_t)(((int64_t)r * lda + min(m0 + 8 * c, M - 8)) * 2);
+      vb[i] = (uint32_t)(((int64_t)r * ldb + min(n0 + 8 * c, N - 8)) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t sa,
+                                        uint32_t sb) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + (w + NW * i) * 512), 16, va[i], (int)sa, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + 64 * 256 + (w + NW * i) * 512), 16, vb[i],
+                                               (int)sb, 0, 0);
+  }
+};
+
+// Whether every byte of A and B lies within an unsigned 32-bit offset of its base.
+static bool t3_buffer_ok(const Gemm& g) {
+  const uint64_t ea = (uint64_t)g.K * (uint64_t)g.lda * 2, eb = (uint64_t)g.K * (uint64_t)g.ldb * 2;
+  return g.batch == 1 && ea < (1ull << 32) && eb < (1ull << 32);
+}
+
+template <int EPI, typename TO, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_tn3(Gemm g) {
+  constexpr int WJ = NW == 4 ? 4 : 2;
+  constexpr int RA = 64 * 256;  // elements of one operand's stage region
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * N3_TILE];
+  const int M = g.M, N = g.N, K = g.K;
+  const bf16* __restrict__ A = (const bf16*)g.A;
+  const bf16* __restrict__ B = (const bf16*)g.B;
+  TO* C = (TO*)g.C;
+  const float* R = g.R;
+  const int tiles_m = (M + N2_BM - 1) / N2_BM, tiles_n = (N + N2_BN - 1) / N2_BN;
+  const int ntiles = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+  const int GM = 4;
+  const int group = GM * tiles_n;
+  const int first_m = (pid / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % group) % gsz;
+  const int tn = (pid % group) / gsz;
+  const int m0 = tm * N2_BM, n0 = tn * N2_BN;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / (NW / 2), wn = w % (NW / 2);
+  f32x16 acc[4][WJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * 32 * WJ + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (col >= N) continue;
-        float v[4];
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  T3Buf<NW> tb;
+  tb.init(g.lda, m0, M, g.ldb, n0, N);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)K * g.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)K * g.ldb * 2), 0x00020000);
+  const uint32_t sa = (uint32_t)(g.lda * 2 * N3_BK), sb = (uint32_t)(g.ldb * 2 * N3_BK);  // bytes per stage
+  auto issue = [&](bf16* stage, int kt) { tb.issue(stage, ra, rb, kt * sa, kt * sb); };
+  int fa[4], fb[WJ];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = g.alpha * acc[i][j][4 * q + e];
-        if (vec && col + 4 <= N) {
-          if constexpr (EPI == EPI_RESID) {
-            const float4 rv = *(const float4*)(rrow + col);
-            v[0] += rv.x; v[1] += rv.y; v[2] += rv.z; v[3] += rv.w;
-          }
-          if constexpr (sizeof(TO) == 4) {
-            if constexpr (EPI == EPI_ACCUM) {
-              const float4 cv = *(const float4*)(crow + col);
-              v[0] += cv.x; v[1] += cv.y; v[2] += cv.z; v[3] += cv.w;
-            }
-            *(float4*)(crow + col) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-            *(bf16x4*)(crow + col) = o;
-          }
-        } else {
+  for (int i = 0; i < 4; ++i) fa[i] = t3_frag_off(wm * 128 + i * 32, lane);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (col + e >= N) break;
-            float x = v[e];
-            if constexpr (EPI == EPI_ACCUM) x += to_f(crow[col + e]);
-            if constexpr (EPI == EPI_RESID) x += rrow[col + e];
-            crow[col + e] = from_f<TO>(x);
-          }
-        }
-      }
+  for (int j = 0; j < WJ; ++j) fb[j] = RA + t3_frag_off(wn * 32 * WJ + j * 32, lane);
+
+  const int nk = K / N3_BK;
+  issue(lds, 0);
+  if (nk > 1) issue(lds + N3_TILE, 1);
+  bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
+  auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = tr_frag(st + fa[i] + kk * 16 * 256);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) b[j] = tr_frag(st + fb[j] + kk * 16 * 256);
+  };
+  auto mma = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  if (nk > 1) {
+    if constexpr (NW == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
+  frags(lds, 0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const bf16* st = lds + (kt & 1) * N3_TILE;
+    frags(st, 1, a1, b1);
+    mma(a0, b0);
+    frags(st, 2, a0, b0);
+    mma(a1, b1);
+    frags(st, 3, a1, b1);
+    mma(a0, b0);
+    if (kt + 1 < nk) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, kt + 2);
+      frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
+    }
+    mma(a1, b1);
+  }
+  n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, m0, n0, wm, wn, lane);
+}
+
+template __global__ void gemm_tn3<EPI_STORE, float, 8>(Gemm);
+template __global__ void gemm_tn3<EPI_STORE, bf16, 8>(Gemm);
+template __global__ void gemm_tn3<EPI_ACCUM, float, 8>(Gemm);
+template __global__ void gemm_tn3<EPI_RESID, float, 8>(Gemm);
+
+template <int EPI, typename TO>
+static int launch_tn3_t(const Gemm& g, hipStream_t s) {
+  const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
+  hipLaunchKernelGGL((gemm_tn3<EPI, TO, 8>), dim3(tiles), dim3(512), 0, s, g);
+  return (int)hipGetLastError();
+}
+
+static int launch_tn3(const Gemm& g, hipStream_t s) {
+  if (g.epi == EPI_STORE) return g.c == DT_BF16 ? launch_tn3_t<EPI_STORE, bf16>(g, s) : launch_tn3_t<EPI_STORE, float>(g, s);
+  if (g.epi == EPI_ACCUM) return launch_tn3_t<EPI_ACCUM, float>(g, s);
+  return launch_tn3_t<EPI_RESID, float>(g, s);
 }
 
 constexpr int NT3_WAVES = 8;
@@ -844,6 +1025,8 @@ int launch_gemm(const Gemm& g, hipStream_t s) {
       if (!g.a_km && !g.b_kn && g.K % N2_BK == 0) return launch_nt2(g, s);
       if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
       if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);
+      if (g.a_km && g.b_kn && g.K % N3_BK == 0 && g.M % 8 == 0 && g.N % 8 == 0 && t3_buffer_ok(g))
+        return launch_tn3(g, s);
       if (g.a_km && g.b_kn) return launch_mfma_l<true, true>(g, s);
       return launch_mfma_l<true, false>(g, s);
     }

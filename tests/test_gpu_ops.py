@@ -98,6 +98,17 @@ def test_gemm_bf16_nt_epilogues(K, N, epi, out_bf16):
     assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < tol
 
 
+# the TN kernel (both operands K-major: the weight-gradient layout) with every epilogue, M and N
+# ragged over several 256 x 256 tiles
+@pytest.mark.parametrize("K", [64, 192])
+@pytest.mark.parametrize("M,N", [(520, 304), (264, 776)])
+@pytest.mark.parametrize("epi,out_bf16", [(0, False), (0, True), (1, False), (2, False)])
+def test_gemm_bf16_tn_epilogues(K, M, N, epi, out_bf16):
+    got, ref = gemm_case(M, N, K, 1, 1, hol.BF16, epi, seed=K + M + epi, out_bf16=out_bf16)
+    tol = 2 ** -8 if out_bf16 else 1e-5
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < tol
+
+
 def test_gemm_bf16_output_rounding():
     got, ref = gemm_case(256, 128, 128, 0, 0, hol.BF16, 0, seed=4, out_bf16=True)
     np.testing.assert_allclose(got, ref, rtol=2 ** -8, atol=1e-3)
