@@ -490,6 +490,183 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// dK/dV for head width 128 without transposed copies: the query-side tiles (Q, dO) stay in their
+// natural [q][d] layout, double-buffered in LDS (one block barrier per iteration), and the dV / dK
+// products read them transposed with ds_read_b64_tr_b16: within each 16-lane group, lane
+// 16 g + 4 a + b receives element b of the 8-byte pieces addressed by lanes 16 g + a + 4 j
+// (j = 0..3). Lane 16 g + a + 4 j therefore addresses row (query) q0 + 4 (g / 2) + j, columns
+// (d) d0 + 16 (g mod 2) + 4 a .. + 3, and a second read 8 rows further completes the fragment in
+// the query order of acc_frag. Tile rows are 256 B; 16-byte chunk c of row r sits at c ^ sw(r),
+// sw(r) = 4 (r mod 4) + (r / 4) mod 4, which keeps both the score products' row reads (16 rows at
+// one chunk) and the transposed reads (4 rows over 4 chunks) on distinct banks.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int qsw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int qoff(int r, int c) { return r * 128 + (((c >> 3) ^ qsw(r)) << 3) + (c & 7); }
+
+typedef short trv4 __attribute__((ext_vector_type(4)));
+typedef short trv8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 tr_pair(const bf16* lo, const bf16* hi) {
+  const trv4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) trv4*)lo);
+  const trv4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) trv4*)hi);
+  const trv8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
+  constexpr int D = 128, BKV = 128, BQ = 64, KP = D + 8, QT = BQ * D;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2 * QT];
+  __shared__ __attribute__((aligned(16))) bf16 Gs[2 * QT];  // dO
+  __shared__ float lse2[2][BQ], dlt[2][BQ];
+  __shared__ bf16 Kb[BKV * KP];
+  __shared__ bf16 Vb[BKV * KP];
+  const int S = a.S;
+  const int nkt = (S + BKV - 1) / BKV;
+  int pair, kt;  // early keys see the most queries: key tile 0 of a pair first
+  if (!pair_unit(nkt, a.nkv * a.n_seq, pair, kt)) return;
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
+  const int group = a.nq / a.nkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int k0 = kt * BKV;
+  const int kj = k0 + 32 * w + lq;  // this lane's key (column of the S / dP accumulators)
+  const int64_t base = (int64_t)seq * S;
+  const float sl2 = LOG2E / sqrtf((float)D);
+  const float scale = 1.f / sqrtf((float)D);
+
+  load_rows<BKV, D>(Kb, KP, (const bf16*)a.k + (int64_t)kvh * D, a.ldk, base + k0, min(BKV, S - k0));
+  load_rows<BKV, D>(Vb, KP, (const bf16*)a.v + (int64_t)kvh * D, a.ldv, base + k0, min(BKV, S - k0));
+  const bf16* kfp = Kb + (32 * w + lq) * KP + 8 * hh;
+  const bf16* vfp = Vb + (32 * w + lq) * KP + 8 * hh;
+  // transposed-read offsets: [half][d block] for k-step 0 (add 16 rows per k-step)
+  int toff[2][D / 32];
+  {
+    const int g = lane >> 4, aa = lane & 3, j = (lane >> 2) & 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) toff[hf][db] = qoff(8 * hf + 4 * (g >> 1) + j, db * 32 + 16 * (g & 1) + 4 * aa);
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    zero(dv[i]);
+    zero(dk[i]);
+  }
+  const int wave_kmin = k0 + 32 * w;
+  const int nqt = (S + BQ - 1) / BQ;
+  const int qt0 = k0 / BQ, nper = nqt - qt0, nit = group * nper;
+  // iteration it: query tile nqt - 1 - it / group (from the last down to the diagonal), q head
+  // kvh * group + it % group; every key tile of a pair walks the query tiles in the same order
+  NatTile<BQ, D> qreg, greg;
+  float lse_r = 0.f, dl_r = 0.f;
+  auto fetch = [&](int it) {
+    const int h = kvh * group + it % group, q0 = (nqt - 1 - it / group) * BQ, nq = min(BQ, S - q0);
+    const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
+    const bf16* G = (const bf16*)a.dO + (int64_t)h * D;
+    qreg.load(Q, a.ldq, base + q0, nq);
+    greg.load(G, a.lddo, base + q0, nq);
+    if (threadIdx.x < BQ) {
+      const int qq = q0 + threadIdx.x;
+      const int64_t hrow = ((int64_t)seq * a.nq + h) * S;
+      lse_r = qq < S ? a.lse[hrow + qq] * LOG2E : 0.f;
+      dl_r = qq < S ? a.delta[hrow + qq] : 0.f;
+    }
+  };
+  // a thread's share of the fetched tile into buffer b (chunk c = tid + 256 i: row c / 16,
+  // logical chunk c % 16)
+  auto put = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < NatTile<BQ, D>::N; ++i) {
+      const int c = threadIdx.x + 256 * i, r = c >> 4, ch = c & 15;
+      const int o = b * QT + r * 128 + ((ch ^ qsw(r)) << 3);
+      *(u32x4*)(Qs + o) = qreg.v[i];
+      *(u32x4*)(Gs + o) = greg.v[i];
+    }
+    if (threadIdx.x < BQ) {
+      lse2[b][threadIdx.x] = lse_r;
+      dlt[b][threadIdx.x] = dl_r;
+    }
+  };
+  fetch(0);
+  put(0);
+  if (nit > 1) fetch(1);
+  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int cur = it & 1;
+    const int q0 = (nqt - 1 - it / group) * BQ;
+    const bf16* Qc = Qs + cur * QT;
+    const bf16* Gc = Gs + cur * QT;
+    if (q0 + BQ - 1 >= wave_kmin) {  // else every query of the tile is before this wave's keys
+      // two 32-query halves in turn: S[q][key] and dP[q][key], then their dV / dK products
+      // (element r of a half qb: query q0 + 32 qb + 8 (r/4) + 4 hh + r%4, key kj)
+      const bool full = q0 >= wave_kmin + 31 && q0 + BQ <= S && kj < S;  // no masking in this tile
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
+        const int qr = qb * 32 + lq;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int o = qoff(qr, 16 * kk + 8 * hh);
+          s = mfma(*(const bf16x8*)(Qc + o), *(const bf16x8*)(kfp + 16 * kk), s);
+          dp = mfma(*(const bf16x8*)(Gc + o), *(const bf16x8*)(vfp + 16 * kk), dp);
+        }
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const float p = ex2(fmaf(s[r], sl2, -lse2[cur][qloc]));
+            s[r] = p;
+            dp[r] = p * (dp[r] - dlt[cur][qloc]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int qq = q0 + qloc;
+            const bool ok = qq < S && kj <= qq && kj < S;
+            const float p = ok ? ex2(fmaf(s[r], sl2, -lse2[cur][qloc])) : 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - dlt[cur][qloc]);
+          }
+        }
+        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+        for (int ksp = 0; ksp < 2; ++ksp) {
+          const int ks = 2 * qb + ksp;
+          const bf16x8 pb = acc_frag(s, ksp);
+          const bf16x8 sb = acc_frag(dp, ksp);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            dv[db] = mfma(tr_pair(Gc + ks * 16 * 128 + toff[0][db], Gc + ks * 16 * 128 + toff[1][db]), pb, dv[db]);
+            dk[db] = mfma(tr_pair(Qc + ks * 16 * 128 + toff[0][db], Qc + ks * 16 * 128 + toff[1][db]), sb, dk[db]);
+          }
+        }
+      }
+    }
+    if (it + 1 < nit) {
+      put(cur ^ 1);  // tile it + 1 (its loads were issued an iteration ago); every wave finished
+                     // reading that buffer before the previous barrier
+      if (it + 2 < nit) fetch(it + 2);
+    }
+    __syncthreads();
+  }
+  if (kj < S) {
+    bf16* dkp = (bf16*)a.dk + (base + kj) * a.lddk + (int64_t)kvh * D;
+    bf16* dvp = (bf16*)a.dv + (base + kj) * a.lddv + (int64_t)kvh * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = db * 32 + 8 * g + 4 * hh;
+        store4(dkp + dd, dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+               dk[db][4 * g + 3] * scale);
+        store4(dvp + dd, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // backward, dQ: block = 4 waves x 32 queries of one q head; key tiles of 64 up to the diagonal
 // ------------------------------------------------------------------------------------------
 template <int D>
@@ -590,6 +767,128 @@ __global__ __launch_bounds__(256, 1) void attn_dq_mfma(Attn a) {
   }
 }
 
+// dQ for head width 128 without the transposed key copy: K and V tiles stay natural in a
+// double-buffered, swizzled LDS pair (the layout of the dK/dV kernel above, one block barrier per
+// key tile) and the dQ product reads K transposed with ds_read_b64_tr_b16.
+__global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
+  constexpr int D = 128, BQ = 128, BK = 64, KT = BK * D;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * KT];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * KT];
+  const int S = a.S;
+  const int nqt = (S + BQ - 1) / BQ;
+  const int group = a.nq / a.nkv;
+  int pair, unit;
+  if (!pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit)) return;
+  const int qt = nqt - 1 - unit / group;  // longest first, the group's heads together
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
+  const int h = kvh * group + unit % group;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int q0 = qt * BQ;
+  const int qi = q0 + 32 * w + lq;
+  const int64_t base = (int64_t)seq * S;
+  const float sl2 = LOG2E / sqrtf((float)D);
+  const float scale = 1.f / sqrtf((float)D);
+  const bf16* K = (const bf16*)a.k + (int64_t)kvh * D;
+  const bf16* V = (const bf16*)a.v + (int64_t)kvh * D;
+
+  bf16x8 qf[D / 16], gf[D / 16];
+  {
+    const int64_t row = base + min(qi, S - 1);
+    const bf16* qp = (const bf16*)a.q + row * a.ldq + (int64_t)h * D;
+    const bf16* gp = (const bf16*)a.dO + row * a.lddo + (int64_t)h * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * hh);
+      gf[kk] = *(const bf16x8*)(gp + 16 * kk + 8 * hh);
+    }
+  }
+  const bool qv = qi < S;
+  const float lse_q = qv ? a.lse[((int64_t)seq * a.nq + h) * S + qi] * LOG2E : 0.f;
+  const float dl_q = qv ? a.delta[((int64_t)seq * a.nq + h) * S + qi] : 0.f;
+  int toff[2][D / 32];
+  {
+    const int g = lane >> 4, aa = lane & 3, j = (lane >> 2) & 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) toff[hf][db] = qoff(8 * hf + 4 * (g >> 1) + j, db * 32 + 16 * (g & 1) + 4 * aa);
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) zero(dq[i]);
+  const int qmax = min(q0 + BQ, S) - 1;
+  const int nkt = qmax / BK + 1;
+  const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
+  NatTile<BK, D> kreg, vreg;
+  auto fetch = [&](int kt) {
+    const int k0 = kt * BK;
+    kreg.load(K, a.ldk, base + k0, min(BK, S - k0));
+    vreg.load(V, a.ldv, base + k0, min(BK, S - k0));
+  };
+  auto put = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < NatTile<BK, D>::N; ++i) {
+      const int c = threadIdx.x + 256 * i, r = c >> 4, ch = c & 15;
+      const int o = b * KT + r * 128 + ((ch ^ qsw(r)) << 3);
+      *(u32x4*)(Ks + o) = kreg.v[i];
+      *(u32x4*)(Vs + o) = vreg.v[i];
+    }
+  };
+  fetch(0);
+  put(0);
+  if (nkt > 1) fetch(1);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK, cur = kt & 1;
+    const bf16* Kc = Ks + cur * KT;
+    const bf16* Vc = Vs + cur * KT;
+    if (k0 <= wave_qmax) {  // else every key of the tile is after this wave's queries
+      f32x16 s[2], dp[2];
+      zero(s[0]); zero(s[1]); zero(dp[0]); zero(dp[1]);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int o = qoff(kb * 32 + lq, 16 * kk + 8 * hh);
+          s[kb] = mfma(*(const bf16x8*)(Kc + o), qf[kk], s[kb]);
+          dp[kb] = mfma(*(const bf16x8*)(Vc + o), gf[kk], dp[kb]);
+        }
+      // element r of block kb: key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = qv && kk <= qi && kk < S;
+          const float p = ok ? ex2(s[kb][r] * sl2 - lse_q) : 0.f;
+          dp[kb][r] = p * (dp[kb][r] - dl_q);
+        }
+      // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const bf16x8 sb = acc_frag(dp[ks >> 1], ks & 1);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dq[db] = mfma(tr_pair(Kc + ks * 16 * 128 + toff[0][db], Kc + ks * 16 * 128 + toff[1][db]), sb, dq[db]);
+      }
+    }
+    if (kt + 1 < nkt) {
+      put(cur ^ 1);  // every wave finished reading that buffer before the previous barrier
+      if (kt + 2 < nkt) fetch(kt + 2);
+    }
+    __syncthreads();
+  }
+  if (qv) {
+    bf16* dqp = (bf16*)a.dq + (base + qi) * a.lddq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(dqp + db * 32 + 8 * g + 4 * hh, dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale,
+               dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+  }
+}
+
 // delta[seq, h, i] = sum_d dO * O  (one wavefront per (token, head))
 __global__ __launch_bounds__(256) void attn_delta_bf16(Attn a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -632,8 +931,8 @@ int launch_attn_bwd_mfma(const Attn& a, hipStream_t s) {
   dim3 gk(pair_grid((a.S + 127) / 128, a.nkv * a.n_seq)),
       gq(pair_grid(((a.S + 127) / 128) * (a.nq / a.nkv), a.nkv * a.n_seq));
   if (a.d == 128) {
-    hipLaunchKernelGGL(attn_dkdv_mfma<128>, gk, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_dq_mfma<128>, gq, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_dkdv_tr128, gk, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_dq_tr128, gq, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(attn_dkdv_mfma<64>, gk, dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_dq_mfma<64>, gq, dim3(256), 0, s, a);
