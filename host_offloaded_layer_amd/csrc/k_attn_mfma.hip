@@ -889,6 +889,152 @@ __global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
   }
 }
 
+// Forward for head width 128 in the same layout: K and V tiles of 64 keys natural, swizzled and
+// double-buffered in LDS (one block barrier per tile); the P V product reads V transposed with
+// ds_read_b64_tr_b16.
+__global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
+  constexpr int D = 128, BQ = 128, BK = 64, KT = BK * D;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * KT];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * KT];
+  const int S = a.S;
+  const int nqt = (S + BQ - 1) / BQ;
+  const int group = a.nq / a.nkv;
+  int pair, unit;
+  if (!pair_unit(group * nqt, a.nkv * a.n_seq, pair, unit)) return;
+  const int qt = nqt - 1 - unit / group;  // longest (latest) query tiles first, the group's heads together
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
+  const int h = kvh * group + unit % group;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int q0 = qt * BQ;
+  const int qi = q0 + 32 * w + lq;  // this lane's query (column of every accumulator)
+  const int64_t base = (int64_t)seq * S;
+  const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
+  const bf16* K = (const bf16*)a.k + (int64_t)kvh * D;
+  const bf16* V = (const bf16*)a.v + (int64_t)kvh * D;
+
+  bf16x8 qf[D / 16];
+  {
+    const bf16* qp = Q + (base + min(qi, S - 1)) * a.ldq;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * hh);
+  }
+  int toff[2][D / 32];
+  {
+    const int g = lane >> 4, aa = lane & 3, j = (lane >> 2) & 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) toff[hf][db] = qoff(8 * hf + 4 * (g >> 1) + j, db * 32 + 16 * (g & 1) + 4 * aa);
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) zero(o[i]);
+  const float sl2 = LOG2E / sqrtf((float)D);
+  float m = -INFINITY, l = 0.f;
+  const int qmax = min(q0 + BQ, S) - 1;
+  const int nkt = qmax / BK + 1;
+  const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
+
+  NatTile<BK, D> kreg, vreg;
+  auto fetch = [&](int kt) {
+    const int k0 = kt * BK;
+    kreg.load(K, a.ldk, base + k0, min(BK, S - k0));
+    vreg.load(V, a.ldv, base + k0, min(BK, S - k0));
+  };
+  auto put = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < NatTile<BK, D>::N; ++i) {
+      const int c = threadIdx.x + 256 * i, r = c >> 4, ch = c & 15;
+      const int off = b * KT + r * 128 + ((ch ^ qsw(r)) << 3);
+      *(u32x4*)(Ks + off) = kreg.v[i];
+      *(u32x4*)(Vs + off) = vreg.v[i];
+    }
+  };
+  fetch(0);
+  put(0);
+  if (nkt > 1) fetch(1);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK, cur = kt & 1;
+    const bf16* Kc = Ks + cur * KT;
+    const bf16* Vc = Vs + cur * KT;
+    if (k0 <= wave_qmax) {  // else every key of this tile is in this wave's future
+      f32x16 s[2];
+      zero(s[0]);
+      zero(s[1]);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = *(const bf16x8*)(Kc + qoff(kb * 32 + lq, 16 * kk + 8 * hh));
+          s[kb] = mfma(kf, qf[kk], s[kb]);
+        }
+      }
+      // s[kb][r] = score(key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi)
+      const bool diag = (k0 + BK - 1 > q0 + 32 * w) || (k0 + BK > S);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = s[kb][r] * sl2;
+          if (diag) {
+            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (kj > qi || kj >= S) v = -INFINITY;
+          }
+          s[kb][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      if (mn > m) {  // the running max moved: rescale (the whole wave skips this once maxima settle)
+        const float corr = ex2(m - mn);
+        l *= corr;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= corr;
+        m = mn;
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = ex2(s[kb][r] - m);
+          s[kb][r] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 32, 64);
+      l += ls;
+      // O^T[d][q] += V^T[d][key] P^T[key][q]
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const bf16x8 pb = acc_frag(s[ks >> 1], ks & 1);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          o[db] = mfma(tr_pair(Vc + ks * 16 * 128 + toff[0][db], Vc + ks * 16 * 128 + toff[1][db]), pb, o[db]);
+      }
+    }
+    if (kt + 1 < nkt) {
+      put(cur ^ 1);  // every wave finished reading that buffer before the previous barrier
+      if (kt + 2 < nkt) fetch(kt + 2);
+    }
+    __syncthreads();
+  }
+  if (qi < S) {
+    const float inv = 1.f / l;
+    bf16* op = (bf16*)a.o + (base + qi) * a.ldo + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(op + db * 32 + 8 * g + 4 * hh, o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+               o[db][4 * g + 3] * inv);
+    if (hh == 0) a.lse[((int64_t)seq * a.nq + h) * S + qi] = (m + __log2f(l)) * LN2;
+  }
+}
+
 // delta[seq, h, i] = sum_d dO * O  (one wavefront per (token, head))
 __global__ __launch_bounds__(256) void attn_delta_bf16(Attn a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -920,7 +1066,7 @@ bool attn_mfma_bwd_supported(const Attn& a) {
 
 int launch_attn_fwd_mfma(const Attn& a, hipStream_t s) {
   dim3 grid(pair_grid(((a.S + 127) / 128) * (a.nq / a.nkv), a.nkv * a.n_seq));
-  if (a.d == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, a);
+  if (a.d == 128) hipLaunchKernelGGL(attn_fwd_tr128, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
