@@ -113,6 +113,10 @@ hol_status hol_get_grad(const hol_model* m, int32_t i, float* dst, int64_t numel
   if (!t || !dst) return einval("hol_get_grad", "bad model, index or pointer");
   if (numel != t->numel) return einval("hol_get_grad", "numel mismatch");
   if (!t->trainable) return einval("hol_get_grad", "tensor is frozen");
+  if (m->grads_stale && t->flat >= m->layer_flat0) {  // consumed by a fused step: logically zero
+    parallel_for(numel, 1 << 18, [&](int64_t lo, int64_t hi) { memset(dst + lo, 0, (size_t)(hi - lo) * 4); });
+    return HOL_OK;
+  }
   const float* src = m->grad + t->flat;
   parallel_for(numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy(dst + lo, src + lo, (size_t)(hi - lo) * 4); });
   return HOL_OK;

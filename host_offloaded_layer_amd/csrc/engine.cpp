@@ -1133,8 +1133,8 @@ static void host_accumulate(void* p) {
   });
 }
 
-static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1, int64_t hi = -1);
-static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k);
+static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1, int64_t hi = -1, bool zero = true);
+static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero = true);
 
 // Host worker of the fused forward_backward + step: runs the optimiser on each unit as soon as
 // that unit's gradient copy (enqueued by the main thread, in backward order) has completed.
@@ -1177,11 +1177,11 @@ struct FusedWorker {
         if (piece) {
           const int c = u - hol_model::TAIL_CODE;
           const int64_t n = m->layer_flat_n, f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * n;
-          adam_unit(m, m->tail_unit, kc, f0 + n * c / hol_model::N_TAIL, f0 + n * (c + 1) / hol_model::N_TAIL);
+          adam_unit(m, m->tail_unit, kc, f0 + n * c / hol_model::N_TAIL, f0 + n * (c + 1) / hol_model::N_TAIL, false);
         } else if (u == m->L + 2) {
-          adam_embed_rows(m, m->emb_untouched, kc);
+          adam_embed_rows(m, m->emb_untouched, kc, false);  // their gradient is zero already
         } else {
-          adam_unit(m, u, kc);
+          adam_unit(m, u, kc, -1, -1, u == 0);  // layer and head blocks: overwritten by the next copies
         }
         const double t1 = now_ms();
         busy_ms += t1 - t0;
@@ -1343,6 +1343,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   const bool direct = m->grads_zero;
   // fused optimiser: only when this call's gradients are the whole gradient (nothing accumulated)
   const bool fused = fuse_step && direct;
+  // a stale head block that this call does not overwrite is cleared now (the layer blocks are
+  // overwritten whole by their copies)
+  const bool head_written = m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE && m->head_trainable;
+  if (m->grads_stale && !head_written && m->head_flat_n > 0) parallel_zero(m->grad + m->head_flat0, m->head_flat_n * 4);
   const hol_config& cf = m->cfg;
   const AdamConsts kc = adam_consts(m->step_t + 1, cf.lr, cf.beta1, cf.beta2, cf.adam_eps);
   FusedWorker worker{m};
@@ -1614,6 +1618,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   for (int64_t t = 0; t < T64; ++t) total += (double)m->loss_stage[t];
   *out = total;
   m->grads_zero = false;
+  m->grads_stale = false;
   m->stats.scatter_done_ms = now_ms() - t_start;
   HSTEP(hipStreamSynchronize(sd));
   m->stats.gpu_done_ms = now_ms() - t_start;
@@ -1629,6 +1634,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     adam_embed_rows(m, m->emb_touched, kc);
     m->step_t += 1;
     m->grads_zero = true;
+    m->grads_stale = true;
     m->stats.step_ms = now_ms() - t_gpu_done;  // optimiser time not hidden under the GPU work
     m->fused_overlap_ms = worker.busy_ms;
   } else if (fuse_step) {
@@ -1690,7 +1696,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 // zeroing of its gradients.
 // Adam (and the image refresh) on the trainable tensors of unit u, restricted to the flat
 // parameter range [lo, hi) when lo >= 0 (the same per-element arithmetic either way).
-static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int64_t hi) {
+static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int64_t hi, bool zero) {
   for (int ti : m->unit_tensors[u]) {
     const TensorDesc& t = m->tensors[ti];
     if (!t.trainable) continue;
@@ -1713,7 +1719,7 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
           if (to_bf16) f32_to_bf16_range(th + a, (uint16_t*)dst + a, n);
           else memcpy((float*)dst + a, th + a, (size_t)n * 4);
         }
-        memset(g + a, 0, (size_t)n * 4);
+        if (zero) memset(g + a, 0, (size_t)n * 4);
       }
     });
   }
@@ -1721,16 +1727,24 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
 
 // Adam on the given rows of the embedding (and zeroing of their gradients): the same per-element
 // arithmetic as adam_unit, split by rows.
-static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k) {
+static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero) {
   if (!m->embed_trainable || rows.empty()) return;
   const int64_t H = m->H, f0 = m->embed_flat0;
   parallel_for((int64_t)rows.size(), 16, [&](int64_t lo, int64_t hi) {
     for (int64_t q = lo; q < hi; ++q) {
       const int64_t o = f0 + (int64_t)rows[q] * H;
       adam_range(m->master + o, m->grad + o, m->mom1 + o, m->mom2 + o, H, k);
-      memset(m->grad + o, 0, (size_t)H * 4);
+      if (zero) memset(m->grad + o, 0, (size_t)H * 4);
     }
   });
+}
+
+// Clears the layer and head gradient blocks a fused step left holding consumed gradients.
+static void clear_stale_grads(hol_model* m) {
+  if (!m->grads_stale) return;
+  const int64_t n = m->n_flat - m->layer_flat0;
+  parallel_zero(m->grad + m->layer_flat0, n * 4);
+  m->grads_stale = false;
 }
 
 hol_status engine_step(hol_model* m) {
@@ -1739,6 +1753,7 @@ hol_status engine_step(hol_model* m) {
     return HOL_ESTATE;
   }
   const double t0 = now_ms();
+  clear_stale_grads(m);  // logically zero
   const hol_config& c = m->cfg;
   const AdamConsts k = adam_consts(m->step_t + 1, c.lr, c.beta1, c.beta2, c.adam_eps);
   for (int u = 0; u < (int)m->unit_tensors.size(); ++u) adam_unit(m, u, k);
@@ -1788,6 +1803,7 @@ hol_status engine_zero_grad(hol_model* m) {
   if (m->sd2h) hipStreamSynchronize(m->sd2h);
   parallel_zero(m->grad, m->n_flat * 4);
   m->grads_zero = true;
+  m->grads_stale = false;
   m->poisoned = false;
   return HOL_OK;
 }

@@ -197,6 +197,10 @@ struct hol_model {
   int64_t step_t = 0;
   bool poisoned = false;
   bool grads_zero = true;
+  // after a fused forward_backward + step the layer and head gradient blocks hold the consumed
+  // gradients instead of zeros (the next call's copies overwrite them whole); they read as zero
+  // and are cleared before anything accumulates into them. The embedding block is always zeroed.
+  bool grads_stale = false;
   hol::Stats stats;
 
   // optimiser units: 0 = embedding, 1 + l = layer l, L + 1 = final norm and LM head

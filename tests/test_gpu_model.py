@@ -204,3 +204,33 @@ def test_results_independent_of_weight_slots_and_grad_buffers_bitwise(wname):
         for n in state:
             for x, y in zip(state[n], runs[0][1][n]):
                 assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+
+
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
+def test_plain_step_after_fused_step_sees_zero_gradients(wname):
+    """After a fused step the gradient blocks read as zero: a following plain step() is Adam on
+    zero gradients, bit for bit the same as on a model whose gradients were zeroed explicitly."""
+    w = TINY if wname == "tiny" else BF16_SMALL
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+    with lib_model(w, params) as a, lib_model(w, params) as b:
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        lib_fb(b, w, batch)
+        b.step()
+        b.zero_grad()
+        for n in a.index:
+            assert not np.any(a.get_grad(n)), n
+        a.step()
+        b.step()
+        sa, sb = _state(a), _state(b)
+        for n in sa:
+            for x, y in zip(sa[n], sb[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+        # and a plain forward_backward after a fused step accumulates from zero
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        b.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        la = lib_fb(a, w, batch)
+        lb = lib_fb(b, w, batch)
+        assert la == lb
+        for n in a.index:
+            assert np.array_equal(a.get_grad(n).view(np.uint32), b.get_grad(n).view(np.uint32)), n
