@@ -1,0 +1,66 @@
+"""The bench workload at its full size (LLaMA-3.1-8B shape, 32 layers, 4 x 4096 tokens, K = 4),
+in the launch configuration bench.py times. The oracle cannot run this size, so the checks are
+properties that hold at any size:
+  - the call is deterministic: the same inputs give the same loss and gradients bit for bit;
+  - the results do not depend on the checkpoint interval (K = 4 and K = 8, bitwise);
+  - at initialisation (weights N(0, 0.02)) every token's cross entropy is ln V plus half the
+    variance of its logits (about 0.02^2 H for unit-RMS final activations), so the returned sum of
+    n_micro micro-batch means lies within n_micro (ln V, ln V + 2);
+  - the micro-batch sum: the 4-micro-batch call's loss equals the sum of 4 one-micro-batch calls
+    over the same sequences (each micro-batch's mean is computed by the same kernels in the same
+    order), and the accumulated gradients of those calls equal the single call's within fp32
+    summation-order rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+import host_offloaded_layer_amd as hol  # noqa: E402
+import workloads as W  # noqa: E402
+from tests.gpu_helpers import lib_model, rel_l2  # noqa: E402
+
+SAMPLE = ["layers.0.wq", "layers.0.w_down", "layers.17.wo", "layers.31.w_gate",
+          "layers.31.attn_norm", "final_norm", "lm_head"]
+
+
+def test_llama8b_full_size_properties():
+    w = W.WORKLOADS["llama8b"]
+    params = W.make_params(w, threads=16)
+    batch = W.make_batch(w)
+    tokens = batch["tokens"]
+    with lib_model(w, params, k=8) as m:
+        del params
+        names = [n for n in SAMPLE if n in m.index] + ["embed"]
+        assert len(names) == len(SAMPLE) + 1, sorted(m.index)[:12]
+
+        def run(k):
+            m.set_ckpt_every_k(k)
+            m.zero_grad()
+            loss = m.forward_backward(w.n_micro, tokens=tokens)
+            return loss, {n: m.get_grad(n) for n in names}
+
+        la, ga = run(4)
+        lb, gb = run(8)
+        lc, gc = run(4)
+        print("loss", la, lb, lc, "n_micro ln V", w.n_micro * math.log(w.shape.vocab))
+        assert la == lb == lc
+        for n in names:
+            assert np.array_equal(ga[n].view(np.uint32), gb[n].view(np.uint32)), n
+            assert np.array_equal(ga[n].view(np.uint32), gc[n].view(np.uint32)), n
+        lnv = math.log(w.shape.vocab)
+        assert w.n_micro * lnv < la < w.n_micro * (lnv + 2.0)
+
+        # the same sequences one micro-batch per call, accumulating
+        m.set_ckpt_every_k(4)
+        m.zero_grad()
+        per = tokens.shape[0] // w.n_micro
+        parts = [m.forward_backward(1, tokens=tokens[i * per:(i + 1) * per]) for i in range(w.n_micro)]
+        gs = {n: m.get_grad(n) for n in names}
+        print("micro-batch losses", parts, "sum", sum(parts))
+        assert sum(parts) == pytest.approx(la, rel=1e-6)
+        for n in names:
+            assert rel_l2(gs[n], ga[n]) < 1e-5, (n, rel_l2(gs[n], ga[n]))
