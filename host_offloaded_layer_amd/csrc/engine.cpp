@@ -483,6 +483,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->tail_mlp_ev, hipEventDisableTiming));
   m->unit_tensors.assign(m->L + 2, {});
   for (int i = 0; i < (int)m->tensors.size(); ++i) {
     const TensorDesc& t = m->tensors[i];
@@ -516,6 +517,7 @@ void engine_destroy(hol_model* m) {
   if (m->ev_h0) hipEventDestroy(m->ev_h0);
   for (auto e : m->ev_tail)
     if (e) hipEventDestroy(e);
+  if (m->tail_mlp_ev) hipEventDestroy(m->tail_mlp_ev);
   for (auto e : m->tev)
     if (e) hipEventDestroy(e);
   for (auto e : m->kev)
@@ -968,6 +970,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
       KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
       KCHECK(run_gemm(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
     }
+    if (m->tail_mlp_armed) HCHECK(hipEventRecord(m->tail_mlp_ev, s));  // w_gate, w_up, w_down final
   }
   if (tw) KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
   KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, tw ? G + m->g_g2 : nullptr,
@@ -1176,8 +1179,8 @@ struct FusedWorker {
         const double t0 = now_ms();
         if (piece) {
           const int c = u - hol_model::TAIL_CODE;
-          const int64_t n = m->layer_flat_n, f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * n;
-          adam_unit(m, m->tail_unit, kc, f0 + n * c / hol_model::N_TAIL, f0 + n * (c + 1) / hol_model::N_TAIL, false);
+          const int64_t f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * m->layer_flat_n;
+          adam_unit(m, m->tail_unit, kc, f0 + m->tail_lo[c], f0 + m->tail_hi[c], false);
         } else if (u == m->L + 2) {
           adam_embed_rows(m, m->emb_untouched, kc, false);  // their gradient is zero already
         } else {
@@ -1541,29 +1544,49 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     } else {  // OP_BWD
       const Act A = act_at(m, op.pos);
       const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
+      const bool tail = fused && j + 1 == ops.size();
+      // dense bf16 layer: [wqkv | wo | w_gate w_up | w_down | attn_norm | mlp_norm]
+      const bool split = tail && m->dt == DT_BF16 && m->NE == 0 && m->base_trainable;
       HSTEP(hipStreamWaitEvent(sc, m->ev_gfree[gi], 0));
       HSTEP(hipEventRecord(ta, sc));
-      STEP(layer_backward(m, w, A, hin, m->gdev[gi], T, n_seq, S, op.pos));
+      m->tail_mlp_armed = split;
+      const hol_status bst = layer_backward(m, w, A, hin, m->gdev[gi], T, n_seq, S, op.pos);
+      m->tail_mlp_armed = false;
+      STEP(bst);
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 4});
       HSTEP(hipEventRecord(m->ev_gdone[gi], sc));
       // gradient offload on the gradient-transfer stream
-      HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
       float* lg = m->grad + m->layer_flat0 + (int64_t)op.layer * m->layer_flat_n;
-      const bool tail = fused && j + 1 == ops.size();
       hipEvent_t a = tev(), e = tev();
       HSTEP(hipEventRecord(a, sd));
       if (tail) {
-        // the call's last gradient: in pieces, each handed to the optimiser as it lands
+        // the call's last gradient: in pieces, each handed to the optimiser as it lands; the MLP
+        // weights' piece as soon as the MLP backward is done
         m->tail_unit = 1 + op.layer;
         const int64_t n = m->layer_flat_n;
-        for (int c = 0; c < hol_model::N_TAIL; ++c) {
-          const int64_t c0 = n * c / hol_model::N_TAIL, c1 = n * (c + 1) / hol_model::N_TAIL;
-          HSTEP(hipMemcpyAsync(lg + c0, m->gdev[gi] + c0, (size_t)(c1 - c0) * 4, hipMemcpyDeviceToHost, sd));
-          HSTEP(hipEventRecord(m->ev_tail[c], sd));
+        m->n_tail = 0;
+        auto piece = [&](int64_t lo, int64_t hi) -> hol_status {
+          const int c = m->n_tail++;
+          m->tail_lo[c] = lo;
+          m->tail_hi[c] = hi;
+          HCHECK(hipMemcpyAsync(lg + lo, m->gdev[gi] + lo, (size_t)(hi - lo) * 4, hipMemcpyDeviceToHost, sd));
+          HCHECK(hipEventRecord(m->ev_tail[c], sd));
           worker.push(hol_model::TAIL_CODE + c);
+          return HOL_OK;
+        };
+        if (split) {
+          HSTEP(hipStreamWaitEvent(sd, m->tail_mlp_ev, 0));
+          STEP(piece(m->g_wgu, m->g_g1));
+          HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
+          STEP(piece(0, m->g_wgu));
+          STEP(piece(m->g_g1, n));
+        } else {
+          HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
+          for (int c = 0; c < hol_model::N_TAIL; ++c) STEP(piece(n * c / hol_model::N_TAIL, n * (c + 1) / hol_model::N_TAIL));
         }
       } else {
+        HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
         HSTEP(hipMemcpyAsync(direct ? lg : m->grad_stage, m->gdev[gi], m->layer_flat_n * 4, hipMemcpyDeviceToHost, sd));
       }
       HSTEP(hipEventRecord(e, sd));

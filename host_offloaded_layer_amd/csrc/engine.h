@@ -215,6 +215,12 @@ struct hol_model {
   static constexpr int N_TAIL = 4, TAIL_CODE = 1 << 20;
   hipEvent_t ev_tail[N_TAIL] = {};
   int tail_unit = -1;
+  int64_t tail_lo[N_TAIL] = {}, tail_hi[N_TAIL] = {};  // piece ranges inside the layer block
+  int n_tail = 0;
+  // dense bf16 last layer: its MLP weight gradients (final once the MLP backward is done) go down
+  // while the layer's attention backward computes; the backward records tail_mlp_ev there
+  hipEvent_t tail_mlp_ev = nullptr;
+  bool tail_mlp_armed = false;
   std::vector<int32_t> emb_touched, emb_untouched;  // embedding rows the call's tokens use / do not
   bool fused_abort = false;
   double fused_overlap_ms = 0, fused_tail_ms = 0;
