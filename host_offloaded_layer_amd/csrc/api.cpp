@@ -1,5 +1,6 @@
 // C ABI of libhol.so (include/hol.h, include/hol_ops.h): argument checking, exception firewall and
 // dispatch into the streaming engine and the kernel launchers. No exception crosses the ABI.
+#include <immintrin.h>
 #include <string.h>
 
 #include <new>
@@ -239,7 +240,10 @@ hol_status hol_host_adam(float* theta, const float* grad, float* mom1, float* mo
 hol_status hol_host_bf16_round(const float* src, uint16_t* dst, int64_t n) {
   GUARD_BEGIN
   if (!src || !dst || n < 0) return einval("hol_host_bf16_round", "bad argument");
-  parallel_for(n, 1 << 16, [&](int64_t lo, int64_t hi) { f32_to_bf16_range(src + lo, dst + lo, hi - lo); });
+  parallel_for(n, 1 << 16, [&](int64_t lo, int64_t hi) {
+    f32_to_bf16_range_stream(src + lo, dst + lo, hi - lo);
+    _mm_sfence();
+  });
   return HOL_OK;
   GUARD_END
 }

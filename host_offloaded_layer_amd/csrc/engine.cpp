@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <immintrin.h>
 #include <sstream>
 
 #include "host_math.h"
@@ -345,6 +346,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->loss_stage = (float*)pinned_alloc(m, T * 4, &st);
   m->lab_stage = (int32_t*)pinned_alloc(m, T * 4, &st);
   m->w_stage = (float*)pinned_alloc(m, T * 4, &st);
+  if (m->embed_trainable) m->ord_stage = (int32_t*)pinned_alloc(m, (2 * T + 1) * 4, &st);
   if (m->NE > 0) m->counts_stage = (int32_t*)pinned_alloc(m, (int64_t)m->NE * 4, &st);
   if (st != HOL_OK) {
     engine_destroy(m);
@@ -362,6 +364,11 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   for (int i = 0; i < m->nslots; ++i) m->slot[i] = (uint8_t*)D(m->layer_img_bytes);
   if (V > 0) m->head_dev = (uint8_t*)D(m->head_img_bytes);
   for (int i = 0; i < m->ngbuf; ++i) m->gdev[i] = (float*)D(m->layer_flat_n * 4);
+  if (m->embed_trainable) {
+    m->ord_dev = (int32_t*)D(T * 4);
+    m->seg_dev = (int32_t*)D((T + 1) * 4);
+    m->erows = (float*)D(T * H * 4);
+  }
   if (V > 0) m->head_gdev = (float*)D(m->head_flat_n * 4);
   m->ckpt = (float*)D((int64_t)m->n_ckpt * T * H * 4);
   // activation block: K layers
@@ -1137,7 +1144,8 @@ static void host_accumulate(void* p) {
 }
 
 static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1, int64_t hi = -1, bool zero = true);
-static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero = true);
+static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero = true,
+                            const float* gsrc = nullptr);
 
 // Host worker of the fused forward_backward + step: runs the optimiser on each unit as soon as
 // that unit's gradient copy (enqueued by the main thread, in backward order) has completed.
@@ -1432,8 +1440,17 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     std::stable_sort(tok_order.begin(), tok_order.end(),
                      [&](int32_t x, int32_t y) { return b->tokens[x] < b->tokens[y]; });
     m->emb_touched.clear();
-    for (int64_t i = 0; i < T64; ++i)
-      if (i == 0 || b->tokens[tok_order[i]] != b->tokens[tok_order[i - 1]]) m->emb_touched.push_back(b->tokens[tok_order[i]]);
+    int32_t* seg = m->ord_stage + T64;
+    for (int64_t i = 0; i < T64; ++i) {
+      m->ord_stage[i] = tok_order[i];
+      if (i == 0 || b->tokens[tok_order[i]] != b->tokens[tok_order[i - 1]]) {
+        seg[m->emb_touched.size()] = (int32_t)i;
+        m->emb_touched.push_back(b->tokens[tok_order[i]]);
+      }
+    }
+    seg[m->emb_touched.size()] = (int32_t)T64;
+    HSTEP(hipMemcpyAsync(m->ord_dev, m->ord_stage, T64 * 4, hipMemcpyHostToDevice, sc));
+    HSTEP(hipMemcpyAsync(m->seg_dev, seg, (m->emb_touched.size() + 1) * 4, hipMemcpyHostToDevice, sc));
     if (fused) {
       m->emb_untouched.clear();
       size_t q = 0;
@@ -1609,31 +1626,27 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   }
   // ---- first-layer gradient (embedding rows) and loss rows back to the host
   m->last_T = T;
+  // (the gradient of each touched embedding row, summed on the device in position order)
+  const int64_t n_rows = m->embed_trainable ? (int64_t)m->emb_touched.size() : 0;
   if (m->embed_trainable) {
-    HSTEP(hipMemcpyAsync(m->h_stage, m->dh, T64 * H * 4, hipMemcpyDeviceToHost, sc));
-    m->stats.d2h_bytes += (double)T64 * H * 4;
+    HSTEP((hipError_t)launch_embed_row_sums(m->dh, m->ord_dev, m->seg_dev, (int)n_rows, H, m->erows, sc));
+    HSTEP(hipMemcpyAsync(m->h_stage, m->erows, n_rows * H * 4, hipMemcpyDeviceToHost, sc));
+    m->stats.d2h_bytes += (double)n_rows * H * 4;
   }
   HSTEP(hipMemcpyAsync(m->loss_stage, m->rowloss_dev, T64 * 4, hipMemcpyDeviceToHost, sc));
-  // the scatter-add below needs only the compute stream's copies; the last gradient copy may
-  // still run
+  // the code below needs only the compute stream's copies; the last gradient copy may still run
   HSTEP(hipStreamSynchronize(sc));
   HSTEP(hipStreamSynchronize(sh));
   HSTEP(hipGetLastError());
-  // embedding gradient: each touched row adds its tokens' first-layer gradients in position order
-  // (rows split over threads: deterministic)
-  if (m->embed_trainable) {
+  // embedding gradient rows: the fused step reads them from the staging buffer in its Adam (the
+  // embedding's gradient block stays zero); otherwise they are added into that block
+  if (m->embed_trainable && !fused) {
     float* gE = m->grad + m->embed_flat0;
-    std::vector<int64_t> starts;
-    for (int64_t i = 0; i < T64; ++i)
-      if (i == 0 || b->tokens[tok_order[i]] != b->tokens[tok_order[i - 1]]) starts.push_back(i);
-    starts.push_back(T64);
-    parallel_for((int64_t)starts.size() - 1, 8, [&](int64_t lo, int64_t hi) {
-      for (int64_t gi = lo; gi < hi; ++gi) {
-        float* dst = gE + (int64_t)b->tokens[tok_order[starts[gi]]] * H;
-        for (int64_t i = starts[gi]; i < starts[gi + 1]; ++i) {
-          const float* src = m->h_stage + (int64_t)tok_order[i] * H;
-          for (int64_t c = 0; c < H; ++c) dst[c] += src[c];
-        }
+    parallel_for(n_rows, 8, [&](int64_t lo, int64_t hi) {
+      for (int64_t u = lo; u < hi; ++u) {
+        float* dst = gE + (int64_t)m->emb_touched[u] * H;
+        const float* src = m->h_stage + u * H;
+        for (int64_t c = 0; c < H; ++c) dst[c] += src[c];
       }
     });
   }
@@ -1653,8 +1666,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
       return fail(HOL_EDEVICE);
     }
-    // the touched embedding rows are complete only after the host scatter-add
-    adam_embed_rows(m, m->emb_touched, kc);
+    // the touched embedding rows: their gradients arrived with the last copies
+    adam_embed_rows(m, m->emb_touched, kc, false, m->h_stage);
     m->step_t += 1;
     m->grads_zero = true;
     m->grads_stale = true;
@@ -1739,24 +1752,27 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
         const int64_t n = std::min<int64_t>(4096, hi - a);
         adam_range(th + a, g + a, m1 + a, m2 + a, n, k);
         if (dst) {
-          if (to_bf16) f32_to_bf16_range(th + a, (uint16_t*)dst + a, n);
+          if (to_bf16) f32_to_bf16_range_stream(th + a, (uint16_t*)dst + a, n);
           else memcpy((float*)dst + a, th + a, (size_t)n * 4);
         }
         if (zero) memset(g + a, 0, (size_t)n * 4);
       }
+      _mm_sfence();  // the image's non-temporal stores are visible before the unit counts as done
     });
   }
 }
 
 // Adam on the given rows of the embedding (and zeroing of their gradients): the same per-element
 // arithmetic as adam_unit, split by rows.
-static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero) {
+// (gsrc: the gradient of rows[q] at gsrc + q H instead of in the gradient block)
+static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero,
+                            const float* gsrc) {
   if (!m->embed_trainable || rows.empty()) return;
   const int64_t H = m->H, f0 = m->embed_flat0;
   parallel_for((int64_t)rows.size(), 16, [&](int64_t lo, int64_t hi) {
     for (int64_t q = lo; q < hi; ++q) {
       const int64_t o = f0 + (int64_t)rows[q] * H;
-      adam_range(m->master + o, m->grad + o, m->mom1 + o, m->mom2 + o, H, k);
+      adam_range(m->master + o, gsrc ? gsrc + q * H : m->grad + o, m->mom1 + o, m->mom2 + o, H, k);
       if (zero) memset(m->grad + o, 0, (size_t)H * 4);
     }
   });

@@ -128,6 +128,7 @@ struct hol_model {
   float* loss_stage = nullptr;   // [Tmax]
   int32_t* lab_stage = nullptr;  // [Tmax]
   float* w_stage = nullptr;      // [Tmax]
+  int32_t* ord_stage = nullptr;  // [2 Tmax + 1] positions by token id, then each token's first index
 
   // device
   hipStream_t sc = nullptr, sh2d = nullptr, sd2h = nullptr;
@@ -139,6 +140,8 @@ struct hol_model {
              ev_head = nullptr, ev_h0 = nullptr;
   uint8_t* head_dev = nullptr;
   float* gdev[MAX_GBUF] = {};
+  int32_t *ord_dev = nullptr, *seg_dev = nullptr;  // the same on the device
+  float* erows = nullptr;                          // [Tmax, H] embedding-row gradients
   float* head_gdev = nullptr;
   float* ckpt = nullptr;
   uint8_t* act_mem = nullptr;

@@ -20,6 +20,8 @@ void adam_range(float* theta, const float* g, float* m, float* v, int64_t n, con
 
 uint16_t f32_to_bf16(float x);
 void f32_to_bf16_range(const float* src, uint16_t* dst, int64_t n);
+// the same values; non-temporal stores (the caller issues a store fence before others read dst)
+void f32_to_bf16_range_stream(const float* src, uint16_t* dst, int64_t n);
 
 // Stage partition; returns false when some layer alone exceeds the memory cap.
 bool partition_stages(const int64_t* t_f, const int64_t* t_b, const int64_t* m_f, const int64_t* m_b,

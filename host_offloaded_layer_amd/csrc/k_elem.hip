@@ -612,6 +612,35 @@ int launch_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, i
 }
 
 // ------------------------------------------------------------------------------------------
+// Embedding-row gradient: out[u] = sum of dh[order[i]] over i in [seg[u], seg[u+1]), added in
+// order of i from zero (the occurrences of one token in position order). One block per row.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void embed_row_sums_k(const float* __restrict__ dh, const int32_t* __restrict__ order,
+                                                        const int32_t* __restrict__ seg, int H, float* __restrict__ out) {
+  const int u = blockIdx.x;
+  const int i0 = seg[u], i1 = seg[u + 1];
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = i0; i < i1; ++i) {
+      const float4 x = *(const float4*)(dh + (int64_t)order[i] * H + c);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    *(float4*)(out + (int64_t)u * H + c) = acc;
+  }
+}
+
+int launch_embed_row_sums(const float* dh, const int32_t* order, const int32_t* seg, int nrows, int H, float* out,
+                          hipStream_t s) {
+  if (nrows <= 0) return 0;
+  if (H % 4) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_row_sums_k, dim3(nrows), dim3(256), 0, s, dh, order, seg, H, out);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // casts and fills
 // ------------------------------------------------------------------------------------------
 template <typename T>

@@ -41,6 +41,9 @@ struct Gemm {
   int ngroups = 0, grp_max_rt = 0;
 };
 int launch_gemm(const Gemm& g, hipStream_t s);
+// out[u][:] = sum over i in [seg[u], seg[u+1]) of dh[order[i]][:], in order of i from zero (fp32)
+int launch_embed_row_sums(const float* dh, const int32_t* order, const int32_t* seg, int nrows, int H, float* out,
+                          hipStream_t s);
 // Row tile of the grouped product.
 constexpr int GEMM_GROUP_BM = 256;
 // Grouped bf16 NT product (K % 64 == 0, 16-byte aligned operands and leading dimensions).
