@@ -70,7 +70,11 @@ def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int
     f_fwd = 2.0 * p_layer * T + attn_fwd
     # backward: dX, plus dW unless the base is frozen (LoRA adapters are negligible); attention 2.5x
     f_bwd = (1 if s.lora_rank else 2) * (2.0 * p_layer * T) + 2.5 * attn_fwd
-    f_layers = L * (f_fwd + f_bwd) + n_recomp * f_fwd
+    # a recomputed block's last layer skips the product that forms its output (dense: the down
+    # projection; the next block restarts from its stored checkpoint)
+    n_blocks_recomp = (L + K - 1) // K - 1
+    f_skip = 0.0 if s.n_experts else n_blocks_recomp * 2.0 * H * F * T
+    f_layers = L * (f_fwd + f_bwd) + n_recomp * f_fwd - f_skip
     f_head = 3 * 2.0 * H * V * T
     return dict(p_layer=p_layer, f_layer=f_layers / L, f_head=f_head, n_recomp=n_recomp,
                 flops=f_layers + f_head,

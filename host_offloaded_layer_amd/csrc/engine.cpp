@@ -754,7 +754,8 @@ static hol_status moe_forward(hol_model* m, const W& w, const Act& A, int T, flo
                                   dt, EPI_STORE)));
     KT(KC_SWIGLU, 0, 3.0 * Tk * Fe * E, launch_swiglu_fwd(A.gup, m->ap, dt, (int)Tk, Fe, s));
     KCHECK(run_grouped(m, grouped(m, A, Tk, H, Fe, m->ap, Fe, w.edown, Fe, (int64_t)H * Fe, A.yp, H, DT_F32, EPI_STORE)));
-    KT(KC_OTHER, 0, (double)T * H * 8 + (double)Tk * H * 4, launch_moe_combine(A.h1, A.yp, A.w, A.slot_pos, T, k, H, hout, s));
+      if (hout)
+      KT(KC_OTHER, 0, (double)T * H * 8 + (double)Tk * H * 4, launch_moe_combine(A.h1, A.yp, A.w, A.slot_pos, T, k, H, hout, s));
     return HOL_OK;
   }
   int64_t off = 0;
@@ -780,7 +781,8 @@ static hol_status moe_forward(hol_model* m, const W& w, const Act& A, int T, flo
                               EPI_STORE)));
     off += me;
   }
-  KT(KC_OTHER, 0, (double)T * H * 8 + (double)Tk * H * 4, launch_moe_combine(A.h1, A.yp, A.w, A.slot_pos, T, k, H, hout, s));
+  if (hout)
+    KT(KC_OTHER, 0, (double)T * H * 8 + (double)Tk * H * 4, launch_moe_combine(A.h1, A.yp, A.w, A.slot_pos, T, k, H, hout, s));
   return HOL_OK;
 }
 
@@ -905,7 +907,8 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   if (m->NE > 0) return moe_forward(m, w, A, T, hout, pos);
   KCHECK(run_gemm(m, gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE)));
   KT(KC_SWIGLU, 0, 3.0 * T * F * E, launch_swiglu_fwd(A.gu, A.a, dt, T, F, s));
-  KCHECK(run_gemm(m, gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H)));
+  if (hout)  // (null: the output is not needed, see the recompute)
+    KCHECK(run_gemm(m, gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H)));
   return HOL_OK;
 }
 
@@ -1553,7 +1556,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       const int l1 = std::min(L, (op.block + 1) * K);
       const Act A = act_at(m, op.pos);
       const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
-      float* hout = (op.layer + 1 < l1) ? act_at(m, op.pos + 1).hin : m->hbuf[0];
+      // the block's last layer: its output (the next block's checkpoint, already stored) is not
+      // needed, and its backward reads only the stored intermediates, so the product that would
+      // form it is skipped
+      float* hout = (op.layer + 1 < l1) ? act_at(m, op.pos + 1).hin : nullptr;
       HSTEP(hipEventRecord(ta, sc));
       STEP(layer_forward(m, w, hin, hout, A, T, n_seq, S, op.pos));
       HSTEP(hipEventRecord(tb, sc));
