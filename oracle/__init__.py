@@ -8,6 +8,8 @@ its Python binding) never does, and the oracle imports nothing from the product.
                   micro-batch summation.
 * ``adam``      - host fp32 Adam and the bf16 refresh of the low-precision copy.
 * ``partition`` - the stage partition by exhaustive search (small L).
+* ``async_opt`` - the staleness-1 asynchronous optimiser schedule (each call's gradient taken at the
+                  parameters from before the previous call's update).
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than itself: finite
 differences, library routines for special cases, closed forms, invariants and the worked
