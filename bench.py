@@ -164,6 +164,10 @@ def main():
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "qwen3_1p7b", "llama8b_16k", "qwen3_235b_slice", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--optimizer", choices=["sync", "async"], default="sync",
+                    help="sync: hol_forward_backward_step (the default, the synchronous step); async: "
+                         "hol_forward_backward_async, the staleness-1 optimiser (each call applies the "
+                         "previous call's update on host threads while it computes)")
     ap.add_argument("--stats-out", default=None,
                     help="write the library's statistics of the last timed step (device timeline included) "
                          "to this JSON file")
@@ -189,7 +193,8 @@ def main():
                           lora_rank=s.lora_rank, lora_scale=s.lora_scale, rope_base=s.rope_base,
                           rms_eps=s.rms_eps, ckpt_every_k=w.ckpt_every_k,
                           compute_dtype=hol.BF16 if w.compute == "bf16" else hol.F32,
-                          max_tokens=w.tokens, max_seq=w.seq, lr=w.lr)
+                          max_tokens=w.tokens, max_seq=w.seq, lr=w.lr,
+                          async_optimizer=int(args.optimizer == "async"))
     t0 = time.perf_counter()
     m = hol.Model(cfg)
     m.set_params(params)
@@ -205,16 +210,22 @@ def main():
     h2d_peak, d2h_peak = link_peak_gbs(torch)
     log(f"[bench] pinned copy peak: H2D {h2d_peak:.1f} GB/s, D2H {d2h_peak:.1f} GB/s")
 
+    mode = {"and_step": True} if args.optimizer == "sync" else {"stale_step": True}
+
     def one_step():
-        # forward_backward + step, with each layer's host Adam overlapped with the rest of the
-        # backward (bitwise the same as the two calls)
+        # sync: forward_backward + step, with each layer's host Adam overlapped with the rest of
+        # the backward (bitwise the same as the two calls); async: forward_backward at the
+        # parameters from before the previous call's update, which runs meanwhile (after the
+        # warmup every timed call applies exactly one update)
         if s.vocab:
-            loss = m.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+            loss = m.forward_backward(w.n_micro, tokens=batch["tokens"], **mode)
         else:
-            loss = m.forward_backward(w.n_micro, hidden=batch["hidden"], loss=hol.LOSS_SUMSQ, and_step=True)
+            loss = m.forward_backward(w.n_micro, hidden=batch["hidden"], loss=hol.LOSS_SUMSQ, **mode)
         st = m.stats()
         return loss, st, st["step_ms"]
 
+    if args.optimizer == "async" and args.warmup < 1:
+        raise SystemExit("--optimizer async needs --warmup >= 1 (the first call applies no update)")
     for i in range(args.warmup):
         loss, fb, step_ms = one_step()
         log(f"[bench] warmup {i}: loss {loss:.4f} fb {fb['fb_ms']:.0f} ms step {step_ms:.0f} ms")
@@ -226,7 +237,9 @@ def main():
         loss, fb, step_ms = one_step()
         recs.append((loss, fb, step_ms))
         log(f"[bench] step {i}: loss {loss:.4f} fb {fb['fb_ms']:.0f} ms step {step_ms:.0f} ms "
-            f"h2d busy {fb['h2d_busy_ms']:.0f} ms compute busy {fb['compute_busy_ms']:.0f} ms")
+            f"h2d busy {fb['h2d_busy_ms']:.0f} ms compute busy {fb['compute_busy_ms']:.0f} ms"
+            + (f" overlapped step {fb['worker_busy_ms']:.0f} ms, copies waited {fb['async_wait_ms']:.0f} ms"
+               if args.optimizer == "async" else ""))
         u = fb.get("units") or []
         if u:
             lag = [e - a for _, a, e in u]
@@ -274,7 +287,9 @@ def main():
                                + (f"{s.n_experts} experts x {s.expert_ffn} top-{s.top_k}" if s.n_experts else f"ffn {s.ffn}")
                                + (f", LoRA r={s.lora_rank} on a frozen base" if s.lora_rank else "")
                                + f", vocab {s.vocab}; {w.n_micro} micro-batches x {w.batch // w.n_micro} x {w.seq} tokens; K={w.ckpt_every_k}",
-                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU, layer streaming)"},
+                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU, layer streaming)",
+                   "optimizer": ("synchronous step (hol_forward_backward_step)" if args.optimizer == "sync" else
+                                 "staleness-1 asynchronous step (hol_forward_backward_async)")},
         "roofline": {"bound": "mfma", "kernel": "gemm_mfma (all decoder and head GEMMs)",
                      "achieved": round(g["tflops"], 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": profiled_traffic(w.name),

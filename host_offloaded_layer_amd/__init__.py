@@ -41,7 +41,7 @@ class Config(C.Structure):
                 ("compute_dtype", C.c_int32), ("lr", C.c_float), ("beta1", C.c_float),
                 ("beta2", C.c_float), ("adam_eps", C.c_float), ("weight_decay", C.c_float),
                 ("device", C.c_int32), ("max_tokens", C.c_int32), ("max_seq", C.c_int32),
-                ("weight_slots", C.c_int32), ("grad_buffers", C.c_int32)]
+                ("weight_slots", C.c_int32), ("grad_buffers", C.c_int32), ("async_optimizer", C.c_int32)]
 
 
 class Batch(C.Structure):
@@ -70,6 +70,7 @@ def _load() -> C.CDLL:
         "hol_set_kernel_timing": [P, I32],
         "hol_forward_backward": [P, C.POINTER(Batch), I32, C.POINTER(D)],
         "hol_forward_backward_step": [P, C.POINTER(Batch), I32, C.POINTER(D)],
+        "hol_forward_backward_async": [P, C.POINTER(Batch), I32, C.POINTER(D)],
         "hol_step": [P],
         "hol_last_stats": [P, C.c_char_p, C.c_size_t],
         "hol_partition": [P, P, P, P, I32, I64, I32, I32, P, C.POINTER(I32), P, C.POINTER(I32),
@@ -109,7 +110,7 @@ lib = _load()
 EXPORTED = ["hol_create", "hol_destroy", "hol_num_tensors", "hol_tensor_info", "hol_set_tensor",
             "hol_get_tensor", "hol_get_grad", "hol_get_routing", "hol_get_adam_state", "hol_set_adam_state",
             "hol_zero_grad", "hol_set_ckpt_every_k", "hol_set_kernel_timing",
-            "hol_forward_backward", "hol_forward_backward_step", "hol_step", "hol_last_stats", "hol_partition",
+            "hol_forward_backward", "hol_forward_backward_step", "hol_forward_backward_async", "hol_step", "hol_last_stats", "hol_partition",
             "hol_host_adam", "hol_host_bf16_round", "hol_last_error", "hol_version",
             "hol_op_gemm", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
             "hol_op_rope", "hol_op_rope_qkv", "hol_op_swiglu_fwd", "hol_op_swiglu_bwd", "hol_op_transpose_bf16", "hol_op_attention_fwd",
@@ -214,7 +215,12 @@ class Model:
 
     def forward_backward(self, n_micro: int, tokens: Optional[np.ndarray] = None,
                          labels: Optional[np.ndarray] = None, hidden: Optional[np.ndarray] = None,
-                         loss: int = LOSS_CE, and_step: bool = False) -> float:
+                         loss: int = LOSS_CE, and_step: bool = False, stale_step: bool = False) -> float:
+        """hol_forward_backward; with ``and_step`` hol_forward_backward_step; with ``stale_step``
+        hol_forward_backward_async (the accumulated gradient's step overlapped, this call's
+        gradient taken at the parameters from before it)."""
+        if and_step and stale_step:
+            raise ValueError("and_step and stale_step are exclusive")
         b = Batch()
         keep = []
         if tokens is not None:
@@ -233,7 +239,8 @@ class Model:
             b.batch, b.seq = hd.shape[0], hd.shape[1]
         b.n_micro = n_micro
         out = C.c_double()
-        fn = lib.hol_forward_backward_step if and_step else lib.hol_forward_backward
+        fn = (lib.hol_forward_backward_step if and_step else
+              lib.hol_forward_backward_async if stale_step else lib.hol_forward_backward)
         check(fn(self._h, C.byref(b), loss, C.byref(out)))
         return out.value
 
@@ -249,10 +256,12 @@ class Model:
 def make_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, *, ckpt_every_k=1,
                 compute_dtype=F32, max_tokens, max_seq, n_experts=0, top_k=0, expert_ffn=0,
                 lora_rank=0, lora_scale=1.0, rope_base=10000.0, rms_eps=1e-5, lr=1e-3, beta1=0.9,
-                beta2=0.999, adam_eps=1e-8, device=0, weight_slots=0, grad_buffers=0) -> Config:
+                beta2=0.999, adam_eps=1e-8, device=0, weight_slots=0, grad_buffers=0,
+                async_optimizer=0) -> Config:
     return Config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_experts, top_k,
                   expert_ffn, lora_rank, lora_scale, rope_base, rms_eps, ckpt_every_k, compute_dtype,
-                  lr, beta1, beta2, adam_eps, 0.0, device, max_tokens, max_seq, weight_slots, grad_buffers)
+                  lr, beta1, beta2, adam_eps, 0.0, device, max_tokens, max_seq, weight_slots, grad_buffers,
+                  async_optimizer)
 
 
 # ------------------------------------------------------------------------------------------

@@ -183,7 +183,14 @@ hol_status hol_forward_backward(hol_model* m, const hol_batch* batch, hol_loss l
 hol_status hol_forward_backward_step(hol_model* m, const hol_batch* batch, hol_loss loss, double* loss_sum_out) {
   GUARD_BEGIN
   if (!m) return einval("hol_forward_backward_step", "null model");
-  return engine_forward_backward(m, batch, loss, loss_sum_out, true);
+  return engine_forward_backward(m, batch, loss, loss_sum_out, FB_FUSED);
+  GUARD_END
+}
+
+hol_status hol_forward_backward_async(hol_model* m, const hol_batch* batch, hol_loss loss, double* loss_sum_out) {
+  GUARD_BEGIN
+  if (!m) return einval("hol_forward_backward_async", "null model");
+  return engine_forward_backward(m, batch, loss, loss_sum_out, FB_ASYNC);
   GUARD_END
 }
 

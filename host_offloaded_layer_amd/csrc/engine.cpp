@@ -106,6 +106,7 @@ static hol_status validate_config(const hol_config& c) {
   if (!(c.rms_eps > 0) || !(c.rope_base > 0)) return bad("rms_eps / rope_base");
   if (c.weight_slots != 0 && (c.weight_slots < 2 || c.weight_slots > 8)) return bad("weight_slots must be 0 or 2..8");
   if (c.grad_buffers != 0 && (c.grad_buffers < 2 || c.grad_buffers > 4)) return bad("grad_buffers must be 0 or 2..4");
+  if (c.async_optimizer != 0 && c.async_optimizer != 1) return bad("async_optimizer must be 0 or 1");
   return HOL_OK;
 }
 
@@ -348,12 +349,14 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->w_stage = (float*)pinned_alloc(m, T * 4, &st);
   if (m->embed_trainable) m->ord_stage = (int32_t*)pinned_alloc(m, (2 * T + 1) * 4, &st);
   if (m->NE > 0) m->counts_stage = (int32_t*)pinned_alloc(m, (int64_t)m->NE * 4, &st);
+  if (c.async_optimizer) m->image_alt = (uint8_t*)pinned_alloc(m, m->image_bytes, &st);
   if (st != HOL_OK) {
     engine_destroy(m);
     return st;
   }
   parallel_zero(m->grad, m->n_flat * 4);
   parallel_zero(m->image, m->image_bytes);
+  if (m->image_alt) parallel_zero(m->image_alt, m->image_bytes);
 
   // ---- device plan
   auto D = [&](int64_t bytes) { return dev_alloc(m, align_up(bytes, 256), &st); };
@@ -545,8 +548,10 @@ void engine_destroy(hol_model* m) {
 // ------------------------------------------------------------------------------------------
 // image refresh (master -> low-precision copy)
 // ------------------------------------------------------------------------------------------
-static uint8_t* image_block(hol_model* m, int block) {
-  return block >= 0 ? m->image + (int64_t)block * m->layer_img_bytes : m->image + (int64_t)m->L * m->layer_img_bytes;
+// block of the image at `base` (m->image unless given)
+static uint8_t* image_block(hol_model* m, int block, uint8_t* base = nullptr) {
+  if (!base) base = m->image;
+  return block >= 0 ? base + (int64_t)block * m->layer_img_bytes : base + (int64_t)m->L * m->layer_img_bytes;
 }
 
 void refresh_image_tensor(hol_model* m, const TensorDesc& t) {
@@ -571,14 +576,18 @@ void read_image_tensor(const hol_model* m, const TensorDesc& t, float* dst) {
   }
 }
 
+// (into both images when the model has two: a frozen tensor's only copy must be in each)
 void write_image_tensor(hol_model* m, const TensorDesc& t, const float* src) {
   if (t.block == -2 || t.img < 0) return;
-  uint8_t* dst = image_block(m, t.block) + t.img;
-  if (t.img_f32 || m->dt == DT_F32) {
-    parallel_for(t.numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy((float*)dst + lo, src + lo, (hi - lo) * 4); });
-  } else {
-    parallel_for(t.numel, 1 << 18,
-                 [&](int64_t lo, int64_t hi) { f32_to_bf16_range(src + lo, (uint16_t*)dst + lo, hi - lo); });
+  for (uint8_t* base : {m->image, m->image_alt}) {
+    if (!base) continue;
+    uint8_t* dst = image_block(m, t.block, base) + t.img;
+    if (t.img_f32 || m->dt == DT_F32) {
+      parallel_for(t.numel, 1 << 18, [&](int64_t lo, int64_t hi) { memcpy((float*)dst + lo, src + lo, (hi - lo) * 4); });
+    } else {
+      parallel_for(t.numel, 1 << 18,
+                   [&](int64_t lo, int64_t hi) { f32_to_bf16_range(src + lo, (uint16_t*)dst + lo, hi - lo); });
+    }
   }
 }
 
@@ -1146,7 +1155,8 @@ static void host_accumulate(void* p) {
   });
 }
 
-static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1, int64_t hi = -1, bool zero = true);
+static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1, int64_t hi = -1, bool zero = true,
+                      float* gbase = nullptr, uint8_t* ibase = nullptr);
 static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero = true,
                             const float* gsrc = nullptr);
 
@@ -1226,14 +1236,96 @@ struct FusedWorker {
   ~FusedWorker() { stop(true); }
 };
 
-hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out, bool fuse_step) {
+// Host step of a staleness-1 call. Once the first layer's inputs are gathered, Adam runs over
+// every unit on a thread of its own with the accumulated gradient, refreshing the second image
+// while the GPU streams from the first, in the order the call's gradient copies land (LM head,
+// layers from the last, embedding). The gradient block is shared: a unit's new gradient copy runs
+// only after the step has read the old one. That wait sits on the gradient-transfer stream (a host
+// function that returns once the unit is done, gate()), so the issuing thread never blocks and the
+// whole call is queued up front. The step clears what the copies do not overwrite (the embedding
+// rows, which the call adds into, and a head the call does not write). finish() waits for the
+// thread and makes its image the streamed one.
+struct AsyncStep {
+  hol_model* m;
+  std::thread th;
+  bool started = false;
+  double busy_ms = 0;
+  std::mutex mu;
+  std::condition_variable cv;
+  std::vector<char> done;  // per unit: old gradient consumed
+  double wait_ms = 0;      // time the transfer stream spent waiting for it
+  double t_call = 0;
+  std::vector<std::array<double, 3>> units, waits;  // {unit, start, end} in ms from the call's start
+  void start(const AdamConsts& kc, bool zero_head, double t_start) {
+    t_call = t_start;
+    const int n = (int)m->unit_tensors.size();  // 0 embedding, 1 + l layer l, L + 1 head
+    done.assign(n, 0);
+    gates.resize(n);
+    for (int u = 0; u < n; ++u) gates[u] = {this, u};
+    started = true;
+    uint8_t* img = m->image_alt;
+    th = std::thread([this, kc, zero_head, n, img] {
+      const double t0 = now_ms();
+      for (int u = n - 1; u >= 0; --u) {
+        const double a = now_ms();
+        adam_unit(m, u, kc, -1, -1, u == 0 || (u == n - 1 && zero_head), m->grad, img);
+        units.push_back({(double)u, a - t_call, now_ms() - t_call});
+        {
+          std::lock_guard<std::mutex> g(mu);
+          done[u] = 1;
+        }
+        cv.notify_all();
+      }
+      busy_ms = now_ms() - t0;
+    });
+  }
+  void wait_unit(int u) {
+    if (!started) return;
+    const double t0 = now_ms();
+    std::unique_lock<std::mutex> lk(mu);
+    cv.wait(lk, [&] { return done[u] != 0; });
+    const double t1 = now_ms();
+    wait_ms += t1 - t0;
+    waits.push_back({(double)u, t0 - t_call, t1 - t_call});
+  }
+  // the stream's later work waits until unit u is done (the host function returns only then; it
+  // depends on host work alone, so it always returns)
+  struct Gate {
+    AsyncStep* a;
+    int u;
+  };
+  std::vector<Gate> gates;
+  static void gate_fn(void* p) {
+    Gate* g = (Gate*)p;
+    g->a->wait_unit(g->u);
+  }
+  hipError_t gate(int u, hipStream_t s) {
+    if (!started) return hipSuccess;
+    return hipLaunchHostFunc(s, gate_fn, &gates[u]);
+  }
+  void finish() {
+    if (!started) return;
+    th.join();
+    started = false;
+    std::swap(m->image, m->image_alt);
+    m->step_t += 1;
+  }
+  ~AsyncStep() {
+    if (started) (void)hipStreamSynchronize(m->sd2h);  // no gate left waiting on this object
+    finish();
+  }
+};
+
+hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out, FbMode mode) {
   const double t_start = now_ms();
+  const bool fuse_step = mode == FB_FUSED, async = mode == FB_ASYNC;
   // ---- validation (nothing touched before this passes)
   auto bad = [](const std::string& s) {
     set_error("hol_forward_backward: " + s);
     return HOL_EINVAL;
   };
   if (!b || !out) return bad("null argument");
+  if (async && !m->image_alt) return bad("the asynchronous optimiser needs a model created with async_optimizer = 1");
   if (m->poisoned) {
     set_error("hol_forward_backward: model poisoned by an earlier device error; call hol_zero_grad");
     return HOL_ESTATE;
@@ -1267,6 +1359,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   }
   m->stats = Stats();
   m->stats.tokens = T;
+  AsyncStep astep{m};
+  const bool apply_prev = async && !m->grads_zero;  // an accumulated gradient to step with
   const int L = m->L, K = m->K;
   const int64_t E = m->E;
   // ---- labels and per-token weights (1/labelled count of the token's micro-batch)
@@ -1354,11 +1448,13 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     for (int l = l1 - 1; l >= l0; --l) ops.push_back({OP_BWD, l, bl, l - l0});
   }
   auto ckpt_of = [&](int idx) { return m->ckpt + (int64_t)idx * T64 * H; };  // idx: block, or nblocks for h_L
-  const bool direct = m->grads_zero;
+  // direct: the copies overwrite the gradient blocks (nothing accumulated, or the accumulated
+  // gradient is consumed by this call's overlapped step before each copy)
+  const bool direct = m->grads_zero || apply_prev;
   // fused optimiser: only when this call's gradients are the whole gradient (nothing accumulated)
-  const bool fused = fuse_step && direct;
+  const bool fused = fuse_step && m->grads_zero;
   // a stale head block that this call does not overwrite is cleared now (the layer blocks are
-  // overwritten whole by their copies)
+  // overwritten whole by their copies; an overlapped step clears it after reading it)
   const bool head_written = m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE && m->head_trainable;
   if (m->grads_stale && !head_written && m->head_flat_n > 0) parallel_zero(m->grad + m->head_flat0, m->head_flat_n * 4);
   const hol_config& cf = m->cfg;
@@ -1429,6 +1525,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 
   STEP(ensure(0, 0));
   gather_h0();
+  // the embedding rows are read: the step may now change the masters
+  if (apply_prev) astep.start(adam_consts(m->step_t + 1, cf.lr, cf.beta1, cf.beta2, cf.adam_eps), !head_written, t_start);
   HSTEP(hipMemcpyAsync(m->ckpt, m->h_stage, T64 * H * 4, hipMemcpyHostToDevice, sc));
   m->stats.h2d_bytes += (double)T64 * H * 4;
   // further weight copies start after h0 is up: the first layer needs both
@@ -1498,6 +1596,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE && m->head_trainable) {
         // head gradient to the host (gradient-transfer stream)
         HSTEP(hipEventRecord(m->ev_gdone[0], sc));
+        HSTEP(astep.gate(m->L + 1, sd));
         HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[0], 0));
         float* dst = direct ? m->grad + m->head_flat0 : m->head_stage;
         hipEvent_t a = tev(), e = tev();
@@ -1581,6 +1680,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       HSTEP(hipEventRecord(m->ev_gdone[gi], sc));
       // gradient offload on the gradient-transfer stream
       float* lg = m->grad + m->layer_flat0 + (int64_t)op.layer * m->layer_flat_n;
+      HSTEP(astep.gate(1 + op.layer, sd));
       hipEvent_t a = tev(), e = tev();
       HSTEP(hipEventRecord(a, sd));
       if (tail) {
@@ -1647,6 +1747,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   // embedding gradient rows: the fused step reads them from the staging buffer in its Adam (the
   // embedding's gradient block stays zero); otherwise they are added into that block
   if (m->embed_trainable && !fused) {
+    astep.wait_unit(0);
     float* gE = m->grad + m->embed_flat0;
     parallel_for(n_rows, 8, [&](int64_t lo, int64_t hi) {
       for (int64_t u = lo; u < hi; ++u) {
@@ -1664,6 +1765,15 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   m->stats.scatter_done_ms = now_ms() - t_start;
   HSTEP(hipStreamSynchronize(sd));
   m->stats.gpu_done_ms = now_ms() - t_start;
+  if (apply_prev) {
+    const double tw = now_ms();
+    astep.finish();
+    m->stats.worker_busy_ms = astep.busy_ms;
+    m->stats.async_wait_ms = astep.wait_ms;
+    m->stats.units = astep.units;
+    m->stats.waits = astep.waits;
+    m->stats.step_ms = now_ms() - tw;  // update time not hidden under the GPU work
+  }
   if (fused) {
     const double t_gpu_done = now_ms();
     worker.stop(false);
@@ -1734,11 +1844,13 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 // ------------------------------------------------------------------------------------------
 // step: host Adam, refresh of the low-precision image, zero_grad
 // ------------------------------------------------------------------------------------------
-// Adam on every trainable tensor of optimiser unit u, refresh of its low-precision image, and
-// zeroing of its gradients.
 // Adam (and the image refresh) on the trainable tensors of unit u, restricted to the flat
-// parameter range [lo, hi) when lo >= 0 (the same per-element arithmetic either way).
-static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int64_t hi, bool zero) {
+// parameter range [lo, hi) when lo >= 0 (the same per-element arithmetic either way); with zero
+// the gradients read are cleared. gbase / ibase: the gradient block read and the image written
+// (m->grad and m->image unless given).
+static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int64_t hi, bool zero, float* gbase,
+                      uint8_t* ibase) {
+  if (!gbase) gbase = m->grad;
   for (int ti : m->unit_tensors[u]) {
     const TensorDesc& t = m->tensors[ti];
     if (!t.trainable) continue;
@@ -1746,12 +1858,12 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
     const int64_t a1 = lo < 0 ? t.numel : std::min<int64_t>(t.numel, hi - t.flat);
     if (a1 <= a0) continue;
     float* th = m->master + t.flat + a0;
-    float* g = m->grad + t.flat + a0;
+    float* g = gbase + t.flat + a0;
     float* m1 = m->mom1 + t.flat + a0;
     float* m2 = m->mom2 + t.flat + a0;
     const bool to_bf16 = !(t.img_f32 || m->dt == DT_F32) && t.img >= 0 && t.block != -2;
     uint8_t* dst = (t.block == -2 || t.img < 0) ? nullptr
-                                                : image_block(m, t.block) + t.img + a0 * (to_bf16 ? 2 : 4);
+                                                : image_block(m, t.block, ibase) + t.img + a0 * (to_bf16 ? 2 : 4);
     parallel_for(a1 - a0, 1 << 16, [&](int64_t lo, int64_t hi) {
       // chunked so the refreshed values are still in cache when converted
       for (int64_t a = lo; a < hi; a += 4096) {
@@ -1866,10 +1978,14 @@ std::string stats_json(const hol_model* m) {
     << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
     << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads()
     << ",\"gpu_done_ms\":" << s.gpu_done_ms << ",\"scatter_done_ms\":" << s.scatter_done_ms
-    << ",\"worker_busy_ms\":" << s.worker_busy_ms << ",\"first_compute_ms\":" << s.first_compute_ms
+    << ",\"worker_busy_ms\":" << s.worker_busy_ms << ",\"async_wait_ms\":" << s.async_wait_ms
+    << ",\"first_compute_ms\":" << s.first_compute_ms
     << ",\"last_compute_end_ms\":" << s.last_compute_end_ms << ",\"units\":[";
   for (size_t i = 0; i < s.units.size(); ++i)
     o << (i ? "," : "") << "[" << (int)s.units[i][0] << "," << s.units[i][1] << "," << s.units[i][2] << "]";
+  o << "],\"async_waits\":[";
+  for (size_t i = 0; i < s.waits.size(); ++i)
+    o << (i ? "," : "") << "[" << (int)s.waits[i][0] << "," << s.waits[i][1] << "," << s.waits[i][2] << "]";
   o << "],\"timeline\":[";
   for (size_t i = 0; i < s.timeline.size(); ++i)
     o << (i ? "," : "") << "[" << (int)s.timeline[i][0] << "," << s.timeline[i][1] << "," << s.timeline[i][2] << "]";

@@ -73,9 +73,12 @@ struct Stats {
   // host timeline of a fused call (ms from the call's start): GPU work drained, embedding
   // scatter-add done; per optimiser unit: gradient arrived on the host, Adam done
   double gpu_done_ms = 0, scatter_done_ms = 0, worker_busy_ms = 0;
+  // staleness-1 call: time the issuing thread waited for the overlapped step to read old gradients
+  double async_wait_ms = 0;
   // device timeline (ms after the first weight copy starts): first compute op starts, last ends
   double first_compute_ms = 0, last_compute_end_ms = 0;
   std::vector<std::array<double, 3>> units;  // {unit, arrived, done}
+  std::vector<std::array<double, 3>> waits;  // staleness-1 call: {unit, wait start, wait end}
   // device spans of the call: {class (0 h2d, 1 d2h, 2 fwd, 3 recompute, 4 bwd, 5 head), start, end}
   // in ms after the first weight copy starts
   std::vector<std::array<float, 3>> timeline;
@@ -106,6 +109,9 @@ struct hol_model {
   float* mom1 = nullptr;
   float* mom2 = nullptr;
   uint8_t* image = nullptr;  // low-precision copy, layer-contiguous, 4 KiB aligned (pinned)
+  // staleness-1 asynchronous optimiser (allocated only when configured): the second image takes
+  // the step's refreshed copy while the GPU streams from the first
+  uint8_t* image_alt = nullptr;
   int64_t layer_img_bytes = 0, head_img_bytes = 0, image_bytes = 0;
   // layer image offsets (bytes); MoE: router [E, H], expert gates [E, Fe, H], ups [E, Fe, H],
   // downs [E, H, Fe]; LoRA factors fp32: A [r, in], B [out, r] for q, k, v, o
@@ -232,8 +238,12 @@ struct hol_model {
 namespace hol {
 hol_status engine_create(const hol_config* cfg, hol_model** out);
 void engine_destroy(hol_model* m);
+// mode: FB_PLAIN (gradients accumulated), FB_FUSED (forward_backward then step, the step
+// overlapped where nothing was accumulated before), FB_ASYNC (the accumulated gradient's step runs
+// on the host while this call computes at the parameters from before it)
+enum FbMode { FB_PLAIN = 0, FB_FUSED = 1, FB_ASYNC = 2 };
 hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss loss, double* out,
-                                  bool fuse_step = false);
+                                  FbMode mode = FB_PLAIN);
 hol_status engine_step(hol_model* m);
 hol_status engine_zero_grad(hol_model* m);
 hol_status engine_set_k(hol_model* m, int k);

@@ -85,6 +85,9 @@ typedef struct {
                                * depend on it. */
   int32_t grad_buffers;       /* HBM layer-gradient buffers awaiting the device->host copy, 2..4;
                                * 0: 3. Results do not depend on it. */
+  int32_t async_optimizer;    /* 1: also allocate a second pinned low-precision image, which
+                               * hol_forward_backward_async needs; 0: none (that call returns
+                               * HOL_EINVAL). */
 } hol_config;
 
 /* One forward_backward input. tokens: int32 [batch*seq] (vocab > 0); labels: int32
@@ -163,11 +166,34 @@ hol_status hol_set_kernel_timing(hol_model* m, int32_t on);
 hol_status hol_forward_backward_step(hol_model* m, const hol_batch* batch, hol_loss loss,
                                      double* loss_sum_out);
 
+/* Staleness-1 asynchronous optimiser (RoundPipe paper summary, 异步优化器 and 方法步骤详情 step 6):
+ * the host optimiser step of one call's gradients runs while the next call computes, and that call
+ * does not wait for it. One call does three things:
+ *   1. a streamed forward + backward of `batch` at the parameters as they stand when the call
+ *      starts (what hol_get_tensor returns then);
+ *   2. meanwhile, if gradients are accumulated (from the previous async call, or from
+ *      hol_forward_backward calls since the last step or zero_grad), hol_step's update with them,
+ *      on host threads (Adam, step counter + 1, refresh of the low-precision copy);
+ *   3. on return this call's gradients are the accumulated gradients (hol_get_grad reads them).
+ * So with theta_0 the starting parameters and g_t the gradient of the t-th call in a row,
+ * g_t = grad L_t(theta_{t-2}) (theta_{-1} = theta_0) and theta_t = Adam(theta_{t-1}, g_t), applied
+ * by call t + 1, or by hol_step at the end. Apart from the parameters the gradient is taken at,
+ * this is hol_forward_backward followed by hol_step, bit for bit. The first call in a row (nothing
+ * accumulated) applies no update. Needs cfg.async_optimizer = 1 (HOL_EINVAL otherwise): the update
+ * refreshes the second image while the GPU streams from the first. The gradient block is shared:
+ * each unit's new gradient copy (LM head, then layers from the last, then the embedding rows) is
+ * issued only once the update has read that unit's old gradient. Every other call keeps its
+ * meaning. A device error poisons the model as in hol_forward_backward; the overlapped update has
+ * then still been applied whole. */
+hol_status hol_forward_backward_async(hol_model* m, const hol_batch* batch, hol_loss loss,
+                                      double* loss_sum_out);
+
 /* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated).
  * Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms, compute_busy_ms,
  * n_weight_streams, per-kernel-class compute ms, and for hol_forward_backward_step the host
  * timeline (gpu_done_ms, scatter_done_ms, worker_busy_ms, units = [unit, start, end] of each
- * optimiser unit in ms from the call's start). HOL_EINVAL, with nothing written, when the
+ * optimiser unit in ms from the call's start); for hol_forward_backward_async worker_busy_ms is the
+ * overlapped step's time and async_wait_ms the time gradient copies waited for it. HOL_EINVAL, with nothing written, when the
  * object does not fit in cap bytes. */
 hol_status hol_last_stats(const hol_model* m, char* json, size_t cap);
 

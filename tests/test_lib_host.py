@@ -105,7 +105,7 @@ def _tiny_cfg(**kw):
                                  dict(ffn=170, compute_dtype=hol.BF16), dict(ckpt_every_k=0),
                                  dict(max_seq=100), dict(vocab=250, compute_dtype=hol.BF16), dict(ffn=0),
                                  dict(weight_slots=1), dict(weight_slots=9), dict(grad_buffers=1),
-                                 dict(grad_buffers=5)])
+                                 dict(grad_buffers=5), dict(async_optimizer=2), dict(async_optimizer=-1)])
 def test_create_rejects_bad_config_before_touching_device(bad):
     h = C.c_void_p()
     cfg = _tiny_cfg(**bad)
@@ -131,6 +131,7 @@ def test_create_rejects_bad_moe_lora_config(bad):
 
 def test_null_arguments_are_einval():
     assert hol.lib.hol_forward_backward(None, None, 0, None) == hol.HOL_EINVAL
+    assert hol.lib.hol_forward_backward_async(None, None, 0, None) == hol.HOL_EINVAL
     assert hol.lib.hol_step(None) == hol.HOL_EINVAL
     assert hol.lib.hol_zero_grad(None) == hol.HOL_EINVAL
     assert b"null" in hol.lib.hol_last_error()
