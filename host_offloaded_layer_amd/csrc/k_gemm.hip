@@ -479,6 +479,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt2(Gemm g) {
 // NT3: the same 256 x 256 block and 8-wave grid with 64-deep stages in a 2-slot ring, so one block
 // barrier covers twice the MFMA work. A tile row (64 bf16) is one 128-byte LDS row; physical
 // 16-byte chunk = logical chunk ^ ((row / 2) % 8) (16 consecutive rows read conflict-free).
+// Ungrouped launches are persistent: one block per CU walks several tiles, and the first two
+// stages of its next tile are in flight while it stores the current one (a block that stored and
+// exited would leave its CU idle through the next block's first loads).
 // ------------------------------------------------------------------------------------------
 constexpr int N3_BK = 64;
 constexpr int N3_TILE = (N2_BM + N2_BN) * N3_BK;  // bf16 elements per stage
@@ -603,9 +606,19 @@ __device__ __forceinline__ void n3_store(const Gemm& g, const f32x16 (&acc)[4][W
   }
 }
 
+// Whether a tile's epilogue is guaranteed to issue one vector store (and, for the accumulate and
+// residual epilogues, one vector load) per quad of every wave: a full tile with the vector path.
+template <int EPI, typename TO>
+__device__ __forceinline__ bool n3_full_tile(const Gemm& g, const TO* C, const float* R, int M, int N, int m0, int n0) {
+  constexpr int VB = 4 * (int)sizeof(TO);
+  return m0 + N2_BM <= M && n0 + N2_BN <= N && g.ldc % 4 == 0 && (uintptr_t)C % VB == 0 &&
+         (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
+}
+
 template <int EPI, typename TO, int NW, bool BUF, bool GRP>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
+  static_assert(NW == 8, "the epilogue count below assumes 8 waves");
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * N3_TILE];
   int M = g.M;
   const int N = g.N, K = g.K;
@@ -616,6 +629,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   const float* R = g.R ? g.R + z * g.sR : nullptr;
   const int tiles_n = (N + N2_BN - 1) / N2_BN;
   int m0, n0;
+  // tile sequence: grouped, one tile; otherwise the tiles are dealt in 8 contiguous ranges, one
+  // per XCD (workgroup i runs on XCD i % 8), and the XCD's blocks take its tiles in turn, so the
+  // 32 tiles in flight on one XCD share A and B panels in its L2
+  int p = 0, p_end = 1, p_step = 1;
+  const int tiles_m = (M + N2_BM - 1) / N2_BM;
+  auto origin = [&](int q) {
+    const int GM = 4;
+    const int group = GM * tiles_n;
+    const int first_m = (q / group) * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    m0 = (first_m + (q % group) % gsz) * N2_BM;
+    n0 = ((q % group) / gsz) * N2_BN;
+  };
   if constexpr (GRP) {
     const int G = g.ngroups;
     const int32_t* roff = g.grp;
@@ -642,18 +668,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
     m0 = (rt - toff[lo]) * N2_BM;
     n0 = tn * N2_BN;
   } else {
-    const int tiles_m = (M + N2_BM - 1) / N2_BM;
     const int ntiles = tiles_m * tiles_n;
-    int pid = blockIdx.x;
-    if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-    const int GM = 4;
-    const int group = GM * tiles_n;
-    const int first_m = (pid / group) * GM;
-    const int gsz = min(tiles_m - first_m, GM);
-    const int tm = first_m + (pid % group) % gsz;
-    const int tn = (pid % group) / gsz;
-    m0 = tm * N2_BM;
-    n0 = tn * N2_BN;
+    const int x = blockIdx.x & 7;
+    p = (int)((int64_t)ntiles * x / 8) + (blockIdx.x >> 3);
+    p_end = (int)((int64_t)ntiles * (x + 1) / 8);
+    p_step = gridDim.x >> 3;
+    if (p >= p_end) return;
+    origin(p);
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w / (NW / 2), wn = w % (NW / 2);
@@ -667,7 +688,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 
   const int nk = K / N3_BK;
   N3Buf<NW> nb;
-  if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N);
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)M * g.lda * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb =
@@ -676,8 +696,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
     if constexpr (BUF) nb.issue(stage, ra, rb, k0);
     else n3_issue<NW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, k0);
   };
-  issue(lds, 0);
-  if (nk > 1) issue(lds + N3_TILE, N3_BK);
+  auto start_tile = [&]() {
+    if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N);
+    issue(lds, 0);
+    if (nk > 1) issue(lds + N3_TILE, N3_BK);
+  };
   bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
   auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
     const bf16* Bs = st + N2_BM * N3_BK;
@@ -693,33 +716,60 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 #pragma unroll
       for (int j = 0; j < WJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
-  // stage 0 ready (stage 1's 64 / NW loads may still be in flight)
-  if (nk > 1) {
-    if constexpr (NW == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  frags(lds, 0, a0, b0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const bf16* st = lds + (kt & 1) * N3_TILE;
-    frags(st, 1, a1, b1);
-    mma(a0, b0);
-    frags(st, 2, a0, b0);
-    mma(a1, b1);
-    frags(st, 3, a1, b1);
-    mma(a0, b0);
-    if (kt + 1 < nk) {
-      // stage kt + 1 is the only load in flight; once every wave has also finished reading this
-      // slot, it takes stage kt + 2
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
-      frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
+  start_tile();
+  // memory operations the previous tile's epilogue issued after this tile's first two stages, at
+  // least (vmcnt counts loads and stores together, in issue order): 0 for the first tile
+  int after = 0;
+  for (;;) {
+    // stage 0 ready (stage 1's loads and the previous epilogue may still be in flight)
+    if (nk > 1) {
+      if (after) asm volatile("s_waitcnt vmcnt(40)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      if (after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    mma(a1, b1);
+    frags(lds, 0, a0, b0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const bf16* st = lds + (kt & 1) * N3_TILE;
+      frags(st, 1, a1, b1);
+      mma(a0, b0);
+      frags(st, 2, a0, b0);
+      mma(a1, b1);
+      frags(st, 3, a1, b1);
+      mma(a0, b0);
+      if (kt + 1 < nk) {
+        // stage kt + 1 is the only load in flight (for the first stage of a tile, behind it at
+        // most the previous epilogue's memory operations); once every wave has also finished
+        // reading this slot, it takes stage kt + 2
+        if (kt == 0 && after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
+        frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
+      }
+      mma(a1, b1);
+    }
+    // next tile: its first two stages go up before this tile's results go out
+    const int cm0 = m0, cn0 = n0;
+    p += p_step;
+    const bool next = !GRP && p < p_end;
+    if (next) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave done with both slots
+      origin(p);
+      start_tile();
+      asm volatile("" ::: "memory");
+    }
+    after = n3_full_tile<EPI, TO>(g, C, R, M, N, cm0, cn0) ? 1 : 0;
+    n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, cm0, cn0, wm, wn, lane);
+    if (!next) break;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
-
-  n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, m0, n0, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -912,11 +962,25 @@ HOL_NT3_INST(false)
 HOL_NT3_INST(true)
 #undef HOL_NT3_INST
 
+// persistent grid of the ungrouped GEMM: one block per CU (a block fills a CU's LDS), in whole
+// XCD rounds of 8
+static int n3_persistent_grid(int ntiles) {
+  static int ncu = 0;
+  if (!ncu) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    ncu = n;
+  }
+  const int g = ntiles < ncu ? ntiles : ncu;
+  return (g + 7) / 8 * 8;
+}
+
 template <int EPI, typename TO, bool GRP>
 static int launch_nt3_t(const Gemm& g, hipStream_t s) {
   const int tn = (g.N + N2_BN - 1) / N2_BN;
   // grouped: an upper bound of the tile count rounded up to the 8 XCD ranges
-  const int tiles = GRP ? (int)((((int64_t)g.grp_max_rt * tn) + 7) / 8 * 8) : ((g.M + N2_BM - 1) / N2_BM) * tn;
+  const int tiles = GRP ? (int)((((int64_t)g.grp_max_rt * tn) + 7) / 8 * 8) : n3_persistent_grid(((g.M + N2_BM - 1) / N2_BM) * tn);
   if (tiles <= 0) return 0;
   if (n3_buffer_ok(g))
     hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true, GRP>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
