@@ -64,3 +64,44 @@ def test_llama8b_full_size_properties():
         assert sum(parts) == pytest.approx(la, rel=1e-6)
         for n in names:
             assert rel_l2(gs[n], ga[n]) < 1e-5, (n, rel_l2(gs[n], ga[n]))
+
+
+def test_llama8b_full_size_staleness_one():
+    """The staleness-1 optimiser at the bench configuration: the first two calls over the same
+    batch both see the starting parameters, so they return the same loss and the same gradients
+    bit for bit; the second call's overlapped update is the host Adam step on the first call's
+    gradient (checked bit for bit on sampled tensors against the oracle's Adam); the third call
+    sees the updated parameters."""
+    from oracle import adam as OA
+
+    w = W.WORKLOADS["llama8b"]
+    params = W.make_params(w, threads=16)
+    batch = W.make_batch(w)
+    tokens = batch["tokens"]
+    small = ["layers.0.wq", "layers.31.attn_norm", "final_norm"]
+    with lib_model(w, params, async_opt=1) as m:
+        theta0 = {n: params[n].astype(np.float32) for n in small}
+        del params
+        names = [n for n in SAMPLE if n in m.index]
+        l1 = m.forward_backward(w.n_micro, tokens=tokens, stale_step=True)
+        g1 = {n: m.get_grad(n) for n in names}
+        l2 = m.forward_backward(w.n_micro, tokens=tokens, stale_step=True)
+        g2 = {n: m.get_grad(n) for n in names}
+        print("losses", l1, l2, m.stats()["worker_busy_ms"], m.stats()["async_wait_ms"])
+        assert l1 == l2
+        for n in names:
+            assert np.array_equal(g1[n].view(np.uint32), g2[n].view(np.uint32)), n
+        for n in small:
+            th = theta0[n].copy()
+            m1 = np.zeros_like(th)
+            m2 = np.zeros_like(th)
+            OA.adam_update(th, g1[n], m1, m2, 1, lr=w.lr, b1=w.beta1, b2=w.beta2, eps=w.adam_eps)
+            a, b, st = m.get_adam_state(n)
+            assert st == 1
+            assert np.array_equal(m.get_tensor(n).view(np.uint32), th.view(np.uint32)), n
+            assert np.array_equal(a.view(np.uint32), m1.view(np.uint32)), n
+            assert np.array_equal(b.view(np.uint32), m2.view(np.uint32)), n
+        l3 = m.forward_backward(w.n_micro, tokens=tokens, stale_step=True)
+        print("third call", l3)
+        assert l3 != l1 and math.isfinite(l3)
+        assert m.get_adam_state(small[0])[2] == 2
