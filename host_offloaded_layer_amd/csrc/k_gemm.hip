@@ -532,7 +532,8 @@ struct N3Buf {
     }
   }
   __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int k0) const {
-    const int w = threadIdx.x >> 6;
+    // wave-uniform, so the LDS destinations are scalar arithmetic
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < 32 / NW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + (w + NW * i) * 8 * N3_BK), 16, va[i], k0 * 2, 0, 0);
@@ -730,7 +731,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     frags(lds, 0, a0, b0);
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt + 1 < nk; ++kt) {
       const bf16* st = lds + (kt & 1) * N3_TILE;
       frags(st, 1, a1, b1);
       mma(a0, b0);
@@ -738,15 +739,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       mma(a1, b1);
       frags(st, 3, a1, b1);
       mma(a0, b0);
-      if (kt + 1 < nk) {
-        // stage kt + 1 is the only load in flight (for the first stage of a tile, behind it at
-        // most the previous epilogue's memory operations); once every wave has also finished
-        // reading this slot, it takes stage kt + 2
-        if (kt == 0 && after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
-        frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
-      }
+      // stage kt + 1 is the only load in flight (for the first stage of a tile, behind it at
+      // most the previous epilogue's memory operations); once every wave has also finished
+      // reading this slot, it takes stage kt + 2
+      if (kt == 0 && after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
+      frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
+      mma(a1, b1);
+    }
+    {  // the tile's last stage
+      const bf16* st = lds + ((nk - 1) & 1) * N3_TILE;
+      frags(st, 1, a1, b1);
+      mma(a0, b0);
+      frags(st, 2, a0, b0);
+      mma(a1, b1);
+      frags(st, 3, a1, b1);
+      mma(a0, b0);
       mma(a1, b1);
     }
     // next tile: its first two stages go up before this tile's results go out
