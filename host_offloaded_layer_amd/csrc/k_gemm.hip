@@ -834,7 +834,7 @@ struct T3Buf {
   }
   __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t sa,
                                         uint32_t sb) const {
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar LDS destinations
 #pragma unroll
     for (int i = 0; i < 32 / NW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + (w + NW * i) * 512), 16, va[i], (int)sa, 0, 0);
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_tn3(Gemm g) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   frags(lds, 0, a0, b0);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     const bf16* st = lds + (kt & 1) * N3_TILE;
     frags(st, 1, a1, b1);
     mma(a0, b0);
@@ -927,11 +927,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_tn3(Gemm g) {
     mma(a1, b1);
     frags(st, 3, a1, b1);
     mma(a0, b0);
-    if (kt + 1 < nk) {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, kt + 2);
-      frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
-    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, kt + 2);
+    frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
+    mma(a1, b1);
+  }
+  {  // the last stage, peeled (as in the NT kernel)
+    const bf16* st = lds + ((nk - 1) & 1) * N3_TILE;
+    frags(st, 1, a1, b1);
+    mma(a0, b0);
+    frags(st, 2, a0, b0);
+    mma(a1, b1);
+    frags(st, 3, a1, b1);
+    mma(a0, b0);
     mma(a1, b1);
   }
   n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, m0, n0, wm, wn, lane);
