@@ -324,6 +324,12 @@ hol_status hol_op_swiglu_bwd(const void* da, const void* gu, void* dgu, hol_dtyp
                   "hol_op_swiglu_bwd");
 }
 
+hol_status hol_op_swiglu_bwd_t(const void* da, const void* gu, void* dgu, void* dgut, int64_t ldt, int32_t T,
+                               int32_t F, void* stream) {
+  if (T < 0 || F < 0) return einval("hol_op_swiglu_bwd_t", "negative size");
+  return launched(launch_swiglu_bwd_tr(da, gu, dgu, dgut, ldt, T, F, (hipStream_t)stream), "hol_op_swiglu_bwd_t");
+}
+
 hol_status hol_op_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, int32_t R, int32_t C,
                                  void* stream) {
   if (R < 0 || C < 0) return einval("hol_op_transpose_bf16", "negative size");

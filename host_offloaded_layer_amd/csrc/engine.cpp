@@ -981,11 +981,16 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
       KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
       KCHECK(run_gemm(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
     }
-    KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
+    // (with weight gradients the SwiGLU backward also writes dgu^T for the dWgu product)
+    const bool dgu_t = tw && F % 64 == 0;
+    if (dgu_t)
+      KT(KC_SWIGLU, 0, 7.0 * T * F * E, launch_swiglu_bwd_tr(m->da, A.gu, m->dgu, m->yT, T, T, F, s));
+    else
+      KT(KC_SWIGLU, 0, 5.0 * T * F * E, launch_swiglu_bwd(m->da, A.gu, m->dgu, dt, T, F, s));
     // dn2 = dgu Wgu, dWgu = dgu^T n2
     KCHECK(run_gemm(m, nt(T, H, 2 * F, m->dgu, 2 * F, WguT, 2 * F, m->dn, H, DT_F32)));
     if (tw) {
-      KCHECK(tr(m, m->dgu, 2 * F, m->yT, T, T, 2 * F));
+      if (!dgu_t) KCHECK(tr(m, m->dgu, 2 * F, m->yT, T, T, 2 * F));
       KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
       KCHECK(run_gemm(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
     }

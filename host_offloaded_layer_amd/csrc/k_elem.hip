@@ -612,6 +612,87 @@ int launch_transpose_bf16(const void* in, int64_t ldi, void* out, int64_t ldo, i
 }
 
 // ------------------------------------------------------------------------------------------
+// SwiGLU backward that also writes its result transposed (bf16): dgu [T][2F] as launch_swiglu_bwd
+// writes it (bit for bit), and dguT [2F][T] for the weight-gradient product, so the gradient is
+// not read back for a separate transpose. A block takes 128 tokens x 64 features: phase 1 reads
+// da, gate and up for its rows (a thread: 8 features of 4 rows), computes the gate and up
+// gradients, stores the dgu rows and parks both 128 x 64 halves in one 128 x 128 LDS tile (gate
+// gradients in columns 0..63, up gradients in 64..127); phase 2 is the transpose kernel's
+// 8 x 8-block pass, writing output rows f0 + c (gate) and F + f0 + c - 64 (up).
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void swiglu_bwd_tr_k(const bf16* __restrict__ da, const bf16* __restrict__ gu,
+                                                       bf16* __restrict__ dgu, bf16* __restrict__ dgut, int64_t ldt,
+                                                       int T, int F) {
+  __shared__ tu32x4 tile[128 * 16];
+  const int t0 = blockIdx.y * 128, f0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+  const int cf = t & 7;  // features f0 + 8 cf .. + 7
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = (t >> 3) + 32 * k, row = t0 + r;
+    float dg[8], du[8];
+    if (row < T) {
+      const bf16* gr = gu + (int64_t)row * 2 * F + f0 + 8 * cf;
+      float g[8], up[8], d[8];
+      ld8(gr, g);
+      ld8(gr + F, up);
+      ld8(da + (int64_t)row * F + f0 + 8 * cf, d);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) swiglu_b(d[j], g[j], up[j], dg[j], du[j]);
+      bf16* dr = dgu + (int64_t)row * 2 * F + f0 + 8 * cf;
+      st8(dr, dg);
+      st8(dr + F, du);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dg[j] = du[j] = 0.f;
+    }
+    bf16x8 xg, xu;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xg[j] = (bf16)dg[j];
+      xu[j] = (bf16)du[j];
+    }
+    tile[r * 16 + (cf ^ ((r >> 3) & 15))] = __builtin_bit_cast(tu32x4, xg);
+    tile[r * 16 + ((8 + cf) ^ ((r >> 3) & 15))] = __builtin_bit_cast(tu32x4, xu);
+  }
+  __syncthreads();
+  // phase 2: thread owns the 8x8 block of token rows rb * 8.., tile columns cb * 8..
+  const int rb = t % 16, cb = t / 16;
+  tu32x4 in8[8], o8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rb * 8 + i;
+    in8[i] = tile[r * 16 + (cb ^ ((r >> 3) & 15))];
+  }
+  tr8x8(in8, o8);
+  const int tok = t0 + rb * 8;                                   // first output column
+  const int64_t orow = cb < 8 ? f0 + cb * 8 : (int64_t)F + f0 + (cb - 8) * 8;  // first output row
+  uint16_t* dst = (uint16_t*)dgut + orow * ldt + tok;
+  if (tok + 8 <= T) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(tu32x4*)(dst + (int64_t)j * ldt) = o8[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint16_t* e = (const uint16_t*)&o8[j];
+      for (int q = 0; q < 8 && tok + q < T; ++q) dst[(int64_t)j * ldt + q] = e[q];
+    }
+  }
+}
+
+int launch_swiglu_bwd_tr(const void* da, const void* gu, void* dgu, void* dgut, int64_t ldt, int T, int F,
+                         hipStream_t s) {
+  if (T <= 0 || F <= 0) return 0;
+  if (F % 64 || T % 8 || ldt % 8 || ldt < T ||
+      (((uintptr_t)da | (uintptr_t)gu | (uintptr_t)dgu | (uintptr_t)dgut) % 16))
+    return (int)hipErrorInvalidValue;
+  dim3 grid(F / 64, (T + 127) / 128);
+  hipLaunchKernelGGL(swiglu_bwd_tr_k, grid, dim3(256), 0, s, (const bf16*)da, (const bf16*)gu, (bf16*)dgu,
+                     (bf16*)dgut, ldt, T, F);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Embedding-row gradient: out[u] = sum of dh[order[i]] over i in [seg[u], seg[u+1]), added in
 // order of i from zero (the occurrences of one token in position order). One block per row.
 // ------------------------------------------------------------------------------------------

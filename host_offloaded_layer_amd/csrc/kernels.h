@@ -76,6 +76,10 @@ int launch_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int T,
 int launch_swiglu_fwd(const void* gu, void* a, DType t, int T, int F, hipStream_t s);
 // dgu = [dg | du] from da.
 int launch_swiglu_bwd(const void* da, const void* gu, void* dgu, DType t, int T, int F, hipStream_t s);
+// bf16 SwiGLU backward writing dgu [T][2F] (as launch_swiglu_bwd) and its transpose dgut [2F][T]
+// (row stride ldt); F % 64 == 0, T % 8 == 0, 16-byte aligned pointers, else hipErrorInvalidValue.
+int launch_swiglu_bwd_tr(const void* da, const void* gu, void* dgu, void* dgut, int64_t ldt, int T, int F,
+                         hipStream_t s);
 
 // out[c][r] = in[r][c] for an R x C bf16 matrix (row strides ldi, ldo; multiples of 8, 16-byte
 // aligned pointers).

@@ -60,6 +60,12 @@ hol_status hol_op_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo,
 hol_status hol_op_swiglu_fwd(const void* gu, void* a, hol_dtype t, int32_t T, int32_t F, void* stream);
 hol_status hol_op_swiglu_bwd(const void* da, const void* gu, void* dgu, hol_dtype t, int32_t T,
                              int32_t F, void* stream);
+/* bf16 SwiGLU backward that also writes its result transposed: dgu [T, 2F] exactly as
+ * hol_op_swiglu_bwd writes it, and dgut [2F, T] (row stride ldt >= T) for the weight-gradient
+ * product dW_gate|up = dgu^T n2. F % 64 == 0, T % 8 == 0, ldt % 8 == 0 and 16-byte aligned
+ * pointers, else HOL_EINVAL. */
+hol_status hol_op_swiglu_bwd_t(const void* da, const void* gu, void* dgu, void* dgut, int64_t ldt,
+                               int32_t T, int32_t F, void* stream);
 
 /* bf16 transpose out[c][r] = in[r][c] of an R x C matrix at row strides ldi, ldo (elements,
  * multiples of 8; 16-byte aligned pointers, else HOL_EINVAL). The backward uses it to present

@@ -292,6 +292,35 @@ def test_swiglu_vector_and_scalar_kernels_agree_bitwise(dt):
     for x, y in zip(outs[0], outs[1]):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
+@pytest.mark.parametrize("T,F,ldt", [(200, 128, 200), (1000, 640, 1008), (128, 64, 136), (8, 64, 8)])
+def test_swiglu_bwd_with_transpose_bitwise(T, F, ldt):
+    """The fused SwiGLU backward writes dgu exactly as hol_op_swiglu_bwd does and dgu^T exactly as
+    hol_op_transpose_bf16 transposes it (ragged token tiles, a padded output stride, one tile row
+    of 8 tokens); nothing is written past column T of the transposed rows."""
+    r = np.random.default_rng(5)
+    gud = dev(r.standard_normal((T, 2 * F)).astype(np.float32) * 2, torch.bfloat16)
+    dad = dev(r.standard_normal((T, F)).astype(np.float32), torch.bfloat16)
+    ref = torch.empty((T, 2 * F), dtype=torch.bfloat16, device=DEV)
+    ref_t = torch.empty((2 * F, T), dtype=torch.bfloat16, device=DEV)
+    hol.check(hol.lib.hol_op_swiglu_bwd(dad.data_ptr(), gud.data_ptr(), ref.data_ptr(), hol.BF16, T, F, None))
+    hol.check(hol.lib.hol_op_transpose_bf16(ref.data_ptr(), 2 * F, ref_t.data_ptr(), T, T, 2 * F, None))
+    dgu = torch.zeros((T, 2 * F), dtype=torch.bfloat16, device=DEV)
+    dgut = torch.full((2 * F, ldt), 7.0, dtype=torch.bfloat16, device=DEV)
+    hol.check(hol.lib.hol_op_swiglu_bwd_t(dad.data_ptr(), gud.data_ptr(), dgu.data_ptr(), dgut.data_ptr(), ldt, T, F,
+                                          None))
+    sync()
+    assert torch.equal(dgu, ref)
+    assert torch.equal(dgut[:, :T], ref_t)
+    assert torch.all(dgut[:, T:] == 7.0)
+
+
+def test_swiglu_bwd_with_transpose_rejects_unsupported_shapes():
+    x = torch.zeros(4096, dtype=torch.bfloat16, device=DEV)
+    p = x.data_ptr()
+    assert hol.lib.hol_op_swiglu_bwd_t(p, p, p, p, 16, 16, 48, None) == hol.HOL_EINVAL   # F % 64
+    assert hol.lib.hol_op_swiglu_bwd_t(p, p, p, p, 16, 12, 64, None) == hol.HOL_EINVAL   # T % 8
+    assert hol.lib.hol_op_swiglu_bwd_t(p, p, p, p, 8, 16, 64, None) == hol.HOL_EINVAL    # ldt < T
+
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("dt,S,nseq,nq,nkv,d", [
     (hol.F32, 32, 2, 4, 4, 16),
