@@ -482,6 +482,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking));
   HCHECK(hipStreamCreateWithFlags(&m->sh2d, hipStreamNonBlocking));
   HCHECK(hipStreamCreateWithFlags(&m->sd2h, hipStreamNonBlocking));
+  HCHECK(hipStreamCreateWithFlags(&m->spf, hipStreamNonBlocking));
   for (int i = 0; i < m->nslots; ++i) {
     HCHECK(hipEventCreateWithFlags(&m->ev_ready[i], hipEventDisableTiming));
     HCHECK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
@@ -491,6 +492,8 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
     HCHECK(hipEventCreateWithFlags(&m->ev_gfree[i], hipEventDisableTiming));
   }
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->ev_head_done, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->ev_head_pf, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->tail_mlp_ev, hipEventDisableTiming));
@@ -515,6 +518,7 @@ void engine_destroy(hol_model* m) {
   if (m->sc) hipStreamSynchronize(m->sc);
   if (m->sh2d) hipStreamSynchronize(m->sh2d);
   if (m->sd2h) hipStreamSynchronize(m->sd2h);
+  if (m->spf) hipStreamSynchronize(m->spf);
   for (int i = 0; i < hol_model::MAX_SLOTS; ++i) {
     if (m->ev_ready[i]) hipEventDestroy(m->ev_ready[i]);
     if (m->ev_free[i]) hipEventDestroy(m->ev_free[i]);
@@ -524,6 +528,8 @@ void engine_destroy(hol_model* m) {
     if (m->ev_gfree[i]) hipEventDestroy(m->ev_gfree[i]);
   }
   if (m->ev_head) hipEventDestroy(m->ev_head);
+  if (m->ev_head_done) hipEventDestroy(m->ev_head_done);
+  if (m->ev_head_pf) hipEventDestroy(m->ev_head_pf);
   if (m->ev_h0) hipEventDestroy(m->ev_h0);
   for (auto e : m->ev_tail)
     if (e) hipEventDestroy(e);
@@ -537,6 +543,7 @@ void engine_destroy(hol_model* m) {
   if (m->sc) hipStreamDestroy(m->sc);
   if (m->sh2d) hipStreamDestroy(m->sh2d);
   if (m->sd2h) hipStreamDestroy(m->sd2h);
+  if (m->spf) hipStreamDestroy(m->spf);
   for (void* p : m->dev_allocs) hipFree(p);
   for (void* p : m->pinned_allocs) hipHostFree(p);
   free(m->master);
@@ -579,6 +586,7 @@ void read_image_tensor(const hol_model* m, const TensorDesc& t, float* dst) {
 // (into both images when the model has two: a frozen tensor's only copy must be in each)
 void write_image_tensor(hol_model* m, const TensorDesc& t, const float* src) {
   if (t.block == -2 || t.img < 0) return;
+  if (t.block == -1) m->head_img_ver++;
   for (uint8_t* base : {m->image, m->image_alt}) {
     if (!base) continue;
     uint8_t* dst = image_block(m, t.block, base) + t.img;
@@ -1172,6 +1180,7 @@ struct FusedWorker {
   std::thread th;
   bool running = false;
   bool failed = false;
+  bool prefetched = false;  // the next call's head weights were sent
   double busy_ms = 0;
   double t_call = 0;
   void start(const AdamConsts& kc, double t_start) {
@@ -1211,12 +1220,30 @@ struct FusedWorker {
           adam_embed_rows(m, m->emb_untouched, kc, false);  // their gradient is zero already
         } else {
           adam_unit(m, u, kc, -1, -1, u == 0);  // layer and head blocks: overwritten by the next copies
+          if (u == m->L + 1 && !prefetch_head()) {
+            failed = true;
+            return;
+          }
         }
         const double t1 = now_ms();
         busy_ms += t1 - t0;
         m->stats.units.push_back({(double)u, t0 - t_call, t1 - t_call});
       }
     });
+  }
+  // the next call's head weights (final now) go up on the prefetch stream once this call's head
+  // op is done with head_dev; the link has slack in the backward
+  bool prefetch_head() {
+    const uint8_t* src = image_block(m, -1);
+    if (hipStreamWaitEvent(m->spf, m->ev_head_done, 0) != hipSuccess ||
+        hipMemcpyAsync(m->head_dev, src, m->head_img_bytes, hipMemcpyHostToDevice, m->spf) != hipSuccess ||
+        hipEventRecord(m->ev_head_pf, m->spf) != hipSuccess)
+      return false;
+    m->head_pf_ver = m->head_img_ver;
+    m->head_pf_src = src;
+    m->head_pf = true;
+    prefetched = true;
+    return true;
   }
   void push(int u) {
     {
@@ -1517,6 +1544,16 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   bool head_loaded = false;
   auto load_head = [&]() -> hol_status {
     if (head_loaded || m->V <= 0 || loss != HOL_LOSS_NEXT_TOKEN_CE) return HOL_OK;
+    if (m->head_pf) {
+      // the previous call's copy of these weights stands (or a stale one may still be landing)
+      HCHECK(hipStreamWaitEvent(sh, m->ev_head_pf, 0));
+      m->head_pf = false;
+      if (m->head_pf_ver == m->head_img_ver && m->head_pf_src == image_block(m, -1)) {
+        HCHECK(hipEventRecord(m->ev_head, sh));
+        head_loaded = true;
+        return HOL_OK;
+      }
+    }
     hipEvent_t a = tev(), e = tev();
     HCHECK(hipEventRecord(a, sh));
     HCHECK(hipMemcpyAsync(m->head_dev, image_block(m, -1), m->head_img_bytes, hipMemcpyHostToDevice, sh));
@@ -1596,6 +1633,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE) HSTEP(hipStreamWaitEvent(sc, m->ev_head, 0));
       HSTEP(hipEventRecord(ta, sc));
       STEP(head_forward_backward(m, ckpt_of(m->nblocks), T, loss));
+      HSTEP(hipEventRecord(m->ev_head_done, sc));  // head_dev free for the next call's weights
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 5});
       if (m->V > 0 && loss == HOL_LOSS_NEXT_TOKEN_CE && m->head_trainable) {
@@ -1783,6 +1821,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     const double t_gpu_done = now_ms();
     worker.stop(false);
     m->stats.worker_busy_ms = worker.busy_ms;
+    if (worker.prefetched) m->stats.h2d_bytes += (double)m->head_img_bytes;  // the next call's head weights
     if (worker.failed) {
       set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
       return fail(HOL_EDEVICE);
@@ -1883,6 +1922,7 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
       _mm_sfence();  // the image's non-temporal stores are visible before the unit counts as done
     });
   }
+  if (u == m->L + 1) m->head_img_ver++;  // the head's image changed
 }
 
 // Adam on the given rows of the embedding (and zeroing of their gradients): the same per-element

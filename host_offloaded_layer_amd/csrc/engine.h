@@ -9,6 +9,7 @@
 #include <string>
 #include <thread>
 #include <array>
+#include <atomic>
 #include <vector>
 
 #include "../../include/hol.h"
@@ -211,6 +212,17 @@ struct hol_model {
   // and are cleared before anything accumulates into them. The embedding block is always zeroed.
   bool grads_stale = false;
   hol::Stats stats;
+
+  // The next call's LM-head weights: the fused step's worker copies them into head_dev as soon as
+  // the head's update is done (early in the backward, where the link has slack, instead of
+  // behind the last forward layer). They are used while the head's image has not been written
+  // since (head_img_ver counts those writes) and the image buffer is the same.
+  hipStream_t spf = nullptr;
+  hipEvent_t ev_head_done = nullptr, ev_head_pf = nullptr;  // head op done with head_dev / copy done
+  bool head_pf = false;  // a copy was issued (it may still be in flight)
+  std::atomic<uint64_t> head_img_ver{0};
+  uint64_t head_pf_ver = 0;
+  const uint8_t* head_pf_src = nullptr;
 
   // optimiser units: 0 = embedding, 1 + l = layer l, L + 1 = final norm and LM head
   std::vector<std::vector<int>> unit_tensors;

@@ -234,3 +234,35 @@ def test_plain_step_after_fused_step_sees_zero_gradients(wname):
         assert la == lb
         for n in a.index:
             assert np.array_equal(a.get_grad(n).view(np.uint32), b.get_grad(n).view(np.uint32)), n
+
+
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
+def test_head_weights_sent_ahead_by_a_fused_step_follow_later_writes(wname):
+    """A fused step sends the next call's LM-head weights to the device during its own backward.
+    A later write of the head (hol_set_tensor, or a plain hol_step) must be what the next call
+    computes with: bit for bit the same as a model that never had the weights sent ahead."""
+    w = TINY if wname == "tiny" else BF16_SMALL
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+    with lib_model(w, params) as a, lib_model(w, params) as b:
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)   # sends the head ahead
+        lib_fb(b, w, batch)
+        b.step()
+        new_head = a.get_tensor("lm_head") * np.float32(1.5)
+        a.set_tensor("lm_head", new_head)
+        b.set_tensor("lm_head", new_head)
+        assert lib_fb(a, w, batch) == lib_fb(b, w, batch)
+        for n in a.index:
+            assert np.array_equal(a.get_grad(n).view(np.uint32), b.get_grad(n).view(np.uint32)), n
+        a.zero_grad()
+        b.zero_grad()
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)   # sends the head ahead
+        a.step()                                                               # then changes it
+        lib_fb(b, w, batch)
+        b.step()
+        b.step()
+        assert lib_fb(a, w, batch) == lib_fb(b, w, batch)
+        sa, sb = _state(a), _state(b)
+        for n in sa:
+            for x, y in zip(sa[n], sb[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
