@@ -482,7 +482,6 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking));
   HCHECK(hipStreamCreateWithFlags(&m->sh2d, hipStreamNonBlocking));
   HCHECK(hipStreamCreateWithFlags(&m->sd2h, hipStreamNonBlocking));
-  HCHECK(hipStreamCreateWithFlags(&m->spf, hipStreamNonBlocking));
   for (int i = 0; i < m->nslots; ++i) {
     HCHECK(hipEventCreateWithFlags(&m->ev_ready[i], hipEventDisableTiming));
     HCHECK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
@@ -518,7 +517,6 @@ void engine_destroy(hol_model* m) {
   if (m->sc) hipStreamSynchronize(m->sc);
   if (m->sh2d) hipStreamSynchronize(m->sh2d);
   if (m->sd2h) hipStreamSynchronize(m->sd2h);
-  if (m->spf) hipStreamSynchronize(m->spf);
   for (int i = 0; i < hol_model::MAX_SLOTS; ++i) {
     if (m->ev_ready[i]) hipEventDestroy(m->ev_ready[i]);
     if (m->ev_free[i]) hipEventDestroy(m->ev_free[i]);
@@ -543,7 +541,6 @@ void engine_destroy(hol_model* m) {
   if (m->sc) hipStreamDestroy(m->sc);
   if (m->sh2d) hipStreamDestroy(m->sh2d);
   if (m->sd2h) hipStreamDestroy(m->sd2h);
-  if (m->spf) hipStreamDestroy(m->spf);
   for (void* p : m->dev_allocs) hipFree(p);
   for (void* p : m->pinned_allocs) hipHostFree(p);
   free(m->master);
@@ -1231,13 +1228,17 @@ struct FusedWorker {
       }
     });
   }
-  // the next call's head weights (final now) go up on the prefetch stream once this call's head
-  // op is done with head_dev; the link has slack in the backward
+  // the next call's head weights (final now) go up on the weight stream once this call's head op
+  // is done with head_dev. By then the backward's layer copies are mostly queued, so the copy
+  // runs late in the backward, where the link has slack. No stream of its own: the runtime maps
+  // streams onto a few hardware queues, and a further stream sharing one with the weight or
+  // gradient stream has stalled the device for a second and more behind its wait and copy.
   bool prefetch_head() {
     const uint8_t* src = image_block(m, -1);
-    if (hipStreamWaitEvent(m->spf, m->ev_head_done, 0) != hipSuccess ||
-        hipMemcpyAsync(m->head_dev, src, m->head_img_bytes, hipMemcpyHostToDevice, m->spf) != hipSuccess ||
-        hipEventRecord(m->ev_head_pf, m->spf) != hipSuccess)
+    std::lock_guard<std::mutex> g(m->h2d_mu);
+    if (hipStreamWaitEvent(m->sh2d, m->ev_head_done, 0) != hipSuccess ||
+        hipMemcpyAsync(m->head_dev, src, m->head_img_bytes, hipMemcpyHostToDevice, m->sh2d) != hipSuccess ||
+        hipEventRecord(m->ev_head_pf, m->sh2d) != hipSuccess)
       return false;
     m->head_pf_ver = m->head_img_ver;
     m->head_pf_src = src;
@@ -1529,6 +1530,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       if (placed) *placed = false;
       return HOL_OK;
     }
+    std::lock_guard<std::mutex> g(m->h2d_mu);
     HCHECK(hipStreamWaitEvent(sh, m->ev_free[best], 0));
     hipEvent_t a = tev(), e = tev();
     HCHECK(hipEventRecord(a, sh));
@@ -1544,6 +1546,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
   bool head_loaded = false;
   auto load_head = [&]() -> hol_status {
     if (head_loaded || m->V <= 0 || loss != HOL_LOSS_NEXT_TOKEN_CE) return HOL_OK;
+    std::lock_guard<std::mutex> g(m->h2d_mu);
     if (m->head_pf) {
       // the previous call's copy of these weights stands (or a stale one may still be landing)
       HCHECK(hipStreamWaitEvent(sh, m->ev_head_pf, 0));

@@ -213,11 +213,13 @@ struct hol_model {
   bool grads_stale = false;
   hol::Stats stats;
 
-  // The next call's LM-head weights: the fused step's worker copies them into head_dev as soon as
-  // the head's update is done (early in the backward, where the link has slack, instead of
-  // behind the last forward layer). They are used while the head's image has not been written
-  // since (head_img_ver counts those writes) and the image buffer is the same.
-  hipStream_t spf = nullptr;
+  // The next call's LM-head weights: the fused step's worker queues their copy into head_dev on the
+  // weight stream as soon as the head's update is done (it runs in the backward, where the link
+  // has slack, instead of behind the last forward layer). They are used while the head's image
+  // has not been written since (head_img_ver counts those writes) and the image buffer is the same.
+  // held around each sequence of calls that queue one copy on the weight stream (the worker's head
+  // copy must not fall between a layer copy and the event that marks that layer ready)
+  std::mutex h2d_mu;
   hipEvent_t ev_head_done = nullptr, ev_head_pf = nullptr;  // head op done with head_dev / copy done
   bool head_pf = false;  // a copy was issued (it may still be in flight)
   std::atomic<uint64_t> head_img_ver{0};

@@ -65,11 +65,11 @@ __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
 }
 
 // rows [row0, row0 + R) of a token-major matrix (row stride ld, D columns starting at col0) into
-// LDS row-major with pitch P; rows >= nvalid are clamped to the last valid row.
-template <int R, int D>
+// LDS row-major with pitch P; rows >= nvalid are clamped to the last valid row. NT threads.
+template <int R, int D, int NT = 256>
 __device__ __forceinline__ void load_rows(bf16* dst, int P, const bf16* src, int64_t ld, int64_t row0, int nvalid) {
   constexpr int CH = R * D / 8;
-  for (int c = threadIdx.x; c < CH; c += 256) {
+  for (int c = threadIdx.x; c < CH; c += NT) {
     const int r = c / (D / 8), k = (c % (D / 8)) * 8;
     const int rr = r < nvalid ? r : nvalid - 1;
     *(u32x4*)(dst + r * P + k) = *(const u32x4*)(src + (row0 + rr) * ld + k);
@@ -142,16 +142,17 @@ __device__ __forceinline__ bool pair_unit(int per, int npairs, int& pair, int& u
 
 // Register-staged tiles: a thread's share of the next tile is fetched into registers while the
 // current tile is computed on, then written to LDS after the next barrier.
-// Natural layout, 16-byte chunks: chunk c = tid + 256 i is row c / (D/8), columns (c % (D/8)) * 8.
-template <int R, int D>
+// Natural layout, 16-byte chunks: chunk c = tid + NT i is row c / (D/8), columns (c % (D/8)) * 8
+// (NT threads in the block).
+template <int R, int D, int NT = 256>
 struct NatTile {
-  static constexpr int N = R * D / 8 / 256;
-  static_assert(R * D / 8 % 256 == 0, "tile must split into whole chunks per thread");
+  static constexpr int N = R * D / 8 / NT;
+  static_assert(R * D / 8 % NT == 0, "tile must split into whole chunks per thread");
   u32x4 v[N];
   __device__ __forceinline__ void load(const bf16* src, int64_t ld, int64_t row0, int nvalid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       const int r = c / (D / 8), k = (c % (D / 8)) * 8;
       const int rr = r < nvalid ? r : nvalid - 1;
       v[i] = *(const u32x4*)(src + (row0 + rr) * ld + k);
@@ -160,7 +161,7 @@ struct NatTile {
   __device__ __forceinline__ void store(bf16* dst, int P) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       *(u32x4*)(dst + (c / (D / 8)) * P + (c % (D / 8)) * 8) = v[i];
     }
   }
@@ -512,13 +513,16 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16* lo, const bf16* hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
-  constexpr int D = 128, BKV = 128, BQ = 64, KP = D + 8, QT = BQ * D;
+// 8 waves, two per SIMD: waves w and w + 4 own the same 32 keys and take the two 32-query halves
+// of every query tile; the second wave's dV / dK partial sums go through LDS to the first at the
+// end (one fixed order, so the result is deterministic).
+__global__ __launch_bounds__(512, 1) void attn_dkdv_tr128(Attn a) {
+  constexpr int D = 128, BKV = 128, BQ = 64, KP = D + 8, QT = BQ * D, NT = 512;
   __shared__ __attribute__((aligned(16))) bf16 Qs[2 * QT];
   __shared__ __attribute__((aligned(16))) bf16 Gs[2 * QT];  // dO
   __shared__ float lse2[2][BQ], dlt[2][BQ];
-  __shared__ bf16 Kb[BKV * KP];
-  __shared__ bf16 Vb[BKV * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Kb[BKV * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vb[BKV * KP];
   const int S = a.S;
   const int nkt = (S + BKV - 1) / BKV;
   int pair, kt;  // early keys see the most queries: key tile 0 of a pair first
@@ -526,16 +530,17 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int group = a.nq / a.nkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int kw = w & 3, qb = w >> 2;  // key group of 32, query half of each tile
   const int k0 = kt * BKV;
-  const int kj = k0 + 32 * w + lq;  // this lane's key (column of the S / dP accumulators)
+  const int kj = k0 + 32 * kw + lq;  // this lane's key (column of the S / dP accumulators)
   const int64_t base = (int64_t)seq * S;
   const float sl2 = LOG2E / sqrtf((float)D);
   const float scale = 1.f / sqrtf((float)D);
 
-  load_rows<BKV, D>(Kb, KP, (const bf16*)a.k + (int64_t)kvh * D, a.ldk, base + k0, min(BKV, S - k0));
-  load_rows<BKV, D>(Vb, KP, (const bf16*)a.v + (int64_t)kvh * D, a.ldv, base + k0, min(BKV, S - k0));
-  const bf16* kfp = Kb + (32 * w + lq) * KP + 8 * hh;
-  const bf16* vfp = Vb + (32 * w + lq) * KP + 8 * hh;
+  load_rows<BKV, D, NT>(Kb, KP, (const bf16*)a.k + (int64_t)kvh * D, a.ldk, base + k0, min(BKV, S - k0));
+  load_rows<BKV, D, NT>(Vb, KP, (const bf16*)a.v + (int64_t)kvh * D, a.ldv, base + k0, min(BKV, S - k0));
+  const bf16* kfp = Kb + (32 * kw + lq) * KP + 8 * hh;
+  const bf16* vfp = Vb + (32 * kw + lq) * KP + 8 * hh;
   // transposed-read offsets: [half][d block] for k-step 0 (add 16 rows per k-step)
   int toff[2][D / 32];
   {
@@ -551,12 +556,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
     zero(dv[i]);
     zero(dk[i]);
   }
-  const int wave_kmin = k0 + 32 * w;
+  const int wave_kmin = k0 + 32 * kw;
   const int nqt = (S + BQ - 1) / BQ;
   const int qt0 = k0 / BQ, nper = nqt - qt0, nit = group * nper;
   // iteration it: query tile nqt - 1 - it / group (from the last down to the diagonal), q head
   // kvh * group + it % group; every key tile of a pair walks the query tiles in the same order
-  NatTile<BQ, D> qreg, greg;
+  NatTile<BQ, D, NT> qreg, greg;
   float lse_r = 0.f, dl_r = 0.f;
   auto fetch = [&](int it) {
     const int h = kvh * group + it % group, q0 = (nqt - 1 - it / group) * BQ, nq = min(BQ, S - q0);
@@ -571,12 +576,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
       dl_r = qq < S ? a.delta[hrow + qq] : 0.f;
     }
   };
-  // a thread's share of the fetched tile into buffer b (chunk c = tid + 256 i: row c / 16,
+  // a thread's share of the fetched tile into buffer b (chunk c = tid + NT i: row c / 16,
   // logical chunk c % 16)
   auto put = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < NatTile<BQ, D>::N; ++i) {
-      const int c = threadIdx.x + 256 * i, r = c >> 4, ch = c & 15;
+    for (int i = 0; i < NatTile<BQ, D, NT>::N; ++i) {
+      const int c = threadIdx.x + NT * i, r = c >> 4, ch = c & 15;
       const int o = b * QT + r * 128 + ((ch ^ qsw(r)) << 3);
       *(u32x4*)(Qs + o) = qreg.v[i];
       *(u32x4*)(Gs + o) = greg.v[i];
@@ -592,55 +597,52 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
   __syncthreads();
   for (int it = 0; it < nit; ++it) {
     const int cur = it & 1;
-    const int q0 = (nqt - 1 - it / group) * BQ;
+    const int q0 = (nqt - 1 - it / group) * BQ, qh0 = q0 + 32 * qb;  // this wave's first query
     const bf16* Qc = Qs + cur * QT;
     const bf16* Gc = Gs + cur * QT;
-    if (q0 + BQ - 1 >= wave_kmin) {  // else every query of the tile is before this wave's keys
-      // two 32-query halves in turn: S[q][key] and dP[q][key], then their dV / dK products
-      // (element r of a half qb: query q0 + 32 qb + 8 (r/4) + 4 hh + r%4, key kj)
-      const bool full = q0 >= wave_kmin + 31 && q0 + BQ <= S && kj < S;  // no masking in this tile
+    if (qh0 + 31 >= wave_kmin) {  // else every query of the half is before this wave's keys
+      // S[q][key] and dP[q][key] for the half, then its dV / dK products (element r: query
+      // qh0 + 8 (r/4) + 4 hh + r%4, key kj)
+      const bool full = qh0 >= wave_kmin + 31 && qh0 + 32 <= S && kj < S;  // no masking here
+      f32x16 s, dp;
+      zero(s);
+      zero(dp);
+      const int qr = qb * 32 + lq;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s, dp;
-        zero(s);
-        zero(dp);
-        const int qr = qb * 32 + lq;
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int o = qoff(qr, 16 * kk + 8 * hh);
+        s = mfma(*(const bf16x8*)(Qc + o), *(const bf16x8*)(kfp + 16 * kk), s);
+        dp = mfma(*(const bf16x8*)(Gc + o), *(const bf16x8*)(vfp + 16 * kk), dp);
+      }
+      if (full) {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const int o = qoff(qr, 16 * kk + 8 * hh);
-          s = mfma(*(const bf16x8*)(Qc + o), *(const bf16x8*)(kfp + 16 * kk), s);
-          dp = mfma(*(const bf16x8*)(Gc + o), *(const bf16x8*)(vfp + 16 * kk), dp);
+        for (int r = 0; r < 16; ++r) {
+          const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const float p = ex2(fmaf(s[r], sl2, -lse2[cur][qloc]));
+          s[r] = p;
+          dp[r] = p * (dp[r] - dlt[cur][qloc]);
         }
-        if (full) {
+      } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float p = ex2(fmaf(s[r], sl2, -lse2[cur][qloc]));
-            s[r] = p;
-            dp[r] = p * (dp[r] - dlt[cur][qloc]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int qq = q0 + qloc;
-            const bool ok = qq < S && kj <= qq && kj < S;
-            const float p = ok ? ex2(fmaf(s[r], sl2, -lse2[cur][qloc])) : 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - dlt[cur][qloc]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int qloc = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int qq = q0 + qloc;
+          const bool ok = qq < S && kj <= qq && kj < S;
+          const float p = ok ? ex2(fmaf(s[r], sl2, -lse2[cur][qloc])) : 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - dlt[cur][qloc]);
         }
-        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+      }
+      // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
 #pragma unroll
-        for (int ksp = 0; ksp < 2; ++ksp) {
-          const int ks = 2 * qb + ksp;
-          const bf16x8 pb = acc_frag(s, ksp);
-          const bf16x8 sb = acc_frag(dp, ksp);
+      for (int ksp = 0; ksp < 2; ++ksp) {
+        const int ks = 2 * qb + ksp;
+        const bf16x8 pb = acc_frag(s, ksp);
+        const bf16x8 sb = acc_frag(dp, ksp);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            dv[db] = mfma(tr_pair(Gc + ks * 16 * 128 + toff[0][db], Gc + ks * 16 * 128 + toff[1][db]), pb, dv[db]);
-            dk[db] = mfma(tr_pair(Qc + ks * 16 * 128 + toff[0][db], Qc + ks * 16 * 128 + toff[1][db]), sb, dk[db]);
-          }
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = mfma(tr_pair(Gc + ks * 16 * 128 + toff[0][db], Gc + ks * 16 * 128 + toff[1][db]), pb, dv[db]);
+          dk[db] = mfma(tr_pair(Qc + ks * 16 * 128 + toff[0][db], Qc + ks * 16 * 128 + toff[1][db]), sb, dk[db]);
         }
       }
     }
@@ -651,17 +653,36 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_tr128(Attn a) {
     }
     __syncthreads();
   }
-  if (kj < S) {
+  // the second-half waves hand their sums to the first-half waves: float4 j4 of accumulator
+  // half hf goes to ((kw * 8 + j4) * 64 + lane) of a 32 KB region (the tile buffers are free
+  // after the last barrier): dv[0..1] -> Qs, dv[2..3] -> Gs, dk[0..1] -> Kb, dk[2..3] -> Vb
+  f32x4* red[4] = {(f32x4*)Qs, (f32x4*)Gs, (f32x4*)Kb, (f32x4*)Vb};
+  if (qb == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j4 = (db & 1) * 4 + g;
+        red[db >> 1][(kw * 8 + j4) * 64 + lane] = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        red[2 + (db >> 1)][(kw * 8 + j4) * 64 + lane] =
+            f32x4{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+      }
+  }
+  __syncthreads();
+  if (qb == 0 && kj < S) {
     bf16* dkp = (bf16*)a.dk + (base + kj) * a.lddk + (int64_t)kvh * D;
     bf16* dvp = (bf16*)a.dv + (base + kj) * a.lddv + (int64_t)kvh * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int dd = db * 32 + 8 * g + 4 * hh;
-        store4(dkp + dd, dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
-               dk[db][4 * g + 3] * scale);
-        store4(dvp + dd, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+        const int dd = db * 32 + 8 * g + 4 * hh, j4 = (db & 1) * 4 + g;
+        const f32x4 pv = red[db >> 1][(kw * 8 + j4) * 64 + lane];
+        const f32x4 pk = red[2 + (db >> 1)][(kw * 8 + j4) * 64 + lane];
+        store4(dkp + dd, (dk[db][4 * g] + pk[0]) * scale, (dk[db][4 * g + 1] + pk[1]) * scale,
+               (dk[db][4 * g + 2] + pk[2]) * scale, (dk[db][4 * g + 3] + pk[3]) * scale);
+        store4(dvp + dd, dv[db][4 * g] + pv[0], dv[db][4 * g + 1] + pv[1], dv[db][4 * g + 2] + pv[2],
+               dv[db][4 * g + 3] + pv[3]);
       }
   }
 }
@@ -770,8 +791,10 @@ __global__ __launch_bounds__(256, 1) void attn_dq_mfma(Attn a) {
 // dQ for head width 128 without the transposed key copy: K and V tiles stay natural in a
 // double-buffered, swizzled LDS pair (the layout of the dK/dV kernel above, one block barrier per
 // key tile) and the dQ product reads K transposed with ds_read_b64_tr_b16.
-__global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
-  constexpr int D = 128, BQ = 128, BK = 64, KT = BK * D;
+// 8 waves, two per SIMD: waves w and w + 4 hold the same 32 queries and take the two 32-key halves
+// of every key tile; the second wave's dQ partial sum goes through LDS to the first at the end.
+__global__ __launch_bounds__(512, 1) void attn_dq_tr128(Attn a) {
+  constexpr int D = 128, BQ = 128, BK = 64, KT = BK * D, NT = 512;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2 * KT];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2 * KT];
   const int S = a.S;
@@ -783,8 +806,9 @@ __global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int h = kvh * group + unit % group;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int qw = w & 3, kb = w >> 2;  // query group of 32, key half of each tile
   const int q0 = qt * BQ;
-  const int qi = q0 + 32 * w + lq;
+  const int qi = q0 + 32 * qw + lq;
   const int64_t base = (int64_t)seq * S;
   const float sl2 = LOG2E / sqrtf((float)D);
   const float scale = 1.f / sqrtf((float)D);
@@ -818,8 +842,8 @@ __global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
   for (int i = 0; i < D / 32; ++i) zero(dq[i]);
   const int qmax = min(q0 + BQ, S) - 1;
   const int nkt = qmax / BK + 1;
-  const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
-  NatTile<BK, D> kreg, vreg;
+  const int wave_qmax = min(q0 + 32 * qw + 31, S - 1);
+  NatTile<BK, D, NT> kreg, vreg;
   auto fetch = [&](int kt) {
     const int k0 = kt * BK;
     kreg.load(K, a.ldk, base + k0, min(BK, S - k0));
@@ -827,8 +851,8 @@ __global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
   };
   auto put = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < NatTile<BK, D>::N; ++i) {
-      const int c = threadIdx.x + 256 * i, r = c >> 4, ch = c & 15;
+    for (int i = 0; i < NatTile<BK, D, NT>::N; ++i) {
+      const int c = threadIdx.x + NT * i, r = c >> 4, ch = c & 15;
       const int o = b * KT + r * 128 + ((ch ^ qsw(r)) << 3);
       *(u32x4*)(Ks + o) = kreg.v[i];
       *(u32x4*)(Vs + o) = vreg.v[i];
@@ -839,34 +863,32 @@ __global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
   if (nkt > 1) fetch(1);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * BK, cur = kt & 1;
+    const int k0 = kt * BK, cur = kt & 1, kh0 = k0 + 32 * kb;  // this wave's first key
     const bf16* Kc = Ks + cur * KT;
     const bf16* Vc = Vs + cur * KT;
-    if (k0 <= wave_qmax) {  // else every key of the tile is after this wave's queries
-      f32x16 s[2], dp[2];
-      zero(s[0]); zero(s[1]); zero(dp[0]); zero(dp[1]);
+    if (kh0 <= wave_qmax) {  // else every key of the half is after this wave's queries
+      f32x16 s, dp;
+      zero(s);
+      zero(dp);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int o = qoff(kb * 32 + lq, 16 * kk + 8 * hh);
+        s = mfma(*(const bf16x8*)(Kc + o), qf[kk], s);
+        dp = mfma(*(const bf16x8*)(Vc + o), gf[kk], dp);
+      }
+      // element r: key kh0 + 8 (r/4) + 4 hh + r%4, query qi
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int o = qoff(kb * 32 + lq, 16 * kk + 8 * hh);
-          s[kb] = mfma(*(const bf16x8*)(Kc + o), qf[kk], s[kb]);
-          dp[kb] = mfma(*(const bf16x8*)(Vc + o), gf[kk], dp[kb]);
-        }
-      // element r of block kb: key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = qv && kk <= qi && kk < S;
-          const float p = ok ? ex2(s[kb][r] * sl2 - lse_q) : 0.f;
-          dp[kb][r] = p * (dp[kb][r] - dl_q);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kh0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool ok = qv && kk <= qi && kk < S;
+        const float p = ok ? ex2(s[r] * sl2 - lse_q) : 0.f;
+        dp[r] = p * (dp[r] - dl_q);
+      }
       // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const bf16x8 sb = acc_frag(dp[ks >> 1], ks & 1);
+      for (int ksp = 0; ksp < 2; ++ksp) {
+        const int ks = 2 * kb + ksp;
+        const bf16x8 sb = acc_frag(dp, ksp);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
           dq[db] = mfma(tr_pair(Kc + ks * 16 * 128 + toff[0][db], Kc + ks * 16 * 128 + toff[1][db]), sb, dq[db]);
@@ -878,14 +900,29 @@ __global__ __launch_bounds__(256, 1) void attn_dq_tr128(Attn a) {
     }
     __syncthreads();
   }
-  if (qv) {
-    bf16* dqp = (bf16*)a.dq + (base + qi) * a.lddq + (int64_t)h * D;
+  // the second-half waves hand their sums to the first-half waves: float4 j4 of accumulator
+  // half hf goes to ((qw * 8 + j4) * 64 + lane) of a 32 KB region (the tile buffers are free
+  // after the last barrier): dq[0..1] -> Ks, dq[2..3] -> Vs
+  f32x4* red[2] = {(f32x4*)Ks, (f32x4*)Vs};
+  if (kb == 1) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store4(dqp + db * 32 + 8 * g + 4 * hh, dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale,
-               dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+        red[db >> 1][(qw * 8 + (db & 1) * 4 + g) * 64 + lane] =
+            f32x4{dq[db][4 * g], dq[db][4 * g + 1], dq[db][4 * g + 2], dq[db][4 * g + 3]};
+  }
+  __syncthreads();
+  if (kb == 0 && qv) {
+    bf16* dqp = (bf16*)a.dq + (base + qi) * a.lddq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pq = red[db >> 1][(qw * 8 + (db & 1) * 4 + g) * 64 + lane];
+        store4(dqp + db * 32 + 8 * g + 4 * hh, (dq[db][4 * g] + pq[0]) * scale, (dq[db][4 * g + 1] + pq[1]) * scale,
+               (dq[db][4 * g + 2] + pq[2]) * scale, (dq[db][4 * g + 3] + pq[3]) * scale);
+      }
   }
 }
 
@@ -1077,8 +1114,8 @@ int launch_attn_bwd_mfma(const Attn& a, hipStream_t s) {
   dim3 gk(pair_grid((a.S + 127) / 128, a.nkv * a.n_seq)),
       gq(pair_grid(((a.S + 127) / 128) * (a.nq / a.nkv), a.nkv * a.n_seq));
   if (a.d == 128) {
-    hipLaunchKernelGGL(attn_dkdv_tr128, gk, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_dq_tr128, gq, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_dkdv_tr128, gk, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(attn_dq_tr128, gq, dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL(attn_dkdv_mfma<64>, gk, dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_dq_mfma<64>, gq, dim3(256), 0, s, a);
