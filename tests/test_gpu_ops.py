@@ -329,6 +329,8 @@ def test_swiglu_bwd_with_transpose_rejects_unsupported_shapes():
     (hol.BF16, 130, 2, 4, 1, 128),
     (hol.BF16, 260, 2, 16, 4, 128),   # 8 (sequence, kv head) pairs: whole pairs dealt to each XCD
     (hol.BF16, 192, 8, 8, 1, 64),
+    (hol.BF16, 40, 3, 8, 2, 128),     # shorter than one 64-query tile: whole halves past the end
+    (hol.BF16, 97, 1, 32, 8, 128),    # the LLaMA-8B head layout, one ragged tile
 ])
 def test_attention_fwd_bwd(dt, S, nseq, nq, nkv, d):
     r = np.random.default_rng(S + nq)
@@ -370,6 +372,37 @@ def test_attention_fwd_bwd(dt, S, nseq, nq, nkv, d):
             np.testing.assert_allclose(host(dk)[sl], rdk.reshape(S, -1), rtol=1e-4, atol=1e-4)
             np.testing.assert_allclose(host(dv)[sl], rdv.reshape(S, -1), rtol=1e-4, atol=1e-4)
         np.testing.assert_allclose(host(lse)[b], rl, rtol=1e-5, atol=1e-5)
+
+
+def test_attention_single_position():
+    """S = 1: the softmax is the single key, so o = v of the head's kv head, dv sums dO over the
+    heads of the group, and dq = dk = 0 (dS = P (dP - rowsum(dO o)) vanishes up to the rounding of
+    the two sums, hence an absolute bound)."""
+    nseq, S, nq, nkv, d = 3, 1, 8, 2, 128
+    r = np.random.default_rng(11)
+    T, g = nseq * S, nq // nkv
+    q, k, v, do = (r.standard_normal((T, n * d)).astype(np.float32) for n in (nq, nkv, nkv, nq))
+    qd, kd, vd, dod = (dev(x, torch.bfloat16) for x in (q, k, v, do))
+    o = torch.empty((T, nq * d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((nseq, nq, S), device=DEV)
+    hol.check(hol.lib.hol_op_attention_fwd(nseq, S, nq, nkv, d, hol.BF16, qd.data_ptr(), nq * d, kd.data_ptr(), nkv * d,
+                                           vd.data_ptr(), nkv * d, o.data_ptr(), nq * d, lse.data_ptr(), None))
+    dq = torch.empty_like(qd); dk = torch.empty_like(kd); dv = torch.empty_like(vd)
+    delta = torch.empty((nseq, nq, S), device=DEV)
+    hol.check(hol.lib.hol_op_attention_bwd(nseq, S, nq, nkv, d, hol.BF16, qd.data_ptr(), nq * d, kd.data_ptr(), nkv * d,
+                                           vd.data_ptr(), nkv * d, o.data_ptr(), nq * d, lse.data_ptr(),
+                                           dod.data_ptr(), nq * d, dq.data_ptr(), nq * d, dk.data_ptr(), nkv * d,
+                                           dv.data_ptr(), nkv * d, delta.data_ptr(), None))
+    sync()
+    q64, k64, v64, do64 = host(qd), host(kd), host(vd), host(dod)
+    o_h = host(o).reshape(T, nq, d)
+    for h in range(nq):
+        np.testing.assert_array_equal(o_h[:, h], v64.reshape(T, nkv, d)[:, h // g])
+        qk = np.einsum("td,td->t", q64.reshape(T, nq, d)[:, h], k64.reshape(T, nkv, d)[:, h // g]) / np.sqrt(d)
+        np.testing.assert_allclose(host(lse)[:, h, 0], qk, rtol=1e-5, atol=1e-5)
+    want_dv = do64.reshape(T, nkv, g, d).sum(axis=2).reshape(T, nkv * d)
+    assert rel(host(dv), want_dv) < 1e-2
+    assert np.abs(host(dq)).max() < 1e-3 and np.abs(host(dk)).max() < 1e-3
 
 
 # ------------------------------------------------------------------ cross entropy
