@@ -493,6 +493,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_head_done, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_head_pf, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->ev_l0_done, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->tail_mlp_ev, hipEventDisableTiming));
@@ -528,6 +529,7 @@ void engine_destroy(hol_model* m) {
   if (m->ev_head) hipEventDestroy(m->ev_head);
   if (m->ev_head_done) hipEventDestroy(m->ev_head_done);
   if (m->ev_head_pf) hipEventDestroy(m->ev_head_pf);
+  if (m->ev_l0_done) hipEventDestroy(m->ev_l0_done);
   if (m->ev_h0) hipEventDestroy(m->ev_h0);
   for (auto e : m->ev_tail)
     if (e) hipEventDestroy(e);
@@ -584,6 +586,7 @@ void read_image_tensor(const hol_model* m, const TensorDesc& t, float* dst) {
 void write_image_tensor(hol_model* m, const TensorDesc& t, const float* src) {
   if (t.block == -2 || t.img < 0) return;
   if (t.block == -1) m->head_img_ver++;
+  if (t.block == 0) m->l0_img_ver++;
   for (uint8_t* base : {m->image, m->image_alt}) {
     if (!base) continue;
     uint8_t* dst = image_block(m, t.block, base) + t.img;
@@ -1178,6 +1181,8 @@ struct FusedWorker {
   bool running = false;
   bool failed = false;
   bool prefetched = false;  // the next call's head weights were sent
+  bool l0_sent = false;     // the next call's first layer was sent
+  int tail_done = 0;        // optimiser pieces of the last layer done
   double busy_ms = 0;
   double t_call = 0;
   void start(const AdamConsts& kc, double t_start) {
@@ -1213,6 +1218,10 @@ struct FusedWorker {
           const int c = u - hol_model::TAIL_CODE;
           const int64_t f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * m->layer_flat_n;
           adam_unit(m, m->tail_unit, kc, f0 + m->tail_lo[c], f0 + m->tail_hi[c], false);
+          if (++tail_done == m->n_tail_expect && m->tail_unit == 1 && m->l0_pf_next >= 0 && !prefetch_l0()) {
+            failed = true;
+            return;
+          }
         } else if (u == m->L + 2) {
           adam_embed_rows(m, m->emb_untouched, kc, false);  // their gradient is zero already
         } else {
@@ -1244,6 +1253,22 @@ struct FusedWorker {
     m->head_pf_src = src;
     m->head_pf = true;
     prefetched = true;
+    return true;
+  }
+  // the next call's first layer (its image final now) into the slot it occupied, once this call's
+  // backward of it is done with that slot; on the weight stream like every slot copy
+  bool prefetch_l0() {
+    const uint8_t* src = image_block(m, 0);
+    const int s = m->l0_pf_next;
+    std::lock_guard<std::mutex> g(m->h2d_mu);
+    if (hipStreamWaitEvent(m->sh2d, m->ev_l0_done, 0) != hipSuccess ||
+        hipMemcpyAsync(m->slot[s], src, m->layer_img_bytes, hipMemcpyHostToDevice, m->sh2d) != hipSuccess ||
+        hipEventRecord(m->ev_ready[s], m->sh2d) != hipSuccess)
+      return false;
+    m->l0_pf_ver = m->l0_img_ver;
+    m->l0_pf_src = src;
+    m->l0_pf_slot = s;
+    l0_sent = true;
     return true;
   }
   void push(int u) {
@@ -1453,11 +1478,17 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 
   HSTEP(hipSetDevice(m->cfg.device));
   hipStream_t sc = m->sc, sh = m->sh2d, sd = m->sd2h;
-  // initial event states: every buffer free
+  // initial event states: every buffer free; a slot holding the first layer as sent by the
+  // previous fused step stays bound to it while that image is unwritten since (its ready event is
+  // that copy's), else it is free (a new copy into it queues behind that one)
+  const bool l0_keep = m->l0_pf_slot >= 0 && m->l0_pf_ver == m->l0_img_ver && m->l0_pf_src == image_block(m, 0);
   for (int i = 0; i < m->nslots; ++i) {
     HSTEP(hipEventRecord(m->ev_free[i], sc));
-    m->slot_layer[i] = -1;
+    m->slot_layer[i] = l0_keep && i == m->l0_pf_slot ? 0 : -1;
   }
+  m->l0_pf_slot = -1;
+  m->l0_pf_next = -1;
+  m->n_tail_expect = 0;
   for (int i = 0; i < m->ngbuf; ++i) HSTEP(hipEventRecord(m->ev_gfree[i], sd));
   m->tev_used = 0;
   m->krec.clear();
@@ -1735,6 +1766,11 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
         m->tail_unit = 1 + op.layer;
         const int64_t n = m->layer_flat_n;
         m->n_tail = 0;
+        m->n_tail_expect = split ? 3 : hol_model::N_TAIL;
+        if (op.layer == 0) {  // its slot takes the next call's copy once this backward is done
+          HSTEP(hipEventRecord(m->ev_l0_done, sc));
+          m->l0_pf_next = s;
+        }
         auto piece = [&](int64_t lo, int64_t hi) -> hol_status {
           const int c = m->n_tail++;
           m->tail_lo[c] = lo;
@@ -1825,6 +1861,10 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     worker.stop(false);
     m->stats.worker_busy_ms = worker.busy_ms;
     if (worker.prefetched) m->stats.h2d_bytes += (double)m->head_img_bytes;  // the next call's head weights
+    if (worker.l0_sent) {  // and first layer
+      m->stats.h2d_bytes += (double)m->layer_img_bytes;
+      m->stats.n_weight_streams++;
+    }
     if (worker.failed) {
       set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
       return fail(HOL_EDEVICE);
@@ -1926,6 +1966,7 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
     });
   }
   if (u == m->L + 1) m->head_img_ver++;  // the head's image changed
+  if (u == 1) m->l0_img_ver++;           // the first layer's
 }
 
 // Adam on the given rows of the embedding (and zeroing of their gradients): the same per-element

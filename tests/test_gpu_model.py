@@ -266,3 +266,52 @@ def test_head_weights_sent_ahead_by_a_fused_step_follow_later_writes(wname):
         for n in sa:
             for x, y in zip(sa[n], sb[n]):
                 assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+
+
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
+def test_first_layer_sent_ahead_by_a_fused_step_follows_later_writes(wname):
+    """A fused step sends the next call's first layer (the backward's last, updated last) into a
+    weight slot before it returns. A later write of that layer (hol_set_tensor, a plain hol_step)
+    must be what the next call computes with, and a staleness-1 call after a fused step computes
+    with the image it finds: bit for bit the same as a model that never sent the layer ahead."""
+    w = TINY if wname == "tiny" else BF16_SMALL
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+    with lib_model(w, params) as a, lib_model(w, params) as b:
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)   # sends layer 0 ahead
+        lib_fb(b, w, batch)
+        b.step()
+        for n in ("layers.0.wq", "layers.0.attn_norm"):
+            new = a.get_tensor(n) * np.float32(1.25)
+            a.set_tensor(n, new)
+            b.set_tensor(n, new)
+        assert lib_fb(a, w, batch) == lib_fb(b, w, batch)
+        for n in a.index:
+            assert np.array_equal(a.get_grad(n).view(np.uint32), b.get_grad(n).view(np.uint32)), n
+        a.zero_grad()
+        b.zero_grad()
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)   # sends layer 0 ahead
+        a.step()                                                               # then changes it
+        lib_fb(b, w, batch)
+        b.step()
+        b.step()
+        assert lib_fb(a, w, batch) == lib_fb(b, w, batch)
+        sa, sb = _state(a), _state(b)
+        for n in sa:
+            for x, y in zip(sa[n], sb[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+    with lib_model(w, params, async_opt=1) as a, lib_model(w, params, async_opt=1) as b:
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)   # sends layer 0 ahead
+        lib_fb(b, w, batch)
+        b.step()
+        for _ in range(2):   # the second call finds the other image buffer
+            assert (a.forward_backward(w.n_micro, tokens=batch["tokens"], stale_step=True) ==
+                    b.forward_backward(w.n_micro, tokens=batch["tokens"], stale_step=True))
+        a.step()
+        b.step()
+        assert (a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True) ==
+                b.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True))
+        sa, sb = _state(a), _state(b)
+        for n in sa:
+            for x, y in zip(sa[n], sb[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
