@@ -104,8 +104,8 @@ typedef struct {
 
 /* Creates a model: plans and allocates all host state (fp32 masters, Adam m/v, pinned fp32
  * gradients, pinned layer-contiguous low-precision image with 4 KiB-aligned sub-tensors) and all
- * device memory (two weight slots, head buffer, checkpoint store, block activation store,
- * gradient buffers). Weights start at zero; load them with hol_set_tensor. */
+ * device memory (the ring of weight slots, head buffer, checkpoint store, block activation
+ * store, gradient buffers). Weights start at zero; load them with hol_set_tensor. */
 hol_status hol_create(const hol_config* cfg, hol_model** out);
 void hol_destroy(hol_model* m);
 
