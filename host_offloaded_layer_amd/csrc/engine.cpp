@@ -363,7 +363,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   // default ring: the K layers of a block stay resident from the recompute through the block's
   // backward, and two more slots take the next block's layers while that backward computes
   m->nslots = c.weight_slots ? c.weight_slots : std::min(8, std::max(4, c.ckpt_every_k + 2));
-  m->ngbuf = c.grad_buffers ? c.grad_buffers : 3;
+  m->ngbuf = c.grad_buffers ? c.grad_buffers : 4;
   for (int i = 0; i < m->nslots; ++i) m->slot[i] = (uint8_t*)D(m->layer_img_bytes);
   if (V > 0) m->head_dev = (uint8_t*)D(m->head_img_bytes);
   for (int i = 0; i < m->ngbuf; ++i) m->gdev[i] = (float*)D(m->layer_flat_n * 4);

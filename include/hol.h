@@ -84,7 +84,7 @@ typedef struct {
                                * where the compute is the longer of the two. Results do not
                                * depend on it. */
   int32_t grad_buffers;       /* HBM layer-gradient buffers awaiting the device->host copy, 2..4;
-                               * 0: 3. Results do not depend on it. */
+                               * 0: 4. Results do not depend on it. */
   int32_t async_optimizer;    /* 1: also allocate a second pinned low-precision image, which
                                * hol_forward_backward_async needs; 0: none (that call returns
                                * HOL_EINVAL). */
