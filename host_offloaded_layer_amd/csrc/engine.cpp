@@ -493,7 +493,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipEventCreateWithFlags(&m->ev_head, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_head_done, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_head_pf, hipEventDisableTiming));
-  HCHECK(hipEventCreateWithFlags(&m->ev_l0_done, hipEventDisableTiming));
+  for (int p = 0; p < hol_model::NPF; ++p) HCHECK(hipEventCreateWithFlags(&m->ev_lpf_done[p], hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->tail_mlp_ev, hipEventDisableTiming));
@@ -529,7 +529,8 @@ void engine_destroy(hol_model* m) {
   if (m->ev_head) hipEventDestroy(m->ev_head);
   if (m->ev_head_done) hipEventDestroy(m->ev_head_done);
   if (m->ev_head_pf) hipEventDestroy(m->ev_head_pf);
-  if (m->ev_l0_done) hipEventDestroy(m->ev_l0_done);
+  for (int p = 0; p < hol_model::NPF; ++p)
+    if (m->ev_lpf_done[p]) hipEventDestroy(m->ev_lpf_done[p]);
   if (m->ev_h0) hipEventDestroy(m->ev_h0);
   for (auto e : m->ev_tail)
     if (e) hipEventDestroy(e);
@@ -586,7 +587,7 @@ void read_image_tensor(const hol_model* m, const TensorDesc& t, float* dst) {
 void write_image_tensor(hol_model* m, const TensorDesc& t, const float* src) {
   if (t.block == -2 || t.img < 0) return;
   if (t.block == -1) m->head_img_ver++;
-  if (t.block == 0) m->l0_img_ver++;
+  if (t.block >= 0 && t.block < hol_model::NPF) m->lpf_img_ver[t.block]++;
   for (uint8_t* base : {m->image, m->image_alt}) {
     if (!base) continue;
     uint8_t* dst = image_block(m, t.block, base) + t.img;
@@ -1181,7 +1182,7 @@ struct FusedWorker {
   bool running = false;
   bool failed = false;
   bool prefetched = false;  // the next call's head weights were sent
-  bool l0_sent = false;     // the next call's first layer was sent
+  int lpf_sent = 0;         // first layers of the next call sent
   int tail_done = 0;        // optimiser pieces of the last layer done
   double busy_ms = 0;
   double t_call = 0;
@@ -1218,7 +1219,7 @@ struct FusedWorker {
           const int c = u - hol_model::TAIL_CODE;
           const int64_t f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * m->layer_flat_n;
           adam_unit(m, m->tail_unit, kc, f0 + m->tail_lo[c], f0 + m->tail_hi[c], false);
-          if (++tail_done == m->n_tail_expect && m->tail_unit == 1 && m->l0_pf_next >= 0 && !prefetch_l0()) {
+          if (++tail_done == m->n_tail_expect && m->tail_unit == 1 && m->lpf_next[0] >= 0 && !prefetch_layer(0)) {
             failed = true;
             return;
           }
@@ -1227,6 +1228,10 @@ struct FusedWorker {
         } else {
           adam_unit(m, u, kc, -1, -1, u == 0);  // layer and head blocks: overwritten by the next copies
           if (u == m->L + 1 && !prefetch_head()) {
+            failed = true;
+            return;
+          }
+          if (u >= 2 && u <= hol_model::NPF && m->lpf_next[u - 1] >= 0 && !prefetch_layer(u - 1)) {
             failed = true;
             return;
           }
@@ -1255,20 +1260,20 @@ struct FusedWorker {
     prefetched = true;
     return true;
   }
-  // the next call's first layer (its image final now) into the slot it occupied, once this call's
-  // backward of it is done with that slot; on the weight stream like every slot copy
-  bool prefetch_l0() {
-    const uint8_t* src = image_block(m, 0);
-    const int s = m->l0_pf_next;
+  // one of the next call's first layers (its image final now) into the slot it occupied, once
+  // this call's backward of it is done with that slot; on the weight stream like every slot copy
+  bool prefetch_layer(int p) {
+    const uint8_t* src = image_block(m, p);
+    const int s = m->lpf_next[p];
     std::lock_guard<std::mutex> g(m->h2d_mu);
-    if (hipStreamWaitEvent(m->sh2d, m->ev_l0_done, 0) != hipSuccess ||
+    if (hipStreamWaitEvent(m->sh2d, m->ev_lpf_done[p], 0) != hipSuccess ||
         hipMemcpyAsync(m->slot[s], src, m->layer_img_bytes, hipMemcpyHostToDevice, m->sh2d) != hipSuccess ||
         hipEventRecord(m->ev_ready[s], m->sh2d) != hipSuccess)
       return false;
-    m->l0_pf_ver = m->l0_img_ver;
-    m->l0_pf_src = src;
-    m->l0_pf_slot = s;
-    l0_sent = true;
+    m->lpf_ver[p] = m->lpf_img_ver[p];
+    m->lpf_src[p] = src;
+    m->lpf_slot[p] = s;
+    ++lpf_sent;
     return true;
   }
   void push(int u) {
@@ -1478,16 +1483,19 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
 
   HSTEP(hipSetDevice(m->cfg.device));
   hipStream_t sc = m->sc, sh = m->sh2d, sd = m->sd2h;
-  // initial event states: every buffer free; a slot holding the first layer as sent by the
-  // previous fused step stays bound to it while that image is unwritten since (its ready event is
-  // that copy's), else it is free (a new copy into it queues behind that one)
-  const bool l0_keep = m->l0_pf_slot >= 0 && m->l0_pf_ver == m->l0_img_ver && m->l0_pf_src == image_block(m, 0);
+  // initial event states: every buffer free; a slot holding one of the first layers as sent by
+  // the previous fused step stays bound to it while that image is unwritten since (its ready event
+  // is that copy's), else it is free (a new copy into it queues behind that one)
   for (int i = 0; i < m->nslots; ++i) {
     HSTEP(hipEventRecord(m->ev_free[i], sc));
-    m->slot_layer[i] = l0_keep && i == m->l0_pf_slot ? 0 : -1;
+    m->slot_layer[i] = -1;
   }
-  m->l0_pf_slot = -1;
-  m->l0_pf_next = -1;
+  for (int p = 0; p < hol_model::NPF && p < L; ++p) {
+    const int ps = m->lpf_slot[p];
+    if (ps >= 0 && m->lpf_ver[p] == m->lpf_img_ver[p] && m->lpf_src[p] == image_block(m, p)) m->slot_layer[ps] = p;
+    m->lpf_slot[p] = -1;
+    m->lpf_next[p] = -1;
+  }
   m->n_tail_expect = 0;
   for (int i = 0; i < m->ngbuf; ++i) HSTEP(hipEventRecord(m->ev_gfree[i], sd));
   m->tev_used = 0;
@@ -1768,8 +1776,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
         m->n_tail = 0;
         m->n_tail_expect = split ? 3 : hol_model::N_TAIL;
         if (op.layer == 0) {  // its slot takes the next call's copy once this backward is done
-          HSTEP(hipEventRecord(m->ev_l0_done, sc));
-          m->l0_pf_next = s;
+          HSTEP(hipEventRecord(m->ev_lpf_done[0], sc));
+          m->lpf_next[0] = s;
         }
         auto piece = [&](int64_t lo, int64_t hi) -> hol_status {
           const int c = m->n_tail++;
@@ -1805,6 +1813,15 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       HSTEP(hipEventRecord(m->ev_gfree[gi], sd));
       if (fused && !tail) {
         HSTEP(hipEventRecord(m->ev_unit[1 + op.layer], sd));
+        // one of the first layers: its slot takes the next call's copy when no copy of this call
+        // can reuse it, i.e. every op left uses another layer that is resident
+        bool rest_resident = op.layer >= 1 && op.layer < hol_model::NPF;
+        for (size_t k = j + 1; rest_resident && k < ops.size(); ++k)
+          if (ops[k].kind != OP_HEAD && (ops[k].layer == op.layer || slot_of(ops[k].layer) < 0)) rest_resident = false;
+        if (rest_resident) {
+          HSTEP(hipEventRecord(m->ev_lpf_done[op.layer], sc));
+          m->lpf_next[op.layer] = s;
+        }
         worker.push(1 + op.layer);
       }
       m->stats.d2h_bytes += (double)m->layer_flat_n * 4;
@@ -1861,10 +1878,8 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     worker.stop(false);
     m->stats.worker_busy_ms = worker.busy_ms;
     if (worker.prefetched) m->stats.h2d_bytes += (double)m->head_img_bytes;  // the next call's head weights
-    if (worker.l0_sent) {  // and first layer
-      m->stats.h2d_bytes += (double)m->layer_img_bytes;
-      m->stats.n_weight_streams++;
-    }
+    m->stats.h2d_bytes += (double)worker.lpf_sent * m->layer_img_bytes;  // and first layers
+    m->stats.n_weight_streams += worker.lpf_sent;
     if (worker.failed) {
       set_error("hol_forward_backward_step: gradient copy failed; the step may be partially applied");
       return fail(HOL_EDEVICE);
@@ -1966,7 +1981,7 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo, int6
     });
   }
   if (u == m->L + 1) m->head_img_ver++;  // the head's image changed
-  if (u == 1) m->l0_img_ver++;           // the first layer's
+  if (u >= 1 && u <= hol_model::NPF) m->lpf_img_ver[u - 1]++;  // one of the first layers''
 }
 
 // Adam on the given rows of the embedding (and zeroing of their gradients): the same per-element

@@ -223,17 +223,20 @@ struct hol_model {
   hipEvent_t ev_head_done = nullptr, ev_head_pf = nullptr;  // head op done with head_dev / copy done
   bool head_pf = false;  // a copy was issued (it may still be in flight)
   std::atomic<uint64_t> head_img_ver{0};
-  // The next call's first layer: layer 0 is the backward's last layer and its update the fused
-  // step's last optimiser pieces; once they are done the worker queues its new image into the slot
-  // it occupied, on the weight stream. The next call keeps that slot while layer 0's image has not
-  // been written since (l0_img_ver) and the image buffer is the same.
-  std::atomic<uint64_t> l0_img_ver{0};
-  uint64_t l0_pf_ver = 0;
-  const uint8_t* l0_pf_src = nullptr;
-  int l0_pf_slot = -1;   // slot of the copy in flight or landed (-1: none)
-  int l0_pf_next = -1;   // this call: layer 0's slot, once its backward is queued
-  int n_tail_expect = 0; // this call: optimiser pieces of the last layer
-  hipEvent_t ev_l0_done = nullptr;  // layer 0's backward done with its slot
+  // The next call's first layers. The backward ends with the first block's layers, and their
+  // updates are the fused step's last units (layer 0's in pieces). Once a layer's update is done
+  // the worker queues its new image into the slot that layer occupied, on the weight stream, when
+  // no copy of this call can reuse that slot (every op left uses another layer that is resident).
+  // The next call keeps such a slot bound while that layer's image has not been written since
+  // (lpf_img_ver) and the image buffer is the same.
+  static constexpr int NPF = 4;
+  std::atomic<uint64_t> lpf_img_ver[NPF]{};
+  uint64_t lpf_ver[NPF] = {};
+  const uint8_t* lpf_src[NPF] = {};
+  int lpf_slot[NPF] = {-1, -1, -1, -1};  // slot of the copy in flight or landed (-1: none)
+  int lpf_next[NPF] = {-1, -1, -1, -1};  // this call: the layer's slot, once its backward is queued
+  int n_tail_expect = 0;         // this call: optimiser pieces of the last layer
+  hipEvent_t ev_lpf_done[NPF] = {};  // the layer's backward done with its slot
   uint64_t head_pf_ver = 0;
   const uint8_t* head_pf_src = nullptr;
 

@@ -269,9 +269,9 @@ def test_head_weights_sent_ahead_by_a_fused_step_follow_later_writes(wname):
 
 
 @pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
-def test_first_layer_sent_ahead_by_a_fused_step_follows_later_writes(wname):
-    """A fused step sends the next call's first layer (the backward's last, updated last) into a
-    weight slot before it returns. A later write of that layer (hol_set_tensor, a plain hol_step)
+def test_first_layers_sent_ahead_by_a_fused_step_follow_later_writes(wname):
+    """A fused step sends the next call's first layers (the backward's last, updated last) into
+    weight slots before it returns. A later write of them (hol_set_tensor, a plain hol_step)
     must be what the next call computes with, and a staleness-1 call after a fused step computes
     with the image it finds: bit for bit the same as a model that never sent the layer ahead."""
     w = TINY if wname == "tiny" else BF16_SMALL
@@ -281,7 +281,7 @@ def test_first_layer_sent_ahead_by_a_fused_step_follows_later_writes(wname):
         a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)   # sends layer 0 ahead
         lib_fb(b, w, batch)
         b.step()
-        for n in ("layers.0.wq", "layers.0.attn_norm"):
+        for n in ("layers.0.wq", "layers.0.attn_norm", "layers.1.wo", "layers.2.mlp_norm"):
             new = a.get_tensor(n) * np.float32(1.25)
             a.set_tensor(n, new)
             b.set_tensor(n, new)
