@@ -277,7 +277,8 @@ def main():
     t_layer = max(alg["f_layer"] / (BF16_PEAK_TFLOPS * 1e12), per_stream_layer * fb0["layer_image_bytes"] / link)
     t_head = max(alg["f_head"] / (BF16_PEAK_TFLOPS * 1e12), fb0["head_image_bytes"] / link)
     t_roof = s.n_layers * t_layer + t_head
-    h2d_gbs_busy = fb0["h2d_bytes"] / (fb0["h2d_busy_ms"] * 1e6) if fb0["h2d_busy_ms"] else 0.0
+    # the rate of the copies the busy time covers (copies sent ahead for the next call have no span)
+    h2d_gbs_busy = fb0.get("h2d_span_bytes", fb0["h2d_bytes"]) / (fb0["h2d_busy_ms"] * 1e6) if fb0["h2d_busy_ms"] else 0.0
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),

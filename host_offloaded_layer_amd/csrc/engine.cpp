@@ -1579,6 +1579,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     HCHECK(hipEventRecord(m->ev_ready[best], sh));
     m->slot_layer[best] = layer;
     m->stats.h2d_bytes += (double)m->layer_img_bytes;
+    m->stats.h2d_span_bytes += (double)m->layer_img_bytes;
     m->stats.n_weight_streams++;
     return HOL_OK;
   };
@@ -1603,6 +1604,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     spans.push_back({a, e, 0});
     HCHECK(hipEventRecord(m->ev_head, sh));
     m->stats.h2d_bytes += (double)m->head_img_bytes;
+    m->stats.h2d_span_bytes += (double)m->head_img_bytes;
     head_loaded = true;
     return HOL_OK;
   };
@@ -2076,6 +2078,7 @@ std::string stats_json(const hol_model* m) {
   o << std::fixed;
   o << "{\"tokens\":" << s.tokens << ",\"fb_ms\":" << s.fb_ms << ",\"step_ms\":" << s.step_ms
     << ",\"h2d_bytes\":" << s.h2d_bytes << ",\"d2h_bytes\":" << s.d2h_bytes << ",\"h2d_busy_ms\":" << s.h2d_busy_ms
+    << ",\"h2d_span_bytes\":" << s.h2d_span_bytes
     << ",\"d2h_busy_ms\":" << s.d2h_busy_ms << ",\"compute_busy_ms\":" << s.compute_busy_ms
     << ",\"fwd_ms\":" << s.fwd_ms << ",\"recomp_ms\":" << s.recomp_ms << ",\"bwd_ms\":" << s.bwd_ms
     << ",\"head_ms\":" << s.head_ms << ",\"host_embed_ms\":" << s.host_embed_ms

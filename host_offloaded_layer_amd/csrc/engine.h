@@ -70,6 +70,7 @@ struct KStat {
 
 struct Stats {
   double fb_ms = 0, step_ms = 0, h2d_bytes = 0, d2h_bytes = 0, h2d_busy_ms = 0, d2h_busy_ms = 0,
+         h2d_span_bytes = 0,  // bytes of the weight copies h2d_busy_ms times (the call's own layer and head copies)
          compute_busy_ms = 0, fwd_ms = 0, recomp_ms = 0, bwd_ms = 0, head_ms = 0, host_embed_ms = 0;
   // host timeline of a fused call (ms from the call's start): GPU work drained, embedding
   // scatter-add done; per optimiser unit: gradient arrived on the host, Adam done

@@ -190,7 +190,9 @@ hol_status hol_forward_backward_async(hol_model* m, const hol_batch* batch, hol_
 
 /* Timing and traffic of the last forward_backward / step as a JSON object (NUL-terminated).
  * Fields: fb_ms, step_ms, h2d_bytes, d2h_bytes, h2d_busy_ms, d2h_busy_ms, compute_busy_ms,
- * n_weight_streams, per-kernel-class compute ms, and for hol_forward_backward_step the host
+ * n_weight_streams, h2d_span_bytes (the bytes of the weight copies h2d_busy_ms times: h2d_bytes
+ * also counts h0 and the copies a fused step sends ahead for the next call, which have no span),
+ * per-kernel-class compute ms, and for hol_forward_backward_step the host
  * timeline (gpu_done_ms, scatter_done_ms, worker_busy_ms, units = [unit, start, end] of each
  * optimiser unit in ms from the call's start); for hol_forward_backward_async worker_busy_ms is the
  * overlapped step's time and async_wait_ms the time gradient copies waited for it. HOL_EINVAL, with nothing written, when the
