@@ -230,3 +230,25 @@ def test_moe_bwd_finite_differences():
     fd_check(f, x, dx)
     for n in P:
         fd_check(f, P[n], G[n], n=6)
+
+
+def test_topk_keeps_largest_probabilities():
+    """The router keeps the k experts of largest probability (the top-k by value): a hand case and
+    random distinct logits against torch.topk, for several token counts, expert counts and k."""
+    # one token whose router logits are (0.1, 3, -1, 2, 0.5): the top-2 are experts 1 then 3
+    logit_col = np.array([[0.1], [3.0], [-1.0], [2.0], [0.5]])
+    probs, ids, w, logits = D.moe_route(np.array([[1.0]]), logit_col, 2)
+    np.testing.assert_array_equal(ids, [[1, 3]])
+    np.testing.assert_allclose(w[0], np.exp([3.0, 2.0]) / np.exp([3.0, 2.0]).sum(), rtol=1e-14)
+    r = np.random.default_rng(11)
+    for T, E, k in [(7, 6, 2), (33, 16, 4), (20, 128, 8), (5, 9, 1)]:
+        n2 = r.standard_normal((T, 12))
+        Wr = r.standard_normal((E, 12))
+        probs, ids, w, _ = D.moe_route(n2, Wr, k)
+        ref_v, ref_i = torch.topk(torch.tensor(probs), k, dim=1)
+        np.testing.assert_array_equal(ids, ref_i.numpy())
+        # every kept probability is at least every dropped one
+        kept = np.take_along_axis(probs, ids, 1)
+        dropped = probs.copy()
+        np.put_along_axis(dropped, ids, -np.inf, 1)
+        assert np.all(kept.min(1) > dropped.max(1))

@@ -211,3 +211,23 @@ def test_float32_oracle_close_to_float64():
     assert abs(l32 - l64) <= 1e-6 * l64
     for n in G64:
         assert np.linalg.norm(G32[n] - G64[n]) <= 1e-4 * np.linalg.norm(G64[n]), n
+
+
+def test_oracle_matches_torch_autograd_moe_unforced_routing():
+    """Both sides choose their own experts (torch.topk on the torch side). The case is checked to
+    have clear top-k margins, so a routing rule that kept other experts than the k most probable
+    would show up as a loss and gradient mismatch."""
+    w, P, hid = moe_lora_case()
+    rec = []
+    loss, G = run(w, P, hidden=hid, record=rec)
+    s = D.Shape.of(w.shape)
+    # no routing decision is near a tie: perturbing the input by 1e-6 relative keeps every id
+    rec2 = []
+    run(w, P, hidden=hid * (1 + 1e-6), record=rec2)
+    for a, b in zip(rec, rec2):
+        np.testing.assert_array_equal(a, b)
+    ref_loss, ref_G = torch_ref.loss_and_grads(P, w.shape, w.n_micro, hidden=hid, loss="sumsq",
+                                               trainable=D.trainable_names(s, P))
+    assert abs(loss - ref_loss) <= 1e-11 * abs(ref_loss)
+    for n, g in G.items():
+        assert np.linalg.norm(g - ref_G[n]) <= 1e-9 * max(np.linalg.norm(ref_G[n]), 1e-30), n
