@@ -113,9 +113,12 @@ BF16_SMALL = W.Workload("bf16_small", W.ModelShape(3, 256, 4, 2, 64, ffn=512, vo
 
 
 # Tensors whose gradients flow through the attention scores. Rounding the attention inputs to
-# bf16 perturbs the scores, and dq / dk sum cancelling terms, so an exact bf16-operand pipeline
-# (simulated in fp32 with the same rounding points) already sits at 2.3-2.6 % relative L2 on them
-# at the 4096-wide shape. Their bound is 3e-2; every other tensor keeps 2e-2.
+# bf16 perturbs the scores, and dq / dk sum cancelling terms. tests/test_bf16_rounding_floor.py
+# runs an exact bf16-operand model of the layer on the CPU (fp32 arithmetic, bf16 rounding at the
+# path's points) at the LLaMA-8B layer shapes of test_bf16_real_layer_shapes_matches_oracle: it
+# puts wq / wk at 2.35 % against this reference while every other tensor stays below 2 %, and
+# below 2 % too once q, k and v are kept in fp32. These tensors are held to 3e-2; every other
+# tensor keeps 2e-2.
 SCORE_INPUTS = ("wq", "wk", "attn_norm")
 
 
