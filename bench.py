@@ -55,6 +55,105 @@ def link_peak_gbs(torch, nbytes=1 << 30, reps=4):
     return h2d, d2h
 
 
+def link_sweep(torch, sizes_mb=(4, 16, 64, 256, 1024), budget_s=0.15):
+    """Pinned hipMemcpyAsync rates (GB/s) by copy size: H2D alone, D2H alone, and both directions
+    at once on two streams (each direction's rate and their sum)."""
+    out = {"sizes_mb": list(sizes_mb), "h2d": [], "d2h": [], "bidir_h2d": [], "bidir_d2h": [], "bidir_total": []}
+    big = max(sizes_mb) << 20
+    h_up = torch.empty(big, dtype=torch.uint8).pin_memory()
+    h_dn = torch.empty(big, dtype=torch.uint8).pin_memory()
+    d_up = torch.empty(big, dtype=torch.uint8, device="cuda")
+    d_dn = torch.empty(big, dtype=torch.uint8, device="cuda")
+    s_up, s_dn = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps
+
+    for mb in sizes_mb:
+        n = mb << 20
+        reps = max(2, int(budget_s * 50e9 / n))
+        up = lambda: d_up[:n].copy_(h_up[:n], non_blocking=True)
+        dn = lambda: h_dn[:n].copy_(d_dn[:n], non_blocking=True)
+
+        def both():
+            with torch.cuda.stream(s_up):
+                d_up[:n].copy_(h_up[:n], non_blocking=True)
+            with torch.cuda.stream(s_dn):
+                h_dn[:n].copy_(d_dn[:n], non_blocking=True)
+
+        t_up, t_dn = timed(up, reps), timed(dn, reps)
+        # both directions at once: each stream's own span from events
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        both()
+        torch.cuda.synchronize()
+        e[0].record(s_up); e[2].record(s_dn)
+        for _ in range(reps):
+            both()
+        e[1].record(s_up); e[3].record(s_dn)
+        torch.cuda.synchronize()
+        tb_up, tb_dn = e[0].elapsed_time(e[1]) / 1e3 / reps, e[2].elapsed_time(e[3]) / 1e3 / reps
+        out["h2d"].append(round(n / t_up / 1e9, 1))
+        out["d2h"].append(round(n / t_dn / 1e9, 1))
+        out["bidir_h2d"].append(round(n / tb_up / 1e9, 1))
+        out["bidir_d2h"].append(round(n / tb_dn / 1e9, 1))
+        out["bidir_total"].append(round(2 * n / max(tb_up, tb_dn) / 1e9, 1))
+    del h_up, h_dn, d_up, d_dn
+    return out
+
+
+def gemm_roles(w: W.Workload):
+    """Names of the decoder GEMM shapes (M, N, K) of one call by the step they belong to."""
+    s = w.shape
+    T, H, d = w.tokens, s.hidden, s.head_dim
+    nqd, QKV, F = s.n_q_heads * d, (s.n_q_heads + 2 * s.n_kv_heads) * d, s.ffn
+    roles = {}
+
+    def add(shape, name):
+        roles[shape] = roles[shape] + " = " + name if shape in roles else name
+
+    if not s.n_experts:
+        add((T, QKV, H), "a4 qkv fwd"); add((T, H, nqd), "a7 o fwd"); add((T, 2 * F, H), "a9 gate/up fwd")
+        add((T, H, F), "a10 down fwd")
+        add((T, H, QKV), "a4 qkv dX"); add((T, nqd, H), "a7 o dX"); add((T, H, 2 * F), "a9 gate/up dX")
+        add((T, F, H), "a10 down dX")
+        add((QKV, H, T), "a4 qkv dW"); add((H, nqd, T), "a7 o dW"); add((2 * F, H, T), "a9 gate/up dW")
+        add((H, F, T), "a10 down dW")
+    return roles
+
+
+def gemm_table(w: W.Workload, st_list, steps):
+    """Per-shape GEMM rates of the timed steps, labelled by row of the hot path."""
+    roles = gemm_roles(w)
+    V = w.shape.vocab
+    acc = {}
+    for st in st_list:
+        for M, N, K, n, ms, fl in st.get("gemm_shapes", []):
+            a = acc.setdefault((M, N, K), [0, 0.0, 0.0])
+            a[0] += n; a[1] += ms; a[2] += fl
+    rows = []
+    for (M, N, K), (n, ms, fl) in sorted(acc.items(), key=lambda kv: -kv[1][1]):
+        if (M, N, K) in roles:
+            name = roles[(M, N, K)]
+        elif V and N == V:
+            name = "a13 head fwd"
+        elif V and K == V:
+            name = "a13 head dX"
+        elif V and M == V:
+            name = "a13 head dW"
+        else:
+            name = "other"
+        rows.append({"gemm": name, "M": M, "N": N, "K": K, "launches_per_step": n // steps,
+                     "avg_us": round(1e3 * ms / n, 1), "tflops": round(fl / ms / 1e9, 1),
+                     "frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)})
+    return rows
+
+
 def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int):
     """Algorithmic FLOPs and streamed bytes of one forward_backward (recompute included)."""
     s = w.shape
@@ -210,6 +309,7 @@ def main():
     h2d_peak, d2h_peak = link_peak_gbs(torch)
     log(f"[bench] pinned copy peak: H2D {h2d_peak:.1f} GB/s, D2H {d2h_peak:.1f} GB/s")
 
+
     mode = {"and_step": True} if args.optimizer == "sync" else {"stale_step": True}
 
     def one_step():
@@ -304,11 +404,15 @@ def main():
         "link": {"h2d_peak_gbs": round(h2d_peak, 1), "d2h_peak_gbs": round(d2h_peak, 1),
                  "h2d_gbs_busy": round(h2d_gbs_busy, 1), "h2d_gbs_wall": round(fb0["h2d_bytes"] / (fb0["fb_ms"] * 1e6), 1),
                  "h2d_bytes": fb0["h2d_bytes"], "d2h_bytes": fb0["d2h_bytes"], "weight_streams": fb0["n_weight_streams"]},
+        "gemm_shapes": gemm_table(w, [r[1] for r in recs], args.steps),
         "model_tflops": round(alg["flops"] / (fb_ms / 1e3) / 1e12, 1),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in kern.items()},
     }
     m.close()
     del m
+    # after the timed steps: the sweep's two extra streams stay in the process once created
+    out["link_sweep"] = link_sweep(torch)
+    log(f"[bench] pinned copy sweep: {out['link_sweep']}")
     if not args.no_cpu_baseline and w.name != "tiny":
         t0 = time.perf_counter()
         out["cpu_baseline"] = cpu_baseline(w)

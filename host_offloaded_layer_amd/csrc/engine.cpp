@@ -656,7 +656,7 @@ static Act act_at(const hol_model* m, int j) {
 // Runs `launch` on the compute stream; with kernel timing on, brackets it with events and
 // records its class and algorithmic work.
 template <typename F>
-static int timed(hol_model* m, int cls, double flops, double bytes, F&& launch) {
+static int timed_shape(hol_model* m, int cls, double flops, double bytes, int gm, int gn, int gk, F&& launch) {
   if (!m->ktiming || (size_t)m->krec.size() * 2 + 2 > m->kev.size()) return launch();
   const int e = (int)m->krec.size() * 2;
   hipError_t r = hipEventRecord(m->kev[e], m->sc);
@@ -665,14 +665,20 @@ static int timed(hol_model* m, int cls, double flops, double bytes, F&& launch) 
   if (rc) return rc;
   r = hipEventRecord(m->kev[e + 1], m->sc);
   if (r != hipSuccess) return (int)r;
-  m->krec.push_back({cls, e, flops, bytes});
+  m->krec.push_back({cls, e, flops, bytes, gm, gn, gk});
   return 0;
+}
+
+template <typename F>
+static int timed(hol_model* m, int cls, double flops, double bytes, F&& launch) {
+  return timed_shape(m, cls, flops, bytes, 0, 0, 0, launch);
 }
 
 static int run_gemm(hol_model* m, const Gemm& g) {
   const double E = (g.ab == DT_BF16) ? 2 : 4, Ec = (g.c == DT_BF16) ? 2 : 4;
   const double bytes = E * ((double)g.M * g.K + (double)g.N * g.K) + Ec * (double)g.M * g.N * (g.epi == EPI_STORE ? 1 : 2);
-  return timed(m, KC_GEMM, 2.0 * g.M * g.N * g.K * g.batch, bytes, [&] { return launch_gemm(g, m->sc); });
+  return timed_shape(m, KC_GEMM, 2.0 * g.M * g.N * g.K * g.batch, bytes, g.M, g.N, g.K,
+                     [&] { return launch_gemm(g, m->sc); });
 }
 
 #define KT(cls, flops, bytes, expr) KCHECK(timed(m, cls, (double)(flops), (double)(bytes), [&] { return (expr); }))
@@ -1935,6 +1941,13 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     k.ms += ms;
     k.flops += r.flops;
     k.bytes += r.bytes;
+    if (r.cls == KC_GEMM) {
+      KStat& gs = m->stats.gemm_shapes[{r.gm, r.gn, r.gk}];
+      gs.launches++;
+      gs.ms += ms;
+      gs.flops += r.flops;
+      gs.bytes += r.bytes;
+    }
   }
   m->krec.clear();
   m->stats.fb_ms = now_ms() - t_start;
@@ -2104,7 +2117,14 @@ std::string stats_json(const hol_model* m) {
     o << "\"" << names[c] << "\":{\"launches\":" << s.k[c].launches << ",\"ms\":" << s.k[c].ms
       << ",\"flops\":" << s.k[c].flops << ",\"bytes\":" << s.k[c].bytes << "}";
   }
-  o << "}}";
+  o << "},\"gemm_shapes\":[";
+  bool first = true;
+  for (const auto& kv : s.gemm_shapes) {
+    o << (first ? "" : ",") << "[" << kv.first[0] << "," << kv.first[1] << "," << kv.first[2] << ","
+      << kv.second.launches << "," << kv.second.ms << "," << kv.second.flops << "]";
+    first = false;
+  }
+  o << "]}";
   return o.str();
 }
 

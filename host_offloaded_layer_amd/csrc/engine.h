@@ -4,12 +4,13 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <array>
+#include <atomic>
 #include <condition_variable>
+#include <map>
 #include <mutex>
 #include <string>
 #include <thread>
-#include <array>
-#include <atomic>
 #include <vector>
 
 #include "../../include/hol.h"
@@ -87,6 +88,7 @@ struct Stats {
   int n_weight_streams = 0;
   int tokens = 0;
   KStat k[KC_N];
+  std::map<std::array<int, 3>, KStat> gemm_shapes;  // per (M, N, K) of the GEMM launches
 };
 
 }  // namespace hol
@@ -202,7 +204,7 @@ struct hol_model {
   int tev_used = 0;
   bool ktiming = false;                 // per-kernel-launch events
   std::vector<hipEvent_t> kev;          // pool for per-kernel events
-  struct KRec { int cls; int ev; double flops, bytes; };
+  struct KRec { int cls; int ev; double flops, bytes; int gm, gn, gk; };  // gm/gn/gk: GEMM shape (0 otherwise)
   std::vector<KRec> krec;
 
   int64_t step_t = 0;

@@ -318,3 +318,53 @@ def test_first_layers_sent_ahead_by_a_fused_step_follow_later_writes(wname):
         for n in sa:
             for x, y in zip(sa[n], sb[n]):
                 assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+
+
+@pytest.mark.parametrize("slots", [0, 2])
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
+def test_first_layers_sent_ahead_are_not_copied_again(wname, slots):
+    """The copies a fused step sends ahead are really used: the next call streams fewer layers
+    (h2d_span_bytes counts the copies a call makes for itself), by whole layer images; once those
+    layers are written (hol_set_tensor, or a plain hol_step) the next call copies them again.
+    Also with the two-slot ring."""
+    w = TINY if wname == "tiny" else BF16_SMALL
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+    L = w.shape.n_layers
+    with lib_model(w, params, slots=slots) as a, lib_model(w, params, slots=slots) as b:
+        lib_fb(b, w, batch)
+        fresh = b.stats()
+        lb, hb = fresh["layer_image_bytes"], fresh["head_image_bytes"]
+
+        def kept_layers(st, head_kept=True):
+            diff = fresh["h2d_span_bytes"] - st["h2d_span_bytes"]
+            n, rest = divmod(diff - (hb if head_kept else 0), lb)   # the head weights are sent ahead too
+            assert rest == 0 and n >= 0, (diff, lb, hb)
+            assert fresh["n_weight_streams"] - st["n_weight_streams"] == n
+            return n
+
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        lib_fb(a, w, batch)
+        n = kept_layers(a.stats())
+        print(wname, "slots", slots, "layers kept from the previous call", n)
+        assert 1 <= n <= L
+        # a write of layer 0 (the last layer the fused step updates, always among those sent): that
+        # one layer is copied again
+        a.zero_grad()
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        a.set_tensor("layers.0.wq", a.get_tensor("layers.0.wq"))
+        lib_fb(a, w, batch)
+        assert kept_layers(a.stats()) == n - 1
+        # writes of every layer: none is kept
+        a.zero_grad()
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        for l in range(L):
+            a.set_tensor(f"layers.{l}.mlp_norm", a.get_tensor(f"layers.{l}.mlp_norm"))
+        lib_fb(a, w, batch)
+        assert kept_layers(a.stats()) == 0
+        # a plain step after the fused one rewrites every layer image
+        a.zero_grad()
+        a.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True)
+        a.step()
+        lib_fb(a, w, batch)
+        assert kept_layers(a.stats(), head_kept=False) == 0
