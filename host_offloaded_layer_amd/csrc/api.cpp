@@ -366,6 +366,23 @@ hol_status hol_op_attention_bwd(int32_t n_seq, int32_t S, int32_t nq, int32_t nk
   return launched(launch_attn_bwd(a, (hipStream_t)stream), "hol_op_attention_bwd");
 }
 
+hol_status hol_op_attention_bwd_noalloc(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d, hol_dtype t,
+                                        const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                                        int64_t ldv, const void* o, int64_t ldo, const float* lse, const void* dO,
+                                        int64_t lddo, void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv,
+                                        int64_t lddv, void* stream) {
+  if ((int64_t)n_seq * nq * S > ATTN_SCRATCH_FLOATS) {
+    const std::string why = "n_seq * n_q_heads * S = " + std::to_string((int64_t)n_seq * nq * S) +
+                            " exceeds the static scratch of " + std::to_string(ATTN_SCRATCH_FLOATS) + " row sums";
+    return einval("hol_op_attention_bwd_noalloc", why.c_str());
+  }
+  Attn a = attn_args(n_seq, S, nq, nkv, d, t, q, ldq, k, ldk, v, ldv);
+  a.o = (void*)o; a.ldo = ldo; a.lse = (float*)lse;
+  a.dO = dO; a.lddo = lddo;
+  a.dq = dq; a.lddq = lddq; a.dk = dk; a.lddk = lddk; a.dv = dv; a.lddv = lddv;
+  return launched(launch_attn_bwd_noalloc(a, (hipStream_t)stream), "hol_op_attention_bwd_noalloc");
+}
+
 hol_status hol_op_cross_entropy(const float* logits, int64_t ld, const int32_t* labels, const float* w,
                                 float* row_loss, void* dlogits, hol_dtype dt, int64_t ldd, int32_t Tc, int32_t V,
                                 void* stream) {

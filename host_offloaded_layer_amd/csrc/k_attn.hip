@@ -7,6 +7,8 @@
 // This file holds the plain LDS-tiled version (fp32 arithmetic on fp32 or bf16 storage): tiles
 // of 64 queries x 64 keys, 4 threads per row. It serves the fp32 path and head widths the matrix-
 // core kernels (k_attn_mfma.hip: bf16, head width 64 or 128) do not take.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -328,6 +330,46 @@ int launch_attn_bwd(const Attn& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_dq_tiled<float>, dim3(nt, a.nq, a.n_seq), dim3(256), sm, s, a);
   }
   return (int)hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------- allocation-free backward
+// The row sums delta of the backward live in this file-scope device array (16 MiB on every GPU the
+// library runs on, held until the process ends) instead of a caller's workspace. Host code never
+// passes the array's name to a kernel: each device's address of it is looked up once, with that
+// device current, and kept.
+static __device__ __align__(256) float scratch[ATTN_SCRATCH_FLOATS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+static int scratch_address(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = (float*)p;
+  }
+  *out = g_scratch_dev[dev];
+  return 0;
+}
+
+int launch_attn_bwd_noalloc(Attn a, hipStream_t s) {
+  if ((int64_t)a.n_seq * a.nq * a.S > ATTN_SCRATCH_FLOATS) return (int)hipErrorInvalidValue;
+  float* p = nullptr;
+  const int e = scratch_address(&p);
+  if (e) return e;
+  a.delta = p;  // every row sum is written by the delta kernel before the gradient kernels read it
+  return launch_attn_bwd(a, s);
 }
 
 }  // namespace hol

@@ -107,6 +107,10 @@ struct Attn {
 };
 int launch_attn_fwd(const Attn& a, hipStream_t s);
 int launch_attn_bwd(const Attn& a, hipStream_t s);
+// The same backward with the row sums delta in the library's static device scratch (a.delta is
+// ignored): nothing is allocated. n_seq * nq * S must not exceed ATTN_SCRATCH_FLOATS.
+constexpr int64_t ATTN_SCRATCH_FLOATS = (int64_t)4 << 20;
+int launch_attn_bwd_noalloc(Attn a, hipStream_t s);
 
 // Next-token cross entropy over one chunk of rows. logits fp32 [Tc, V]; labels int32 (-1 =
 // ignore); w fp32 per-row weight (1/count of the row's micro-batch, 0 if ignored).

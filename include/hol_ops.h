@@ -88,6 +88,23 @@ hol_status hol_op_attention_bwd(int32_t n_seq, int32_t S, int32_t nq, int32_t nk
                                 int64_t lddq, void* dk, int64_t lddk, void* dv, int64_t lddv,
                                 float* delta, void* stream);
 
+/* hol_op_attention_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and results,
+ * with no delta argument. The row sums live in a static device array of the library, 16 MiB on
+ * each GPU it runs on (4,194,304 floats, held until the process ends); its address is looked up
+ * once per device on the first call with that device current. `stream` must belong to the current
+ * device. Nothing is allocated or freed. n_seq * nq * S above 4,194,304 returns HOL_EINVAL with
+ * the limit in hol_last_error() and launches nothing. Every call on one GPU shares that array and
+ * leaves its last row sums there (each call writes every row sum it reads, so nothing needs
+ * clearing); calls that overlap on one GPU (different streams or threads) race on it and must be
+ * serialised by the caller. */
+hol_status hol_op_attention_bwd_noalloc(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d,
+                                        hol_dtype t, const void* q, int64_t ldq, const void* k,
+                                        int64_t ldk, const void* v, int64_t ldv, const void* o,
+                                        int64_t ldo, const float* lse, const void* dO, int64_t lddo,
+                                        void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv,
+                                        int64_t lddv, void* stream);
+
 /* Cross entropy rows (loss anchor): logits fp32 [Tc, V] (row stride ld); labels int32 [Tc]
  * (-1 ignored); w fp32 [Tc] per-row weight. row_loss[t] = w[t] (logsumexp - z[label]);
  * dlogits [Tc, V] (dtype dt, row stride ldd) = w[t] (softmax - onehot). */
