@@ -154,6 +154,50 @@ def gemm_table(w: W.Workload, st_list, steps):
     return rows
 
 
+def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
+    """The workload's decoder GEMMs one shape at a time, with the epilogue and output type the
+    step uses (fp32 out; bf16 out for gate/up forward and the down-projection data gradient;
+    residual epilogue for the o and down projections), in the order listed, `reps` launches each
+    after one warm-up launch."""
+    s = w.shape
+    T, H, d = w.tokens, s.hidden, s.head_dim
+    nqd, QKV, F = s.n_q_heads * d, (s.n_q_heads + 2 * s.n_kv_heads) * d, s.ffn
+    # (name, M, N, K, epilogue, bf16 output)
+    shapes = [("a4 qkv fwd", T, QKV, H, 0, False), ("a7 o fwd", T, H, nqd, 2, False),
+              ("a9 gate/up fwd", T, 2 * F, H, 0, True), ("a10 down fwd", T, H, F, 2, False),
+              ("a10 down dX", T, F, H, 0, True), ("a9 gate/up dX", T, H, 2 * F, 0, False),
+              ("a7 o dX", T, nqd, H, 0, True), ("a4 qkv dX", T, H, QKV, 0, False),
+              ("a10 down dW", H, F, T, 0, False), ("a9 gate/up dW", 2 * F, H, T, 0, False),
+              ("a7 o dW", H, nqd, T, 0, False), ("a4 qkv dW", QKV, H, T, 0, False)]
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name, M, N, K, epi, bf in shapes:
+        a = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        b = torch.randn((N, K), device="cuda").to(torch.bfloat16)
+        c = torch.empty((M, N), device="cuda", dtype=torch.bfloat16 if bf else torch.float32)
+        r = torch.randn((M, N), device="cuda") if epi == 2 else None
+
+        def launch():
+            hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c.data_ptr(), N,
+                                          r.data_ptr() if r is not None else None, N, hol.BF16,
+                                          hol.BF16 if bf else hol.F32, epi, 1.0, stream.cuda_stream))
+
+        launch()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record(stream)
+            launch()
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)]))
+        tf = 2.0 * M * N * K / us / 1e6
+        rows.append({"gemm": name, "M": M, "N": N, "K": K, "avg_us": round(us, 1), "tflops": round(tf, 1),
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        log(f"[bench] {name:16s} {M:6d} x {N:6d} x {K:6d}: {us:8.1f} us {tf:7.1f} TFLOP/s")
+        del a, b, c, r
+    return {"workload": w.name, "gemm_shapes_alone": rows, "launches_per_shape": reps}
+
+
 def algorithmic(w: W.Workload, n_streams: int, layer_bytes: int, head_bytes: int):
     """Algorithmic FLOPs and streamed bytes of one forward_backward (recompute included)."""
     s = w.shape
@@ -273,6 +317,10 @@ def main():
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
+    ap.add_argument("--gemm-shapes", action="store_true",
+                    help="instead of training steps: each decoder GEMM shape of the workload alone "
+                         "(hol_op_gemm on random bf16 operands, the step's epilogue and output type), "
+                         "timed with HIP events; one JSON line per-shape")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -281,6 +329,9 @@ def main():
     import torch
     import host_offloaded_layer_amd as hol
     w = W.WORKLOADS[args.workload]
+    if args.gemm_shapes:
+        print(json.dumps(gemm_shapes_alone(torch, hol, w, args.steps)), flush=True)
+        return
     s = w.shape
     log(f"[bench] workload {w.name}: L={s.n_layers} H={s.hidden} tokens={w.tokens} K={w.ckpt_every_k}")
     t0 = time.perf_counter()
