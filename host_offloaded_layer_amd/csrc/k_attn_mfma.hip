@@ -107,6 +107,18 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; ex2(-inf) = 0
 
+// Reductions over the two halves of a wave (lanes l and l ^ 32), by v_permlane32_swap: swapping
+// the upper half of one copy of x with the lower half of another leaves x[l % 32] in the first and
+// x[32 + l % 32] in the second, in both halves, so both halves get the same result bit for bit.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Block order: `per` units for each (sequence, kv head) pair, unit 0 of a pair the longest.
 // Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8), so that the blocks an XCD runs
 // at once stream the tiles of one pair through its L2:
@@ -164,6 +176,25 @@ struct NatTile {
       const int c = threadIdx.x + NT * i;
       *(u32x4*)(dst + (c / (D / 8)) * P + (c % (D / 8)) * 8) = v[i];
     }
+  }
+};
+
+// Per-thread offsets of a NatTile's chunks from the tile's first row, for one row stride: a whole
+// tile then loads with one address add per chunk; a ragged last tile takes NatTile::load, which
+// clamps rows.
+template <int R, int D, int NT = 256>
+struct NatOff {
+  int64_t off[NatTile<R, D, NT>::N];
+  __device__ __forceinline__ void init(int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < NatTile<R, D, NT>::N; ++i) {
+      const int c = threadIdx.x + NT * i;
+      off[i] = (int64_t)(c / (D / 8)) * ld + (c % (D / 8)) * 8;
+    }
+  }
+  __device__ __forceinline__ void load(NatTile<R, D, NT>& t, const bf16* row0) const {
+#pragma unroll
+    for (int i = 0; i < NatTile<R, D, NT>::N; ++i) t.v[i] = *(const u32x4*)(row0 + off[i]);
   }
 };
 
@@ -529,7 +560,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_tr128(Attn a) {
   if (!pair_unit(nkt, a.nkv * a.n_seq, pair, kt)) return;
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int group = a.nq / a.nkv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: tile tests are scalar branches
   const int kw = w & 3, qb = w >> 2;  // key group of 32, query half of each tile
   const int k0 = kt * BKV;
   const int kj = k0 + 32 * kw + lq;  // this lane's key (column of the S / dP accumulators)
@@ -562,13 +594,21 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_tr128(Attn a) {
   // iteration it: query tile nqt - 1 - it / group (from the last down to the diagonal), q head
   // kvh * group + it % group; every key tile of a pair walks the query tiles in the same order
   NatTile<BQ, D, NT> qreg, greg;
+  NatOff<BQ, D, NT> qoffs, goffs;
+  qoffs.init(a.ldq);
+  goffs.init(a.lddo);
   float lse_r = 0.f, dl_r = 0.f;
   auto fetch = [&](int it) {
     const int h = kvh * group + it % group, q0 = (nqt - 1 - it / group) * BQ, nq = min(BQ, S - q0);
     const bf16* Q = (const bf16*)a.q + (int64_t)h * D;
     const bf16* G = (const bf16*)a.dO + (int64_t)h * D;
-    qreg.load(Q, a.ldq, base + q0, nq);
-    greg.load(G, a.lddo, base + q0, nq);
+    if (nq == BQ) {
+      qoffs.load(qreg, Q + (base + q0) * a.ldq);
+      goffs.load(greg, G + (base + q0) * a.lddo);
+    } else {
+      qreg.load(Q, a.ldq, base + q0, nq);
+      greg.load(G, a.lddo, base + q0, nq);
+    }
     if (threadIdx.x < BQ) {
       const int qq = q0 + threadIdx.x;
       const int64_t hrow = ((int64_t)seq * a.nq + h) * S;
@@ -603,7 +643,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_tr128(Attn a) {
     if (qh0 + 31 >= wave_kmin) {  // else every query of the half is before this wave's keys
       // S[q][key] and dP[q][key] for the half, then its dV / dK products (element r: query
       // qh0 + 8 (r/4) + 4 hh + r%4, key kj)
-      const bool full = qh0 >= wave_kmin + 31 && qh0 + 32 <= S && kj < S;  // no masking here
+      const bool full = qh0 >= wave_kmin + 31 && qh0 + 32 <= S && wave_kmin + 32 <= S;  // no masking here (wave-uniform)
       f32x16 s, dp;
       zero(s);
       zero(dp);
@@ -805,7 +845,8 @@ __global__ __launch_bounds__(512, 1) void attn_dq_tr128(Attn a) {
   const int qt = nqt - 1 - unit / group;  // longest first, the group's heads together
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int h = kvh * group + unit % group;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: tile tests are scalar branches
   const int qw = w & 3, kb = w >> 2;  // query group of 32, key half of each tile
   const int q0 = qt * BQ;
   const int qi = q0 + 32 * qw + lq;
@@ -844,10 +885,18 @@ __global__ __launch_bounds__(512, 1) void attn_dq_tr128(Attn a) {
   const int nkt = qmax / BK + 1;
   const int wave_qmax = min(q0 + 32 * qw + 31, S - 1);
   NatTile<BK, D, NT> kreg, vreg;
+  NatOff<BK, D, NT> koffs, voffs;
+  koffs.init(a.ldk);
+  voffs.init(a.ldv);
   auto fetch = [&](int kt) {
     const int k0 = kt * BK;
-    kreg.load(K, a.ldk, base + k0, min(BK, S - k0));
-    vreg.load(V, a.ldv, base + k0, min(BK, S - k0));
+    if (k0 + BK <= S) {
+      koffs.load(kreg, K + (base + k0) * a.ldk);
+      voffs.load(vreg, V + (base + k0) * a.ldv);
+    } else {
+      kreg.load(K, a.ldk, base + k0, S - k0);
+      vreg.load(V, a.ldv, base + k0, S - k0);
+    }
   };
   auto put = [&](int b) {
 #pragma unroll
@@ -876,13 +925,18 @@ __global__ __launch_bounds__(512, 1) void attn_dq_tr128(Attn a) {
         s = mfma(*(const bf16x8*)(Kc + o), qf[kk], s);
         dp = mfma(*(const bf16x8*)(Vc + o), gf[kk], dp);
       }
-      // element r: key kh0 + 8 (r/4) + 4 hh + r%4, query qi
+      // element r: key kh0 + 8 (r/4) + 4 hh + r%4, query qi; P as the dK/dV kernel forms it
+      if (kh0 + 31 <= q0 + 32 * qw && q0 + 32 * qw + 31 < S) {  // every key at or before every query (wave-uniform)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kh0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool ok = qv && kk <= qi && kk < S;
-        const float p = ok ? ex2(s[r] * sl2 - lse_q) : 0.f;
-        dp[r] = p * (dp[r] - dl_q);
+        for (int r = 0; r < 16; ++r) dp[r] = ex2(fmaf(s[r], sl2, -lse_q)) * (dp[r] - dl_q);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kh0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = qv && kk <= qi && kk < S;
+          const float p = ok ? ex2(fmaf(s[r], sl2, -lse_q)) : 0.f;
+          dp[r] = p * (dp[r] - dl_q);
+        }
       }
       // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
 #pragma unroll
@@ -941,7 +995,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
   const int qt = nqt - 1 - unit / group;  // longest (latest) query tiles first, the group's heads together
   const int kvh = pair % a.nkv, seq = pair / a.nkv;
   const int h = kvh * group + unit % group;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, lq = lane & 31;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: the mask test below is a scalar branch
   const int q0 = qt * BQ;
   const int qi = q0 + 32 * w + lq;  // this lane's query (column of every accumulator)
   const int64_t base = (int64_t)seq * S;
@@ -973,10 +1028,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
   const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
 
   NatTile<BK, D> kreg, vreg;
+  NatOff<BK, D> koff, voff;
+  koff.init(a.ldk);
+  voff.init(a.ldv);
   auto fetch = [&](int kt) {
     const int k0 = kt * BK;
-    kreg.load(K, a.ldk, base + k0, min(BK, S - k0));
-    vreg.load(V, a.ldv, base + k0, min(BK, S - k0));
+    if (k0 + BK <= S) {  // (scalar branch)
+      koff.load(kreg, K + (base + k0) * a.ldk);
+      voff.load(vreg, V + (base + k0) * a.ldv);
+    } else {
+      kreg.load(K, a.ldk, base + k0, S - k0);
+      vreg.load(V, a.ldv, base + k0, S - k0);
+    }
   };
   auto put = [&](int b) {
 #pragma unroll
@@ -1007,23 +1070,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
           s[kb] = mfma(kf, qf[kk], s[kb]);
         }
       }
-      // s[kb][r] = score(key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi)
-      const bool diag = (k0 + BK - 1 > q0 + 32 * w) || (k0 + BK > S);
+      // s[kb][r] = unscaled score(key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi)
+      const bool diag = (k0 + BK - 1 > q0 + 32 * w) || (k0 + BK > S);  // wave-uniform
+      if (diag) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            s[kb][r] = (kj > qi || kj >= S) ? -INFINITY : s[kb][r];
+          }
+      }
+      // the maximum of the unscaled scores (scaling by sl2 > 0 keeps the order), over both
+      // halves of the wave, which hold the same query
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[kb][r] * sl2;
-          if (diag) {
-            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (kj > qi || kj >= S) v = -INFINITY;
-          }
-          s[kb][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = xhalf_max(mx);
+      const float mn = fmaxf(m, mx * sl2);
       if (mn > m) {  // the running max moved: rescale (the whole wave skips this once maxima settle)
         const float corr = ex2(m - mn);
         l *= corr;
@@ -1033,16 +1099,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
           for (int r = 0; r < 16; ++r) o[i][r] *= corr;
         m = mn;
       }
-      float ls = 0.f;
+      // p = 2^(s sl2 - m); four partial row sums
+      float ls4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = ex2(s[kb][r] - m);
+          const float p = ex2(fmaf(s[kb][r], sl2, -m));
           s[kb][r] = p;
-          ls += p;
+          ls4[r & 3] += p;
         }
-      ls += __shfl_xor(ls, 32, 64);
+      float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+      ls = xhalf_sum(ls);
       l += ls;
       // O^T[d][q] += V^T[d][key] P^T[key][q]
 #pragma unroll
