@@ -3,8 +3,9 @@
  * The GPU holds no persistent model state (RoundPipe popular article §二, the computation-dispatch
  * paradigm; MegaTrain summary page, 研究动机 and 核心方法: host memory owns parameters, optimiser
  * state and accumulated gradients, device memory holds only a template pool). One call of
- * hol_forward_backward streams every decoder layer's weights host->HBM into one of two slots,
- * binds them to a weight-free layer template, runs the forward pass keeping a checkpoint every K
+ * hol_forward_backward streams every decoder layer's weights host->HBM into a ring of device
+ * slots (2 to 8, `weight_slots`; the pages' double buffer is the 2-slot case), binds them to a
+ * weight-free layer template, runs the forward pass keeping a checkpoint every K
  * layers, then runs the loss anchor and a block-wise backward (recompute each block from its
  * checkpoint, then backward layer by layer), streaming each layer's gradient back to the host
  * (MegaTrain summary page, 方法步骤详情 phases 1-3). hol_step runs Adam on the host (phase 4).
@@ -74,7 +75,10 @@ typedef struct {
   int32_t ckpt_every_k;       /* keep h_0, h_K, h_2K, ... in HBM (MegaTrain: checkpoint every K) */
   hol_dtype compute_dtype;    /* HOL_F32 or HOL_BF16 (bf16 operands, fp32 accumulation) */
   float lr, beta1, beta2, adam_eps, weight_decay; /* weight_decay must be 0 */
-  int32_t device;             /* HIP device ordinal */
+  int32_t device;             /* HIP device ordinal. (There is no pinned-memory budget: hol_create
+                               * pins the whole low-precision image, and the gradient block, so every
+                               * weight and gradient copy is one DMA from or to its final place;
+                               * a host that cannot pin them gets HOL_ENOMEM_HOST from hol_create.) */
   int32_t max_tokens;         /* largest batch*seq passed to forward_backward (sizes the HBM plan) */
   int32_t max_seq;            /* longest sequence (sizes the RoPE table) */
   int32_t weight_slots;       /* HBM slots of the weight ring, 2..8; 0: min(8, max(4, K + 2)) for
