@@ -311,6 +311,10 @@ def main():
                     help="sync: hol_forward_backward_step (the default, the synchronous step); async: "
                          "hol_forward_backward_async, the staleness-1 optimiser (each call applies the "
                          "previous call's update on host threads while it computes)")
+    ap.add_argument("--pinned-budget-gb", type=float, default=0.0,
+                    help="pinned host memory the weight image may use (GB); below the image size the "
+                         "image stays pageable and every weight copy is staged through the pinned ring. "
+                         "0 (default): the whole image is pinned")
     ap.add_argument("--stats-out", default=None,
                     help="write the library's statistics of the last timed step (device timeline included) "
                          "to this JSON file")
@@ -344,7 +348,8 @@ def main():
                           rms_eps=s.rms_eps, ckpt_every_k=w.ckpt_every_k,
                           compute_dtype=hol.BF16 if w.compute == "bf16" else hol.F32,
                           max_tokens=w.tokens, max_seq=w.seq, lr=w.lr,
-                          async_optimizer=int(args.optimizer == "async"))
+                          async_optimizer=int(args.optimizer == "async"),
+                          pinned_budget_bytes=int(args.pinned_budget_gb * 1e9))
     t0 = time.perf_counter()
     m = hol.Model(cfg)
     m.set_params(params)
@@ -441,7 +446,9 @@ def main():
                                + f", vocab {s.vocab}; {w.n_micro} micro-batches x {w.batch // w.n_micro} x {w.seq} tokens; K={w.ckpt_every_k}",
                    "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (1 GPU, layer streaming)",
                    "optimizer": ("synchronous step (hol_forward_backward_step)" if args.optimizer == "sync" else
-                                 "staleness-1 asynchronous step (hol_forward_backward_async)")},
+                                 "staleness-1 asynchronous step (hol_forward_backward_async)"),
+                   "weight_image": ("pinned" if not args.pinned_budget_gb else
+                                    f"pageable, staged through the pinned ring ({args.pinned_budget_gb:g} GB budget)")},
         "roofline": {"bound": "mfma", "kernel": "gemm_mfma (all decoder and head GEMMs)",
                      "achieved": round(g["tflops"], 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": profiled_traffic(w.name),
@@ -454,7 +461,9 @@ def main():
                          "model": "sum over layers of max(layer FLOPs / bf16 peak, streamed layer bytes / measured H2D peak) + head"},
         "link": {"h2d_peak_gbs": round(h2d_peak, 1), "d2h_peak_gbs": round(d2h_peak, 1),
                  "h2d_gbs_busy": round(h2d_gbs_busy, 1), "h2d_gbs_wall": round(fb0["h2d_bytes"] / (fb0["fb_ms"] * 1e6), 1),
-                 "h2d_bytes": fb0["h2d_bytes"], "d2h_bytes": fb0["d2h_bytes"], "weight_streams": fb0["n_weight_streams"]},
+                 "h2d_bytes": fb0["h2d_bytes"], "d2h_bytes": fb0["d2h_bytes"], "weight_streams": fb0["n_weight_streams"],
+                 **({"ring_segments": fb0["ring_segments"], "staged_bytes": fb0["staged_bytes"],
+                     "staging_ms": round(fb0["staging_ms"], 1)} if fb0.get("ring_segments") else {})},
         "gemm_shapes": gemm_table(w, [r[1] for r in recs], args.steps),
         "model_tflops": round(alg["flops"] / (fb_ms / 1e3) / 1e12, 1),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in kern.items()},

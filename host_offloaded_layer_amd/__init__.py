@@ -41,7 +41,8 @@ class Config(C.Structure):
                 ("compute_dtype", C.c_int32), ("lr", C.c_float), ("beta1", C.c_float),
                 ("beta2", C.c_float), ("adam_eps", C.c_float), ("weight_decay", C.c_float),
                 ("device", C.c_int32), ("max_tokens", C.c_int32), ("max_seq", C.c_int32),
-                ("weight_slots", C.c_int32), ("grad_buffers", C.c_int32), ("async_optimizer", C.c_int32)]
+                ("weight_slots", C.c_int32), ("grad_buffers", C.c_int32), ("async_optimizer", C.c_int32),
+                ("pinned_budget_bytes", C.c_uint64)]
 
 
 class Batch(C.Structure):
@@ -78,6 +79,7 @@ def _load() -> C.CDLL:
         "hol_host_adam": [P, P, P, P, I64, I64, F, F, F, F],
         "hol_host_bf16_round": [P, P, I64],
         "hol_op_gemm": [I32, I32, I32, P, I64, I32, P, I64, I32, P, I64, P, I64, I32, I32, I32, F, P],
+        "hol_op_gemm_swiglu": [I32, I32, I32, P, I64, P, I64, P, I64, P, I64, I32, P],
         "hol_op_rmsnorm_fwd": [P, P, F, P, I32, P, I32, I32, P],
         "hol_op_rmsnorm_bwd": [P, P, P, P, P, I32, P, P, I32, I32, P],
         "hol_op_rope": [P, I32, I64, I32, I32, I32, I32, P, P, I32, P],
@@ -115,7 +117,7 @@ EXPORTED = ["hol_create", "hol_destroy", "hol_num_tensors", "hol_tensor_info", "
             "hol_zero_grad", "hol_set_ckpt_every_k", "hol_set_kernel_timing",
             "hol_forward_backward", "hol_forward_backward_step", "hol_forward_backward_async", "hol_step", "hol_last_stats", "hol_partition",
             "hol_host_adam", "hol_host_bf16_round", "hol_last_error", "hol_version",
-            "hol_op_gemm", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
+            "hol_op_gemm", "hol_op_gemm_swiglu", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
             "hol_op_rope", "hol_op_rope_qkv", "hol_op_swiglu_fwd", "hol_op_swiglu_bwd", "hol_op_swiglu_bwd_t", "hol_op_transpose_bf16", "hol_op_attention_fwd",
             "hol_op_attention_bwd", "hol_op_attention_bwd_noalloc", "hol_op_cross_entropy", "hol_op_sync"]
 
@@ -260,11 +262,11 @@ def make_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, *
                 compute_dtype=F32, max_tokens, max_seq, n_experts=0, top_k=0, expert_ffn=0,
                 lora_rank=0, lora_scale=1.0, rope_base=10000.0, rms_eps=1e-5, lr=1e-3, beta1=0.9,
                 beta2=0.999, adam_eps=1e-8, device=0, weight_slots=0, grad_buffers=0,
-                async_optimizer=0) -> Config:
+                async_optimizer=0, pinned_budget_bytes=0) -> Config:
     return Config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_experts, top_k,
                   expert_ffn, lora_rank, lora_scale, rope_base, rms_eps, ckpt_every_k, compute_dtype,
                   lr, beta1, beta2, adam_eps, 0.0, device, max_tokens, max_seq, weight_slots, grad_buffers,
-                  async_optimizer)
+                  async_optimizer, pinned_budget_bytes)
 
 
 # ------------------------------------------------------------------------------------------

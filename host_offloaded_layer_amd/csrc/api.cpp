@@ -282,6 +282,19 @@ hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t l
   return launched(launch_gemm(g, (hipStream_t)stream), "hol_op_gemm");
 }
 
+hol_status hol_op_gemm_swiglu(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                              void* gu, int64_t ldgu, void* a, int64_t ld_a, hol_dtype t, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return einval("hol_op_gemm_swiglu", "negative size");
+  if (N % 2) return einval("hol_op_gemm_swiglu", "N (gate and up columns) must be even");
+  Gemm g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = gu; g.ldc = ldgu;
+  g.ab = g.c = t == HOL_BF16 ? DT_BF16 : DT_F32;
+  return launched(launch_gemm_swiglu(g, a, ld_a, (hipStream_t)stream), "hol_op_gemm_swiglu");
+}
+
 hol_status hol_op_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, hol_dtype yt, float* rstd,
                               int32_t T, int32_t H, void* stream) {
   return launched(launch_rmsnorm_fwd(x, gamma, eps, y, yt == HOL_BF16 ? DT_BF16 : DT_F32, rstd, T, H,

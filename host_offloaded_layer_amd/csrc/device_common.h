@@ -48,3 +48,20 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
   return t;
 }
+
+// SwiGLU element operations. Contraction is off so that every kernel that calls them (the
+// element-wise kernels and the fused gate/up GEMM epilogue) rounds the same way. The logistic
+// function takes the hardware reciprocal (v_rcp_f32, 1 ulp) rather than a correctly rounded
+// division: a third of the instructions, which matters in the GEMM epilogue, and an error far
+// below the bf16 rounding of every value it feeds (1 / inf = 0 and 1 / 1 = 1 at the extremes).
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float swiglu_f(float g, float u) {
+#pragma clang fp contract(off)
+  return g * sigm(g) * u;
+}
+__device__ __forceinline__ void swiglu_b(float d, float g, float u, float& dg, float& du) {
+#pragma clang fp contract(off)
+  const float sg = sigm(g);
+  dg = d * u * sg * (1.f + g * (1.f - sg));
+  du = d * g * sg;
+}

@@ -339,7 +339,34 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   parallel_zero(m->mom2, m->n_flat * 4);
   st = HOL_OK;
   m->grad = (float*)pinned_alloc(m, m->n_flat * 4, &st);
-  m->image = (uint8_t*)pinned_alloc(m, m->image_bytes, &st);
+  // the image: pinned whole, or pageable behind a ring of pinned segments when the pinned budget
+  // is smaller than the image(s)
+  const uint64_t img_total = (uint64_t)m->image_bytes * (c.async_optimizer ? 2u : 1u);
+  if (c.pinned_budget_bytes == 0 || c.pinned_budget_bytes >= img_total) {
+    m->image = (uint8_t*)pinned_alloc(m, m->image_bytes, &st);
+  } else {
+    m->ring_seg = align_up(m->layer_img_bytes, 4096);
+    const uint64_t r = c.pinned_budget_bytes / (uint64_t)m->ring_seg;
+    if (r < 2 || c.async_optimizer) {
+      set_error(r < 2 ? "hol_create: pinned_budget_bytes " + std::to_string(c.pinned_budget_bytes) +
+                            " is below the image (" + std::to_string(img_total) + " bytes) and below two ring segments of " +
+                            std::to_string(m->ring_seg) + " bytes"
+                      : std::string("hol_create: the pinned ring (pinned_budget_bytes below the image size) does not "
+                                    "serve async_optimizer"));
+      engine_destroy(m);
+      return HOL_EINVAL;
+    }
+    m->nring = (int)std::min<uint64_t>(8, r);
+    for (int i = 0; i < m->nring; ++i) m->ring[i] = (uint8_t*)pinned_alloc(m, m->ring_seg, &st);
+    void* p = nullptr;
+    if (posix_memalign(&p, 4096, (size_t)m->image_bytes) != 0) {
+      set_error("hol_create: pageable allocation of the " + std::to_string(m->image_bytes) + "-byte image failed");
+      engine_destroy(m);
+      return HOL_ENOMEM_HOST;
+    }
+    m->host_allocs.push_back(p);
+    m->image = (uint8_t*)p;
+  }
   const int64_t T = m->Tmax;
   m->h_stage = (float*)pinned_alloc(m, T * H * 4, &st);
   m->grad_stage = (float*)pinned_alloc(m, m->layer_flat_n * 4, &st);
@@ -497,6 +524,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->tail_mlp_ev, hipEventDisableTiming));
+  for (int i = 0; i < m->nring; ++i) HCHECK(hipEventCreateWithFlags(&m->ring_ev[i], hipEventDisableTiming));
   m->unit_tensors.assign(m->L + 2, {});
   for (int i = 0; i < (int)m->tensors.size(); ++i) {
     const TensorDesc& t = m->tensors[i];
@@ -546,6 +574,9 @@ void engine_destroy(hol_model* m) {
   if (m->sd2h) hipStreamDestroy(m->sd2h);
   for (void* p : m->dev_allocs) hipFree(p);
   for (void* p : m->pinned_allocs) hipHostFree(p);
+  for (void* p : m->host_allocs) free(p);
+  for (auto e : m->ring_ev)
+    if (e) hipEventDestroy(e);
   free(m->master);
   free(m->mom1);
   free(m->mom2);
@@ -559,6 +590,32 @@ void engine_destroy(hol_model* m) {
 static uint8_t* image_block(hol_model* m, int block, uint8_t* base = nullptr) {
   if (!base) base = m->image;
   return block >= 0 ? base + (int64_t)block * m->layer_img_bytes : base + (int64_t)m->L * m->layer_img_bytes;
+}
+
+// Queues the copy of `bytes` of the image at src into device memory at dst on the weight stream
+// s (the caller holds h2d_mu). Pinned image: one DMA. Pinned ring: piece by piece, each piece
+// copied by the host pool into the next ring segment once the DMA that last read that segment is
+// done (its event; that DMA depends only on work queued before it), then one DMA from the segment.
+static hipError_t image_h2d(hol_model* m, void* dst, const uint8_t* src, int64_t bytes, hipStream_t s) {
+  if (m->nring == 0) return hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyHostToDevice, s);
+  for (int64_t off = 0; off < bytes; off += m->ring_seg) {
+    const int64_t n = std::min<int64_t>(m->ring_seg, bytes - off);
+    const int r = m->ring_next;
+    m->ring_next = (r + 1) % m->nring;
+    hipError_t e = hipEventSynchronize(m->ring_ev[r]);
+    if (e != hipSuccess) return e;
+    const double t0 = now_ms();
+    uint8_t* seg = m->ring[r];
+    const uint8_t* from = src + off;
+    parallel_for(n, 1 << 22, [&](int64_t lo, int64_t hi) { memcpy(seg + lo, from + lo, (size_t)(hi - lo)); });
+    m->stats.staging_ms += now_ms() - t0;
+    m->stats.staged_bytes += (double)n;
+    e = hipMemcpyAsync((uint8_t*)dst + off, seg, (size_t)n, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(m->ring_ev[r], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 void refresh_image_tensor(hol_model* m, const TensorDesc& t) {
@@ -679,6 +736,14 @@ static int run_gemm(hol_model* m, const Gemm& g) {
   const double bytes = E * ((double)g.M * g.K + (double)g.N * g.K) + Ec * (double)g.M * g.N * (g.epi == EPI_STORE ? 1 : 2);
   return timed_shape(m, KC_GEMM, 2.0 * g.M * g.N * g.K * g.batch, bytes, g.M, g.N, g.K,
                      [&] { return launch_gemm(g, m->sc); });
+}
+
+// the gate/up product with SwiGLU (launch_gemm_swiglu); a: [M, N/2] at row stride ld_a
+static int run_gemm_swiglu(hol_model* m, const Gemm& g, void* a, int64_t ld_a) {
+  const double E = (g.ab == DT_BF16) ? 2 : 4, Ec = (g.c == DT_BF16) ? 2 : 4;
+  const double bytes = E * ((double)g.M * g.K + (double)g.N * g.K) + Ec * 1.5 * (double)g.M * g.N;
+  return timed_shape(m, KC_GEMM, 2.0 * g.M * g.N * g.K, bytes, g.M, g.N, g.K,
+                     [&] { return launch_gemm_swiglu(g, a, ld_a, m->sc); });
 }
 
 #define KT(cls, flops, bytes, expr) KCHECK(timed(m, cls, (double)(flops), (double)(bytes), [&] { return (expr); }))
@@ -929,8 +994,9 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   if (m->R > 0) STEP_OK(lora_fwd(m, A.o, nqd, nqd, H, w.lA[3], w.lB[3], A.h1, H, T));
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(A.h1, w.g2, m->cfg.rms_eps, A.n2, dt, A.r2, T, H, s));
   if (m->NE > 0) return moe_forward(m, w, A, T, hout, pos);
-  KCHECK(run_gemm(m, gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE)));
-  KT(KC_SWIGLU, 0, 3.0 * T * F * E, launch_swiglu_fwd(A.gu, A.a, dt, T, F, s));
+  // gate/up product with SwiGLU in its epilogue (one kernel for bf16 with F % 32 == 0; else the
+  // product and the element-wise kernel, timed together as one GEMM record)
+  KCHECK(run_gemm_swiglu(m, gemm(T, 2 * F, H, A.n2, H, false, w.wgu, H, false, A.gu, 2 * F, dt, dt, EPI_STORE), A.a, F));
   if (hout)  // (null: the output is not needed, see the recompute)
     KCHECK(run_gemm(m, gemm(T, H, F, A.a, F, false, w.wd, F, false, hout, H, dt, DT_F32, EPI_RESID, A.h1, H)));
   return HOL_OK;
@@ -988,8 +1054,11 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   if (m->NE > 0) {
     STEP_OK(moe_backward(m, w, A, T, G, pos));
   } else {
-    // MLP: da = dh Wd, dWd = dh^T a
-    KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+    // MLP: da = dh Wd, dWd = dh^T a (dhb is normally written with dh by the RMSNorm backward
+    // above this layer)
+    if (!m->dhb_current)
+      KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
+    m->dhb_current = true;
     KCHECK(run_gemm(m, nt(T, F, H, m->dhb, H, WdT, H, m->da, F, dt)));
     if (tw) {
       KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
@@ -1012,10 +1081,10 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
     if (m->tail_mlp_armed) HCHECK(hipEventRecord(m->tail_mlp_ev, s));  // w_gate, w_up, w_down final
   }
   if (tw) KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
-  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true, tw ? G + m->g_g2 : nullptr,
-                                                      m->partial, T, H, s));
+  // (the RMSNorm backward also writes dh rounded to bf16 into dhb)
+  KT(KC_RMSNORM, 0, (16.0 + E) * T * H, launch_rmsnorm_bwd(m->dn, A.h1, w.g2, A.r2, m->dh, true,
+                                                             tw ? G + m->g_g2 : nullptr, m->partial, T, H, s, m->dhb));
   // attention output projection: dO = dh1 Wo (+ LoRA), dWo = dh1^T o
-  KT(KC_OTHER, 0, (double)T * H * (4 + E), launch_cast_f32(m->dh, m->dhb, dt, (int64_t)T * H, s));
   if (m->R > 0) {
     float* dO32 = m->qkvf;  // fp32 [T, nqd]
     KCHECK(run_gemm(m, nt(T, nqd, H, m->dhb, H, WoT, H, dO32, nqd, DT_F32)));
@@ -1054,8 +1123,9 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
     KCHECK(tr(m, A.n1, H, m->xT, T, T, H));
     KCHECK(run_gemm(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
   }
-  KT(KC_RMSNORM, 0, 16.0 * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true, tw ? G + m->g_g1 : nullptr,
-                                                      m->partial, T, H, s));
+  KT(KC_RMSNORM, 0, (16.0 + E) * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true,
+                                                             tw ? G + m->g_g1 : nullptr, m->partial, T, H, s, m->dhb));
+  m->dhb_current = true;
   return HOL_OK;
 }
 
@@ -1121,6 +1191,7 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
   const int H = m->H;
   if (loss == HOL_LOSS_SUM_SQUARES) {
     KT(KC_OTHER, 0, 8.0 * T * H, launch_sumsq(hL, m->rowloss_dev, m->dh, T, H, s));
+    m->dhb_current = false;
     return HOL_OK;
   }
   const int V = m->V;
@@ -1155,8 +1226,10 @@ static hol_status head_forward_backward(hol_model* m, const float* hL, int T, ho
                               r0 == 0 ? EPI_STORE : EPI_ACCUM)));
   }
   if (ht) KCHECK(launch_fill_f32(m->head_gdev, 0.f, H, s));
-  KT(KC_RMSNORM, 0, 12.0 * T * H, launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, ht ? m->head_gdev : nullptr,
-                                                      m->partial, T, H, s));
+  void* dhb = dt == DT_BF16 ? m->dhb : nullptr;  // (bf16: the layer below reads dh rounded)
+  KT(KC_RMSNORM, 0, (12.0 + (dhb ? 2 : 0)) * T * H,
+     launch_rmsnorm_bwd(m->dn, hL, gf, m->rz, m->dh, false, ht ? m->head_gdev : nullptr, m->partial, T, H, s, dhb));
+  m->dhb_current = dhb != nullptr;
   return HOL_OK;
 }
 
@@ -1257,7 +1330,7 @@ struct FusedWorker {
     const uint8_t* src = image_block(m, -1);
     std::lock_guard<std::mutex> g(m->h2d_mu);
     if (hipStreamWaitEvent(m->sh2d, m->ev_head_done, 0) != hipSuccess ||
-        hipMemcpyAsync(m->head_dev, src, m->head_img_bytes, hipMemcpyHostToDevice, m->sh2d) != hipSuccess ||
+        image_h2d(m, m->head_dev, src, m->head_img_bytes, m->sh2d) != hipSuccess ||
         hipEventRecord(m->ev_head_pf, m->sh2d) != hipSuccess)
       return false;
     m->head_pf_ver = m->head_img_ver;
@@ -1273,7 +1346,7 @@ struct FusedWorker {
     const int s = m->lpf_next[p];
     std::lock_guard<std::mutex> g(m->h2d_mu);
     if (hipStreamWaitEvent(m->sh2d, m->ev_lpf_done[p], 0) != hipSuccess ||
-        hipMemcpyAsync(m->slot[s], src, m->layer_img_bytes, hipMemcpyHostToDevice, m->sh2d) != hipSuccess ||
+        image_h2d(m, m->slot[s], src, m->layer_img_bytes, m->sh2d) != hipSuccess ||
         hipEventRecord(m->ev_ready[s], m->sh2d) != hipSuccess)
       return false;
     m->lpf_ver[p] = m->lpf_img_ver[p];
@@ -1579,7 +1652,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     HCHECK(hipStreamWaitEvent(sh, m->ev_free[best], 0));
     hipEvent_t a = tev(), e = tev();
     HCHECK(hipEventRecord(a, sh));
-    HCHECK(hipMemcpyAsync(m->slot[best], image_block(m, layer), m->layer_img_bytes, hipMemcpyHostToDevice, sh));
+    HCHECK(image_h2d(m, m->slot[best], image_block(m, layer), m->layer_img_bytes, sh));
     HCHECK(hipEventRecord(e, sh));
     spans.push_back({a, e, 0});
     HCHECK(hipEventRecord(m->ev_ready[best], sh));
@@ -1605,7 +1678,7 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
     }
     hipEvent_t a = tev(), e = tev();
     HCHECK(hipEventRecord(a, sh));
-    HCHECK(hipMemcpyAsync(m->head_dev, image_block(m, -1), m->head_img_bytes, hipMemcpyHostToDevice, sh));
+    HCHECK(image_h2d(m, m->head_dev, image_block(m, -1), m->head_img_bytes, sh));
     HCHECK(hipEventRecord(e, sh));
     spans.push_back({a, e, 0});
     HCHECK(hipEventRecord(m->ev_head, sh));
@@ -2097,6 +2170,8 @@ std::string stats_json(const hol_model* m) {
     << ",\"head_ms\":" << s.head_ms << ",\"host_embed_ms\":" << s.host_embed_ms
     << ",\"n_weight_streams\":" << s.n_weight_streams << ",\"layer_image_bytes\":" << m->layer_img_bytes
     << ",\"head_image_bytes\":" << m->head_img_bytes << ",\"host_threads\":" << pool_threads()
+    << ",\"ring_segments\":" << m->nring << ",\"ring_segment_bytes\":" << m->ring_seg
+    << ",\"staged_bytes\":" << s.staged_bytes << ",\"staging_ms\":" << s.staging_ms
     << ",\"gpu_done_ms\":" << s.gpu_done_ms << ",\"scatter_done_ms\":" << s.scatter_done_ms
     << ",\"worker_busy_ms\":" << s.worker_busy_ms << ",\"async_wait_ms\":" << s.async_wait_ms
     << ",\"first_compute_ms\":" << s.first_compute_ms

@@ -87,6 +87,8 @@ struct Stats {
   std::vector<std::array<float, 3>> timeline;
   int n_weight_streams = 0;
   int tokens = 0;
+  // pinned ring: bytes staged through it and host time spent copying into its segments
+  double staged_bytes = 0, staging_ms = 0;
   KStat k[KC_N];
   std::map<std::array<int, 3>, KStat> gemm_shapes;  // per (M, N, K) of the GEMM launches
 };
@@ -112,7 +114,16 @@ struct hol_model {
   float* grad = nullptr;     // fp32 accumulated gradients (pinned)
   float* mom1 = nullptr;
   float* mom2 = nullptr;
-  uint8_t* image = nullptr;  // low-precision copy, layer-contiguous, 4 KiB aligned (pinned)
+  uint8_t* image = nullptr;  // low-precision copy, layer-contiguous, 4 KiB aligned (pinned, or
+                             // pageable under a pinned budget smaller than the image)
+  // Pinned ring (a pinned budget below the image size): nring pinned segments of ring_seg bytes
+  // through which every image-to-HBM copy is staged; segment s is reused once the DMA that last
+  // read it (ring_ev[s]) is done. Guarded by h2d_mu, like every weight copy.
+  int nring = 0, ring_next = 0;
+  int64_t ring_seg = 0;
+  uint8_t* ring[8] = {};
+  hipEvent_t ring_ev[8] = {};
+  std::vector<void*> host_allocs;  // pageable images (freed at destroy)
   // staleness-1 asynchronous optimiser (allocated only when configured): the second image takes
   // the step's refreshed copy while the GPU streams from the first
   uint8_t* image_alt = nullptr;
@@ -175,6 +186,7 @@ struct hol_model {
   float* dh = nullptr;
   float* dn = nullptr;
   void* dhb = nullptr;
+  bool dhb_current = false;  // dhb holds dh rounded to bf16 (kept by the writers of dh)
   void* dqkv = nullptr;
   void* dO = nullptr;
   void* da = nullptr;

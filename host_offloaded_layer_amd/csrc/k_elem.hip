@@ -105,7 +105,8 @@ template <int NV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_row_k(const float* __restrict__ dy, const float* __restrict__ x,
                                                          const float* __restrict__ g, const float* __restrict__ rstd,
                                                          float* __restrict__ dx, int accumulate,
-                                                         float* __restrict__ partial, int T, int H) {
+                                                         float* __restrict__ partial, int T, int H,
+                                                         bf16* __restrict__ dxb) {
   __shared__ float red[2][4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float4 dg[NV], gv[NV];
@@ -150,6 +151,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_row_k(const float* __restrict
         o.x = r * (dv[i].x - xv[i].x * r * dot) + pv[i].x; o.y = r * (dv[i].y - xv[i].y * r * dot) + pv[i].y;
         o.z = r * (dv[i].z - xv[i].z * r * dot) + pv[i].z; o.w = r * (dv[i].w - xv[i].w * r * dot) + pv[i].w;
         *(float4*)(dxr + j) = o;
+        if (dxb) {
+          const bf16x4 ob = {(bf16)o.x, (bf16)o.y, (bf16)o.z, (bf16)o.w};
+          *(bf16x4*)(dxb + (int64_t)row * H + j) = ob;
+        }
       }
     }
   }
@@ -165,7 +170,8 @@ template <int NV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ g, const float* __restrict__ rstd,
                                                      float* __restrict__ dx, int accumulate,
-                                                     float* __restrict__ partial, int T, int H) {
+                                                     float* __restrict__ partial, int T, int H,
+                                                     bf16* __restrict__ dxb) {
   __shared__ float red[4][NV * 256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float4 dg[NV];
@@ -205,6 +211,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ d
           o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
         }
         *(float4*)(dxr + j) = o;
+        if (dxb) {
+          const bf16x4 ob = {(bf16)o.x, (bf16)o.y, (bf16)o.z, (bf16)o.w};
+          *(bf16x4*)(dxb + (int64_t)row * H + j) = ob;
+        }
       }
     }
   }
@@ -236,14 +246,17 @@ __global__ __launch_bounds__(1024) void reduce_cols_add_k(const float* __restric
 }
 
 int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd, float* dx_out,
-                       bool accumulate, float* dgamma_acc, float* partial, int T, int H, hipStream_t s) {
+                       bool accumulate, float* dgamma_acc, float* partial, int T, int H, hipStream_t s,
+                       void* dx_bf16) {
   if (T <= 0) return 0;
   if (H % 4 || H > 4096) return (int)hipErrorInvalidValue;
+  if ((uintptr_t)dx_bf16 % 8) return (int)hipErrorInvalidValue;
+  bf16* dxb = (bf16*)dx_bf16;
   const int nb = rmsnorm_bwd_blocks(T);
   if (H >= 1024) {
 #define RR(NVV)                                                                                       \
   hipLaunchKernelGGL(rmsnorm_bwd_row_k<NVV>, dim3(nb), dim3(256), 0, s, dy, x, gamma, rstd, dx_out, \
-                     (int)accumulate, partial, T, H)
+                     (int)accumulate, partial, T, H, dxb)
     if (H <= 2048) RR(2);
     else RR(4);
 #undef RR
@@ -253,7 +266,7 @@ int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, cons
   const int nv = (H + 255) / 256;
 #define RB(NVV)                                                                                   \
   hipLaunchKernelGGL(rmsnorm_bwd_k<NVV>, dim3(nb), dim3(256), 0, s, dy, x, gamma, rstd, dx_out, \
-                     (int)accumulate, partial, T, H)
+                     (int)accumulate, partial, T, H, dxb)
   if (nv <= 1) RB(1);
   else if (nv <= 2) RB(2);
   else if (nv <= 4) RB(4);
@@ -384,19 +397,7 @@ int launch_rope_qkv(const float* in, int64_t ldi, void* out, int64_t ldo, int T,
 // ------------------------------------------------------------------------------------------
 // SwiGLU
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
-
-// Contraction is off in these two so that every kernel below that calls them rounds the same way.
-__device__ __forceinline__ float swiglu_f(float g, float u) {
-#pragma clang fp contract(off)
-  return g * sigm(g) * u;
-}
-__device__ __forceinline__ void swiglu_b(float d, float g, float u, float& dg, float& du) {
-#pragma clang fp contract(off)
-  const float sg = sigm(g);
-  dg = d * u * sg * (1.f + g * (1.f - sg));
-  du = d * g * sg;
-}
+// (sigm, swiglu_f and swiglu_b live in device_common.h: the gate/up GEMM epilogue shares them)
 
 template <typename T>
 __global__ void swiglu_fwd_k(const T* __restrict__ gu, T* __restrict__ a, int Tn, int F) {

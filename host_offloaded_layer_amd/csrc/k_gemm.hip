@@ -488,9 +488,19 @@ constexpr int N3_TILE = (N2_BM + N2_BN) * N3_BK;  // bf16 elements per stage
 
 __device__ __forceinline__ int n3_off(int r, int c) { return r * N3_BK + ((c ^ ((r >> 1) & 7)) << 3); }
 
+// Row of B that feeds output column v. Plain: v. SW (the gate/up product with SwiGLU in the
+// epilogue, B = [W_gate; W_up] with F = N / 2 rows each, F % 32 == 0): the columns of each 64-wide
+// block c are the gate rows 32 c .. 32 c + 31 followed by the up rows F + 32 c .. F + 32 c + 31,
+// so a wave's two 32-column blocks hold the gate and up values of the same 32 features.
+template <bool SW>
+__device__ __forceinline__ int n3_brow(int v, int F) {
+  if constexpr (!SW) return v;
+  else return ((v >> 6) << 5) + (v & 31) + ((v & 32) ? F : 0);
+}
+
 // this wave's 64 / NW loads of one stage: LDS rows [8 q, 8 q + 8) for q = wave + NW i of A, then
 // of B
-template <int NW>
+template <int NW, bool SW = false>
 __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A, int64_t lda, int m0, int M,
                                          const bf16* __restrict__ B, int64_t ldb, int n0, int N, int k0) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -508,7 +518,7 @@ __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A
     const int R = (w + NW * i) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ ((R >> 1) & 7);
     int gr = n0 + R;
-    gr = gr < N ? gr : N - 1;
+    gr = n3_brow<SW>(gr < N ? gr : N - 1, N >> 1);
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(B + (int64_t)gr * ldb + k0 + lc * 8),
                                      (lds_ptr_t)(stage + N2_BM * N3_BK + (w + NW * i) * 8 * N3_BK), 16, 0, 0);
   }
@@ -518,7 +528,7 @@ __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A
 // a third fewer LDS fragment reads per MFMA).
 // The same loads through buffer resources: a lane's byte offset into A (B) is fixed for the whole
 // tile (rows clamped as above), the stage's k offset is a scalar, so no per-load address arithmetic.
-template <int NW>
+template <int NW, bool SW = false>
 struct N3Buf {
   uint32_t va[32 / NW], vb[32 / NW];
   __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N) {
@@ -528,7 +538,7 @@ struct N3Buf {
       const int R = (w + NW * i) * 8 + (lane >> 3);
       const int lc = (lane & 7) ^ ((R >> 1) & 7);
       va[i] = (uint32_t)(min(m0 + R, M - 1) * lda * 2 + lc * 16);
-      vb[i] = (uint32_t)(min(n0 + R, N - 1) * ldb * 2 + lc * 16);
+      vb[i] = (uint32_t)(n3_brow<SW>(min(n0 + R, N - 1), N >> 1) * ldb * 2 + lc * 16);
     }
   }
   __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int k0) const {
@@ -616,7 +626,40 @@ __device__ __forceinline__ bool n3_full_tile(const Gemm& g, const TO* C, const f
          (EPI != EPI_RESID || (g.ldr % 4 == 0 && (uintptr_t)R % 16 == 0));
 }
 
-template <int EPI, typename TO, int NW, bool BUF, bool GRP>
+// SwiGLU epilogue (B rows interleaved by n3_brow<true>): block j = 0 of a wave holds the gate and
+// j = 1 the up value of feature f = (n0 + 64 wn) / 2 + 8 q + 4 (lane / 32) + e. C receives gate |
+// up rounded to bf16, exactly as the plain product stores them, and C2 (row stride ldc2) the
+// SwiGLU of the rounded pair. Vector stores only: F % 32 == 0, ldc and ldc2 multiples of 4 and
+// 8-byte aligned C, C2 (checked by the launcher). 48 stores per wave for a full tile.
+__device__ __forceinline__ void n3_store_swiglu(const Gemm& g, const f32x16 (&acc)[4][2], bf16* C, int M, int N,
+                                                int m0, int n0, int wm, int wn, int lane) {
+  const int F = N >> 1;
+  bf16* C2 = (bf16*)g.C2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (row >= M) continue;
+    bf16* crow = C + (int64_t)row * g.ldc;
+    bf16* arow = C2 + (int64_t)row * g.ldc2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = (n0 >> 1) + wn * 32 + 8 * q + 4 * (lane >> 5);
+      if (f >= F) continue;
+      bf16x4 gb, ub, ab;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gb[e] = (bf16)(g.alpha * acc[i][0][4 * q + e]);
+        ub[e] = (bf16)(g.alpha * acc[i][1][4 * q + e]);
+        ab[e] = (bf16)swiglu_f((float)gb[e], (float)ub[e]);
+      }
+      *(bf16x4*)(crow + f) = gb;
+      *(bf16x4*)(crow + F + f) = ub;
+      *(bf16x4*)(arow + f) = ab;
+    }
+  }
+}
+
+template <int EPI, typename TO, int NW, bool BUF, bool GRP, bool SW = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
   static_assert(NW == 8, "the epilogue count below assumes 8 waves");
@@ -687,15 +730,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  static_assert(!SW || (EPI == EPI_STORE && sizeof(TO) == 2 && !GRP && WJ == 2), "SwiGLU: bf16 store, one group");
   const int nk = K / N3_BK;
-  N3Buf<NW> nb;
+  N3Buf<NW, SW> nb;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)M * g.lda * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)N * g.ldb * 2), 0x00020000);
   auto issue = [&](bf16* stage, int k0) {
     if constexpr (BUF) nb.issue(stage, ra, rb, k0);
-    else n3_issue<NW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, k0);
+    else n3_issue<NW, SW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, k0);
   };
   auto start_tile = [&]() {
     if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N);
@@ -723,11 +767,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   int after = 0;
   for (;;) {
     // stage 0 ready (stage 1's loads and the previous epilogue may still be in flight)
+    // (the epilogue issues 32 memory operations per wave, 48 with SwiGLU)
     if (nk > 1) {
-      if (after) asm volatile("s_waitcnt vmcnt(40)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (after && SW) asm volatile("s_waitcnt vmcnt(56)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (after) asm volatile("s_waitcnt vmcnt(40)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else {
-      if (after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (after && SW) asm volatile("s_waitcnt vmcnt(48)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     frags(lds, 0, a0, b0);
@@ -742,7 +789,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       // stage kt + 1 is the only load in flight (for the first stage of a tile, behind it at
       // most the previous epilogue's memory operations); once every wave has also finished
       // reading this slot, it takes stage kt + 2
-      if (kt == 0 && after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt == 0 && after && SW) asm volatile("s_waitcnt vmcnt(48)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (kt == 0 && after) asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
       frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
@@ -768,8 +816,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       start_tile();
       asm volatile("" ::: "memory");
     }
-    after = n3_full_tile<EPI, TO>(g, C, R, M, N, cm0, cn0) ? 1 : 0;
-    n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, cm0, cn0, wm, wn, lane);
+    if constexpr (SW) {
+      after = cm0 + N2_BM <= M && cn0 + N2_BN <= N ? 1 : 0;
+      n3_store_swiglu(g, acc, C, M, N, cm0, cn0, wm, wn, lane);
+    } else {
+      after = n3_full_tile<EPI, TO>(g, C, R, M, N, cm0, cn0) ? 1 : 0;
+      n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, cm0, cn0, wm, wn, lane);
+    }
     if (!next) break;
     asm volatile("" ::: "memory");
 #pragma unroll
@@ -978,6 +1031,8 @@ constexpr int NT3_WAVES = 8;
 HOL_NT3_INST(false)
 HOL_NT3_INST(true)
 #undef HOL_NT3_INST
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, true>(Gemm);
 
 // persistent grid of the ungrouped GEMM: one block per CU (a block fills a CU's LDS), in whole
 // XCD rounds of 8
@@ -1087,6 +1142,35 @@ static int launch_mfma_l(const Gemm& g, hipStream_t s) {
   if (g.c != DT_F32) return (int)hipErrorInvalidValue;
   if (g.epi == EPI_ACCUM) return launch_mfma_t<AK, BK_, EPI_ACCUM, float>(g, s);
   return launch_mfma_t<AK, BK_, EPI_RESID, float>(g, s);
+}
+
+int launch_gemm_swiglu(const Gemm& g0, void* a, int64_t ld_a, hipStream_t s) {
+  if (g0.M <= 0 || g0.N <= 0) return 0;
+  if (g0.N % 2 || g0.epi != EPI_STORE || g0.batch != 1 || !a) return (int)hipErrorInvalidValue;
+  Gemm g = g0;
+  g.C2 = a;
+  g.ldc2 = ld_a;
+  const int F = g.N / 2;
+  const DType tb = g.bt < 0 ? g.ab : (DType)g.bt;
+  const bool fused = g.ab == DT_BF16 && tb == DT_BF16 && g.c == DT_BF16 && !g.a_km && !g.b_kn && g.K > 0 &&
+                     g.K % N3_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+                     (((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0) && F % 32 == 0 && g.ldc % 4 == 0 &&
+                     ld_a % 4 == 0 && (((uintptr_t)g.C | (uintptr_t)a) % 8 == 0);
+  if (fused) {
+    const int tiles = n3_persistent_grid(((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN));
+    if (n3_buffer_ok(g))
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, true>), dim3(tiles), dim3(64 * NT3_WAVES), 0,
+                         s, g);
+    else
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, true>), dim3(tiles), dim3(64 * NT3_WAVES),
+                         0, s, g);
+    return (int)hipGetLastError();
+  }
+  // otherwise the plain product and the element-wise kernel, which needs the packed layouts
+  if (g.ldc != g.N || ld_a != F) return (int)hipErrorInvalidValue;
+  const int e = launch_gemm(g0, s);
+  if (e) return e;
+  return launch_swiglu_fwd(g.C, a, g.c, g.M, F, s);
 }
 
 int launch_gemm(const Gemm& g, hipStream_t s) {

@@ -39,8 +39,19 @@ struct Gemm {
   // M bounds the total rows; grp_max_rt bounds the total 256-row tiles (sizes the grid).
   const int32_t* grp = nullptr;
   int ngroups = 0, grp_max_rt = 0;
+  // second output of launch_gemm_swiglu (set by it)
+  void* C2 = nullptr;
+  int64_t ldc2 = 0;
 };
 int launch_gemm(const Gemm& g, hipStream_t s);
+// Gate/up product with the SwiGLU activation: g is the plain product gu [M, N] = x [gate; up]^T
+// (EPI_STORE, no batch; gate in columns [0, N/2), up in [N/2, N)); also writes a [M, N/2] (row
+// stride ld_a) = swiglu(gate, up) of the values as stored in gu. Bit for bit the result of
+// launch_gemm(g) then launch_swiglu_fwd. One kernel (SwiGLU in the epilogue) when the operands
+// are bf16 and NT with K % 64 == 0, N/2 % 32 == 0, 16-byte aligned A and B, ldc and ld_a
+// multiples of 4 and 8-byte aligned outputs; otherwise the two launches, which need ldc = N and
+// ld_a = N/2.
+int launch_gemm_swiglu(const Gemm& g, void* a, int64_t ld_a, hipStream_t s);
 // out[u][:] = sum over i in [seg[u], seg[u+1]) of dh[order[i]][:], in order of i from zero (fp32)
 int launch_embed_row_sums(const float* dh, const int32_t* order, const int32_t* seg, int nrows, int H, float* out,
                           hipStream_t s);
@@ -56,11 +67,12 @@ int launch_gemm_group_table(const int32_t* counts, int G, int32_t* tab, hipStrea
 int launch_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, DType yt,
                        float* rstd, int T, int H, hipStream_t s);
 // RMSNorm backward. dx_out = (accumulate ? dx_out : 0) + dx; dgamma_acc += sum_t dy*x*rstd.
-// `partial` is scratch of nb*H floats, nb = rmsnorm_bwd_blocks(T).
+// `partial` is scratch of nb*H floats, nb = rmsnorm_bwd_blocks(T). dx_bf16 (optional, 8-byte
+// aligned, [T,H]) also receives dx_out rounded to bf16 (what launch_cast_f32 would make of it).
 int rmsnorm_bwd_blocks(int T);
 int launch_rmsnorm_bwd(const float* dy, const float* x, const float* gamma, const float* rstd,
                        float* dx_out, bool accumulate, float* dgamma_acc, float* partial,
-                       int T, int H, hipStream_t s);
+                       int T, int H, hipStream_t s, void* dx_bf16 = nullptr);
 
 // RoPE (rotate-half) on `heads` heads of width d at row stride ld (elements); position = t % S.
 // inverse = rotation by the negative angle (the backward).

@@ -75,10 +75,7 @@ typedef struct {
   int32_t ckpt_every_k;       /* keep h_0, h_K, h_2K, ... in HBM (MegaTrain: checkpoint every K) */
   hol_dtype compute_dtype;    /* HOL_F32 or HOL_BF16 (bf16 operands, fp32 accumulation) */
   float lr, beta1, beta2, adam_eps, weight_decay; /* weight_decay must be 0 */
-  int32_t device;             /* HIP device ordinal. (There is no pinned-memory budget: hol_create
-                               * pins the whole low-precision image, and the gradient block, so every
-                               * weight and gradient copy is one DMA from or to its final place;
-                               * a host that cannot pin them gets HOL_ENOMEM_HOST from hol_create.) */
+  int32_t device;             /* HIP device ordinal */
   int32_t max_tokens;         /* largest batch*seq passed to forward_backward (sizes the HBM plan) */
   int32_t max_seq;            /* longest sequence (sizes the RoPE table) */
   int32_t weight_slots;       /* HBM slots of the weight ring, 2..8; 0: min(8, max(4, K + 2)) for
@@ -92,6 +89,19 @@ typedef struct {
   int32_t async_optimizer;    /* 1: also allocate a second pinned low-precision image, which
                                * hol_forward_backward_async needs; 0: none (that call returns
                                * HOL_EINVAL). */
+  uint64_t pinned_budget_bytes; /* Host memory the low-precision image may pin (MegaTrain summary
+                               * page, 技术新颖性: pinned segments reused across layers instead of
+                               * pinning the whole model). 0, or at least the image size (twice it
+                               * with async_optimizer): the whole image is pinned and every weight
+                               * copy is one DMA from its final place. Smaller: the image stays in
+                               * pageable memory and every weight copy is staged by the host through
+                               * a ring of R = min(8, budget / S) pinned segments of S bytes (S =
+                               * one layer's block rounded up to 4 KiB; the LM-head block goes in
+                               * pieces of S), a segment being reused once the DMA that read it is
+                               * done; budget < 2 S is HOL_EINVAL, and so is the ring together with
+                               * async_optimizer. Results do not depend on it. The fp32 gradient
+                               * block and the small staging buffers are always pinned; a host that
+                               * cannot pin what is asked gets HOL_ENOMEM_HOST from hol_create. */
 } hol_config;
 
 /* One forward_backward input. tokens: int32 [batch*seq] (vocab > 0); labels: int32
@@ -107,7 +117,8 @@ typedef struct {
 } hol_batch;
 
 /* Creates a model: plans and allocates all host state (fp32 masters, Adam m/v, pinned fp32
- * gradients, pinned layer-contiguous low-precision image with 4 KiB-aligned sub-tensors) and all
+ * gradients, layer-contiguous low-precision image with 4 KiB-aligned sub-tensors, pinned or
+ * behind the pinned ring of pinned_budget_bytes) and all
  * device memory (the ring of weight slots, head buffer, checkpoint store, block activation
  * store, gradient buffers). Weights start at zero; load them with hol_set_tensor. */
 hol_status hol_create(const hol_config* cfg, hol_model** out);

@@ -30,6 +30,19 @@ hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t l
                        const float* R, int64_t ldr, hol_dtype ab, hol_dtype c, int32_t epi,
                        float alpha, void* stream);
 
+/* Gate/up projection with the SwiGLU activation (MegaTrain summary page, 核心方法: the MLP block
+ * of the layer template, here with the activation fused into the product's epilogue):
+ * gu [M, N] = A B^T with A [M, K] (row stride lda) and B = [W_gate; W_up] [N, K] (ldb), so gate
+ * in columns [0, N/2) and up in [N/2, N) of gu (row stride ldgu), and a [M, N/2] (row stride ld_a)
+ * = silu(gate) * up of the values as stored in gu. Every array is of dtype t. The result is bit
+ * for bit that of hol_op_gemm (EPI_STORE, alpha 1) followed by hol_op_swiglu_fwd. One kernel when
+ * t is bf16, K % 64 == 0, (N/2) % 32 == 0, lda and ldb multiples of 8 with 16-byte aligned A, B,
+ * ldgu and ld_a multiples of 4 with 8-byte aligned gu, a; otherwise the two kernels, which need
+ * ldgu == N and ld_a == N/2 (else HOL_EINVAL). Odd N: HOL_EINVAL. */
+hol_status hol_op_gemm_swiglu(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, void* gu, int64_t ldgu, void* a, int64_t ld_a, hol_dtype t,
+                              void* stream);
+
 /* RMSNorm: y = x * rstd * gamma, rstd = 1/sqrt(mean(x^2) + eps); x fp32 [T,H], y [T,H] of
  * dtype yt, rstd fp32 [T]. H % 4 == 0. */
 hol_status hol_op_rmsnorm_fwd(const float* x, const float* gamma, float eps, void* y, hol_dtype yt,

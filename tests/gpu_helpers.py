@@ -8,7 +8,7 @@ import workloads as W
 from oracle import decoder as D
 
 
-def lib_model(w: W.Workload, params, k=None, slots=0, gbufs=0, async_opt=0) -> hol.Model:
+def lib_model(w: W.Workload, params, k=None, slots=0, gbufs=0, async_opt=0, pinned_budget=0) -> hol.Model:
     s = w.shape
     cfg = hol.make_config(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab,
                           n_experts=s.n_experts, top_k=s.top_k, expert_ffn=s.expert_ffn,
@@ -17,7 +17,7 @@ def lib_model(w: W.Workload, params, k=None, slots=0, gbufs=0, async_opt=0) -> h
                           compute_dtype=hol.BF16 if w.compute == "bf16" else hol.F32,
                           max_tokens=w.batch * w.seq, max_seq=w.seq, lr=w.lr, beta1=w.beta1,
                           beta2=w.beta2, adam_eps=w.adam_eps, weight_slots=slots, grad_buffers=gbufs,
-                          async_optimizer=async_opt)
+                          async_optimizer=async_opt, pinned_budget_bytes=pinned_budget)
     m = hol.Model(cfg)
     m.set_params(params)
     return m

@@ -209,6 +209,63 @@ def test_results_independent_of_weight_slots_and_grad_buffers_bitwise(wname):
                 assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
 
 
+@pytest.mark.parametrize("wname", ["tiny", "bf16_small", "bf16_big_head"])
+def test_pinned_ring_gives_identical_results_bitwise(wname):
+    """A pinned budget below the image size keeps the image pageable and stages every weight copy
+    through a ring of pinned segments of one layer block each (the LM head in pieces): two fused
+    steps and a plain forward_backward + step give the same losses, weights and Adam moments bit
+    for bit as the fully pinned image, and every streamed weight byte went through the ring."""
+    # (bf16_big_head: a vocabulary of 8000 makes the LM-head block larger than a layer block, so
+    # the head goes through the ring in pieces)
+    w = {"tiny": TINY, "bf16_small": BF16_SMALL, "bf16_big_head": BF16_SMALL.with_shape(vocab=8000)}[wname]
+    params = W.make_params(w, threads=8)
+    batch = W.make_batch(w)
+
+    def run(budget):
+        with lib_model(w, params, pinned_budget=budget) as m:
+            losses, stats = [], []
+            for _ in range(2):
+                losses.append(m.forward_backward(w.n_micro, tokens=batch["tokens"], and_step=True))
+                stats.append(m.stats())
+            losses.append(lib_fb(m, w, batch))
+            stats.append(m.stats())
+            m.step()
+            return losses, _state(m), stats
+
+    ref_losses, ref_state, st0 = run(0)
+    assert all(st["ring_segments"] == 0 and st["staged_bytes"] == 0 for st in st0)
+    seg = -(-st0[0]["layer_image_bytes"] // 4096) * 4096
+    print(wname, "layer block", st0[0]["layer_image_bytes"], "head block", st0[0]["head_image_bytes"], "segment", seg)
+    if wname == "bf16_big_head":
+        assert st0[0]["head_image_bytes"] > 2 * seg
+    for nseg, budget in ((2, 2 * seg), (3, 3 * seg + 4095)):
+        losses, state, stats = run(budget)
+        assert all(st["ring_segments"] == nseg and st["ring_segment_bytes"] == seg for st in stats)
+        # every layer copy a call queues is staged (a fused call also stages the next call's head
+        # and first layers, which that call then does not copy again)
+        for st in stats:
+            assert st["staged_bytes"] >= st["n_weight_streams"] * st["layer_image_bytes"], st
+        assert stats[0]["staged_bytes"] > 0
+        assert losses == ref_losses
+        for n in state:
+            for x, y in zip(state[n], ref_state[n]):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), n
+
+
+def test_pinned_budget_rejections():
+    """A budget below two ring segments, or the ring together with the asynchronous optimiser's
+    second image, is HOL_EINVAL at create time."""
+    w = TINY
+    params = W.make_params(w, threads=8)
+    with lib_model(w, params) as m:
+        m.forward_backward(w.n_micro, tokens=W.make_batch(w)["tokens"])
+        seg = -(-m.stats()["layer_image_bytes"] // 4096) * 4096
+    for kw in (dict(pinned_budget=seg + 4096), dict(pinned_budget=2 * seg, async_opt=1)):
+        with pytest.raises(hol.HolError) as e:
+            lib_model(w, params, **kw)
+        assert e.value.status == hol.HOL_EINVAL, kw
+
+
 @pytest.mark.parametrize("wname", ["tiny", "bf16_small"])
 def test_plain_step_after_fused_step_sees_zero_gradients(wname):
     """After a fused step the gradient blocks read as zero: a following plain step() is Adam on

@@ -129,6 +129,59 @@ def test_gemm_rejects_misaligned_bf16():
     assert st == hol.HOL_EINVAL
 
 
+# ------------------------------------------------------------------ gate/up product with SwiGLU
+# hol_op_gemm_swiglu is bit for bit hol_op_gemm (bf16 or fp32 store) followed by hol_op_swiglu_fwd;
+# those two are held to the oracle above and below, and the fused result to the oracle here too.
+@pytest.mark.parametrize("M,F,K,pad,dt", [
+    (300, 96, 128, 0, hol.BF16),     # one partial 256-column tile, ragged rows: fused kernel
+    (530, 160, 192, 8, hol.BF16),    # padded row strides of gu and a: fused kernel
+    (4352, 2176, 192, 0, hol.BF16),  # 17 x 17 = 289 tiles over 256 blocks: the persistent path
+    (260, 100, 128, 0, hol.BF16),    # F % 32 != 0: the product and the element-wise kernel
+    (300, 96, 72, 0, hol.BF16),      # K % 64 != 0: likewise
+    (130, 48, 64, 0, hol.F32),       # fp32: likewise
+])
+def test_gemm_swiglu_matches_gemm_then_swiglu(M, F, K, pad, dt):
+    N = 2 * F
+    r = np.random.default_rng(M + F + K)
+    tdt = torch.bfloat16 if dt == hol.BF16 else torch.float32
+    x = dev(r.standard_normal((M, K)) * 0.5, tdt)
+    w = dev(r.standard_normal((N, K)) / math.sqrt(K), tdt)
+    ldgu, lda = N + pad, F + pad // 2
+    gu = torch.full((M, ldgu), 3.0, dtype=tdt, device=DEV)
+    act = torch.full((M, lda), 3.0, dtype=tdt, device=DEV)
+    hol.check(hol.lib.hol_op_gemm_swiglu(M, N, K, x.data_ptr(), K, w.data_ptr(), K, gu.data_ptr(), ldgu,
+                                         act.data_ptr(), lda, dt, None))
+    gu_ref = torch.zeros((M, N), dtype=tdt, device=DEV)
+    a_ref = torch.zeros((M, F), dtype=tdt, device=DEV)
+    hol.check(hol.lib.hol_op_gemm(M, N, K, x.data_ptr(), K, 0, w.data_ptr(), K, 0, gu_ref.data_ptr(), N, None, 0,
+                                  dt, dt, 0, 1.0, None))
+    hol.check(hol.lib.hol_op_swiglu_fwd(gu_ref.data_ptr(), a_ref.data_ptr(), dt, M, F, None))
+    sync()
+    assert torch.equal(gu[:, :N], gu_ref) and torch.equal(act[:, :F], a_ref)
+    if pad:  # the padding columns are not written
+        assert bool((gu[:, N:] == 3.0).all()) and bool((act[:, F:] == 3.0).all())
+    # and the oracle: x W^T on the (rounded) inputs in fp64, then SwiGLU of the stored gate / up
+    rows = np.arange(0, M, max(1, M // 64))
+    ref = host(x)[rows] @ host(w).T
+    got_gu = host(gu[:, :N])[rows]
+    tol = 2 ** -8 if dt == hol.BF16 else 1e-5
+    assert np.max(np.abs(got_gu - ref) / (np.abs(ref) + 1)) < tol
+    np.testing.assert_allclose(host(act[:, :F])[rows], D.swiglu(got_gu[:, :F], got_gu[:, F:]), rtol=tol, atol=tol)
+
+
+def test_gemm_swiglu_rejects_odd_n_and_unpacked_fallback():
+    x = torch.zeros(64, 64, dtype=torch.bfloat16, device=DEV)
+    gu = torch.zeros(64, 208, dtype=torch.bfloat16, device=DEV)
+    a = torch.zeros(64, 104, dtype=torch.bfloat16, device=DEV)
+    st = hol.lib.hol_op_gemm_swiglu(64, 199, 64, x.data_ptr(), 64, gu.data_ptr(), 64, gu.data_ptr(), 208,
+                                    a.data_ptr(), 104, hol.BF16, None)
+    assert st == hol.HOL_EINVAL
+    # F = 100 takes the two-kernel path, which needs packed gu and a
+    st = hol.lib.hol_op_gemm_swiglu(64, 200, 64, x.data_ptr(), 64, gu.data_ptr(), 64, gu.data_ptr(), 208,
+                                    a.data_ptr(), 104, hol.BF16, None)
+    assert st == hol.HOL_EINVAL
+
+
 # ------------------------------------------------------------------ transpose (pure data movement: bit-exact)
 @pytest.mark.parametrize("R,C,ldi,ldo", [(256, 384, 384, 256), (300, 136, 136, 304), (1000, 2056, 2064, 1008),
                                          (8, 8, 8, 8), (129, 127, 128, 136)])
