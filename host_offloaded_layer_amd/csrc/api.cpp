@@ -282,6 +282,26 @@ hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t l
   return launched(launch_gemm(g, (hipStream_t)stream), "hol_op_gemm");
 }
 
+int64_t hol_op_gemm_workspace_floats(void) { return GEMM_SPLIT_WS_FLOATS; }
+
+hol_status hol_op_gemm_ws(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_km, const void* B,
+                          int64_t ldb, int32_t b_kn, void* C, int64_t ldc, const float* R, int64_t ldr, hol_dtype ab,
+                          hol_dtype c, int32_t epi, float alpha, float* workspace, int64_t workspace_floats,
+                          void* stream) {
+  if (epi < 0 || epi > 2) return einval("hol_op_gemm_ws", "bad epilogue");
+  if (workspace_floats < 0 || (workspace_floats > 0 && !workspace)) return einval("hol_op_gemm_ws", "bad workspace");
+  Gemm g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.a_km = a_km != 0;
+  g.B = B; g.ldb = ldb; g.b_kn = b_kn != 0;
+  g.C = C; g.ldc = ldc; g.R = R; g.ldr = ldr;
+  g.ab = ab == HOL_BF16 ? DT_BF16 : DT_F32;
+  g.c = c == HOL_BF16 ? DT_BF16 : DT_F32;
+  g.epi = epi; g.alpha = alpha;
+  g.ws = workspace; g.ws_floats = workspace_floats;
+  return launched(launch_gemm(g, (hipStream_t)stream), "hol_op_gemm_ws");
+}
+
 hol_status hol_op_gemm_swiglu(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                               void* gu, int64_t ldgu, void* a, int64_t ld_a, hol_dtype t, void* stream) {
   if (M < 0 || N < 0 || K < 0) return einval("hol_op_gemm_swiglu", "negative size");

@@ -392,6 +392,7 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   m->nslots = c.weight_slots ? c.weight_slots : std::min(8, std::max(4, c.ckpt_every_k + 2));
   m->ngbuf = c.grad_buffers ? c.grad_buffers : 4;
   for (int i = 0; i < m->nslots; ++i) m->slot[i] = (uint8_t*)D(m->layer_img_bytes);
+  if (m->dt == DT_BF16) m->gemm_ws = (float*)D(GEMM_SPLIT_WS_FLOATS * 4);
   if (V > 0) m->head_dev = (uint8_t*)D(m->head_img_bytes);
   for (int i = 0; i < m->ngbuf; ++i) m->gdev[i] = (float*)D(m->layer_flat_n * 4);
   if (m->embed_trainable) {
@@ -738,6 +739,18 @@ static int run_gemm(hol_model* m, const Gemm& g) {
                      [&] { return launch_gemm(g, m->sc); });
 }
 
+// A weight-gradient product dW = dY^T X (K = tokens) of the dense bf16 backward: given the split
+// workspace, a product whose tiles leave the last round of the grid part-empty splits those
+// tiles along K (deterministic). Only these: a split changes the rounding with the token count,
+// and every product over model dimensions must give each token's row the same bits whatever the
+// batch it is in.
+static int run_gemm_dw(hol_model* m, const Gemm& g0) {
+  Gemm g = g0;
+  g.ws = m->gemm_ws;
+  g.ws_floats = m->gemm_ws ? GEMM_SPLIT_WS_FLOATS : 0;
+  return run_gemm(m, g);
+}
+
 // the gate/up product with SwiGLU (launch_gemm_swiglu); a: [M, N/2] at row stride ld_a
 static int run_gemm_swiglu(hol_model* m, const Gemm& g, void* a, int64_t ld_a) {
   const double E = (g.ab == DT_BF16) ? 2 : 4, Ec = (g.c == DT_BF16) ? 2 : 4;
@@ -1063,7 +1076,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
     if (tw) {
       KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
       KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
-      KCHECK(run_gemm(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
+      KCHECK(run_gemm_dw(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
     }
     // (with weight gradients the SwiGLU backward also writes dgu^T for the dWgu product)
     const bool dgu_t = tw && F % 64 == 0;
@@ -1076,7 +1089,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
     if (tw) {
       if (!dgu_t) KCHECK(tr(m, m->dgu, 2 * F, m->yT, T, T, 2 * F));
       KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
-      KCHECK(run_gemm(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
+      KCHECK(run_gemm_dw(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
     }
     if (m->tail_mlp_armed) HCHECK(hipEventRecord(m->tail_mlp_ev, s));  // w_gate, w_up, w_down final
   }
@@ -1096,7 +1109,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   if (tw) {
     KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));
     KCHECK(tr(m, A.o, nqd, m->xT, T, T, nqd));
-    KCHECK(run_gemm(m, nt(H, nqd, T, m->yT, T, m->xT, T, G + m->g_wo, nqd, DT_F32)));
+    KCHECK(run_gemm_dw(m, nt(H, nqd, T, m->yT, T, m->xT, T, G + m->g_wo, nqd, DT_F32)));
   }
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
@@ -1121,7 +1134,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   if (tw) {
     KCHECK(tr(m, m->dqkv, QKV, m->yT, T, T, QKV));
     KCHECK(tr(m, A.n1, H, m->xT, T, T, H));
-    KCHECK(run_gemm(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
+    KCHECK(run_gemm_dw(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
   }
   KT(KC_RMSNORM, 0, (16.0 + E) * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true,
                                                              tw ? G + m->g_g1 : nullptr, m->partial, T, H, s, m->dhb));

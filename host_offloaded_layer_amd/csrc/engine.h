@@ -210,6 +210,7 @@ struct hol_model {
   void* xT = nullptr;     // transposed activation (largest: [F, T])
   void* woutT = nullptr;  // transposed LM head [H, V]
   float* qkvf = nullptr;  // fp32 q/k/v projection output before RoPE and the single bf16 rounding
+  float* gemm_ws = nullptr;  // GEMM split-tail workspace (GEMM_SPLIT_WS_FLOATS floats)
   std::vector<void*> dev_allocs;
   std::vector<void*> pinned_allocs;
   std::vector<hipEvent_t> tev;  // timing events

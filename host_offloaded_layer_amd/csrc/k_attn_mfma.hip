@@ -34,6 +34,14 @@ __device__ __forceinline__ void zero(f32x16& x) {
   for (int r = 0; r < 16; ++r) x[r] = 0.f;
 }
 
+// Online softmax of the forward: the reference m that the probabilities 2^(s - m) are taken
+// against is raised only when a tile's maximum exceeds it by more than RESCALE_SLACK (log2 units).
+// The probabilities then stay below 2^8, far inside fp32 and without effect on the relative
+// precision of their bf16 rounding, the final o / l and lse = m + log l are unchanged up to
+// rounding, and the rescale of the output accumulators (64 products a lane) runs in a few tiles
+// of a row instead of in most.
+constexpr float RESCALE_SLACK = 8.f;
+
 // B fragment of k-step ks' (0 or 1) inside a 32-row accumulator block
 __device__ __forceinline__ bf16x8 acc_frag(const f32x16& acc, int ksp) {
   bf16x8 b;
@@ -342,15 +350,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(Attn a) {
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    if (mn > m) {  // the running max moved: rescale (the whole wave skips this once maxima settle)
-      const float corr = ex2(m - mn);
+    if (mx > m + RESCALE_SLACK) {  // the reference moves (m = -inf before the first tile: corr = 0)
+      const float corr = ex2(m - mx);
       l *= corr;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= corr;
-      m = mn;
+      m = mx;
     }
     float ls = 0.f;
 #pragma unroll
@@ -1089,15 +1096,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = xhalf_max(mx);
-      const float mn = fmaxf(m, mx * sl2);
-      if (mn > m) {  // the running max moved: rescale (the whole wave skips this once maxima settle)
-        const float corr = ex2(m - mn);
+      const float tm = mx * sl2;
+      if (tm > m + RESCALE_SLACK) {  // the reference moves (m = -inf before the first tile: corr = 0)
+        const float corr = ex2(m - tm);
         l *= corr;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[i][r] *= corr;
-        m = mn;
+        m = tm;
       }
       // p = 2^(s sl2 - m); four partial row sums
       float ls4[4] = {0.f, 0.f, 0.f, 0.f};

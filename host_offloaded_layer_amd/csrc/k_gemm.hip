@@ -659,7 +659,23 @@ __device__ __forceinline__ void n3_store_swiglu(const Gemm& g, const f32x16 (&ac
   }
 }
 
-template <int EPI, typename TO, int NW, bool BUF, bool GRP, bool SW = false>
+// Tile origin of tile q in the grouped order: groups of 4 row tiles, column-major inside a group
+// (the 32 tiles an XCD runs at once share A and B panels in its L2).
+__device__ __forceinline__ void n3_origin(int q, int tiles_m, int tiles_n, int& m0, int& n0) {
+  const int GM = 4;
+  const int group = GM * tiles_n;
+  const int first_m = (q / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  m0 = (first_m + (q % group) % gsz) * N2_BM;
+  n0 = ((q % group) / gsz) * N2_BN;
+}
+
+// SPL (split tail, fp32 store only): an XCD's tiles that do not fill a last round of its blocks
+// are each cut along K into g.spl_f equal parts. A block's work items are then its whole tiles
+// (g.spl_full per XCD, the full rounds) followed by at most one part, whose raw sums go to the
+// workspace (one 256 x 256 fp32 slot per part: slot x r f + q f + part for the XCD's q-th split
+// tile); gemm_split_reduce_k adds the parts in order and applies alpha.
+template <int EPI, typename TO, int NW, bool BUF, bool GRP, bool SW = false, bool SPL = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
   static_assert(NW == 8, "the epilogue count below assumes 8 waves");
@@ -678,13 +694,27 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   // 32 tiles in flight on one XCD share A and B panels in its L2
   int p = 0, p_end = 1, p_step = 1;
   const int tiles_m = (M + N2_BM - 1) / N2_BM;
-  auto origin = [&](int q) {
-    const int GM = 4;
-    const int group = GM * tiles_n;
-    const int first_m = (q / group) * GM;
-    const int gsz = min(tiles_m - first_m, GM);
-    m0 = (first_m + (q % group) % gsz) * N2_BM;
-    n0 = ((q % group) / gsz) * N2_BN;
+  auto origin = [&](int q) { n3_origin(q, tiles_m, tiles_n, m0, n0); };
+  // K range of the current work item, and its workspace slot (-1: a whole tile, stored normally)
+  int kbeg = 0, kend = K, slot = -1;
+  int xstart = 0;  // SPL: first tile of this XCD's range
+  auto item = [&](int i) {
+    if constexpr (SPL) {
+      if (i < g.spl_full) {
+        origin(xstart + i);
+        kbeg = 0;
+        kend = K;
+        slot = -1;
+      } else {
+        const int j = i - g.spl_full, kp = K / g.spl_f;
+        origin(xstart + g.spl_full + j / g.spl_f);
+        kbeg = (j % g.spl_f) * kp;
+        kend = kbeg + kp;
+        slot = (blockIdx.x & 7) * (p_end - g.spl_full) + j;
+      }
+    } else {
+      origin(i);
+    }
   };
   if constexpr (GRP) {
     const int G = g.ngroups;
@@ -714,11 +744,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   } else {
     const int ntiles = tiles_m * tiles_n;
     const int x = blockIdx.x & 7;
-    p = (int)((int64_t)ntiles * x / 8) + (blockIdx.x >> 3);
-    p_end = (int)((int64_t)ntiles * (x + 1) / 8);
     p_step = gridDim.x >> 3;
+    if constexpr (SPL) {  // items, not tiles (ntiles % 8 == 0: every XCD has ntiles / 8 tiles)
+      xstart = (ntiles >> 3) * x;
+      p = blockIdx.x >> 3;
+      p_end = g.spl_full + ((ntiles >> 3) - g.spl_full) * g.spl_f;
+    } else {
+      p = (int)((int64_t)ntiles * x / 8) + (blockIdx.x >> 3);
+      p_end = (int)((int64_t)ntiles * (x + 1) / 8);
+    }
     if (p >= p_end) return;
-    origin(p);
+    item(p);
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w / (NW / 2), wn = w % (NW / 2);
@@ -731,15 +767,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   static_assert(!SW || (EPI == EPI_STORE && sizeof(TO) == 2 && !GRP && WJ == 2), "SwiGLU: bf16 store, one group");
-  const int nk = K / N3_BK;
+  static_assert(!SPL || (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP && !SW), "split tail: fp32 store, one group");
+  int nk = (kend - kbeg) / N3_BK;
   N3Buf<NW, SW> nb;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)M * g.lda * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)N * g.ldb * 2), 0x00020000);
-  auto issue = [&](bf16* stage, int k0) {
-    if constexpr (BUF) nb.issue(stage, ra, rb, k0);
-    else n3_issue<NW, SW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, k0);
+  auto issue = [&](bf16* stage, int k0) {  // k0 relative to the item's first k
+    if constexpr (BUF) nb.issue(stage, ra, rb, kbeg + k0);
+    else n3_issue<NW, SW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, kbeg + k0);
   };
   auto start_tile = [&]() {
     if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N);
@@ -807,18 +844,26 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       mma(a1, b1);
     }
     // next tile: its first two stages go up before this tile's results go out
-    const int cm0 = m0, cn0 = n0;
+    const int cm0 = m0, cn0 = n0, cslot = slot;
     p += p_step;
     const bool next = !GRP && p < p_end;
     if (next) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave done with both slots
-      origin(p);
+      item(p);
+      nk = (kend - kbeg) / N3_BK;
       start_tile();
       asm volatile("" ::: "memory");
     }
     if constexpr (SW) {
       after = cm0 + N2_BM <= M && cn0 + N2_BN <= N ? 1 : 0;
       n3_store_swiglu(g, acc, C, M, N, cm0, cn0, wm, wn, lane);
+    } else if (SPL && cslot >= 0) {  // a part of a split tile: raw sums, whole 256 x 256 slot
+      Gemm gw = g;
+      gw.ldc = N2_BN;
+      gw.alpha = 1.f;
+      after = 1;  // 32 vector stores a wave, as a whole fp32 tile
+      n3_store<EPI_STORE, TO, WJ>(gw, acc, (TO*)(g.ws + (int64_t)cslot * (N2_BM * N2_BN)), nullptr, N2_BM, N2_BN, 0, 0,
+                                  wm, wn, lane);
     } else {
       after = n3_full_tile<EPI, TO>(g, C, R, M, N, cm0, cn0) ? 1 : 0;
       n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, cm0, cn0, wm, wn, lane);
@@ -1033,6 +1078,40 @@ HOL_NT3_INST(true)
 #undef HOL_NT3_INST
 template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, true>(Gemm);
 template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, false, true>(Gemm);
+
+// Sum of the parts of the split tiles (gemm_nt3 with SPL): one block per split tile; thread t
+// owns columns 4 (t mod 64) .. + 3 of rows t / 64 + 4 i. Parts are added in order 0, 1, ... so the
+// result does not depend on which part finished first.
+__global__ __launch_bounds__(256) void gemm_split_reduce_k(Gemm g) {
+  const int tiles_m = (g.M + N2_BM - 1) / N2_BM, tiles_n = (g.N + N2_BN - 1) / N2_BN;
+  const int n_x = tiles_m * tiles_n / 8, r = n_x - g.spl_full;  // split tiles per XCD range
+  const int x = blockIdx.x / r, q = blockIdx.x % r;
+  int m0, n0;
+  n3_origin(n_x * x + g.spl_full + q, tiles_m, tiles_n, m0, n0);
+  const float* part = g.ws + (int64_t)(x * r + q) * g.spl_f * (N2_BM * N2_BN);
+  float* C = (float*)g.C;
+  const int c = 4 * (threadIdx.x & 63);
+  const int col = n0 + c;
+  const bool vec = g.ldc % 4 == 0 && ((uintptr_t)C & 15) == 0 && col + 4 <= g.N;
+  for (int rr = threadIdx.x >> 6; rr < N2_BM; rr += 4) {
+    const int row = m0 + rr;
+    if (row >= g.M || col >= g.N) continue;
+    float4 v = *(const float4*)(part + rr * N2_BN + c);
+    for (int f = 1; f < g.spl_f; ++f) {
+      const float4 u = *(const float4*)(part + (int64_t)f * (N2_BM * N2_BN) + rr * N2_BN + c);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    v.x *= g.alpha; v.y *= g.alpha; v.z *= g.alpha; v.w *= g.alpha;
+    float* crow = C + (int64_t)row * g.ldc;
+    if (vec) {
+      *(float4*)(crow + col) = v;
+    } else {
+      const float e[4] = {v.x, v.y, v.z, v.w};
+      for (int k = 0; k < 4 && col + k < g.N; ++k) crow[col + k] = e[k];
+    }
+  }
+}
 
 // persistent grid of the ungrouped GEMM: one block per CU (a block fills a CU's LDS), in whole
 // XCD rounds of 8
@@ -1048,12 +1127,41 @@ static int n3_persistent_grid(int ntiles) {
   return (g + 7) / 8 * 8;
 }
 
+// Split-tail plan for an fp32-store product: with every XCD range holding n tiles for its c
+// blocks, n = R c + r with R >= 1 and 0 < r <= c / 2, the r tail tiles are cut into f = 2 or 4 K
+// parts (r f <= c, K % 64 f == 0), so the last round runs r f part tiles instead of r whole
+// ones. Returns false when the plan does not apply.
+static bool n3_split_plan(const Gemm& g, int grid, Gemm& out) {
+  if (!g.ws || g.batch != 1 || g.epi != EPI_STORE || g.c != DT_F32 || !n3_buffer_ok(g)) return false;
+  const int ntiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
+  if (ntiles % 8 || grid % 8) return false;
+  const int c = grid / 8, n = ntiles / 8, R = n / c, r = n % c;
+  if (R < 1 || r == 0 || 2 * r > c) return false;
+  int f = 4 * r <= c ? 4 : 2;
+  while (f > 1 && g.K % (N3_BK * f)) f /= 2;
+  if (f < 2 || (int64_t)8 * r * f * N2_BM * N2_BN > g.ws_floats) return false;
+  out = g;
+  out.spl_full = R * c;
+  out.spl_f = f;
+  return true;
+}
+
 template <int EPI, typename TO, bool GRP>
 static int launch_nt3_t(const Gemm& g, hipStream_t s) {
   const int tn = (g.N + N2_BN - 1) / N2_BN;
   // grouped: an upper bound of the tile count rounded up to the 8 XCD ranges
   const int tiles = GRP ? (int)((((int64_t)g.grp_max_rt * tn) + 7) / 8 * 8) : n3_persistent_grid(((g.M + N2_BM - 1) / N2_BM) * tn);
   if (tiles <= 0) return 0;
+  if constexpr (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP) {
+    Gemm gs;
+    if (n3_split_plan(g, tiles, gs)) {
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, false, true>), dim3(tiles), dim3(64 * NT3_WAVES),
+                         0, s, gs);
+      const int nsplit = (((g.M + N2_BM - 1) / N2_BM) * tn / 8 - gs.spl_full) * 8;
+      hipLaunchKernelGGL(gemm_split_reduce_k, dim3(nsplit), dim3(256), 0, s, gs);
+      return (int)hipGetLastError();
+    }
+  }
   if (n3_buffer_ok(g))
     hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true, GRP>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
   else

@@ -42,7 +42,15 @@ struct Gemm {
   // second output of launch_gemm_swiglu (set by it)
   void* C2 = nullptr;
   int64_t ldc2 = 0;
+  // optional fp32 workspace of ws_floats floats (GEMM_SPLIT_WS_FLOATS suffice): with it an fp32
+  // store whose tiles leave the last round of the persistent grid part-empty splits those tiles
+  // along K and adds the parts in a fixed order (results deterministic, not bitwise those of the
+  // unsplit product). spl_full / spl_f are set by the launcher.
+  float* ws = nullptr;
+  int64_t ws_floats = 0;
+  int spl_full = 0, spl_f = 1;
 };
+constexpr int64_t GEMM_SPLIT_WS_FLOATS = (int64_t)256 * 256 * 256;  // 256 tile parts (64 MiB)
 int launch_gemm(const Gemm& g, hipStream_t s);
 // Gate/up product with the SwiGLU activation: g is the plain product gu [M, N] = x [gate; up]^T
 // (EPI_STORE, no batch; gate in columns [0, N/2), up in [N/2, N)); also writes a [M, N/2] (row

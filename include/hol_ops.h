@@ -30,6 +30,22 @@ hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t l
                        const float* R, int64_t ldr, hol_dtype ab, hol_dtype c, int32_t epi,
                        float alpha, void* stream);
 
+/* hol_op_gemm with an fp32 device workspace of workspace_floats floats (at most
+ * hol_op_gemm_workspace_floats() are used; 0 / NULL: exactly hol_op_gemm). With it, a bf16 NT
+ * product with an fp32 store (EPI_STORE) whose 256 x 256 tiles leave the last round of the
+ * persistent grid at most half full (every XCD with R >= 1 full rounds and r <= half a round of
+ * tiles left) cuts those r tiles along K into 2 or 4 parts, runs the parts in the last round and
+ * adds them in part order in a second kernel: the weight-gradient products dW = dY^T X of the
+ * q/k/v and down projections at the LLaMA-8B shape (MegaTrain summary page, 核心方法: the
+ * per-layer backward). The result is deterministic and within fp32 accumulation error of the
+ * unsplit product, not bit for bit equal to it. The caller owns the workspace; calls that share
+ * one must not overlap. */
+int64_t hol_op_gemm_workspace_floats(void);
+hol_status hol_op_gemm_ws(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_km,
+                          const void* B, int64_t ldb, int32_t b_kn, void* C, int64_t ldc,
+                          const float* R, int64_t ldr, hol_dtype ab, hol_dtype c, int32_t epi,
+                          float alpha, float* workspace, int64_t workspace_floats, void* stream);
+
 /* Gate/up projection with the SwiGLU activation (MegaTrain summary page, 核心方法: the MLP block
  * of the layer template, here with the activation fused into the product's epilogue):
  * gu [M, N] = A B^T with A [M, K] (row stride lda) and B = [W_gate; W_up] [N, K] (ldb), so gate

@@ -121,6 +121,53 @@ def test_gemm_f32_tiled(a_km, b_kn, epi):
     assert np.max(np.abs(got - ref) / (np.abs(ref) + 8)) < 1e-6
 
 
+# Split tail (hol_op_gemm_ws): 384 tiles = one full round of the 256-block persistent grid plus
+# 16 tiles an XCD left, cut in 2 K parts; 320 tiles leave 8 an XCD, cut in 4. Ragged edges, alpha.
+@pytest.mark.parametrize("M,N,K", [(6100, 4000, 256), (5000, 4000, 256)])
+def test_gemm_split_tail(M, N, K):
+    r = np.random.default_rng(M + N)
+    A = r.standard_normal((M, K)).astype(np.float32)
+    B = r.standard_normal((N, K)).astype(np.float32)
+    a, b = dev(A, torch.bfloat16), dev(B, torch.bfloat16)
+    wsn = hol.lib.hol_op_gemm_workspace_floats()
+    ws = torch.full((wsn,), float("nan"), device=DEV)  # every slot read is written first
+    outs = []
+    for _ in range(2):
+        c = torch.full((M, N), 7.0, device=DEV)
+        hol.check(hol.lib.hol_op_gemm_ws(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c.data_ptr(), N, None, 0,
+                                         hol.BF16, hol.F32, 0, 0.5, ws.data_ptr(), wsn, None))
+        outs.append(c)
+    plain = torch.zeros((M, N), device=DEV)
+    hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, plain.data_ptr(), N, None, 0,
+                                  hol.BF16, hol.F32, 0, 0.5, None))
+    sync()
+    assert torch.equal(outs[0], outs[1])  # deterministic
+    got = host(outs[0])
+    assert np.isfinite(got).all()
+    rows = np.arange(0, M, 7)
+    ref = 0.5 * (bf(A)[rows] @ bf(B).T)
+    assert np.max(np.abs(got[rows] - ref) / (np.abs(ref) + math.sqrt(K))) < 1e-5
+    assert np.max(np.abs(got - host(plain)) / (np.abs(host(plain)) + math.sqrt(K))) < 1e-5
+
+
+def test_gemm_ws_leaves_other_epilogues_unsplit():
+    """With a workspace, products that are not an fp32 store run exactly as without one."""
+    M, N, K = 6100, 4000, 256
+    r = np.random.default_rng(5)
+    a = dev(r.standard_normal((M, K)), torch.bfloat16)
+    b = dev(r.standard_normal((N, K)), torch.bfloat16)
+    c0 = dev(r.standard_normal((M, N)))
+    wsn = hol.lib.hol_op_gemm_workspace_floats()
+    ws = torch.zeros((wsn,), device=DEV)
+    c1, c2 = c0.clone(), c0.clone()
+    hol.check(hol.lib.hol_op_gemm_ws(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c1.data_ptr(), N, None, 0,
+                                     hol.BF16, hol.F32, 1, 1.0, ws.data_ptr(), wsn, None))
+    hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c2.data_ptr(), N, None, 0,
+                                  hol.BF16, hol.F32, 1, 1.0, None))
+    sync()
+    assert torch.equal(c1, c2)
+
+
 def test_gemm_rejects_misaligned_bf16():
     a = torch.zeros(64, 12, dtype=torch.bfloat16, device=DEV)
     c = torch.zeros(64, 64, device=DEV)
