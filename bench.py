@@ -155,10 +155,11 @@ def gemm_table(w: W.Workload, st_list, steps):
 
 
 def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
-    """The workload's decoder GEMMs one shape at a time, with the epilogue and output type the
-    step uses (fp32 out; bf16 out for gate/up forward and the down-projection data gradient;
-    residual epilogue for the o and down projections), in the order listed, `reps` launches each
-    after one warm-up launch."""
+    """The workload's decoder GEMMs one shape at a time, as the step launches them: fp32 out;
+    bf16 out for the down-projection and o data gradients; residual epilogue for the o and down
+    projections; the gate/up forward with its SwiGLU epilogue (hol_op_gemm_swiglu); the weight
+    gradients with the split-tail workspace (hol_op_gemm_ws). In the order listed, `reps` launches
+    each after one warm-up launch."""
     s = w.shape
     T, H, d = w.tokens, s.hidden, s.head_dim
     nqd, QKV, F = s.n_q_heads * d, (s.n_q_heads + 2 * s.n_kv_heads) * d, s.ffn
@@ -170,17 +171,26 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
               ("a10 down dW", H, F, T, 0, False), ("a9 gate/up dW", 2 * F, H, T, 0, False),
               ("a7 o dW", H, nqd, T, 0, False), ("a4 qkv dW", QKV, H, T, 0, False)]
     stream = torch.cuda.current_stream()
+    wsn = hol.lib.hol_op_gemm_workspace_floats()
+    ws = torch.empty((wsn,), device="cuda")
     rows = []
     for name, M, N, K, epi, bf in shapes:
         a = torch.randn((M, K), device="cuda").to(torch.bfloat16)
         b = torch.randn((N, K), device="cuda").to(torch.bfloat16)
         c = torch.empty((M, N), device="cuda", dtype=torch.bfloat16 if bf else torch.float32)
         r = torch.randn((M, N), device="cuda") if epi == 2 else None
+        act = torch.empty((M, N // 2), device="cuda", dtype=torch.bfloat16) if name.startswith("a9 gate/up fwd") else None
+        dw = name.endswith("dW")
 
         def launch():
-            hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c.data_ptr(), N,
-                                          r.data_ptr() if r is not None else None, N, hol.BF16,
-                                          hol.BF16 if bf else hol.F32, epi, 1.0, stream.cuda_stream))
+            if act is not None:
+                hol.check(hol.lib.hol_op_gemm_swiglu(M, N, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), N,
+                                                     act.data_ptr(), N // 2, hol.BF16, stream.cuda_stream))
+                return
+            hol.check(hol.lib.hol_op_gemm_ws(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c.data_ptr(), N,
+                                             r.data_ptr() if r is not None else None, N, hol.BF16,
+                                             hol.BF16 if bf else hol.F32, epi, 1.0,
+                                             ws.data_ptr() if dw else None, wsn if dw else 0, stream.cuda_stream))
 
         launch()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
@@ -194,7 +204,7 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
         rows.append({"gemm": name, "M": M, "N": N, "K": K, "avg_us": round(us, 1), "tflops": round(tf, 1),
                      "frac": round(tf / BF16_PEAK_TFLOPS, 4)})
         log(f"[bench] {name:16s} {M:6d} x {N:6d} x {K:6d}: {us:8.1f} us {tf:7.1f} TFLOP/s")
-        del a, b, c, r
+        del a, b, c, r, act
     return {"workload": w.name, "gemm_shapes_alone": rows, "launches_per_shape": reps}
 
 
