@@ -399,6 +399,22 @@ hol_status hol_op_attention_bwd(int32_t n_seq, int32_t S, int32_t nq, int32_t nk
   return launched(launch_attn_bwd(a, (hipStream_t)stream), "hol_op_attention_bwd");
 }
 
+hol_status hol_op_attention_bwd_rope(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d, hol_dtype t,
+                                     const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                                     int64_t ldv, const void* o, int64_t ldo, const float* lse, const void* dO,
+                                     int64_t lddo, void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv,
+                                     int64_t lddv, float* delta, const float* cos_t, const float* sin_t, void* stream) {
+  if (!cos_t || !sin_t) return einval("hol_op_attention_bwd_rope", "null RoPE table");
+  if (d % 2) return einval("hol_op_attention_bwd_rope", "odd head width");
+  Attn a = attn_args(n_seq, S, nq, nkv, d, t, q, ldq, k, ldk, v, ldv);
+  a.o = (void*)o; a.ldo = ldo; a.lse = (float*)lse;
+  a.dO = dO; a.lddo = lddo;
+  a.dq = dq; a.lddq = lddq; a.dk = dk; a.lddk = lddk; a.dv = dv; a.lddv = lddv;
+  a.delta = delta;
+  a.rope_cos = cos_t; a.rope_sin = sin_t;
+  return launched(launch_attn_bwd(a, (hipStream_t)stream), "hol_op_attention_bwd_rope");
+}
+
 hol_status hol_op_attention_bwd_noalloc(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d, hol_dtype t,
                                         const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                                         int64_t ldv, const void* o, int64_t ldo, const float* lse, const void* dO,

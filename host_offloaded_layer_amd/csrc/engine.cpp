@@ -1120,9 +1120,9 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   at.dq = m->dqkv; at.dk = (uint8_t*)m->dqkv + (int64_t)nqd * E; at.dv = (uint8_t*)m->dqkv + (int64_t)(nqd + m->nkv * d) * E;
   at.lddq = at.lddk = at.lddv = QKV;
   at.delta = m->delta;
+  at.rope_cos = m->cos_dev;  // dq and dk leave with the RoPE backward applied
+  at.rope_sin = m->sin_dev;
   KT(KC_ATTN_BWD, 5.0 * d * m->nq * (double)S * (S + 1) * n_seq, (double)T * (2 * QKV + 3 * nqd) * E, launch_attn_bwd(at, s));
-  KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(m->dqkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, true, s));
-  KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)m->dqkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, true, s));
   // q/k/v projections: dn1 = dqkv Wqkv (+ LoRA), dWqkv = dqkv^T n1
   KCHECK(run_gemm(m, nt(T, H, QKV, m->dqkv, QKV, WqkvT, QKV, m->dn, H, DT_F32)));
   if (m->R > 0) {

@@ -309,10 +309,24 @@ int launch_attn_fwd(const Attn& a, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
+// The RoPE backward of dq and dk for the kernels that do not apply it in their epilogue.
+static int attn_rope_back(const Attn& a, hipStream_t s) {
+  if (!a.rope_cos) return 0;
+  const int T = a.n_seq * a.S;
+  int e = launch_rope(a.dq, a.t, a.lddq, T, a.nq, a.d, a.S, a.rope_cos, a.rope_sin, true, s);
+  if (e) return e;
+  return launch_rope(a.dk, a.t, a.lddk, T, a.nkv, a.d, a.S, a.rope_cos, a.rope_sin, true, s);
+}
+
 int launch_attn_bwd(const Attn& a, hipStream_t s) {
   if (a.n_seq <= 0 || a.S <= 0) return 0;
   if (a.d > 128 || a.nkv <= 0 || a.nq % a.nkv) return (int)hipErrorInvalidValue;
-  if (attn_mfma_bwd_supported(a)) return launch_attn_bwd_mfma(a, s);
+  if (a.rope_cos && a.d % 2) return (int)hipErrorInvalidValue;
+  if (attn_mfma_bwd_supported(a)) {
+    const int e = launch_attn_bwd_mfma(a, s);  // (head width 128: the RoPE backward is in its epilogues)
+    if (e || a.d == 128) return e;
+    return attn_rope_back(a, s);
+  }
   const size_t sm = tiled_smem(a.d);
   const int64_t rows = (int64_t)a.n_seq * a.S * a.nq;
   const int nt = (a.S + AT_B - 1) / AT_B;
@@ -329,7 +343,9 @@ int launch_attn_bwd(const Attn& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_dkdv_tiled<float>, dim3(nt, a.nkv, a.n_seq), dim3(256), sm, s, a);
     hipLaunchKernelGGL(attn_dq_tiled<float>, dim3(nt, a.nq, a.n_seq), dim3(256), sm, s, a);
   }
-  return (int)hipGetLastError();
+  const int e = (int)hipGetLastError();
+  if (e) return e;
+  return attn_rope_back(a, s);
 }
 
 

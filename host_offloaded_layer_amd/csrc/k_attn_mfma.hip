@@ -115,6 +115,28 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; ex2(-inf) = 0
 
+// The RoPE backward of one row of a head-width-128 gradient held as v[db][4 g + e] = column
+// 32 db + 8 g + 4 hh + e: pairs (j, j + 64) for j < 64 (blocks db and db + 2, same lane) are
+// rotated by minus the angle of position p (tables [S][64]), in fp32 before the single rounding.
+__device__ __forceinline__ void rope_back_row(float (&v)[4][16], const float* cs, const float* sn, int p, int hh) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = db * 32 + 8 * g + 4 * hh;
+      const float4 c4 = *(const float4*)(cs + (int64_t)p * 64 + j);
+      const float4 s4 = *(const float4*)(sn + (int64_t)p * 64 + j);
+      const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = v[db][4 * g + e], b = v[db + 2][4 * g + e], s_ = -sv[e];
+        v[db][4 * g + e] = a * c[e] - b * s_;
+        v[db + 2][4 * g + e] = b * c[e] + a * s_;
+      }
+    }
+}
+
 // Reductions over the two halves of a wave (lanes l and l ^ 32), by v_permlane32_swap: swapping
 // the upper half of one copy of x with the lower half of another leaves x[l % 32] in the first and
 // x[32 + l % 32] in the second, in both halves, so both halves get the same result bit for bit.
@@ -719,6 +741,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_tr128(Attn a) {
   if (qb == 0 && kj < S) {
     bf16* dkp = (bf16*)a.dk + (base + kj) * a.lddk + (int64_t)kvh * D;
     bf16* dvp = (bf16*)a.dv + (base + kj) * a.lddv + (int64_t)kvh * D;
+    float kv[D / 32][16];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -726,11 +749,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_tr128(Attn a) {
         const int dd = db * 32 + 8 * g + 4 * hh, j4 = (db & 1) * 4 + g;
         const f32x4 pv = red[db >> 1][(kw * 8 + j4) * 64 + lane];
         const f32x4 pk = red[2 + (db >> 1)][(kw * 8 + j4) * 64 + lane];
-        store4(dkp + dd, (dk[db][4 * g] + pk[0]) * scale, (dk[db][4 * g + 1] + pk[1]) * scale,
-               (dk[db][4 * g + 2] + pk[2]) * scale, (dk[db][4 * g + 3] + pk[3]) * scale);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[db][4 * g + e] = (dk[db][4 * g + e] + pk[e]) * scale;
         store4(dvp + dd, dv[db][4 * g] + pv[0], dv[db][4 * g + 1] + pv[1], dv[db][4 * g + 2] + pv[2],
                dv[db][4 * g + 3] + pv[3]);
       }
+    if (a.rope_cos) rope_back_row(kv, a.rope_cos, a.rope_sin, kj, hh);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(dkp + db * 32 + 8 * g + 4 * hh, kv[db][4 * g], kv[db][4 * g + 1], kv[db][4 * g + 2], kv[db][4 * g + 3]);
   }
 }
 
@@ -976,14 +1005,21 @@ __global__ __launch_bounds__(512, 1) void attn_dq_tr128(Attn a) {
   __syncthreads();
   if (kb == 0 && qv) {
     bf16* dqp = (bf16*)a.dq + (base + qi) * a.lddq + (int64_t)h * D;
+    float qv4[D / 32][16];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 pq = red[db >> 1][(qw * 8 + (db & 1) * 4 + g) * 64 + lane];
-        store4(dqp + db * 32 + 8 * g + 4 * hh, (dq[db][4 * g] + pq[0]) * scale, (dq[db][4 * g + 1] + pq[1]) * scale,
-               (dq[db][4 * g + 2] + pq[2]) * scale, (dq[db][4 * g + 3] + pq[3]) * scale);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv4[db][4 * g + e] = (dq[db][4 * g + e] + pq[e]) * scale;
       }
+    if (a.rope_cos) rope_back_row(qv4, a.rope_cos, a.rope_sin, qi, hh);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(dqp + db * 32 + 8 * g + 4 * hh, qv4[db][4 * g], qv4[db][4 * g + 1], qv4[db][4 * g + 2], qv4[db][4 * g + 3]);
   }
 }
 

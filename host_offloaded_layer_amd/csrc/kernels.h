@@ -124,6 +124,10 @@ struct Attn {
   void* dq = nullptr; void* dk = nullptr; void* dv = nullptr;
   int64_t lddq = 0, lddk = 0, lddv = 0;
   float* delta = nullptr;    // scratch fp32 [n_seq, nq, S]
+  // backward, optional: RoPE tables (fp32 [S, d/2], position = token index within its sequence);
+  // when set, dq and dk leave rotated back by the RoPE inverse (the RoPE backward applied)
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
 };
 int launch_attn_fwd(const Attn& a, hipStream_t s);
 int launch_attn_bwd(const Attn& a, hipStream_t s);

@@ -117,6 +117,20 @@ hol_status hol_op_attention_bwd(int32_t n_seq, int32_t S, int32_t nq, int32_t nk
                                 int64_t lddq, void* dk, int64_t lddk, void* dv, int64_t lddv,
                                 float* delta, void* stream);
 
+/* The backward followed by the RoPE backward of dq and dk (MegaTrain summary page, 核心方法: the
+ * attention block of the layer template; q and k entered attention rotated by RoPE at position
+ * t mod S): dq and dk are rotated back by the negative angle, with fp32 tables cos_t / sin_t
+ * [S, d/2] as for hol_op_rope. Head width 128 (bf16) applies the rotation in the kernels' own
+ * epilogues before the single rounding of dq and dk; other shapes run hol_op_rope(inverse) after
+ * the backward. NULL tables or odd d: HOL_EINVAL. Other arguments as hol_op_attention_bwd. */
+hol_status hol_op_attention_bwd_rope(int32_t n_seq, int32_t S, int32_t nq, int32_t nkv, int32_t d,
+                                     hol_dtype t, const void* q, int64_t ldq, const void* k,
+                                     int64_t ldk, const void* v, int64_t ldv, const void* o,
+                                     int64_t ldo, const float* lse, const void* dO, int64_t lddo,
+                                     void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv,
+                                     int64_t lddv, float* delta, const float* cos_t,
+                                     const float* sin_t, void* stream);
+
 /* hol_op_attention_bwd for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and results,
  * with no delta argument. The row sums live in a static device array of the library, 16 MiB on

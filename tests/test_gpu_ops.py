@@ -474,6 +474,54 @@ def test_attention_fwd_bwd(dt, S, nseq, nq, nkv, d):
         np.testing.assert_allclose(host(lse)[b], rl, rtol=1e-5, atol=1e-5)
 
 
+# the backward with the RoPE backward of dq and dk: head width 128 applies it in the kernels'
+# epilogues (one rounding), width 64 through hol_op_rope afterwards; both against the oracle's
+# attention_bwd then rope_bwd, and dv exactly as hol_op_attention_bwd writes it
+@pytest.mark.parametrize("S,nseq,nq,nkv,d", [(260, 2, 8, 2, 128), (300, 1, 4, 4, 64)])
+def test_attention_bwd_rope(S, nseq, nq, nkv, d):
+    r = np.random.default_rng(S + d)
+    T = nseq * S
+    tdt = torch.bfloat16
+    qd, kd, vd, dod = (dev(r.standard_normal((T, n * d)), tdt) for n in (nq, nkv, nkv, nq))
+    o = torch.empty((T, nq * d), dtype=tdt, device=DEV)
+    lse = torch.empty((nseq, nq, S), device=DEV)
+    hol.check(hol.lib.hol_op_attention_fwd(nseq, S, nq, nkv, d, hol.BF16, qd.data_ptr(), nq * d, kd.data_ptr(),
+                                           nkv * d, vd.data_ptr(), nkv * d, o.data_ptr(), nq * d, lse.data_ptr(), None))
+    cs, sn = D.rope_tables(S, d, 10000.0, np.float32)
+    csd, snd = dev(cs), dev(sn)
+    outs = []
+    for fn in ("hol_op_attention_bwd_rope", "hol_op_attention_bwd"):
+        dq = torch.empty_like(qd); dk = torch.empty_like(kd); dv = torch.empty_like(vd)
+        delta = torch.empty((nseq, nq, S), device=DEV)
+        args = [nseq, S, nq, nkv, d, hol.BF16, qd.data_ptr(), nq * d, kd.data_ptr(), nkv * d, vd.data_ptr(), nkv * d,
+                o.data_ptr(), nq * d, lse.data_ptr(), dod.data_ptr(), nq * d, dq.data_ptr(), nq * d, dk.data_ptr(),
+                nkv * d, dv.data_ptr(), nkv * d, delta.data_ptr()]
+        if fn.endswith("rope"):
+            args += [csd.data_ptr(), snd.data_ptr()]
+        hol.check(getattr(hol.lib, fn)(*args, None))
+        outs.append((dq, dk, dv))
+    sync()
+    (dq, dk, dv), (_, _, dv0) = outs
+    assert torch.equal(dv, dv0)
+    q64, k64, v64, do64, o64 = host(qd), host(kd), host(vd), host(dod), host(o)
+    c64, s64 = cs.astype(np.float64), sn.astype(np.float64)
+    for b in range(nseq):
+        sl = slice(b * S, (b + 1) * S)
+        _, rl = D.attention(q64[sl].reshape(S, nq, d), k64[sl].reshape(S, nkv, d), v64[sl].reshape(S, nkv, d))
+        rdq, rdk, _ = D.attention_bwd(do64[sl].reshape(S, nq, d), q64[sl].reshape(S, nq, d), k64[sl].reshape(S, nkv, d),
+                                      v64[sl].reshape(S, nkv, d), o64[sl].reshape(S, nq, d), rl)
+        assert rel(host(dq)[sl], D.rope_bwd(rdq, c64, s64).reshape(S, -1)) < 1e-2
+        assert rel(host(dk)[sl], D.rope_bwd(rdk, c64, s64).reshape(S, -1)) < 1e-2
+
+
+def test_attention_bwd_rope_rejects_missing_tables():
+    z = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    st = hol.lib.hol_op_attention_bwd_rope(1, 4, 1, 1, 16, hol.BF16, *([z.data_ptr(), 16] * 4), z.data_ptr(),
+                                           z.data_ptr(), 16, z.data_ptr(), 16, z.data_ptr(), 16, z.data_ptr(), 16,
+                                           z.data_ptr(), None, None, None)
+    assert st == hol.HOL_EINVAL
+
+
 def test_attention_single_position():
     """S = 1: the softmax is the single key, so o = v of the head's kv head, dv sums dO over the
     heads of the group, and dq = dk = 0 (dS = P (dP - rowsum(dO o)) vanishes up to the rounding of
