@@ -80,6 +80,7 @@ def _load() -> C.CDLL:
         "hol_host_bf16_round": [P, P, I64],
         "hol_op_gemm": [I32, I32, I32, P, I64, I32, P, I64, I32, P, I64, P, I64, I32, I32, I32, F, P],
         "hol_op_gemm_swiglu": [I32, I32, I32, P, I64, P, I64, P, I64, P, I64, I32, P],
+        "hol_op_gemm_rope": [I32, I32, I32, P, I64, P, I64, P, I64, I32, I32, P, P, P],
         "hol_op_gemm_ws": [I32, I32, I32, P, I64, I32, P, I64, I32, P, I64, P, I64, I32, I32, I32, F, P, I64, P],
         "hol_op_gemm_workspace_floats": [],
         "hol_op_rmsnorm_fwd": [P, P, F, P, I32, P, I32, I32, P],
@@ -122,7 +123,7 @@ EXPORTED = ["hol_create", "hol_destroy", "hol_num_tensors", "hol_tensor_info", "
             "hol_zero_grad", "hol_set_ckpt_every_k", "hol_set_kernel_timing",
             "hol_forward_backward", "hol_forward_backward_step", "hol_forward_backward_async", "hol_step", "hol_last_stats", "hol_partition",
             "hol_host_adam", "hol_host_bf16_round", "hol_last_error", "hol_version",
-            "hol_op_gemm", "hol_op_gemm_ws", "hol_op_gemm_workspace_floats", "hol_op_gemm_swiglu", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
+            "hol_op_gemm", "hol_op_gemm_rope", "hol_op_gemm_ws", "hol_op_gemm_workspace_floats", "hol_op_gemm_swiglu", "hol_op_rmsnorm_fwd", "hol_op_rmsnorm_bwd_workspace", "hol_op_rmsnorm_bwd",
             "hol_op_rope", "hol_op_rope_qkv", "hol_op_swiglu_fwd", "hol_op_swiglu_bwd", "hol_op_swiglu_bwd_t", "hol_op_transpose_bf16", "hol_op_attention_fwd",
             "hol_op_attention_bwd", "hol_op_attention_bwd_rope", "hol_op_attention_bwd_noalloc", "hol_op_cross_entropy", "hol_op_sync"]
 

@@ -302,6 +302,21 @@ hol_status hol_op_gemm_ws(int32_t M, int32_t N, int32_t K, const void* A, int64_
   return launched(launch_gemm(g, (hipStream_t)stream), "hol_op_gemm_ws");
 }
 
+hol_status hol_op_gemm_rope(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                            void* C, int64_t ldc, int32_t n_rot, int32_t S, const float* cos_t, const float* sin_t,
+                            void* stream) {
+  if (M < 0 || N < 0 || K < 0 || S <= 0) return einval("hol_op_gemm_rope", "bad size");
+  Gemm g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.ab = g.c = DT_BF16;
+  if (M > 0 && N > 0 && !gemm_rope_supported(g, n_rot, cos_t, sin_t))
+    return einval("hol_op_gemm_rope", "unsupported shape, stride or alignment");
+  return launched(launch_gemm_rope(g, n_rot, S, cos_t, sin_t, (hipStream_t)stream), "hol_op_gemm_rope");
+}
+
 hol_status hol_op_gemm_swiglu(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                               void* gu, int64_t ldgu, void* a, int64_t ld_a, hol_dtype t, void* stream) {
   if (M < 0 || N < 0 || K < 0) return einval("hol_op_gemm_swiglu", "negative size");

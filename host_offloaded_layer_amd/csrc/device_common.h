@@ -65,3 +65,11 @@ __device__ __forceinline__ void swiglu_b(float d, float g, float u, float& dg, f
   dg = d * u * sg * (1.f + g * (1.f - sg));
   du = d * g * sg;
 }
+
+// One RoPE-rotated pair (x, y) = (a c - b s, b c + a s). Contraction off so that every kernel that
+// calls it (the element-wise RoPE kernels and the q/k/v GEMM epilogue) rounds the same way.
+__device__ __forceinline__ void rot_pair(float a, float b, float c, float s, float& x, float& y) {
+#pragma clang fp contract(off)
+  x = a * c - b * s;
+  y = b * c + a * s;
+}

@@ -982,20 +982,30 @@ static hol_status layer_forward(hol_model* m, const W& w, const float* hin, floa
   const int64_t E = m->E;
   hipStream_t s = m->sc;
   KT(KC_RMSNORM, 0, (double)T * H * (4 + E), launch_rmsnorm_fwd(hin, w.g1, m->cfg.rms_eps, A.n1, dt, A.r1, T, H, s));
-  // fp32 q | k | v projection output (the bf16 path rounds once, after RoPE)
-  float* qkv32 = dt == DT_BF16 ? m->qkvf : (float*)A.qkv;
-  KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, qkv32, QKV, dt, DT_F32, EPI_STORE)));
-  if (m->R > 0) {
-    const int c0[3] = {0, nqd, nqd + kvd}, outd[3] = {nqd, kvd, kvd};
-    for (int j = 0; j < 3; ++j)
-      STEP_OK(lora_fwd(m, A.n1, H, H, outd[j], w.lA[j], w.lB[j], qkv32 + c0[j], QKV, T));
-  }
-  if (dt == DT_BF16) {
-    KT(KC_ROPE, 0, (double)T * QKV * (4 + E), launch_rope_qkv(m->qkvf, QKV, A.qkv, QKV, T, m->nq, m->nkv, d, S,
-                                                              m->cos_dev, m->sin_dev, s));
+  // q/k/v projection and RoPE. bf16 without adapters: one product with RoPE in its epilogue, each
+  // value rounded once. Otherwise an fp32 product (to which the adapters add), then RoPE with the
+  // single bf16 rounding.
+  const int nrot = (m->nq + m->nkv) * d;
+  const Gemm gq = gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, A.qkv, QKV, dt, dt, EPI_STORE);
+  if (dt == DT_BF16 && m->R == 0 && d == 128 && gemm_rope_supported(gq, nrot, m->cos_dev, m->sin_dev)) {
+    KCHECK(timed_shape(m, KC_GEMM, 2.0 * T * QKV * H, 2.0 * ((double)T * H + (double)QKV * H + (double)T * QKV), T, QKV,
+                       H, [&] { return launch_gemm_rope(gq, nrot, S, m->cos_dev, m->sin_dev, s); }));
   } else {
-    KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
-    KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
+    // fp32 q | k | v projection output (the bf16 path rounds once, after RoPE)
+    float* qkv32 = dt == DT_BF16 ? m->qkvf : (float*)A.qkv;
+    KCHECK(run_gemm(m, gemm(T, QKV, H, A.n1, H, false, w.wqkv, H, false, qkv32, QKV, dt, DT_F32, EPI_STORE)));
+    if (m->R > 0) {
+      const int c0[3] = {0, nqd, nqd + kvd}, outd[3] = {nqd, kvd, kvd};
+      for (int j = 0; j < 3; ++j)
+        STEP_OK(lora_fwd(m, A.n1, H, H, outd[j], w.lA[j], w.lB[j], qkv32 + c0[j], QKV, T));
+    }
+    if (dt == DT_BF16) {
+      KT(KC_ROPE, 0, (double)T * QKV * (4 + E), launch_rope_qkv(m->qkvf, QKV, A.qkv, QKV, T, m->nq, m->nkv, d, S,
+                                                                m->cos_dev, m->sin_dev, s));
+    } else {
+      KT(KC_ROPE, 0, 2.0 * T * nqd * E, launch_rope(A.qkv, dt, QKV, T, m->nq, d, S, m->cos_dev, m->sin_dev, false, s));
+      KT(KC_ROPE, 0, 2.0 * T * m->nkv * d * E, launch_rope((uint8_t*)A.qkv + (int64_t)nqd * E, dt, QKV, T, m->nkv, d, S, m->cos_dev, m->sin_dev, false, s));
+    }
   }
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;

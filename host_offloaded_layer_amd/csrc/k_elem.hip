@@ -312,12 +312,7 @@ int launch_rope(void* x, DType xt, int64_t ld, int T, int heads, int d, int S, c
 
 // RoPE fused with the cast of the projection output: in = fp32 [T, QKV] rows (q heads, k heads,
 // v heads), out = bf16 rows with q and k rotated; one rounding per element. One thread per pair.
-// One rotated pair, contraction off so that every RoPE kernel that calls it rounds the same way.
-__device__ __forceinline__ void rot_pair(float a, float b, float c, float s, float& x, float& y) {
-#pragma clang fp contract(off)
-  x = a * c - b * s;
-  y = b * c + a * s;
-}
+// (rot_pair, one rotated pair, lives in device_common.h: the q/k/v GEMM epilogue shares it)
 
 __global__ void rope_qkv_k(const float* __restrict__ in, int64_t ldi, bf16* __restrict__ out, int64_t ldo, int Tn,
                            int nq, int nkv, int d, int S, const float* __restrict__ cs, const float* __restrict__ sn) {

@@ -488,21 +488,27 @@ constexpr int N3_TILE = (N2_BM + N2_BN) * N3_BK;  // bf16 elements per stage
 
 __device__ __forceinline__ int n3_off(int r, int c) { return r * N3_BK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// Row of B that feeds output column v. Plain: v. SW (the gate/up product with SwiGLU in the
-// epilogue, B = [W_gate; W_up] with F = N / 2 rows each, F % 32 == 0): the columns of each 64-wide
-// block c are the gate rows 32 c .. 32 c + 31 followed by the up rows F + 32 c .. F + 32 c + 31,
-// so a wave's two 32-column blocks hold the gate and up values of the same 32 features.
-template <bool SW>
-__device__ __forceinline__ int n3_brow(int v, int F) {
-  if constexpr (!SW) return v;
-  else return ((v >> 6) << 5) + (v & 31) + ((v & 32) ? F : 0);
+// Pair modes of the NT3 product: the B rows are read in an order that puts both members of every
+// pair an epilogue combines into the same wave (its two 32-column blocks).
+constexpr int PM_NONE = 0, PM_SWIGLU = 1, PM_ROPE = 2;
+// Row of B that feeds output column v. PM_NONE: v. PM_SWIGLU (the gate/up product, B = [W_gate;
+// W_up] with F = pp rows each, F % 32 == 0): the columns of each 64-wide block c are the gate rows
+// 32 c .. 32 c + 31 followed by the up rows F + 32 c .. F + 32 c + 31. PM_ROPE (the q/k/v product,
+// heads of 128 columns, the first pp columns rotated): inside a rotated head, block c (0 or 1)
+// holds rows 32 c .. 32 c + 31 of the head and then their rotation partners 64 + 32 c ..; the
+// columns past pp keep their order.
+template <int PM>
+__device__ __forceinline__ int n3_brow(int v, int pp) {
+  if constexpr (PM == PM_SWIGLU) return ((v >> 6) << 5) + (v & 31) + ((v & 32) ? pp : 0);
+  else if constexpr (PM == PM_ROPE) return v < pp ? (v & ~127) + (((v >> 6) & 1) << 5) + (v & 31) + ((v & 32) ? 64 : 0) : v;
+  else return v;
 }
 
 // this wave's 64 / NW loads of one stage: LDS rows [8 q, 8 q + 8) for q = wave + NW i of A, then
 // of B
-template <int NW, bool SW = false>
+template <int NW, int PM = PM_NONE>
 __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A, int64_t lda, int m0, int M,
-                                         const bf16* __restrict__ B, int64_t ldb, int n0, int N, int k0) {
+                                         const bf16* __restrict__ B, int64_t ldb, int n0, int N, int k0, int pp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 32 / NW; ++i) {
@@ -518,7 +524,7 @@ __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A
     const int R = (w + NW * i) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ ((R >> 1) & 7);
     int gr = n0 + R;
-    gr = n3_brow<SW>(gr < N ? gr : N - 1, N >> 1);
+    gr = n3_brow<PM>(gr < N ? gr : N - 1, pp);
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(B + (int64_t)gr * ldb + k0 + lc * 8),
                                      (lds_ptr_t)(stage + N2_BM * N3_BK + (w + NW * i) * 8 * N3_BK), 16, 0, 0);
   }
@@ -528,17 +534,17 @@ __device__ __forceinline__ void n3_issue(bf16* stage, const bf16* __restrict__ A
 // a third fewer LDS fragment reads per MFMA).
 // The same loads through buffer resources: a lane's byte offset into A (B) is fixed for the whole
 // tile (rows clamped as above), the stage's k offset is a scalar, so no per-load address arithmetic.
-template <int NW, bool SW = false>
+template <int NW, int PM = PM_NONE>
 struct N3Buf {
   uint32_t va[32 / NW], vb[32 / NW];
-  __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N) {
+  __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N, int pp) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < 32 / NW; ++i) {
       const int R = (w + NW * i) * 8 + (lane >> 3);
       const int lc = (lane & 7) ^ ((R >> 1) & 7);
       va[i] = (uint32_t)(min(m0 + R, M - 1) * lda * 2 + lc * 16);
-      vb[i] = (uint32_t)(n3_brow<SW>(min(n0 + R, N - 1), N >> 1) * ldb * 2 + lc * 16);
+      vb[i] = (uint32_t)(n3_brow<PM>(min(n0 + R, N - 1), pp) * ldb * 2 + lc * 16);
     }
   }
   __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int k0) const {
@@ -675,7 +681,55 @@ __device__ __forceinline__ void n3_origin(int q, int tiles_m, int tiles_n, int& 
 // (g.spl_full per XCD, the full rounds) followed by at most one part, whose raw sums go to the
 // workspace (one 256 x 256 fp32 slot per part: slot x r f + q f + part for the XCD's q-th split
 // tile); gemm_split_reduce_k adds the parts in order and applies alpha.
-template <int EPI, typename TO, int NW, bool BUF, bool GRP, bool SW = false, bool SPL = false>
+// RoPE epilogue (B rows read by n3_brow<PM_ROPE>): in a rotated head, block j = 0 of a wave holds
+// column jj = 32 c + 8 q + 4 (lane / 32) + e of the head (c = the wave's 64-column block within
+// the head) and block j = 1 its partner jj + 64; they are rotated with the table row of the
+// token's position (row mod S, tables [S][64]) exactly as the element-wise RoPE does on the fp32
+// product, and rounded to bf16 once. Columns past the rotated ones (v) are stored as they are.
+// 32 vector stores a wave for a full tile (and the table loads before them).
+__device__ __forceinline__ void n3_store_rope(const Gemm& g, const f32x16 (&acc)[4][2], bf16* C, int M, int N,
+                                              int m0, int n0, int wm, int wn, int lane) {
+  const int cb = n0 + wn * 64;  // this wave's first (virtual) column
+  if (cb >= N) return;
+  const bool rot = cb < g.rope_nr;
+  const int hb = cb & ~127, c = (cb >> 6) & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (row >= M) continue;
+    bf16* crow = C + (int64_t)row * g.ldc;
+    const int pos = row % g.rope_S;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int jj = 32 * c + 8 * q + 4 * (lane >> 5);
+      bf16x4 x, y;
+      if (rot) {
+        const float4 c4 = *(const float4*)(g.rope_cos + (int64_t)pos * 64 + jj);
+        const float4 s4 = *(const float4*)(g.rope_sin + (int64_t)pos * 64 + jj);
+        const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float xx, yy;
+          rot_pair(g.alpha * acc[i][0][4 * q + e], g.alpha * acc[i][1][4 * q + e], cv[e], sv[e], xx, yy);
+          x[e] = (bf16)xx;
+          y[e] = (bf16)yy;
+        }
+        *(bf16x4*)(crow + hb + jj) = x;
+        *(bf16x4*)(crow + hb + 64 + jj) = y;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = (bf16)(g.alpha * acc[i][0][4 * q + e]);
+          y[e] = (bf16)(g.alpha * acc[i][1][4 * q + e]);
+        }
+        *(bf16x4*)(crow + cb + 8 * q + 4 * (lane >> 5)) = x;
+        *(bf16x4*)(crow + cb + 32 + 8 * q + 4 * (lane >> 5)) = y;
+      }
+    }
+  }
+}
+
+template <int EPI, typename TO, int NW, bool BUF, bool GRP, int PM = PM_NONE, bool SPL = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
   static_assert(NW == 8, "the epilogue count below assumes 8 waves");
@@ -766,20 +820,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  static_assert(!SW || (EPI == EPI_STORE && sizeof(TO) == 2 && !GRP && WJ == 2), "SwiGLU: bf16 store, one group");
-  static_assert(!SPL || (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP && !SW), "split tail: fp32 store, one group");
+  static_assert(PM == PM_NONE || (EPI == EPI_STORE && sizeof(TO) == 2 && !GRP && WJ == 2), "pair modes: bf16 store, one group");
+  static_assert(!SPL || (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP && PM == PM_NONE), "split tail: fp32 store, one group");
+  constexpr bool SW = PM == PM_SWIGLU;
+  const int pp = PM == PM_SWIGLU ? N >> 1 : (PM == PM_ROPE ? g.rope_nr : 0);
   int nk = (kend - kbeg) / N3_BK;
-  N3Buf<NW, SW> nb;
+  N3Buf<NW, PM> nb;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)M * g.lda * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)N * g.ldb * 2), 0x00020000);
   auto issue = [&](bf16* stage, int k0) {  // k0 relative to the item's first k
     if constexpr (BUF) nb.issue(stage, ra, rb, kbeg + k0);
-    else n3_issue<NW, SW>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, kbeg + k0);
+    else n3_issue<NW, PM>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, kbeg + k0, pp);
   };
   auto start_tile = [&]() {
-    if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N);
+    if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N, pp);
     issue(lds, 0);
     if (nk > 1) issue(lds + N3_TILE, N3_BK);
   };
@@ -857,6 +913,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
     if constexpr (SW) {
       after = cm0 + N2_BM <= M && cn0 + N2_BN <= N ? 1 : 0;
       n3_store_swiglu(g, acc, C, M, N, cm0, cn0, wm, wn, lane);
+    } else if constexpr (PM == PM_ROPE) {
+      after = cm0 + N2_BM <= M && cn0 + N2_BN <= N ? 1 : 0;  // (32 stores a wave; the table loads only add)
+      n3_store_rope(g, acc, C, M, N, cm0, cn0, wm, wn, lane);
     } else if (SPL && cslot >= 0) {  // a part of a split tile: raw sums, whole 256 x 256 slot
       Gemm gw = g;
       gw.ldc = N2_BN;
@@ -1076,9 +1135,11 @@ constexpr int NT3_WAVES = 8;
 HOL_NT3_INST(false)
 HOL_NT3_INST(true)
 #undef HOL_NT3_INST
-template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, true>(Gemm);
-template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, true>(Gemm);
-template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, PM_SWIGLU>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, PM_SWIGLU>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, PM_ROPE>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, PM_ROPE>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, true>(Gemm);
 
 // Sum of the parts of the split tiles (gemm_nt3 with SPL): one block per split tile; thread t
 // owns columns 4 (t mod 64) .. + 3 of rows t / 64 + 4 i. Parts are added in order 0, 1, ... so the
@@ -1155,7 +1216,7 @@ static int launch_nt3_t(const Gemm& g, hipStream_t s) {
   if constexpr (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP) {
     Gemm gs;
     if (n3_split_plan(g, tiles, gs)) {
-      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, false, true>), dim3(tiles), dim3(64 * NT3_WAVES),
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, true>), dim3(tiles), dim3(64 * NT3_WAVES),
                          0, s, gs);
       const int nsplit = (((g.M + N2_BM - 1) / N2_BM) * tn / 8 - gs.spl_full) * 8;
       hipLaunchKernelGGL(gemm_split_reduce_k, dim3(nsplit), dim3(256), 0, s, gs);
@@ -1267,10 +1328,10 @@ int launch_gemm_swiglu(const Gemm& g0, void* a, int64_t ld_a, hipStream_t s) {
   if (fused) {
     const int tiles = n3_persistent_grid(((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN));
     if (n3_buffer_ok(g))
-      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, true>), dim3(tiles), dim3(64 * NT3_WAVES), 0,
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, PM_SWIGLU>), dim3(tiles), dim3(64 * NT3_WAVES), 0,
                          s, g);
     else
-      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, true>), dim3(tiles), dim3(64 * NT3_WAVES),
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, PM_SWIGLU>), dim3(tiles), dim3(64 * NT3_WAVES),
                          0, s, g);
     return (int)hipGetLastError();
   }
@@ -1279,6 +1340,33 @@ int launch_gemm_swiglu(const Gemm& g0, void* a, int64_t ld_a, hipStream_t s) {
   const int e = launch_gemm(g0, s);
   if (e) return e;
   return launch_swiglu_fwd(g.C, a, g.c, g.M, F, s);
+}
+
+bool gemm_rope_supported(const Gemm& g, int nrot, const float* cos_t, const float* sin_t) {
+  const DType tb = g.bt < 0 ? g.ab : (DType)g.bt;
+  return g.ab == DT_BF16 && tb == DT_BF16 && g.c == DT_BF16 && g.epi == EPI_STORE && g.batch == 1 && !g.a_km &&
+         !g.b_kn && g.K > 0 && g.K % N3_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         (((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0) && g.N % 128 == 0 && nrot >= 0 && nrot % 128 == 0 &&
+         nrot <= g.N && g.ldc % 4 == 0 && (uintptr_t)g.C % 8 == 0 && cos_t && sin_t &&
+         (((uintptr_t)cos_t | (uintptr_t)sin_t) % 16 == 0);
+}
+
+int launch_gemm_rope(const Gemm& g0, int nrot, int S, const float* cos_t, const float* sin_t, hipStream_t s) {
+  if (g0.M <= 0 || g0.N <= 0) return 0;
+  if (S <= 0 || !gemm_rope_supported(g0, nrot, cos_t, sin_t)) return (int)hipErrorInvalidValue;
+  Gemm g = g0;
+  g.rope_cos = cos_t;
+  g.rope_sin = sin_t;
+  g.rope_S = S;
+  g.rope_nr = nrot;
+  const int tiles = n3_persistent_grid(((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN));
+  if (n3_buffer_ok(g))
+    hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, PM_ROPE>), dim3(tiles), dim3(64 * NT3_WAVES), 0,
+                       s, g);
+  else
+    hipLaunchKernelGGL((gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, PM_ROPE>), dim3(tiles), dim3(64 * NT3_WAVES),
+                       0, s, g);
+  return (int)hipGetLastError();
 }
 
 int launch_gemm(const Gemm& g, hipStream_t s) {

@@ -49,6 +49,10 @@ struct Gemm {
   float* ws = nullptr;
   int64_t ws_floats = 0;
   int spl_full = 0, spl_f = 1;
+  // launch_gemm_rope: RoPE tables [rope_S][64] and the number of rotated columns (set by it)
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  int rope_S = 0, rope_nr = 0;
 };
 constexpr int64_t GEMM_SPLIT_WS_FLOATS = (int64_t)256 * 256 * 256;  // 256 tile parts (64 MiB)
 int launch_gemm(const Gemm& g, hipStream_t s);
@@ -60,6 +64,15 @@ int launch_gemm(const Gemm& g, hipStream_t s);
 // multiples of 4 and 8-byte aligned outputs; otherwise the two launches, which need ldc = N and
 // ld_a = N/2.
 int launch_gemm_swiglu(const Gemm& g, void* a, int64_t ld_a, hipStream_t s);
+// The q/k/v product with RoPE in its epilogue: g is the plain product C [M, N] = x Wqkv^T with a
+// bf16 store (EPI_STORE, no batch), columns in heads of 128; the first nrot columns (the q and k
+// heads) leave rotated at position row mod S (tables [S][64]), each value rounded to bf16 once:
+// bit for bit launch_gemm into fp32 followed by launch_rope_qkv. Needs bf16 NT operands with
+// K % 64 == 0, 16-byte aligned A and B with lda, ldb multiples of 8, N % 128 == 0, nrot % 128 == 0,
+// ldc % 4 == 0, 8-byte aligned C and 16-byte aligned tables (gemm_rope_supported), else
+// hipErrorInvalidValue.
+bool gemm_rope_supported(const Gemm& g, int nrot, const float* cos_t, const float* sin_t);
+int launch_gemm_rope(const Gemm& g, int nrot, int S, const float* cos_t, const float* sin_t, hipStream_t s);
 // out[u][:] = sum over i in [seg[u], seg[u+1]) of dh[order[i]][:], in order of i from zero (fp32)
 int launch_embed_row_sums(const float* dh, const int32_t* order, const int32_t* seg, int nrows, int H, float* out,
                           hipStream_t s);

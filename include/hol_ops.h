@@ -46,6 +46,18 @@ hol_status hol_op_gemm_ws(int32_t M, int32_t N, int32_t K, const void* A, int64_
                           const float* R, int64_t ldr, hol_dtype ab, hol_dtype c, int32_t epi,
                           float alpha, float* workspace, int64_t workspace_floats, void* stream);
 
+/* q/k/v projection with RoPE in the product's epilogue (MegaTrain summary page, 核心方法: the
+ * attention block of the layer template): C [M, N] (bf16, row stride ldc) = A B^T with A [M, K]
+ * and B [N, K] bf16 (NT, row strides lda, ldb), where the columns form heads of 128 and the first
+ * n_rot columns (the q and k heads) are rotated by RoPE at position row mod S with fp32 tables
+ * cos_t / sin_t [S, 64] as for hol_op_rope; every value is rounded to bf16 once. Bit for bit the
+ * fp32 product of hol_op_gemm followed by hol_op_rope_qkv. K % 64 == 0, N % 128 == 0,
+ * n_rot % 128 == 0, n_rot <= N, lda and ldb multiples of 8 with 16-byte aligned A, B and tables,
+ * ldc % 4 == 0 and 8-byte aligned C, S > 0; else HOL_EINVAL. */
+hol_status hol_op_gemm_rope(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, void* C, int64_t ldc, int32_t n_rot, int32_t S,
+                            const float* cos_t, const float* sin_t, void* stream);
+
 /* Gate/up projection with the SwiGLU activation (MegaTrain summary page, 核心方法: the MLP block
  * of the layer template, here with the activation fused into the product's epilogue):
  * gu [M, N] = A B^T with A [M, K] (row stride lda) and B = [W_gate; W_up] [N, K] (ldb), so gate

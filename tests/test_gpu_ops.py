@@ -216,6 +216,51 @@ def test_gemm_swiglu_matches_gemm_then_swiglu(M, F, K, pad, dt):
     np.testing.assert_allclose(host(act[:, :F])[rows], D.swiglu(got_gu[:, :F], got_gu[:, F:]), rtol=tol, atol=tol)
 
 
+# q/k/v product with RoPE in the epilogue: bit for bit the fp32 product then hol_op_rope_qkv
+@pytest.mark.parametrize("T,S,nq,nkv,K", [
+    (300, 100, 4, 2, 128),     # ragged rows, 3 sequences
+    (260, 260, 2, 1, 64),      # N = 512 + 128: a last tile with one head of v
+    (4352, 1088, 32, 8, 192),  # 17 x 24 tiles over 256 blocks: the persistent path
+])
+def test_gemm_rope_matches_gemm_then_rope(T, S, nq, nkv, K):
+    d = 128
+    N = (nq + 2 * nkv) * d
+    r = np.random.default_rng(T + N)
+    x = dev(r.standard_normal((T, K)) * 0.5, torch.bfloat16)
+    w = dev(r.standard_normal((N, K)) / math.sqrt(K), torch.bfloat16)
+    cs, sn = D.rope_tables(S, d, 10000.0, np.float32)
+    csd, snd = dev(cs), dev(sn)
+    out = torch.full((T, N), 3.0, dtype=torch.bfloat16, device=DEV)
+    hol.check(hol.lib.hol_op_gemm_rope(T, N, K, x.data_ptr(), K, w.data_ptr(), K, out.data_ptr(), N, (nq + nkv) * d, S,
+                                       csd.data_ptr(), snd.data_ptr(), None))
+    f32 = torch.zeros((T, N), device=DEV)
+    hol.check(hol.lib.hol_op_gemm(T, N, K, x.data_ptr(), K, 0, w.data_ptr(), K, 0, f32.data_ptr(), N, None, 0,
+                                  hol.BF16, hol.F32, 0, 1.0, None))
+    ref = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    hol.check(hol.lib.hol_op_rope_qkv(f32.data_ptr(), N, ref.data_ptr(), N, T, nq, nkv, d, S, csd.data_ptr(),
+                                      snd.data_ptr(), None))
+    sync()
+    assert torch.equal(out, ref)
+    # and the oracle on sampled rows: x W^T in fp64, RoPE on q and k at position t mod S
+    rows = np.arange(0, T, max(1, T // 48))
+    y = host(x)[rows] @ host(w).T
+    heads = y.reshape(len(rows), nq + 2 * nkv, d)  # (the oracle's rope takes one position per row)
+    rot = D.rope(heads[:, :nq + nkv, :], cs[rows % S].astype(np.float64), sn[rows % S].astype(np.float64))
+    want = np.concatenate([rot.reshape(len(rows), -1), y[:, (nq + nkv) * d:]], 1)
+    got = host(out)[rows]
+    assert np.max(np.abs(got - want) / (np.abs(want) + 1)) < 2 ** -7
+
+
+def test_gemm_rope_rejects_unsupported():
+    z = torch.zeros(256 * 256, dtype=torch.bfloat16, device=DEV)
+    t = torch.zeros(64, device=DEV)
+    # N not a multiple of 128; rotated columns not a multiple of 128; missing tables
+    for N, nrot, tab in ((200, 128, t.data_ptr()), (256, 100, t.data_ptr()), (256, 128, None)):
+        st = hol.lib.hol_op_gemm_rope(8, N, 64, z.data_ptr(), 64, z.data_ptr(), 64, z.data_ptr(), N, nrot, 1, tab, tab,
+                                      None)
+        assert st == hol.HOL_EINVAL
+
+
 def test_gemm_swiglu_rejects_odd_n_and_unpacked_fallback():
     x = torch.zeros(64, 64, dtype=torch.bfloat16, device=DEV)
     gu = torch.zeros(64, 208, dtype=torch.bfloat16, device=DEV)
