@@ -729,6 +729,24 @@ __device__ __forceinline__ void n3_store_rope(const Gemm& g, const f32x16 (&acc)
   }
 }
 
+// Instruction order of one k-step: the first six of its 8 MFMAs each followed by one of the 6
+// fragment reads of the next k-step, the last two MFMAs alone. Left to itself the compiler moved each read down
+// next to the MFMA that consumes it, so a wave waited for LDS before most of its MFMAs; with the
+// reads spread over the step they have ≈6 MFMAs to land (2.5–3 % over the decoder shapes,
+// bitwise the same products). Off for the global_load_lds path (operands past 4 GiB), where the
+// longer-lived fragments would push more registers to scratch.
+template <bool ON>
+__device__ __forceinline__ void n3_interleave() {
+  if constexpr (ON) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
 template <int EPI, typename TO, int NW, bool BUF, bool GRP, int PM = PM_NONE, bool SPL = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
@@ -875,10 +893,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       const bf16* st = lds + (kt & 1) * N3_TILE;
       frags(st, 1, a1, b1);
       mma(a0, b0);
+      n3_interleave<BUF>();
       frags(st, 2, a0, b0);
       mma(a1, b1);
+      n3_interleave<BUF>();
       frags(st, 3, a1, b1);
       mma(a0, b0);
+      n3_interleave<BUF>();
       // stage kt + 1 is the only load in flight (for the first stage of a tile, behind it at
       // most the previous epilogue's memory operations); once every wave has also finished
       // reading this slot, it takes stage kt + 2
@@ -888,15 +909,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
       frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
       mma(a1, b1);
+      n3_interleave<BUF>();
     }
     {  // the tile's last stage
       const bf16* st = lds + ((nk - 1) & 1) * N3_TILE;
       frags(st, 1, a1, b1);
       mma(a0, b0);
+      n3_interleave<BUF>();
       frags(st, 2, a0, b0);
       mma(a1, b1);
+      n3_interleave<BUF>();
       frags(st, 3, a1, b1);
       mma(a0, b0);
+      n3_interleave<BUF>();
       mma(a1, b1);
     }
     // next tile: its first two stages go up before this tile's results go out
