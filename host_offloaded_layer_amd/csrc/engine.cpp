@@ -524,7 +524,10 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   for (int p = 0; p < hol_model::NPF; ++p) HCHECK(hipEventCreateWithFlags(&m->ev_lpf_done[p], hipEventDisableTiming));
   HCHECK(hipEventCreateWithFlags(&m->ev_h0, hipEventDisableTiming));
   for (auto& e : m->ev_tail) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  HCHECK(hipEventCreateWithFlags(&m->tail_mlp_ev, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->ev_wd_final, hipEventDisableTiming));
+  HCHECK(hipEventCreateWithFlags(&m->ev_mlp_final, hipEventDisableTiming));
+  m->ev_piece.resize(3 * (size_t)m->L);
+  for (auto& e : m->ev_piece) HCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   for (int i = 0; i < m->nring; ++i) HCHECK(hipEventCreateWithFlags(&m->ring_ev[i], hipEventDisableTiming));
   m->unit_tensors.assign(m->L + 2, {});
   for (int i = 0; i < (int)m->tensors.size(); ++i) {
@@ -563,7 +566,10 @@ void engine_destroy(hol_model* m) {
   if (m->ev_h0) hipEventDestroy(m->ev_h0);
   for (auto e : m->ev_tail)
     if (e) hipEventDestroy(e);
-  if (m->tail_mlp_ev) hipEventDestroy(m->tail_mlp_ev);
+  if (m->ev_wd_final) hipEventDestroy(m->ev_wd_final);
+  if (m->ev_mlp_final) hipEventDestroy(m->ev_mlp_final);
+  for (auto e : m->ev_piece)
+    if (e) hipEventDestroy(e);
   for (auto e : m->tev)
     if (e) hipEventDestroy(e);
   for (auto e : m->kev)
@@ -1087,6 +1093,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
       KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
       KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
       KCHECK(run_gemm_dw(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
+      if (m->pieces_armed) HCHECK(hipEventRecord(m->ev_wd_final, s));  // w_down final
     }
     // (with weight gradients the SwiGLU backward also writes dgu^T for the dWgu product)
     const bool dgu_t = tw && F % 64 == 0;
@@ -1101,7 +1108,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
       KCHECK(tr(m, A.n2, H, m->xT, T, T, H));
       KCHECK(run_gemm_dw(m, nt(2 * F, H, T, m->yT, T, m->xT, T, G + m->g_wgu, H, DT_F32)));
     }
-    if (m->tail_mlp_armed) HCHECK(hipEventRecord(m->tail_mlp_ev, s));  // w_gate, w_up, w_down final
+    if (m->pieces_armed) HCHECK(hipEventRecord(m->ev_mlp_final, s));  // w_gate, w_up final
   }
   if (tw) KCHECK(launch_fill_f32(G + m->g_g1, 0.f, 2 * (int64_t)H, s));
   // (the RMSNorm backward also writes dh rounded to bf16 into dhb)
@@ -1276,6 +1283,17 @@ static void adam_unit(hol_model* m, int u, const AdamConsts& k, int64_t lo = -1,
 static void adam_embed_rows(hol_model* m, const std::vector<int32_t>& rows, const AdamConsts& k, bool zero = true,
                             const float* gsrc = nullptr);
 
+// Waits for an event by polling it. A blocking wait (hipEventSynchronize) on an event still
+// pending when it was called returned ≈8 ms after the copy it marks had finished, which the
+// optimiser thread paid at the first unit of every block.
+static hipError_t wait_event(hipEvent_t ev) {
+  for (;;) {
+    const hipError_t e = hipEventQuery(ev);
+    if (e != hipErrorNotReady) return e;
+    std::this_thread::sleep_for(std::chrono::microseconds(50));
+  }
+}
+
 // Host worker of the fused forward_backward + step: runs the optimiser on each unit as soon as
 // that unit's gradient copy (enqueued by the main thread, in backward order) has completed.
 struct FusedWorker {
@@ -1293,6 +1311,7 @@ struct FusedWorker {
     {
       std::lock_guard<std::mutex> g(m->fmu);
       m->unit_queue.clear();
+      m->pjobs.clear();
       m->fused_abort = false;
     }
     running = true;
@@ -1301,23 +1320,35 @@ struct FusedWorker {
       size_t next = 0;
       for (;;) {
         int u;
+        hol_model::PieceJob job{};
         {
           std::unique_lock<std::mutex> lk(m->fmu);
           m->fcv.wait(lk, [&] { return m->fused_abort || next < m->unit_queue.size(); });
           if (m->fused_abort) return;
           u = m->unit_queue[next++];
+          if (u >= hol_model::PIECE_CODE) job = m->pjobs[u - hol_model::PIECE_CODE];
         }
         if (u < 0) return;  // every unit handed over
-        const bool piece = u >= hol_model::TAIL_CODE;
+        const bool pjob = u >= hol_model::PIECE_CODE;
+        const bool piece = !pjob && u >= hol_model::TAIL_CODE;
         // unit L + 2: embedding rows no token of this call touches (their gradient is zero and
         // known from the start)
-        hipEvent_t ev = piece ? m->ev_tail[u - hol_model::TAIL_CODE] : (u != m->L + 2 ? m->ev_unit[u] : nullptr);
-        if (ev && hipEventSynchronize(ev) != hipSuccess) {
+        hipEvent_t ev = pjob    ? job.ev
+                        : piece ? m->ev_tail[u - hol_model::TAIL_CODE]
+                                : (u != m->L + 2 ? m->ev_unit[u] : nullptr);
+        if (ev && wait_event(ev) != hipSuccess) {
           failed = true;
           return;
         }
         const double t0 = now_ms();
-        if (piece) {
+        if (pjob) {
+          adam_unit(m, job.unit, kc, job.lo, job.hi, false);
+          const int l = job.unit - 1;  // the layer's last piece: the next call's copy of it may go up
+          if (job.last && l < hol_model::NPF && m->lpf_next[l] >= 0 && !prefetch_layer(l)) {
+            failed = true;
+            return;
+          }
+        } else if (piece) {
           const int c = u - hol_model::TAIL_CODE;
           const int64_t f0 = m->layer_flat0 + (int64_t)(m->tail_unit - 1) * m->layer_flat_n;
           adam_unit(m, m->tail_unit, kc, f0 + m->tail_lo[c], f0 + m->tail_hi[c], false);
@@ -1382,6 +1413,14 @@ struct FusedWorker {
     {
       std::lock_guard<std::mutex> g(m->fmu);
       m->unit_queue.push_back(u);
+    }
+    m->fcv.notify_one();
+  }
+  void push_job(const hol_model::PieceJob& j) {
+    {
+      std::lock_guard<std::mutex> g(m->fmu);
+      m->pjobs.push_back(j);
+      m->unit_queue.push_back(hol_model::PIECE_CODE + (int)m->pjobs.size() - 1);
     }
     m->fcv.notify_one();
   }
@@ -1856,55 +1895,70 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
       const Act A = act_at(m, op.pos);
       const float* hin = op.pos == 0 ? ckpt_of(op.block) : A.hin;
       const bool tail = fused && j + 1 == ops.size();
-      // dense bf16 layer: [wqkv | wo | w_gate w_up | w_down | attn_norm | mlp_norm]
-      const bool split = tail && m->dt == DT_BF16 && m->NE == 0 && m->base_trainable;
+      // dense bf16 layer with trainable weights, gradient block [wqkv | wo | w_gate w_up | w_down |
+      // attn_norm | mlp_norm ...]: copied in three pieces, each as soon as it is final
+      const bool pieces = direct && m->dt == DT_BF16 && m->NE == 0 && m->base_trainable;
       HSTEP(hipStreamWaitEvent(sc, m->ev_gfree[gi], 0));
       HSTEP(hipEventRecord(ta, sc));
-      m->tail_mlp_armed = split;
+      m->pieces_armed = pieces;
       const hol_status bst = layer_backward(m, w, A, hin, m->gdev[gi], T, n_seq, S, op.pos);
-      m->tail_mlp_armed = false;
+      m->pieces_armed = false;
       STEP(bst);
       HSTEP(hipEventRecord(tb, sc));
       spans.push_back({ta, tb, 4});
       HSTEP(hipEventRecord(m->ev_gdone[gi], sc));
+      // one of the first layers: its slot takes the next call's copy once this backward is done,
+      // when no copy of this call can reuse it, i.e. every op left uses another layer that is
+      // resident (always for the call's last op)
+      if (fused && op.layer < hol_model::NPF) {
+        bool rest_resident = true;
+        for (size_t k = j + 1; rest_resident && k < ops.size(); ++k)
+          if (ops[k].kind != OP_HEAD && (ops[k].layer == op.layer || slot_of(ops[k].layer) < 0)) rest_resident = false;
+        if (rest_resident) {
+          HSTEP(hipEventRecord(m->ev_lpf_done[op.layer], sc));
+          m->lpf_next[op.layer] = s;
+        }
+      }
       // gradient offload on the gradient-transfer stream
       float* lg = m->grad + m->layer_flat0 + (int64_t)op.layer * m->layer_flat_n;
       HSTEP(astep.gate(1 + op.layer, sd));
       hipEvent_t a = tev(), e = tev();
       HSTEP(hipEventRecord(a, sd));
-      if (tail) {
-        // the call's last gradient: in pieces, each handed to the optimiser as it lands; the MLP
-        // weights' piece as soon as the MLP backward is done
+      const int64_t n = m->layer_flat_n;
+      hipEvent_t* pe = pieces ? &m->ev_piece[3 * (size_t)op.layer] : nullptr;
+      if (pieces) {
+        const float* gd = m->gdev[gi];
+        auto copy = [&](int64_t lo, int64_t hi) {
+          return hipMemcpyAsync(lg + lo, gd + lo, (size_t)(hi - lo) * 4, hipMemcpyDeviceToHost, sd);
+        };
+        HSTEP(hipStreamWaitEvent(sd, m->ev_wd_final, 0));
+        HSTEP(copy(m->g_wd, m->g_g1));
+        HSTEP(hipEventRecord(pe[0], sd));
+        HSTEP(hipStreamWaitEvent(sd, m->ev_mlp_final, 0));
+        HSTEP(copy(m->g_wgu, m->g_wd));
+        HSTEP(hipEventRecord(pe[1], sd));
+        HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
+        HSTEP(copy(0, m->g_wgu));
+        HSTEP(copy(m->g_g1, n));
+        HSTEP(hipEventRecord(pe[2], sd));
+      } else if (tail) {
+        // the call's last gradient: in pieces, each handed to the optimiser as it lands
         m->tail_unit = 1 + op.layer;
-        const int64_t n = m->layer_flat_n;
         m->n_tail = 0;
-        m->n_tail_expect = split ? 3 : hol_model::N_TAIL;
-        if (op.layer == 0) {  // its slot takes the next call's copy once this backward is done
-          HSTEP(hipEventRecord(m->ev_lpf_done[0], sc));
-          m->lpf_next[0] = s;
-        }
-        auto piece = [&](int64_t lo, int64_t hi) -> hol_status {
-          const int c = m->n_tail++;
+        m->n_tail_expect = hol_model::N_TAIL;
+        HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
+        for (int c = 0; c < hol_model::N_TAIL; ++c) {
+          const int64_t lo = n * c / hol_model::N_TAIL, hi = n * (c + 1) / hol_model::N_TAIL;
           m->tail_lo[c] = lo;
           m->tail_hi[c] = hi;
-          HCHECK(hipMemcpyAsync(lg + lo, m->gdev[gi] + lo, (size_t)(hi - lo) * 4, hipMemcpyDeviceToHost, sd));
-          HCHECK(hipEventRecord(m->ev_tail[c], sd));
+          m->n_tail++;
+          HSTEP(hipMemcpyAsync(lg + lo, m->gdev[gi] + lo, (size_t)(hi - lo) * 4, hipMemcpyDeviceToHost, sd));
+          HSTEP(hipEventRecord(m->ev_tail[c], sd));
           worker.push(hol_model::TAIL_CODE + c);
-          return HOL_OK;
-        };
-        if (split) {
-          HSTEP(hipStreamWaitEvent(sd, m->tail_mlp_ev, 0));
-          STEP(piece(m->g_wgu, m->g_g1));
-          HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
-          STEP(piece(0, m->g_wgu));
-          STEP(piece(m->g_g1, n));
-        } else {
-          HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
-          for (int c = 0; c < hol_model::N_TAIL; ++c) STEP(piece(n * c / hol_model::N_TAIL, n * (c + 1) / hol_model::N_TAIL));
         }
       } else {
         HSTEP(hipStreamWaitEvent(sd, m->ev_gdone[gi], 0));
-        HSTEP(hipMemcpyAsync(direct ? lg : m->grad_stage, m->gdev[gi], m->layer_flat_n * 4, hipMemcpyDeviceToHost, sd));
+        HSTEP(hipMemcpyAsync(direct ? lg : m->grad_stage, m->gdev[gi], n * 4, hipMemcpyDeviceToHost, sd));
       }
       HSTEP(hipEventRecord(e, sd));
       spans.push_back({a, e, 1});
@@ -1915,17 +1969,15 @@ hol_status engine_forward_backward(hol_model* m, const hol_batch* b, hol_loss lo
         HSTEP(hipLaunchHostFunc(sd, host_accumulate, &jobs[op.layer]));
       }
       HSTEP(hipEventRecord(m->ev_gfree[gi], sd));
-      if (fused && !tail) {
+      if (fused && pieces) {  // the pieces' optimiser jobs, in the order they land
+        const int u = 1 + op.layer;
+        const int64_t f0 = m->layer_flat0 + (int64_t)op.layer * n;
+        worker.push_job({u, f0 + m->g_wd, f0 + m->g_g1, pe[0], false});
+        worker.push_job({u, f0 + m->g_wgu, f0 + m->g_wd, pe[1], false});
+        worker.push_job({u, f0, f0 + m->g_wgu, pe[2], false});
+        worker.push_job({u, f0 + m->g_g1, f0 + n, pe[2], true});
+      } else if (fused && !tail) {
         HSTEP(hipEventRecord(m->ev_unit[1 + op.layer], sd));
-        // one of the first layers: its slot takes the next call's copy when no copy of this call
-        // can reuse it, i.e. every op left uses another layer that is resident
-        bool rest_resident = op.layer >= 1 && op.layer < hol_model::NPF;
-        for (size_t k = j + 1; rest_resident && k < ops.size(); ++k)
-          if (ops[k].kind != OP_HEAD && (ops[k].layer == op.layer || slot_of(ops[k].layer) < 0)) rest_resident = false;
-        if (rest_resident) {
-          HSTEP(hipEventRecord(m->ev_lpf_done[op.layer], sc));
-          m->lpf_next[op.layer] = s;
-        }
         worker.push(1 + op.layer);
       }
       m->stats.d2h_bytes += (double)m->layer_flat_n * 4;

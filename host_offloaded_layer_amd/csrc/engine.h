@@ -270,10 +270,23 @@ struct hol_model {
   int tail_unit = -1;
   int64_t tail_lo[N_TAIL] = {}, tail_hi[N_TAIL] = {};  // piece ranges inside the layer block
   int n_tail = 0;
-  // dense bf16 last layer: its MLP weight gradients (final once the MLP backward is done) go down
-  // while the layer's attention backward computes; the backward records tail_mlp_ev there
-  hipEvent_t tail_mlp_ev = nullptr;
-  bool tail_mlp_armed = false;
+  // dense bf16 layers with trainable weights: the gradient goes down in three pieces, each as soon
+  // as it is final: w_down (its product is the MLP backward's first), then w_gate | w_up (the MLP
+  // backward's last), then the rest once the layer's backward is done. The backward records
+  // ev_wd_final and ev_mlp_final on the compute stream when pieces_armed. In a fused call every
+  // piece is also its own optimiser job (queue code PIECE_CODE + index into pjobs), so the Adam of
+  // a layer's MLP weights runs while its attention backward computes.
+  hipEvent_t ev_wd_final = nullptr, ev_mlp_final = nullptr;
+  bool pieces_armed = false;
+  std::vector<hipEvent_t> ev_piece;  // 3 per layer, recorded on the d2h stream after each piece
+  struct PieceJob {
+    int unit;
+    int64_t lo, hi;  // flat parameter range
+    hipEvent_t ev;
+    bool last;  // the unit's last job
+  };
+  static constexpr int PIECE_CODE = 1 << 21;
+  std::vector<PieceJob> pjobs;  // this call's piece jobs (only the main thread appends, before the push)
   std::vector<int32_t> emb_touched, emb_untouched;  // embedding rows the call's tokens use / do not
   bool fused_abort = false;
   double fused_overlap_ms = 0, fused_tail_ms = 0;
