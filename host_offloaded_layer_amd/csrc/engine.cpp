@@ -480,8 +480,8 @@ hol_status engine_create(const hol_config* cfg, hol_model** out) {
   if (m->dt == DT_BF16) {
     m->wT = D(m->wT_bytes);
     const int64_t Tc64 = V > 0 ? m->Tc : 0;
-    // the dW products read the upstream gradient and the activation transposed (the NT kernel
-    // with transposes measured as fast as the TN kernel reading them as stored, at these shapes)
+    // transposed operands of the weight-gradient products run in the GEMM's NT layout (dgu^T is
+    // written by the SwiGLU backward)
     m->yT = D(std::max<int64_t>(T * std::max<int64_t>(2 * F, std::max<int64_t>(QKV, H)), Tc64 * V) * 2);
     m->xT = D(std::max<int64_t>(T * std::max<int64_t>(F, std::max<int64_t>(nqd, H)), Tc64 * H) * 2);
     if (V > 0) m->woutT = D(V * H * 2);
@@ -1046,6 +1046,31 @@ static Gemm nt(int M, int N, int K, const void* A, int64_t lda, const void* B, i
   return g;
 }
 
+// Whether a weight gradient Y^T X of token-major bf16 activations Y [T, M], X [T, N] can run in
+// the GEMM's TN layout, reading both as stored (K = T a multiple of 64, 16-byte rows and bases,
+// byte offsets within 32 bits).
+static bool dw_tn_ok(int M, int N, int T, const void* Y, int64_t ldy, const void* X, int64_t ldx) {
+  return T % 64 == 0 && M % 8 == 0 && N % 8 == 0 && ldy % 8 == 0 && ldx % 8 == 0 &&
+         (((uintptr_t)Y | (uintptr_t)X) % 16) == 0 && (uint64_t)T * ldy * 2 < (1ull << 32) &&
+         (uint64_t)T * ldx * 2 < (1ull << 32);
+}
+
+// G [M, N] (fp32, row stride ldg) = Y^T X: the TN layout when asked for (tn) and dw_tn_ok, else
+// both operands transposed into yT / xT for the NT layout (the same products, bit for bit, and
+// the same split tail). The TN layout reads each fragment with two transposing LDS reads instead
+// of one, and runs 7-24 % slower than NT on the LLaMA-8B weight-gradient shapes; it pays where
+// the two transposes cost more than that (the o and q/k/v products: 2 x 134 MB and 201 + 134 MB
+// transposed for 0.5-0.7 ms products), not for w_down, w_gate|w_up or the LM head.
+static int dw_bf16(hol_model* m, int M, int N, int T, const void* Y, int64_t ldy, const void* X, int64_t ldx, float* G,
+                   int64_t ldg, bool tn) {
+  if (tn && dw_tn_ok(M, N, T, Y, ldy, X, ldx))
+    return run_gemm_dw(m, gemm(M, N, T, Y, ldy, true, X, ldx, true, G, ldg, DT_BF16, DT_F32, EPI_STORE));
+  int e = tr(m, Y, ldy, m->yT, T, T, M);
+  if (!e) e = tr(m, X, ldx, m->xT, T, T, N);
+  if (!e) e = run_gemm_dw(m, nt(M, N, T, m->yT, T, m->xT, T, G, ldg, DT_F32));
+  return e;
+}
+
 // Transposes the resident layer's weights into m->wT (same sub-tensor offsets as the slot):
 // Wqkv^T [H, QKV], Wo^T [nqd, H], and for a dense MLP Wgu^T [H, 2F], Wd^T [F, H].
 static hol_status transpose_layer_weights(hol_model* m, const W& w) {
@@ -1090,9 +1115,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
     m->dhb_current = true;
     KCHECK(run_gemm(m, nt(T, F, H, m->dhb, H, WdT, H, m->da, F, dt)));
     if (tw) {
-      KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));   // dh^T [H, T]
-      KCHECK(tr(m, A.a, F, m->xT, T, T, F));      // a^T [F, T]
-      KCHECK(run_gemm_dw(m, nt(H, F, T, m->yT, T, m->xT, T, G + m->g_wd, F, DT_F32)));
+      KCHECK(dw_bf16(m, H, F, T, m->dhb, H, A.a, F, G + m->g_wd, F, false));  // dWd = dh^T a
       if (m->pieces_armed) HCHECK(hipEventRecord(m->ev_wd_final, s));  // w_down final
     }
     // (with weight gradients the SwiGLU backward also writes dgu^T for the dWgu product)
@@ -1123,11 +1146,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
   } else {
     KCHECK(run_gemm(m, nt(T, nqd, H, m->dhb, H, WoT, H, m->dO, nqd, dt)));
   }
-  if (tw) {
-    KCHECK(tr(m, m->dhb, H, m->yT, T, T, H));
-    KCHECK(tr(m, A.o, nqd, m->xT, T, T, nqd));
-    KCHECK(run_gemm_dw(m, nt(H, nqd, T, m->yT, T, m->xT, T, G + m->g_wo, nqd, DT_F32)));
-  }
+  if (tw) KCHECK(dw_bf16(m, H, nqd, T, m->dhb, H, A.o, nqd, G + m->g_wo, nqd, true));  // dWo = dh1^T o
   Attn at;
   at.n_seq = n_seq; at.S = S; at.nq = m->nq; at.nkv = m->nkv; at.d = d; at.t = dt;
   at.q = A.qkv; at.k = (uint8_t*)A.qkv + (int64_t)nqd * E; at.v = (uint8_t*)A.qkv + (int64_t)(nqd + m->nkv * d) * E;
@@ -1148,11 +1167,7 @@ static hol_status layer_backward_bf16(hol_model* m, const W& w, const Act& A, co
       STEP_OK(lora_bwd(m, (const uint8_t*)m->dqkv + (int64_t)c0[j] * E, QKV, A.n1, H, H, outd[j], w.lA[j], w.lB[j],
                        G + m->g_lA[j], G + m->g_lB[j], m->dn, H, T));
   }
-  if (tw) {
-    KCHECK(tr(m, m->dqkv, QKV, m->yT, T, T, QKV));
-    KCHECK(tr(m, A.n1, H, m->xT, T, T, H));
-    KCHECK(run_gemm_dw(m, nt(QKV, H, T, m->yT, T, m->xT, T, G + m->g_wqkv, H, DT_F32)));
-  }
+  if (tw) KCHECK(dw_bf16(m, QKV, H, T, m->dqkv, QKV, A.n1, H, G + m->g_wqkv, H, true));  // dWqkv = dqkv^T n1
   KT(KC_RMSNORM, 0, (16.0 + E) * T * H, launch_rmsnorm_bwd(m->dn, hin, w.g1, A.r1, m->dh, true,
                                                              tw ? G + m->g_g1 : nullptr, m->partial, T, H, s, m->dhb));
   m->dhb_current = true;

@@ -566,6 +566,77 @@ static bool n3_buffer_ok(const Gemm& g) {
   return g.batch == 1 && ea < (1ull << 32) && eb < (1ull << 32);
 }
 
+// ------------------------------------------------------------------------------------------
+// TN layout of the NT3 kernel: C = Aᵀ B with both operands stored K-major (A [K][M], B [K][N], row
+// strides lda, ldb), the layout of the weight-gradient products dW = dYᵀ X over saved activations,
+// read as stored (no transposes). Same block, waves, ring, persistence and split tail. A stage holds 64 k-rows
+// of 256 values (512 B) per operand, 16-byte chunk c of row k at physical chunk c ^ 4 (k mod 4).
+// An MFMA fragment (8 consecutive k of one m) is two ds_read_b64_tr_b16: within each 16-lane
+// group, lane 16 g + 4 a + b receives element b of the 8-byte pieces addressed by lanes
+// 16 g + a + 4 j (j = 0..3), so lane 16 g + a + 4 j addresses row k0 + j, columns
+// m0 + 16 (g mod 2) + 4 a .. + 3, and lane l ends with m = m0 + l mod 32, k = k0 + 0..3. The
+// swizzle keeps each half-wave's 4 rows x 64 bytes on distinct banks.
+// ------------------------------------------------------------------------------------------
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+
+typedef short tr8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ tr4_t tr_read(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr4_t*)p);
+}
+
+// fragment of 8 consecutive k: rows k0 .. k0 + 3 at p, k0 + 4 .. k0 + 7 four rows further
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* p) {
+  const tr4_t lo = tr_read(p), hi = tr_read(p + 4 * 256);
+  const tr8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// element offset, inside one operand's stage region, of this lane's transposed-read piece for
+// the 32-wide block at column c0, k-row offset 0 (add 256 k for row k)
+__device__ __forceinline__ int t3_frag_off(int c0, int lane) {
+  const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+  const int col = c0 + 16 * (g & 1) + 4 * a;
+  const int pc = (col >> 3) ^ (4 * j);
+  return (8 * (g >> 1) + j) * 256 + pc * 8 + (col & 4);
+}
+
+// Stage loads: instruction q = w + NW i fills stage rows 2 q, 2 q + 1 (1 KB) of an operand;
+// lane: row 2 q + lane / 32, physical chunk lane % 32 = logical chunk (lane % 32) ^ 4 (row % 4).
+// Columns past M (N) are clamped (their products land in rows that are not stored).
+template <int NW>
+struct T3Buf {
+  uint32_t va[32 / NW], vb[32 / NW];
+  __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int r = 2 * (w + NW * i) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (r & 3));
+      va[i] = (uint32_t)(((int64_t)r * lda + min(m0 + 8 * c, M - 8)) * 2);
+      vb[i] = (uint32_t)(((int64_t)r * ldb + min(n0 + 8 * c, N - 8)) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t sa,
+                                        uint32_t sb) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar LDS destinations
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + (w + NW * i) * 512), 16, va[i], (int)sa, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + 64 * 256 + (w + NW * i) * 512), 16, vb[i],
+                                               (int)sb, 0, 0);
+  }
+};
+
+// Whether every byte of A and B lies within an unsigned 32-bit offset of its base.
+static bool t3_buffer_ok(const Gemm& g) {
+  const uint64_t ea = (uint64_t)g.K * (uint64_t)g.lda * 2, eb = (uint64_t)g.K * (uint64_t)g.ldb * 2;
+  return g.batch == 1 && ea < (1ull << 32) && eb < (1ull << 32);
+}
+
+
 // GRP: one launch over groups of rows (the experts of a mixture-of-experts layer). The table gives
 // each group's first row and first row tile; the grid is an upper bound, the real tile count is
 // read from the table, dealt in 8 equal contiguous ranges (one per XCD) with the surplus blocks
@@ -735,19 +806,21 @@ __device__ __forceinline__ void n3_store_rope(const Gemm& g, const f32x16 (&acc)
 // reads spread over the step they have ≈6 MFMAs to land (2.5–3 % over the decoder shapes,
 // bitwise the same products). Off for the global_load_lds path (operands past 4 GiB), where the
 // longer-lived fragments would push more registers to scratch.
-template <bool ON>
+// (RD: LDS reads per fragment, 2 in the TN layout)
+template <bool ON, int RD = 1>
 __device__ __forceinline__ void n3_interleave() {
   if constexpr (ON) {
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);  // one fragment's LDS reads
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
 }
 
-template <int EPI, typename TO, int NW, bool BUF, bool GRP, int PM = PM_NONE, bool SPL = false>
+// TN: both operands K-major (the TN layout above); buffer path only, no groups, no pair modes.
+template <int EPI, typename TO, int NW, bool BUF, bool GRP, int PM = PM_NONE, bool SPL = false, bool TN = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   constexpr int WJ = NW == 4 ? 4 : 2;  // 32-column blocks per wave
   static_assert(NW == 8, "the epilogue count below assumes 8 waves");
@@ -840,31 +913,50 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
 
   static_assert(PM == PM_NONE || (EPI == EPI_STORE && sizeof(TO) == 2 && !GRP && WJ == 2), "pair modes: bf16 store, one group");
   static_assert(!SPL || (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP && PM == PM_NONE), "split tail: fp32 store, one group");
+  static_assert(!TN || (BUF && !GRP && PM == PM_NONE), "TN layout: buffer path, one group, no pair mode");
   constexpr bool SW = PM == PM_SWIGLU;
   const int pp = PM == PM_SWIGLU ? N >> 1 : (PM == PM_ROPE ? g.rope_nr : 0);
   int nk = (kend - kbeg) / N3_BK;
   N3Buf<NW, PM> nb;
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)M * g.lda * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)N * g.ldb * 2), 0x00020000);
+  T3Buf<NW> tb;
+  const int64_t ea = TN ? (int64_t)K * g.lda * 2 : (int64_t)M * g.lda * 2;
+  const int64_t eb = TN ? (int64_t)K * g.ldb * 2 : (int64_t)N * g.ldb * 2;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)ea, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)eb, 0x00020000);
   auto issue = [&](bf16* stage, int k0) {  // k0 relative to the item's first k
-    if constexpr (BUF) nb.issue(stage, ra, rb, kbeg + k0);
+    if constexpr (TN) tb.issue(stage, ra, rb, (uint32_t)((kbeg + k0) * g.lda * 2), (uint32_t)((kbeg + k0) * g.ldb * 2));
+    else if constexpr (BUF) nb.issue(stage, ra, rb, kbeg + k0);
     else n3_issue<NW, PM>(stage, A, g.lda, m0, M, B, g.ldb, n0, N, kbeg + k0, pp);
   };
   auto start_tile = [&]() {
-    if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N, pp);
+    if constexpr (TN) tb.init(g.lda, m0, M, g.ldb, n0, N);
+    else if constexpr (BUF) nb.init(g.lda, m0, M, g.ldb, n0, N, pp);
     issue(lds, 0);
     if (nk > 1) issue(lds + N3_TILE, N3_BK);
   };
+  // TN: this lane's transposed-read offsets inside a stage (A region, then B at 64 x 256)
+  int fa[4], fb[WJ];
+  if constexpr (TN) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = t3_frag_off(wm * 128 + i * 32, lane);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) fb[j] = 64 * 256 + t3_frag_off(wn * 32 * WJ + j * 32, lane);
+  }
   bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
   auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
-    const bf16* Bs = st + N2_BM * N3_BK;
-    const int c = kk * 2 + (lane >> 5);
+    if constexpr (TN) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + n3_off(wm * 128 + i * 32 + (lane & 31), c));
+      for (int i = 0; i < 4; ++i) a[i] = tr_frag(st + fa[i] + kk * 16 * 256);
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) b[j] = *(const bf16x8*)(Bs + n3_off(wn * 32 * WJ + j * 32 + (lane & 31), c));
+      for (int j = 0; j < WJ; ++j) b[j] = tr_frag(st + fb[j] + kk * 16 * 256);
+    } else {
+      const bf16* Bs = st + N2_BM * N3_BK;
+      const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + n3_off(wm * 128 + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) b[j] = *(const bf16x8*)(Bs + n3_off(wn * 32 * WJ + j * 32 + (lane & 31), c));
+    }
   };
   auto mma = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
@@ -893,13 +985,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       const bf16* st = lds + (kt & 1) * N3_TILE;
       frags(st, 1, a1, b1);
       mma(a0, b0);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
       frags(st, 2, a0, b0);
       mma(a1, b1);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
       frags(st, 3, a1, b1);
       mma(a0, b0);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
       // stage kt + 1 is the only load in flight (for the first stage of a tile, behind it at
       // most the previous epilogue's memory operations); once every wave has also finished
       // reading this slot, it takes stage kt + 2
@@ -909,19 +1001,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
       if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, (kt + 2) * N3_BK);
       frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
       mma(a1, b1);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
     }
     {  // the tile's last stage
       const bf16* st = lds + ((nk - 1) & 1) * N3_TILE;
       frags(st, 1, a1, b1);
       mma(a0, b0);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
       frags(st, 2, a0, b0);
       mma(a1, b1);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
       frags(st, 3, a1, b1);
       mma(a0, b0);
-      n3_interleave<BUF>();
+      n3_interleave<BUF, TN ? 2 : 1>();
       mma(a1, b1);
     }
     // next tile: its first two stages go up before this tile's results go out
@@ -963,188 +1055,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_nt3(Gemm g) {
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// TN3: C = Aᵀ B with both operands stored K-major (A [K][M], B [K][N], row strides lda, ldb), the
-// layout of the weight-gradient products dW = dYᵀ X over saved activations, read as stored (no
-// transposes). The 256 x 256 x 64 block, 8 waves and 2-slot ring of NT3. A stage holds 64 k-rows
-// of 256 values (512 B) per operand, 16-byte chunk c of row k at physical chunk c ^ 4 (k mod 4).
-// An MFMA fragment (8 consecutive k of one m) is two ds_read_b64_tr_b16: within each 16-lane
-// group, lane 16 g + 4 a + b receives element b of the 8-byte pieces addressed by lanes
-// 16 g + a + 4 j (j = 0..3), so lane 16 g + a + 4 j addresses row k0 + j, columns
-// m0 + 16 (g mod 2) + 4 a .. + 3, and lane l ends with m = m0 + l mod 32, k = k0 + 0..3. The
-// swizzle keeps each half-wave's 4 rows x 64 bytes on distinct banks.
-// ------------------------------------------------------------------------------------------
-typedef short tr4_t __attribute__((ext_vector_type(4)));
-
-typedef short tr8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ tr4_t tr_read(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr4_t*)p);
-}
-
-// fragment of 8 consecutive k: rows k0 .. k0 + 3 at p, k0 + 4 .. k0 + 7 four rows further
-__device__ __forceinline__ bf16x8 tr_frag(const bf16* p) {
-  const tr4_t lo = tr_read(p), hi = tr_read(p + 4 * 256);
-  const tr8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, x);
-}
-
-// element offset, inside one operand's stage region, of this lane's transposed-read piece for
-// the 32-wide block at column c0, k-row offset 0 (add 256 k for row k)
-__device__ __forceinline__ int t3_frag_off(int c0, int lane) {
-  const int g = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
-  const int col = c0 + 16 * (g & 1) + 4 * a;
-  const int pc = (col >> 3) ^ (4 * j);
-  return (8 * (g >> 1) + j) * 256 + pc * 8 + (col & 4);
-}
-
-// Stage loads: instruction q = w + NW i fills stage rows 2 q, 2 q + 1 (1 KB) of an operand;
-// lane: row 2 q + lane / 32, physical chunk lane % 32 = logical chunk (lane % 32) ^ 4 (row % 4).
-// Columns past M (N) are clamped (their products land in rows that are not stored).
-template <int NW>
-struct T3Buf {
-  uint32_t va[32 / NW], vb[32 / NW];
-  __device__ __forceinline__ void init(int64_t lda, int m0, int M, int64_t ldb, int n0, int N) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < 32 / NW; ++i) {
-      const int r = 2 * (w + NW * i) + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (r & 3));
-      va[i] = (uint32_t)(((int64_t)r * lda + min(m0 + 8 * c, M - 8)) * 2);
-      vb[i] = (uint32_t)(((int64_t)r * ldb + min(n0 + 8 * c, N - 8)) * 2);
-    }
-  }
-  __device__ __forceinline__ void issue(bf16* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t sa,
-                                        uint32_t sb) const {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar LDS destinations
-#pragma unroll
-    for (int i = 0; i < 32 / NW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + (w + NW * i) * 512), 16, va[i], (int)sa, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 32 / NW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + 64 * 256 + (w + NW * i) * 512), 16, vb[i],
-                                               (int)sb, 0, 0);
-  }
-};
-
-// Whether every byte of A and B lies within an unsigned 32-bit offset of its base.
-static bool t3_buffer_ok(const Gemm& g) {
-  const uint64_t ea = (uint64_t)g.K * (uint64_t)g.lda * 2, eb = (uint64_t)g.K * (uint64_t)g.ldb * 2;
-  return g.batch == 1 && ea < (1ull << 32) && eb < (1ull << 32);
-}
-
-template <int EPI, typename TO, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_tn3(Gemm g) {
-  constexpr int WJ = NW == 4 ? 4 : 2;
-  constexpr int RA = 64 * 256;  // elements of one operand's stage region
-  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * N3_TILE];
-  const int M = g.M, N = g.N, K = g.K;
-  const bf16* __restrict__ A = (const bf16*)g.A;
-  const bf16* __restrict__ B = (const bf16*)g.B;
-  TO* C = (TO*)g.C;
-  const float* R = g.R;
-  const int tiles_m = (M + N2_BM - 1) / N2_BM, tiles_n = (N + N2_BN - 1) / N2_BN;
-  const int ntiles = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-  const int GM = 4;
-  const int group = GM * tiles_n;
-  const int first_m = (pid / group) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (pid % group) % gsz;
-  const int tn = (pid % group) / gsz;
-  const int m0 = tm * N2_BM, n0 = tn * N2_BN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w / (NW / 2), wn = w % (NW / 2);
-  f32x16 acc[4][WJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < WJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  T3Buf<NW> tb;
-  tb.init(g.lda, m0, M, g.ldb, n0, N);
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(uint32_t)((int64_t)K * g.lda * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(uint32_t)((int64_t)K * g.ldb * 2), 0x00020000);
-  const uint32_t sa = (uint32_t)(g.lda * 2 * N3_BK), sb = (uint32_t)(g.ldb * 2 * N3_BK);  // bytes per stage
-  auto issue = [&](bf16* stage, int kt) { tb.issue(stage, ra, rb, kt * sa, kt * sb); };
-  int fa[4], fb[WJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = t3_frag_off(wm * 128 + i * 32, lane);
-#pragma unroll
-  for (int j = 0; j < WJ; ++j) fb[j] = RA + t3_frag_off(wn * 32 * WJ + j * 32, lane);
-
-  const int nk = K / N3_BK;
-  issue(lds, 0);
-  if (nk > 1) issue(lds + N3_TILE, 1);
-  bf16x8 a0[4], b0[WJ], a1[4], b1[WJ];
-  auto frags = [&](const bf16* st, int kk, bf16x8* a, bf16x8* b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = tr_frag(st + fa[i] + kk * 16 * 256);
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) b[j] = tr_frag(st + fb[j] + kk * 16 * 256);
-  };
-  auto mma = [&](const bf16x8* a, const bf16x8* b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-  };
-  if (nk > 1) {
-    if constexpr (NW == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  frags(lds, 0, a0, b0);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const bf16* st = lds + (kt & 1) * N3_TILE;
-    frags(st, 1, a1, b1);
-    mma(a0, b0);
-    frags(st, 2, a0, b0);
-    mma(a1, b1);
-    frags(st, 3, a1, b1);
-    mma(a0, b0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 2 < nk) issue(lds + (kt & 1) * N3_TILE, kt + 2);
-    frags(lds + ((kt + 1) & 1) * N3_TILE, 0, a0, b0);
-    mma(a1, b1);
-  }
-  {  // the last stage, peeled (as in the NT kernel)
-    const bf16* st = lds + ((nk - 1) & 1) * N3_TILE;
-    frags(st, 1, a1, b1);
-    mma(a0, b0);
-    frags(st, 2, a0, b0);
-    mma(a1, b1);
-    frags(st, 3, a1, b1);
-    mma(a0, b0);
-    mma(a1, b1);
-  }
-  n3_store<EPI, TO, WJ>(g, acc, C, R, M, N, m0, n0, wm, wn, lane);
-}
-
-template __global__ void gemm_tn3<EPI_STORE, float, 8>(Gemm);
-template __global__ void gemm_tn3<EPI_STORE, bf16, 8>(Gemm);
-template __global__ void gemm_tn3<EPI_ACCUM, float, 8>(Gemm);
-template __global__ void gemm_tn3<EPI_RESID, float, 8>(Gemm);
-
-template <int EPI, typename TO>
-static int launch_tn3_t(const Gemm& g, hipStream_t s) {
-  const int tiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
-  hipLaunchKernelGGL((gemm_tn3<EPI, TO, 8>), dim3(tiles), dim3(512), 0, s, g);
-  return (int)hipGetLastError();
-}
-
-static int launch_tn3(const Gemm& g, hipStream_t s) {
-  if (g.epi == EPI_STORE) return g.c == DT_BF16 ? launch_tn3_t<EPI_STORE, bf16>(g, s) : launch_tn3_t<EPI_STORE, float>(g, s);
-  if (g.epi == EPI_ACCUM) return launch_tn3_t<EPI_ACCUM, float>(g, s);
-  return launch_tn3_t<EPI_RESID, float>(g, s);
-}
-
 constexpr int NT3_WAVES = 8;
 // (explicit instantiations: the host pass does not always emit the launch stubs of the
 // buffer-path instantiations on its own)
@@ -1165,6 +1075,11 @@ template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, PM_S
 template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, PM_ROPE>(Gemm);
 template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, false, false, PM_ROPE>(Gemm);
 template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, bf16, NT3_WAVES, true, false, PM_NONE, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_ACCUM, float, NT3_WAVES, true, false, PM_NONE, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_RESID, float, NT3_WAVES, true, false, PM_NONE, false, true>(Gemm);
+template __global__ void gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, true, true>(Gemm);
 
 // Sum of the parts of the split tiles (gemm_nt3 with SPL): one block per split tile; thread t
 // owns columns 4 (t mod 64) .. + 3 of rows t / 64 + 4 i. Parts are added in order 0, 1, ... so the
@@ -1218,7 +1133,8 @@ static int n3_persistent_grid(int ntiles) {
 // parts (r f <= c, K % 64 f == 0), so the last round runs r f part tiles instead of r whole
 // ones. Returns false when the plan does not apply.
 static bool n3_split_plan(const Gemm& g, int grid, Gemm& out) {
-  if (!g.ws || g.batch != 1 || g.epi != EPI_STORE || g.c != DT_F32 || !n3_buffer_ok(g)) return false;
+  if (!g.ws || g.batch != 1 || g.epi != EPI_STORE || g.c != DT_F32 || !(g.a_km ? t3_buffer_ok(g) : n3_buffer_ok(g)))
+    return false;
   const int ntiles = ((g.M + N2_BM - 1) / N2_BM) * ((g.N + N2_BN - 1) / N2_BN);
   if (ntiles % 8 || grid % 8) return false;
   const int c = grid / 8, n = ntiles / 8, R = n / c, r = n % c;
@@ -1232,7 +1148,8 @@ static bool n3_split_plan(const Gemm& g, int grid, Gemm& out) {
   return true;
 }
 
-template <int EPI, typename TO, bool GRP>
+// TN: both operands K-major (checked by the caller: buffer path, M and N multiples of 8)
+template <int EPI, typename TO, bool GRP, bool TN = false>
 static int launch_nt3_t(const Gemm& g, hipStream_t s) {
   const int tn = (g.N + N2_BN - 1) / N2_BN;
   // grouped: an upper bound of the tile count rounded up to the 8 XCD ranges
@@ -1241,26 +1158,29 @@ static int launch_nt3_t(const Gemm& g, hipStream_t s) {
   if constexpr (EPI == EPI_STORE && sizeof(TO) == 4 && !GRP) {
     Gemm gs;
     if (n3_split_plan(g, tiles, gs)) {
-      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, true>), dim3(tiles), dim3(64 * NT3_WAVES),
-                         0, s, gs);
+      hipLaunchKernelGGL((gemm_nt3<EPI_STORE, float, NT3_WAVES, true, false, PM_NONE, true, TN>), dim3(tiles),
+                         dim3(64 * NT3_WAVES), 0, s, gs);
       const int nsplit = (((g.M + N2_BM - 1) / N2_BM) * tn / 8 - gs.spl_full) * 8;
       hipLaunchKernelGGL(gemm_split_reduce_k, dim3(nsplit), dim3(256), 0, s, gs);
       return (int)hipGetLastError();
     }
   }
-  if (n3_buffer_ok(g))
+  if constexpr (TN)
+    hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true, false, PM_NONE, false, true>), dim3(tiles), dim3(64 * NT3_WAVES),
+                       0, s, g);
+  else if (n3_buffer_ok(g))
     hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, true, GRP>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
   else
     hipLaunchKernelGGL((gemm_nt3<EPI, TO, NT3_WAVES, false, GRP>), dim3(tiles, g.batch), dim3(64 * NT3_WAVES), 0, s, g);
   return (int)hipGetLastError();
 }
 
-template <bool GRP>
+template <bool GRP, bool TN = false>
 static int launch_nt3(const Gemm& g, hipStream_t s) {
   if (g.epi == EPI_STORE)
-    return g.c == DT_BF16 ? launch_nt3_t<EPI_STORE, bf16, GRP>(g, s) : launch_nt3_t<EPI_STORE, float, GRP>(g, s);
-  if (g.epi == EPI_ACCUM) return launch_nt3_t<EPI_ACCUM, float, GRP>(g, s);
-  return launch_nt3_t<EPI_RESID, float, GRP>(g, s);
+    return g.c == DT_BF16 ? launch_nt3_t<EPI_STORE, bf16, GRP, TN>(g, s) : launch_nt3_t<EPI_STORE, float, GRP, TN>(g, s);
+  if (g.epi == EPI_ACCUM) return launch_nt3_t<EPI_ACCUM, float, GRP, TN>(g, s);
+  return launch_nt3_t<EPI_RESID, float, GRP, TN>(g, s);
 }
 
 int launch_gemm_grouped(const Gemm& g, hipStream_t s) {
@@ -1412,7 +1332,7 @@ int launch_gemm(const Gemm& g, hipStream_t s) {
       if (!g.a_km && !g.b_kn) return launch_mfma_l<false, false>(g, s);
       if (!g.a_km && g.b_kn) return launch_mfma_l<false, true>(g, s);
       if (g.a_km && g.b_kn && g.K % N3_BK == 0 && g.M % 8 == 0 && g.N % 8 == 0 && t3_buffer_ok(g))
-        return launch_tn3(g, s);
+        return launch_nt3<false, true>(g, s);
       if (g.a_km && g.b_kn) return launch_mfma_l<true, true>(g, s);
       return launch_mfma_l<true, false>(g, s);
     }

@@ -31,8 +31,9 @@ hol_status hol_op_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t l
                        float alpha, void* stream);
 
 /* hol_op_gemm with an fp32 device workspace of workspace_floats floats (at most
- * hol_op_gemm_workspace_floats() are used; 0 / NULL: exactly hol_op_gemm). With it, a bf16 NT
- * product with an fp32 store (EPI_STORE) whose 256 x 256 tiles leave the last round of the
+ * hol_op_gemm_workspace_floats() are used; 0 / NULL: exactly hol_op_gemm). With it, a bf16
+ * product in the NT layout, or with both operands K-major (a_km = b_kn = 1: the weight-gradient
+ * layout), with an fp32 store (EPI_STORE) whose 256 x 256 tiles leave the last round of the
  * persistent grid at most half full (every XCD with R >= 1 full rounds and r <= half a round of
  * tiles left) cuts those r tiles along K into 2 or 4 parts, runs the parts in the last round and
  * adds them in part order in a second kernel: the weight-gradient products dW = dY^T X of the

@@ -28,7 +28,7 @@ from tests.gpu_helpers import lib_fb, lib_model, oracle_fb, rel_l2  # noqa: E402
 from tests.test_gpu_moe_lora import MOE_FULL_BF16, MOE_LORA_BF16, bf16_weights as moe_bf16_weights  # noqa: E402
 from tests.test_gpu_moe_lora import run_parity  # noqa: E402
 from tests.test_gpu_model import SCORE_INPUTS  # noqa: E402
-from tests.test_gpu_ops import dev, gemm_case, host, sync  # noqa: E402
+from tests.test_gpu_ops import bf, dev, gemm_case, host, sync  # noqa: E402
 
 DEV = "cuda"
 
@@ -146,6 +146,43 @@ def test_gemm_persistent_many_tiles(K, epi, out_bf16):
     tol = 2 ** -8 if out_bf16 else 1e-5
     err = np.abs(got - ref) / (np.abs(ref) + 8)
     assert np.max(err) < tol, np.unravel_index(np.argmax(err), err.shape)
+
+
+# the TN layout (both operands K-major, the weight-gradient products) through the same persistent
+# kernel: 18 x 17 tiles, ragged last row and column (M, N multiples of 8 as that layout needs)
+@pytest.mark.parametrize("K", [192, 64])
+@pytest.mark.parametrize("epi,out_bf16", [(0, False), (0, True), (1, False), (2, False)])
+def test_gemm_persistent_many_tiles_tn(K, epi, out_bf16):
+    got, ref = gemm_case(4392, 4304, K, 1, 1, hol.BF16, epi, seed=K + 10 * epi + out_bf16 + 3, out_bf16=out_bf16)
+    tol = 2 ** -8 if out_bf16 else 1e-5
+    err = np.abs(got - ref) / (np.abs(ref) + 8)
+    assert np.max(err) < tol, np.unravel_index(np.argmax(err), err.shape)
+
+
+def test_gemm_tn_equals_nt_on_transposed_operands_bitwise():
+    """dW = dY^T X read as stored (TN) and from transposed copies (NT): the same fragments reach
+    the same MFMAs in the same order, with and without the split-tail workspace."""
+    T, M, N = 1024, 6144, 4096  # 24 x 16 = 384 tiles: one full round plus a split tail
+    r = np.random.default_rng(8)
+    y = dev(r.standard_normal((T, M)), torch.bfloat16)
+    x = dev(r.standard_normal((T, N)), torch.bfloat16)
+    yt, xt = y.t().contiguous(), x.t().contiguous()
+    wsn = hol.lib.hol_op_gemm_workspace_floats()
+    ws = torch.zeros((wsn,), device=DEV)
+    for use_ws in (False, True):
+        c_tn = torch.zeros((M, N), device=DEV)
+        c_nt = torch.zeros((M, N), device=DEV)
+        w, n = (ws.data_ptr(), wsn) if use_ws else (None, 0)
+        hol.check(hol.lib.hol_op_gemm_ws(M, N, T, y.data_ptr(), M, 1, x.data_ptr(), N, 1, c_tn.data_ptr(), N, None, 0,
+                                         hol.BF16, hol.F32, 0, 1.0, w, n, None))
+        hol.check(hol.lib.hol_op_gemm_ws(M, N, T, yt.data_ptr(), T, 0, xt.data_ptr(), T, 0, c_nt.data_ptr(), N, None, 0,
+                                         hol.BF16, hol.F32, 0, 1.0, w, n, None))
+        sync()
+        assert torch.equal(c_tn, c_nt), use_ws
+    rows = np.arange(0, M, 97)
+    ref = bf(host(y).astype(np.float32))[:, rows].T @ bf(host(x).astype(np.float32))
+    got = host(c_tn)[rows]
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + math.sqrt(T))) < 1e-5
 
 
 def test_gemm_persistent_long_walk():
