@@ -157,8 +157,10 @@ def gemm_table(w: W.Workload, st_list, steps):
 def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
     """The workload's decoder GEMMs one shape at a time, as the step launches them: fp32 out;
     bf16 out for the down-projection and o data gradients; residual epilogue for the o and down
-    projections; the gate/up forward with its SwiGLU epilogue (hol_op_gemm_swiglu); the weight
-    gradients with the split-tail workspace (hol_op_gemm_ws). In the order listed, `reps` launches
+    projections; the q/k/v forward with its RoPE epilogue (hol_op_gemm_rope, bf16 out); the
+    gate/up forward with its SwiGLU epilogue (hol_op_gemm_swiglu); the weight gradients with the
+    split-tail workspace (hol_op_gemm_ws), the o and q/k/v ones reading both operands K-major as
+    the step does (the others over transposed copies, NT). In the order listed, `reps` launches
     each after one warm-up launch."""
     s = w.shape
     T, H, d = w.tokens, s.hidden, s.head_dim
@@ -173,11 +175,17 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
     stream = torch.cuda.current_stream()
     wsn = hol.lib.hol_op_gemm_workspace_floats()
     ws = torch.empty((wsn,), device="cuda")
+    S, n_rot = w.seq, (s.n_q_heads + s.n_kv_heads) * d
+    cos_t = torch.rand((S, d // 2), device="cuda")
+    sin_t = torch.rand((S, d // 2), device="cuda")
     rows = []
     for name, M, N, K, epi, bf in shapes:
-        a = torch.randn((M, K), device="cuda").to(torch.bfloat16)
-        b = torch.randn((N, K), device="cuda").to(torch.bfloat16)
-        c = torch.empty((M, N), device="cuda", dtype=torch.bfloat16 if bf else torch.float32)
+        km = name in ("a7 o dW", "a4 qkv dW")  # both operands K-major ([K][M], [K][N])
+        a = torch.randn((K, M) if km else (M, K), device="cuda").to(torch.bfloat16)
+        b = torch.randn((K, N) if km else (N, K), device="cuda").to(torch.bfloat16)
+        lda, ldb = (M, N) if km else (K, K)
+        rope = name == "a4 qkv fwd" and d == 128
+        c = torch.empty((M, N), device="cuda", dtype=torch.bfloat16 if (bf or rope) else torch.float32)
         r = torch.randn((M, N), device="cuda") if epi == 2 else None
         act = torch.empty((M, N // 2), device="cuda", dtype=torch.bfloat16) if name.startswith("a9 gate/up fwd") else None
         dw = name.endswith("dW")
@@ -187,8 +195,12 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
                 hol.check(hol.lib.hol_op_gemm_swiglu(M, N, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), N,
                                                      act.data_ptr(), N // 2, hol.BF16, stream.cuda_stream))
                 return
-            hol.check(hol.lib.hol_op_gemm_ws(M, N, K, a.data_ptr(), K, 0, b.data_ptr(), K, 0, c.data_ptr(), N,
-                                             r.data_ptr() if r is not None else None, N, hol.BF16,
+            if rope:
+                hol.check(hol.lib.hol_op_gemm_rope(M, N, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), N, n_rot, S,
+                                                   cos_t.data_ptr(), sin_t.data_ptr(), stream.cuda_stream))
+                return
+            hol.check(hol.lib.hol_op_gemm_ws(M, N, K, a.data_ptr(), lda, int(km), b.data_ptr(), ldb, int(km),
+                                             c.data_ptr(), N, r.data_ptr() if r is not None else None, N, hol.BF16,
                                              hol.BF16 if bf else hol.F32, epi, 1.0,
                                              ws.data_ptr() if dw else None, wsn if dw else 0, stream.cuda_stream))
 
