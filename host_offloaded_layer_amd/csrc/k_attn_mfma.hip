@@ -561,6 +561,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_mfma(Attn a) {
 // sw(r) = 4 (r mod 4) + (r / 4) mod 4, which keeps both the score products' row reads (16 rows at
 // one chunk) and the transposed reads (4 rows over 4 chunks) on distinct banks.
 // ------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* fa_lptr;
+typedef __attribute__((address_space(1))) const void* fa_gptr;
 __device__ __forceinline__ int qsw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 __device__ __forceinline__ int qoff(int r, int c) { return r * 128 + (((c >> 3) ^ qsw(r)) << 3) + (c & 7); }
 
@@ -1028,8 +1030,8 @@ __global__ __launch_bounds__(512, 1) void attn_dq_tr128(Attn a) {
 // ds_read_b64_tr_b16.
 __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
   constexpr int D = 128, BQ = 128, BK = 64, KT = BK * D;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2 * KT];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2 * KT];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2 * KT];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2 * KT];
   const int S = a.S;
   const int nqt = (S + BQ - 1) / BQ;
   const int group = a.nq / a.nkv;
@@ -1070,105 +1072,110 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_tr128(Attn a) {
   const int nkt = qmax / BK + 1;
   const int wave_qmax = min(q0 + 32 * w + 31, S - 1);
 
-  NatTile<BK, D> kreg, vreg;
-  NatOff<BK, D> koff, voff;
-  koff.init(a.ldk);
-  voff.init(a.ldv);
-  auto fetch = [&](int kt) {
+  // Tiles go straight into LDS (no register staging): instruction i of wave w fills rows
+  // 4 (w + 4 i) .. + 3 of a 64-row tile (1 KB); lane l takes row 4 (w + 4 i) + l / 16, physical
+  // 16-byte chunk l % 16, i.e. logical chunk (l % 16) ^ qsw(row); rows past S are clamped.
+  auto load_tile = [&](bf16* dst, const bf16* src, int64_t ld, int kt) {
     const int k0 = kt * BK;
-    if (k0 + BK <= S) {  // (scalar branch)
-      koff.load(kreg, K + (base + k0) * a.ldk);
-      voff.load(vreg, V + (base + k0) * a.ldv);
-    } else {
-      kreg.load(K, a.ldk, base + k0, S - k0);
-      vreg.load(V, a.ldv, base + k0, S - k0);
-    }
-  };
-  auto put = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < NatTile<BK, D>::N; ++i) {
-      const int c = threadIdx.x + 256 * i, r = c >> 4, ch = c & 15;
-      const int off = b * KT + r * 128 + ((ch ^ qsw(r)) << 3);
-      *(u32x4*)(Ks + off) = kreg.v[i];
-      *(u32x4*)(Vs + off) = vreg.v[i];
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * (w + 4 * i) + (lane >> 4);
+      const int c = (lane & 15) ^ qsw(r);
+      const int rr = min(r, S - 1 - k0);
+      __builtin_amdgcn_global_load_lds((fa_gptr)(src + (base + k0 + rr) * ld + c * 8), (fa_lptr)(dst + 4 * (w + 4 * i) * 128),
+                                       16, 0, 0);
     }
   };
-  fetch(0);
-  put(0);
-  if (nkt > 1) fetch(1);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
+  // the unscaled scores of a tile: s[kb][r] = score(key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi)
+  auto scores = [&](f32x16* s, const bf16* Kc) {
+    zero(s[0]);
+    zero(s[1]);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *(const bf16x8*)(Kc + qoff(kb * 32 + lq, 16 * kk + 8 * hh));
+        s[kb] = mfma(kf, qf[kk], s[kb]);
+      }
+  };
+  // Software pipeline: iteration kt computes the scores of tile kt + 1 among the exponentials of
+  // tile kt, so the matrix unit works beside the vector unit (+5-8 % at 4K-16K tokens, the same
+  // bits). K buffer kt % 2 takes tile kt + 2 once every wave has the scores of tile kt; V buffer
+  // (kt + 1) % 2 takes tile kt + 1 once every wave is past the products of tile kt - 1; both are
+  // issued at the start of iteration kt, so each tile has one iteration to land.
+  auto step = [&](int kt, f32x16* sc, f32x16* sn) {
     const int k0 = kt * BK, cur = kt & 1;
-    const bf16* Kc = Ks + cur * KT;
-    const bf16* Vc = Vs + cur * KT;
-    if (k0 <= wave_qmax) {  // else every key of this tile is in this wave's future
-      f32x16 s[2];
-      zero(s[0]);
-      zero(s[1]);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *(const bf16x8*)(Kc + qoff(kb * 32 + lq, 16 * kk + 8 * hh));
-          s[kb] = mfma(kf, qf[kk], s[kb]);
-        }
-      }
-      // s[kb][r] = unscaled score(key k0 + 32 kb + 8 (r/4) + 4 hh + r%4, query qi)
-      const bool diag = (k0 + BK - 1 > q0 + 32 * w) || (k0 + BK > S);  // wave-uniform
-      if (diag) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            s[kb][r] = (kj > qi || kj >= S) ? -INFINITY : s[kb][r];
-          }
-      }
-      // the maximum of the unscaled scores (scaling by sl2 > 0 keeps the order), over both
-      // halves of the wave, which hold the same query
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = xhalf_max(mx);
-      const float tm = mx * sl2;
-      if (tm > m + RESCALE_SLACK) {  // the reference moves (m = -inf before the first tile: corr = 0)
-        const float corr = ex2(m - tm);
-        l *= corr;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= corr;
-        m = tm;
-      }
-      // p = 2^(s sl2 - m); four partial row sums
-      float ls4[4] = {0.f, 0.f, 0.f, 0.f};
+    // K of tile kt + 1 and V of tile kt landed; every wave is done with iteration kt - 1
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 2 < nkt) load_tile(Ks + cur * KT, K, a.ldk, kt + 2);
+    if (kt + 1 < nkt) load_tile(Vs + (cur ^ 1) * KT, V, a.ldv, kt + 1);
+    if (k0 > wave_qmax) return;  // every key of this tile is in this wave's future
+    f32x16* s = sc;
+    const bool diag = (k0 + BK - 1 > q0 + 32 * w) || (k0 + BK > S);  // wave-uniform
+    if (diag) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = ex2(fmaf(s[kb][r], sl2, -m));
-          s[kb][r] = p;
-          ls4[r & 3] += p;
+          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          s[kb][r] = (kj > qi || kj >= S) ? -INFINITY : s[kb][r];
         }
-      float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
-      ls = xhalf_sum(ls);
-      l += ls;
-      // O^T[d][q] += V^T[d][key] P^T[key][q]
+    }
+    // the maximum of the unscaled scores (scaling by sl2 > 0 keeps the order), over both halves
+    // of the wave, which hold the same query
+    float mx = -INFINITY;
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const bf16x8 pb = acc_frag(s[ks >> 1], ks & 1);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          o[db] = mfma(tr_pair(Vc + ks * 16 * 128 + toff[0][db], Vc + ks * 16 * 128 + toff[1][db]), pb, o[db]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xhalf_max(mx);
+    const float tm = mx * sl2;
+    if (tm > m + RESCALE_SLACK) {  // the reference moves (m = -inf before the first tile: corr = 0)
+      const float corr = ex2(m - tm);
+      l *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= corr;
+      m = tm;
+    }
+    // the scores of tile kt + 1, in the same block as the exponentials below so that they can
+    // interleave (also when that tile is past this wave's queries or past the sequence: then its
+    // buffer holds stale keys and the scores are never read)
+    scores(sn, Ks + (cur ^ 1) * KT);
+    // p = 2^(s sl2 - m); four partial row sums
+    float ls4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = ex2(fmaf(s[kb][r], sl2, -m));
+        s[kb][r] = p;
+        ls4[r & 3] += p;
       }
+    float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    ls = xhalf_sum(ls);
+    l += ls;
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
+    const bf16* Vc = Vs + cur * KT;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const bf16x8 pb = acc_frag(s[ks >> 1], ks & 1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        o[db] = mfma(tr_pair(Vc + ks * 16 * 128 + toff[0][db], Vc + ks * 16 * 128 + toff[1][db]), pb, o[db]);
     }
-    if (kt + 1 < nkt) {
-      put(cur ^ 1);  // every wave finished reading that buffer before the previous barrier
-      if (kt + 2 < nkt) fetch(kt + 2);
-    }
-    __syncthreads();
+  };
+  load_tile(Ks, K, a.ldk, 0);
+  if (nkt > 1) load_tile(Ks + KT, K, a.ldk, 1);
+  load_tile(Vs, V, a.ldv, 0);
+  if (nkt > 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  // K of tile 0
+  else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  f32x16 sa[2], sb[2];
+  scores(sa, Ks);  // every wave sees tile 0
+  for (int kt = 0; kt < nkt; kt += 2) {  // two iterations a trip, the score sets swapped
+    step(kt, sa, sb);
+    if (kt + 1 < nkt) step(kt + 1, sb, sa);
   }
   if (qi < S) {
     const float inv = 1.f / l;
