@@ -251,7 +251,7 @@ struct hol_model {
   const uint8_t* lpf_src[NPF] = {};
   int lpf_slot[NPF] = {-1, -1, -1, -1};  // slot of the copy in flight or landed (-1: none)
   int lpf_next[NPF] = {-1, -1, -1, -1};  // this call: the layer's slot, once its backward is queued
-  int n_tail_expect = 0;         // this call: optimiser pieces of the last layer
+  int n_tail_expect = 0;         // this call: N_TAIL pieces of a last layer copied that way, else 0
   hipEvent_t ev_lpf_done[NPF] = {};  // the layer's backward done with its slot
   uint64_t head_pf_ver = 0;
   const uint8_t* head_pf_src = nullptr;
@@ -263,8 +263,9 @@ struct hol_model {
   std::mutex fmu;
   std::condition_variable fcv;
   std::vector<int> unit_queue;         // units whose gradient copy has been enqueued, in order
-  // the last layer of a fused call copies its gradient in N_TAIL pieces, each handed to the
-  // worker on its own (queue code TAIL_CODE + piece), so its Adam overlaps the rest of the copy
+  // a layer that is not copied in pieces (below: MoE, adapters, fp32) copies its gradient whole,
+  // except the last one of a fused call, in N_TAIL pieces each handed to the worker on its own
+  // (queue code TAIL_CODE + piece), so its Adam overlaps the rest of the copy
   static constexpr int N_TAIL = 4, TAIL_CODE = 1 << 20;
   hipEvent_t ev_tail[N_TAIL] = {};
   int tail_unit = -1;
