@@ -161,7 +161,9 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
     gate/up forward with its SwiGLU epilogue (hol_op_gemm_swiglu); the weight gradients with the
     split-tail workspace (hol_op_gemm_ws), the o and q/k/v ones reading both operands K-major as
     the step does (the others over transposed copies, NT). In the order listed, `reps` launches
-    each after one warm-up launch."""
+    each after one warm-up launch; before the first shape, half a second of its launches brings
+    the device clocks to their loaded steady state (timed from an idle device, the first shape
+    read 15-20 % slow)."""
     s = w.shape
     T, H, d = w.tokens, s.hidden, s.head_dim
     nqd, QKV, F = s.n_q_heads * d, (s.n_q_heads + 2 * s.n_kv_heads) * d, s.ffn
@@ -205,6 +207,12 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
                                              ws.data_ptr() if dw else None, wsn if dw else 0, stream.cuda_stream))
 
         launch()
+        if not rows:
+            t_end = time.perf_counter() + 0.5
+            while time.perf_counter() < t_end:
+                for _ in range(5):
+                    launch()
+                torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
         for i in range(reps):
             ev[2 * i].record(stream)

@@ -159,6 +159,30 @@ def test_gemm_persistent_many_tiles_tn(K, epi, out_bf16):
     assert np.max(err) < tol, np.unravel_index(np.argmax(err), err.shape)
 
 
+@pytest.mark.parametrize("a_km", [0, 1])
+def test_gemm_residual_in_place_bitwise(a_km):
+    """C = R + A.B with R the output itself (the residual stream updated in place, as the layer
+    does): bit for bit the out-of-place result, over 18 x 17 tiles with ragged edges."""
+    M, N, K = 4392, 4304, 128
+    r = np.random.default_rng(21 + a_km)
+    a = dev(r.standard_normal((K, M) if a_km else (M, K)), torch.bfloat16)
+    b = dev(r.standard_normal((K, N) if a_km else (N, K)), torch.bfloat16)
+    res = dev(r.standard_normal((M, N)))
+    lda, ldb = (M, N) if a_km else (K, K)
+    out = torch.zeros((M, N), device=DEV)
+    hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), lda, a_km, b.data_ptr(), ldb, a_km, out.data_ptr(), N,
+                                  res.data_ptr(), N, hol.BF16, hol.F32, 2, 1.0, None))
+    inplace = res.clone()
+    hol.check(hol.lib.hol_op_gemm(M, N, K, a.data_ptr(), lda, a_km, b.data_ptr(), ldb, a_km, inplace.data_ptr(), N,
+                                  inplace.data_ptr(), N, hol.BF16, hol.F32, 2, 1.0, None))
+    sync()
+    assert torch.equal(out, inplace)
+    rows = np.arange(0, M, 61)
+    am, bm = host(a), host(b)
+    ref = (am.T[rows] if a_km else am[rows]) @ (bm if a_km else bm.T) + host(res)[rows]
+    assert np.max(np.abs(host(out)[rows] - ref) / (np.abs(ref) + 8)) < 1e-5
+
+
 def test_gemm_tn_equals_nt_on_transposed_operands_bitwise():
     """dW = dY^T X read as stored (TN) and from transposed copies (NT): the same fragments reach
     the same MFMAs in the same order, with and without the split-tail workspace."""
