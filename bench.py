@@ -183,14 +183,18 @@ def gemm_shapes_alone(torch, hol, w: W.Workload, reps: int):
     rows = []
     for name, M, N, K, epi, bf in shapes:
         km = name in ("a7 o dW", "a4 qkv dW")  # both operands K-major ([K][M], [K][N])
-        a = torch.randn((K, M) if km else (M, K), device="cuda").to(torch.bfloat16)
-        b = torch.randn((K, N) if km else (N, K), device="cuda").to(torch.bfloat16)
-        lda, ldb = (M, N) if km else (K, K)
+        dw = name.endswith("dW")
+        # (the step's NT weight gradients read transposed copies whose rows are padded: K rounded
+        # up to 8, plus 64)
+        lda = ldb = (K + 7) // 8 * 8 + 64 if dw else K
+        if km:
+            lda, ldb = M, N
+        a = torch.randn((K, M) if km else (M, lda), device="cuda").to(torch.bfloat16)
+        b = torch.randn((K, N) if km else (N, ldb), device="cuda").to(torch.bfloat16)
         rope = name == "a4 qkv fwd" and d == 128
         c = torch.empty((M, N), device="cuda", dtype=torch.bfloat16 if (bf or rope) else torch.float32)
         r = torch.randn((M, N), device="cuda") if epi == 2 else None
         act = torch.empty((M, N // 2), device="cuda", dtype=torch.bfloat16) if name.startswith("a9 gate/up fwd") else None
-        dw = name.endswith("dW")
 
         def launch():
             if act is not None:
