@@ -226,15 +226,26 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const float* __restrict__ d
 }
 
 // out[j] += sum_b partial[b][j]: a block of 16 waves owns 64 columns (one per lane); wave w sums
-// rows w, w + 16, ..., then the 16 wave sums are added in a fixed order.
+// rows w, w + 16, ..., then the 16 wave sums are added in a fixed order. The loads of 8 rows go
+// out before their adds (same order of additions, same bits): with one load in flight per wave
+// the 16 MB of partial sums at the LLaMA-8B shape (1024 x 4096) took ≈17 µs, with 8 ≈5.5 µs.
 __global__ __launch_bounds__(1024) void reduce_cols_add_k(const float* __restrict__ partial, int nb, int H,
                                                           float* __restrict__ out) {
   __shared__ float red[16][64];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = blockIdx.x * 64 + lane;
   float s = 0.f;
-  if (j < H)
-    for (int b = w; b < nb; b += 16) s += partial[(int64_t)b * H + j];
+  if (j < H) {
+    int b = w;
+    for (; b + 16 * 7 < nb; b += 16 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(b + 16 * u) * H + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < nb; b += 16) s += partial[(int64_t)b * H + j];
+  }
   red[w][lane] = s;
   __syncthreads();
   if (w == 0 && j < H) {
